@@ -1,0 +1,240 @@
+"""fp64 CPU oracle for the Mamba-2 SSD mixer core (conv, scan, decode step).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  It
+shares no code with the HIP library (``selective_state_space_14_amd``) and
+does not import it.
+
+The arithmetic lives in ``ssd_oracle.c`` (plain C, fp64, one token at a time);
+this module only marshals numpy arrays into it.  ``closed_forms`` holds the
+independent numpy forms the oracle is pinned against.
+
+``Oracle(path)`` binds one compiled copy of the C source; the module-level
+functions use the default build next to this file.  (The pin tests also bind
+deliberately mutated copies to show that the pins catch planted mistakes.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ssd_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle C source with gcc (-O2, OpenMP over (batch, head))."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                           "-Wall", "-Wno-unknown-pragmas", src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ssd_oracle.c next to itself (only when stale, unless force)."""
+    if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
+        compile_source(SOURCE, LIB_PATH)
+    return LIB_PATH
+
+
+def _in(a, shape=None):
+    """Contiguous fp64 copy (or None) and its pointer."""
+    if a is None:
+        return None, None
+    if hasattr(a, "detach"):            # torch tensor
+        a = a.detach().cpu().double().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"oracle: expected shape {tuple(shape)}, got {a.shape}")
+    return a, a.ctypes.data_as(_dp)
+
+
+def _ids(a, shape):
+    if a is None:
+        return None, None
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if a.shape != tuple(shape):
+        raise ValueError(f"oracle: doc_ids shape {a.shape} != {tuple(shape)}")
+    return a, a.ctypes.data_as(_ip)
+
+
+def _shape(a):
+    return tuple(a.shape)
+
+
+def _out(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+class Oracle:
+    """One compiled copy of ssd_oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i, d = ctypes.c_int, ctypes.c_double
+        lib.oracle_round_bf16.restype = d
+        lib.oracle_round_bf16.argtypes = [d]
+        lib.oracle_softplus.restype = d
+        lib.oracle_softplus.argtypes = [d]
+        lib.oracle_silu.restype = d
+        lib.oracle_silu.argtypes = [d]
+        lib.oracle_conv.restype = i
+        lib.oracle_conv.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _dp, i, i, _dp, _dp]
+        lib.oracle_scan.restype = i
+        lib.oracle_scan.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, i, _dp, _dp, _dp, _dp, _ip,
+                                    _dp, _dp, _dp]
+        lib.oracle_step.restype = i
+        lib.oracle_step.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                    i, i, _dp]
+        self._lib = lib
+        self.path = path
+
+    def round_bf16(self, v: float) -> float:
+        return self._lib.oracle_round_bf16(float(v))
+
+    def softplus(self, v: float) -> float:
+        return self._lib.oracle_softplus(float(v))
+
+    def silu(self, v: float) -> float:
+        return self._lib.oracle_silu(float(v))
+
+    def conv(self, raw, w, bias=None, dt_raw=None, dt_bias=None, doc_ids=None, state_in=None,
+             act: int = 0, round_bf16: bool = False, want_state: bool = False):
+        """Causal depthwise conv (+SiLU) over raw [B, L, C]; dt = softplus(dt_raw + dt_bias).
+
+        Returns (out [B,L,C], dt_out [B,L,H] or None, state_out [B,K-1,C] or None)."""
+        raw_c, raw_p = _in(raw)
+        Bsz, L, C = raw_c.shape
+        w_c, w_p = _in(w)
+        K = w_c.shape[1]
+        if w_c.shape != (C, K):
+            raise ValueError("oracle.conv: w must be [conv_dim, K]")
+        b_c, b_p = _in(bias, (C,))
+        dr_c, dr_p = _in(dt_raw)
+        H = 0 if dr_c is None else dr_c.shape[2]
+        if dr_c is not None and dr_c.shape != (Bsz, L, H):
+            raise ValueError("oracle.conv: dt_raw must be [B, L, H]")
+        db_c, db_p = _in(dt_bias, (H,) if dt_bias is not None else None)
+        d_c, d_p = _ids(doc_ids, (Bsz, L))
+        si_c, si_p = _in(state_in, (Bsz, K - 1, C))
+        out = np.empty((Bsz, L, C), np.float64)
+        dt_out = np.empty((Bsz, L, H), np.float64) if dr_c is not None else None
+        st_out = np.empty((Bsz, K - 1, C), np.float64) if want_state else None
+        rc = self._lib.oracle_conv(Bsz, L, C, K, H, raw_p, w_p, b_p, dr_p, db_p, d_p, si_p, _out(st_out),
+                                   int(act), int(bool(round_bf16)), _out(out), _out(dt_out))
+        if rc != 0:
+            raise ValueError("oracle_conv rejected its arguments")
+        return out, dt_out, st_out
+
+    def scan(self, x, Bm, Cm, dt, A, D=None, z=None, doc_ids=None, init_state=None, *, H, P, N, G,
+             dt_softplus: bool = False, dt_bias=None, want_state: bool = False):
+        """Sequential fp64 SSD recurrence.  x [B,L,H*P], Bm/Cm [B,L,G*N], dt [B,L,H].
+
+        Returns (y [B,L,H*P], final_state [B,H,P,N] or None)."""
+        x_c, x_p = _in(x)
+        Bsz, L = x_c.shape[0], x_c.shape[1]
+        if x_c.shape != (Bsz, L, H * P):
+            raise ValueError("oracle.scan: x must be [B, L, H*P]")
+        b_c, b_p = _in(Bm, (Bsz, L, G * N))
+        c_c, c_p = _in(Cm, (Bsz, L, G * N))
+        dt_c, dt_p = _in(dt, (Bsz, L, H))
+        db_c, db_p = _in(dt_bias, (H,) if dt_bias is not None else None)
+        a_c, a_p = _in(A, (H,))
+        dd_c, dd_p = _in(D, (H,) if D is not None else None)
+        z_c, z_p = _in(z, (Bsz, L, H * P) if z is not None else None)
+        d_c, d_p = _ids(doc_ids, (Bsz, L))
+        h0_c, h0_p = _in(init_state, (Bsz, H, P, N) if init_state is not None else None)
+        y = np.empty((Bsz, L, H * P), np.float64)
+        fs = np.empty((Bsz, H, P, N), np.float64) if want_state else None
+        rc = self._lib.oracle_scan(Bsz, L, H, P, N, G, x_p, b_p, c_p, dt_p, int(bool(dt_softplus)), db_p,
+                                   a_p, dd_p, z_p, d_p, h0_p, _out(fs), _out(y))
+        if rc != 0:
+            raise ValueError("oracle_scan rejected its arguments")
+        return y, fs
+
+    def step(self, raw, dt_raw, z, w, bias, dt_bias, A, D, conv_state, ssm_state, *, H, P, N, G,
+             act: int = 0, round_bf16: bool = False):
+        """One decode token.  conv_state [B,K-1,C] and ssm_state [B,H,P,N] (C-contiguous
+        float64 ndarrays) are updated in place.  Returns y [B, H*P]."""
+        r_c, r_p = _in(raw)
+        Bsz, C = r_c.shape
+        w_c, w_p = _in(w, None)
+        K = w_c.shape[1]
+        for name, arr in (("conv_state", conv_state), ("ssm_state", ssm_state)):
+            if not (isinstance(arr, np.ndarray) and arr.dtype == np.float64 and arr.flags.c_contiguous):
+                raise TypeError(f"oracle.step: {name} must be a C-contiguous float64 ndarray")
+        if conv_state.shape != (Bsz, K - 1, C) or ssm_state.shape != (Bsz, H, P, N) or w_c.shape != (C, K):
+            raise ValueError("oracle.step: shape mismatch")
+        dr_c, dr_p = _in(dt_raw, (Bsz, H))
+        z_c, z_p = _in(z, (Bsz, H * P) if z is not None else None)
+        b_c, b_p = _in(bias, (C,) if bias is not None else None)
+        db_c, db_p = _in(dt_bias, (H,) if dt_bias is not None else None)
+        a_c, a_p = _in(A, (H,))
+        dd_c, dd_p = _in(D, (H,) if D is not None else None)
+        y = np.empty((Bsz, H * P), np.float64)
+        rc = self._lib.oracle_step(Bsz, H, P, N, G, K, r_p, dr_p, z_p, w_p, b_p, db_p, a_p, dd_p,
+                                   _out(conv_state), _out(ssm_state), int(act), int(bool(round_bf16)),
+                                   _out(y))
+        if rc != 0:
+            raise ValueError("oracle_step rejected its arguments")
+        return y
+
+    def forward(self, raw, w, bias, dt_raw, dt_bias, A, D, z, *, H, P, N, G, doc_ids=None,
+                conv_state_in=None, init_state=None, act: int = 0, round_bf16: bool = False):
+        """Conv prologue then scan (the mixer core end to end).
+
+        Returns (y, final_state, conv_state_out, xbc, dt)."""
+        xbc, dt, cst = self.conv(raw, w, bias, dt_raw, dt_bias, doc_ids, conv_state_in, act=act,
+                                 round_bf16=round_bf16, want_state=True)
+        HP, GN = H * P, G * N
+        y, fs = self.scan(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, A, D, z, doc_ids,
+                          init_state, H=H, P=P, N=N, G=G, want_state=True)
+        return y, fs, cst, xbc, dt
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle(build())
+    return _default
+
+
+def round_bf16(v):
+    return default().round_bf16(v)
+
+
+def softplus(v):
+    return default().softplus(v)
+
+
+def silu(v):
+    return default().silu(v)
+
+
+def conv(*a, **k):
+    return default().conv(*a, **k)
+
+
+def scan(*a, **k):
+    return default().scan(*a, **k)
+
+
+def step(*a, **k):
+    return default().step(*a, **k)
+
+
+def forward(*a, **k):
+    return default().forward(*a, **k)

@@ -1,0 +1,278 @@
+/*
+ * ssd_oracle.c -- plain fp64 CPU oracle for the Mamba-2 SSD mixer core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the product path never
+ * calls it.
+ *
+ * What it computes, and where that is written down:
+ *
+ *  - The selective state-space recurrence of Mamba-2 (state-space duality),
+ *    taken token by token, per (batch row, head), with no chunking:
+ *        a_t  = exp(dt_t * A_h)
+ *        h_t  = a_t * h_{t-1} + dt_t * B_t x_t^T        (h is N x P)
+ *        y_t  = C_t^T h_t + D_h * x_t                   (h_t after token t)
+ *    This is the SSD layer that the Codestral-Mamba weight-port header
+ *    (builderforce-memory-engine diff, codestral_mamba.ts, tensor layout and
+ *    "reconciliations" 2-3) and the Mini-K3-1H model card ("Architecture",
+ *    "Checkpoint and training") both refer to.  The chunked GPU scan reaches
+ *    the same result up to floating-point association, so the oracle is the
+ *    definition itself.
+ *  - A = -exp(A_log): codestral_mamba.ts header, reconciliation 2.  The
+ *    oracle takes A itself (A <= 0), as the library does.
+ *  - dt = softplus(dt_raw + dt_bias): falcon_mamba.ts header (the dt bias is
+ *    added inside the softplus), and the inverse-softplus reparameterisation
+ *    of dt_bias in the Mamba-1/2 -> Mamba-3 transplant article ("The
+ *    Methodology", item 3).
+ *  - Causal depthwise conv over the [x | B | C] columns, conv_dim =
+ *    d_inner + 2*n_groups*d_state, weight [conv_dim, 1, d_conv]:
+ *    codestral_mamba.ts tensor layout.  Reading of the tap order: plain
+ *    causal cross-correlation, w[c][K-1] multiplies the current token.
+ *  - Activation after the conv: SiLU (the published Mamba-2 block's
+ *    convention, which the port pages defer to); act = 1 turns it off.
+ *  - Gate y * silu(z): codestral_mamba.ts reconciliation 3 (upstream computes
+ *    norm(y * silu(z)); the RMSNorm itself is outside this core).
+ *  - Document isolation: the same document ids drive the conv and the scan;
+ *    conv history and recurrent state reset at every boundary (Mini-K3-1H
+ *    card, "Checkpoint and training").  Reading: a boundary sits at t > 0
+ *    exactly where doc[t] != doc[t-1]; t = 0 always continues the carried
+ *    state.
+ *  - Caller-owned state read at entry and written at exit; a step is the
+ *    same computation as a forward of length 1 with the state carried
+ *    (mojolearn.Mamba3Block docs, forward() and step()).
+ *
+ * Layouts (all arrays fp64, contiguous):
+ *   raw / conv out  [B][L][conv_dim]   columns [x (H*P, head-major) | B (G*N,
+ *                                       group-major) | C (G*N)]
+ *   x, z, y         [B][L][H*P]
+ *   Bm, Cm          [B][L][G*N]
+ *   dt              [B][L][H]
+ *   ssm state       [B][H][P][N]       (entry (p,n) is h[n][p] of the math)
+ *   conv state      [B][K-1][conv_dim] (raw rows, oldest first)
+ *   head h uses group h / (H/G).
+ *
+ * Every routine below is a straight loop in the notation above.  The
+ * per-token helpers conv_channel() and ssm_token() are shared by the prefill
+ * routines and the step so that a prefill followed by steps runs the very
+ * same fp64 operations as one longer prefill.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MAXK 8
+
+/* softplus(v) = log(1 + e^v), written so that it does not overflow. */
+static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
+
+/* silu(v) = v * sigmoid(v). */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* Round to the nearest bfloat16 value (8 significant bits), ties to even.
+ * Used only where the contract stores a tensor in bf16 (the conv output of a
+ * bf16 pipeline).  rint() rounds ties to even under the default mode. */
+double oracle_round_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e = ilogb(v);                 /* v = m * 2^e, 1 <= |m| < 2 */
+    if (e < -126) e = -126;           /* bf16 subnormal spacing */
+    double q = ldexp(1.0, e - 7);     /* spacing of bf16 values near v */
+    double r = rint(v / q) * q;
+    if (fabs(r) > 3.3895313892515355e38) r = copysign(INFINITY, v);
+    return r;
+}
+
+double oracle_softplus(double v) { return softplus(v); }
+double oracle_silu(double v) { return silu(v); }
+
+/* One conv output channel at one token: bias + sum_k w[k] * win[k], where
+ * win[K-1] is the current token and win[0] the oldest tap. */
+static double conv_channel(const double *w, double bias, const double *win, int K, int act) {
+    double v = bias;
+    for (int k = 0; k < K; ++k) v += w[k] * win[k];
+    return act == 0 ? silu(v) : v;
+}
+
+/* One head at one token: update S (P x N, stored [p][n]) and write y[p]. */
+static void ssm_token(int P, int N, double dt, double A, double Dh,
+                      const double *x, const double *Bv, const double *Cv,
+                      double *S, double *y) {
+    double a = exp(dt * A);
+    for (int p = 0; p < P; ++p)
+        for (int n = 0; n < N; ++n)
+            S[(size_t)p * N + n] = a * S[(size_t)p * N + n] + dt * x[p] * Bv[n];
+    for (int p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int n = 0; n < N; ++n) acc += Cv[n] * S[(size_t)p * N + n];
+        y[p] = acc + Dh * x[p];
+    }
+}
+
+/* Last position r in [0, t] at which a new document starts (0 if none). */
+static int seg_start(const int32_t *doc_row, int t) {
+    if (!doc_row) return 0;
+    for (int r = t; r > 0; --r)
+        if (doc_row[r] != doc_row[r - 1]) return r;
+    return 0;
+}
+
+/* Raw conv input seen by token t at tap position tau (tau <= t): the raw row
+ * if tau lies in t's document, else the carried conv state (only while t is
+ * still in the first document of the call), else zero. */
+static double conv_src(const double *raw_b, const double *state_b, int C, int K,
+                       int seg, int tau, int c) {
+    if (tau >= 0) return tau >= seg ? raw_b[(size_t)tau * C + c] : 0.0;
+    if (seg == 0 && state_b) return state_b[(size_t)(K - 1 + tau) * C + c];
+    return 0.0;
+}
+
+/*
+ * Causal depthwise conv (+ SiLU) over [B, L, C] and dt = softplus(dt_raw +
+ * dt_bias) over [B, L, H].  round_bf16 != 0 rounds every conv output to
+ * bf16, as a bf16 pipeline stores it.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_conv(int B, int L, int C, int K, int H,
+                const double *raw, const double *w, const double *bias,
+                const double *dt_raw, const double *dt_bias,
+                const int32_t *doc, const double *state_in, double *state_out,
+                int act, int round_bf16, double *out, double *dt_out) {
+    if (B < 0 || L < 0 || C <= 0 || K < 1 || K > ORACLE_MAXK || !raw || !w || !out) return -1;
+    for (int b = 0; b < B; ++b) {
+        const double *raw_b = raw + (size_t)b * L * C;
+        const double *st_b = state_in ? state_in + (size_t)b * (K - 1) * C : NULL;
+        const int32_t *doc_b = doc ? doc + (size_t)b * L : NULL;
+        double win[ORACLE_MAXK];
+        for (int t = 0; t < L; ++t) {
+            int seg = seg_start(doc_b, t);
+            for (int c = 0; c < C; ++c) {
+                for (int k = 0; k < K; ++k)
+                    win[k] = conv_src(raw_b, st_b, C, K, seg, t - (K - 1) + k, c);
+                double v = conv_channel(w + (size_t)c * K, bias ? bias[c] : 0.0, win, K, act);
+                out[((size_t)b * L + t) * C + c] = round_bf16 ? oracle_round_bf16(v) : v;
+            }
+            if (dt_raw && dt_out)
+                for (int h = 0; h < H; ++h) {
+                    size_t i = ((size_t)b * L + t) * H + h;
+                    dt_out[i] = softplus(dt_raw[i] + (dt_bias ? dt_bias[h] : 0.0));
+                }
+        }
+    }
+    /* Conv state after the call: the K-1 taps the next token would read,
+     * judged from the last token's document (so all reads of state_in above
+     * are complete before it may be overwritten in place). */
+    if (state_out) {
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)(K > 1 ? K - 1 : 1) * C);
+        if (!tmp) return -1;
+        for (int b = 0; b < B; ++b) {
+            const double *raw_b = raw + (size_t)b * L * C;
+            const double *st_b = state_in ? state_in + (size_t)b * (K - 1) * C : NULL;
+            const int32_t *doc_b = doc ? doc + (size_t)b * L : NULL;
+            int seg = L > 0 ? seg_start(doc_b, L - 1) : 0;
+            for (int j = 0; j < K - 1; ++j)
+                for (int c = 0; c < C; ++c)
+                    tmp[(size_t)j * C + c] = conv_src(raw_b, st_b, C, K, seg, L - (K - 1) + j, c);
+            memcpy(state_out + (size_t)b * (K - 1) * C, tmp, sizeof(double) * (size_t)(K - 1) * C);
+        }
+        free(tmp);
+    }
+    return 0;
+}
+
+/*
+ * Sequential SSD recurrence over [B, L] for all heads.  dt_softplus != 0
+ * means dt holds raw values and dt := softplus(dt + dt_bias) is applied
+ * first.  D, z, doc, init_state, final_state may be NULL.
+ */
+int oracle_scan(int B, int L, int H, int P, int N, int G,
+                const double *x, const double *Bm, const double *Cm,
+                const double *dt, int dt_softplus, const double *dt_bias,
+                const double *A, const double *D, const double *z,
+                const int32_t *doc, const double *init_state, double *final_state,
+                double *y) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    if ((L > 0 && (!x || !Bm || !Cm || !dt || !y)) || !A) return -1;
+    const int HP = H * P, GN = G * N, hpg = H / G;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int g = h / hpg;
+            double *S = (double *)calloc((size_t)P * N, sizeof(double));
+            double *yp = (double *)malloc(sizeof(double) * (size_t)P);
+            if (!S || !yp) { bad = 1; free(S); free(yp); continue; }
+            if (init_state)
+                memcpy(S, init_state + ((size_t)b * H + h) * P * N, sizeof(double) * (size_t)P * N);
+            for (int t = 0; t < L; ++t) {
+                size_t row = (size_t)b * L + t;
+                if (doc && t > 0 && doc[row] != doc[row - 1])
+                    memset(S, 0, sizeof(double) * (size_t)P * N);
+                double d = dt[row * H + h];
+                if (dt_softplus) d = softplus(d + (dt_bias ? dt_bias[h] : 0.0));
+                ssm_token(P, N, d, A[h], D ? D[h] : 0.0,
+                          x + row * HP + (size_t)h * P, Bm + row * GN + (size_t)g * N,
+                          Cm + row * GN + (size_t)g * N, S, yp);
+                for (int p = 0; p < P; ++p) {
+                    double v = yp[p];
+                    if (z) v *= silu(z[row * HP + (size_t)h * P + p]);
+                    y[row * HP + (size_t)h * P + p] = v;
+                }
+            }
+            if (final_state)
+                memcpy(final_state + ((size_t)b * H + h) * P * N, S, sizeof(double) * (size_t)P * N);
+            free(S);
+            free(yp);
+        }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One decode token per sequence.  The conv window is the K-1 carried raw
+ * rows followed by the new raw row; the buffer then shifts by one.  The conv
+ * output is rounded to bf16 when round_bf16 != 0 (as a bf16 prefill stores
+ * it), then the state update is exactly one token of oracle_scan.
+ *   raw [B][C], dt_raw [B][H], z [B][H*P] or NULL, y [B][H*P]
+ *   conv_state [B][K-1][C] and ssm_state [B][H][P][N] are read and updated.
+ */
+int oracle_step(int B, int H, int P, int N, int G, int K,
+                const double *raw, const double *dt_raw, const double *z,
+                const double *w, const double *bias, const double *dt_bias,
+                const double *A, const double *D,
+                double *conv_state, double *ssm_state, int act, int round_bf16,
+                double *y) {
+    if (B < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || K < 1 || K > ORACLE_MAXK) return -1;
+    const int HP = H * P, GN = G * N, C = HP + 2 * GN, hpg = H / G;
+    double *xbc = (double *)malloc(sizeof(double) * (size_t)C);
+    double *yp = (double *)malloc(sizeof(double) * (size_t)P);
+    if (!xbc || !yp) { free(xbc); free(yp); return -1; }
+    double win[ORACLE_MAXK];
+    for (int b = 0; b < B; ++b) {
+        double *cs = conv_state + (size_t)b * (K - 1) * C;
+        const double *rb = raw + (size_t)b * C;
+        for (int c = 0; c < C; ++c) {
+            for (int k = 0; k < K - 1; ++k) win[k] = cs[(size_t)k * C + c];
+            win[K - 1] = rb[c];
+            double v = conv_channel(w + (size_t)c * K, bias ? bias[c] : 0.0, win, K, act);
+            xbc[c] = round_bf16 ? oracle_round_bf16(v) : v;
+        }
+        for (int k = 0; k + 1 < K - 1; ++k)
+            memcpy(cs + (size_t)k * C, cs + (size_t)(k + 1) * C, sizeof(double) * (size_t)C);
+        if (K > 1) memcpy(cs + (size_t)(K - 2) * C, rb, sizeof(double) * (size_t)C);
+        for (int h = 0; h < H; ++h) {
+            const int g = h / hpg;
+            double d = softplus(dt_raw[(size_t)b * H + h] + (dt_bias ? dt_bias[h] : 0.0));
+            double *S = ssm_state + ((size_t)b * H + h) * P * N;
+            ssm_token(P, N, d, A[h], D ? D[h] : 0.0, xbc + (size_t)h * P,
+                      xbc + HP + (size_t)g * N, xbc + HP + GN + (size_t)g * N, S, yp);
+            for (int p = 0; p < P; ++p) {
+                double v = yp[p];
+                if (z) v *= silu(z[(size_t)b * HP + (size_t)h * P + p]);
+                y[(size_t)b * HP + (size_t)h * P + p] = v;
+            }
+        }
+    }
+    free(xbc);
+    free(yp);
+    return 0;
+}

@@ -1,0 +1,82 @@
+"""The fp64 oracle against its pins (CPU only), and proof that the pins bite:
+mutated copies of the oracle source, each carrying one plausible mistake, must
+fail at least one pin."""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(o, pin):
+    pin(o)
+
+
+_UPDATE = """    for (int p = 0; p < P; ++p)
+        for (int n = 0; n < N; ++n)
+            S[(size_t)p * N + n] = a * S[(size_t)p * N + n] + dt * x[p] * Bv[n];
+"""
+_READ = """    for (int p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int n = 0; n < N; ++n) acc += Cv[n] * S[(size_t)p * N + n];
+        y[p] = acc + Dh * x[p];
+    }
+"""
+
+# One plausible mistake per entry: (name, text in ssd_oracle.c, replacement).
+MUTATIONS = [
+    ("dropped_decay", "S[(size_t)p * N + n] = a * S[(size_t)p * N + n]", "S[(size_t)p * N + n] = S[(size_t)p * N + n]"),
+    ("dropped_dt_on_input", "+ dt * x[p] * Bv[n]", "+ x[p] * Bv[n]"),
+    ("decay_sign", "double a = exp(dt * A);", "double a = exp(-dt * A);"),
+    ("read_with_B", "acc += Cv[n] * S", "acc += Bv[n] * S"),
+    ("output_before_update", _UPDATE + _READ, _READ + _UPDATE),
+    ("dropped_skip", "y[p] = acc + Dh * x[p];", "y[p] = acc;"),
+    ("taps_reversed", "v += w[k] * win[k];", "v += w[K - 1 - k] * win[k];"),
+    ("conv_offset", "t - (K - 1) + k, c);", "t - K + k, c);"),
+    ("no_doc_reset_scan", "if (doc && t > 0 && doc[row] != doc[row - 1])", "if (0)"),
+    ("no_doc_reset_conv", "return tau >= seg ? raw_b[(size_t)tau * C + c] : 0.0;", "return raw_b[(size_t)tau * C + c];"),
+    ("wrong_group", "const int g = h / hpg;\n            double *S", "const int g = h % G;\n            double *S"),
+    ("softplus_no_bias", "d = softplus(d + (dt_bias ? dt_bias[h] : 0.0));", "d = softplus(d);"),
+    ("gate_sigmoid_only", "if (z) v *= silu(z[row * HP", "if (z) v *= 1.0 / (1.0 + exp(-z[row * HP"),
+    ("state_transposed", "S[(size_t)p * N + n] = a * S[(size_t)p * N + n] + dt * x[p] * Bv[n];",
+     "S[(size_t)n * P + p] = a * S[(size_t)n * P + p] + dt * x[p] * Bv[n];"),
+    ("conv_state_shift", "memcpy(cs + (size_t)k * C, cs + (size_t)(k + 1) * C", "memcpy(cs + (size_t)(k + 1) * C, cs + (size_t)k * C"),
+    ("step_no_round", "xbc[c] = round_bf16 ? oracle_round_bf16(v) : v;", "xbc[c] = v;"),
+    ("round_truncates", "double r = rint(v / q) * q;", "double r = trunc(v / q) * q;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistakes(name, old, new):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation {name}: pattern not found in the oracle source"
+    if name == "gate_sigmoid_only":
+        new_src = src.replace(old, new).replace("+ (size_t)h * P + p]);\n                    y[row",
+                                                "+ (size_t)h * P + p]));\n                    y[row", 1)
+    else:
+        new_src = src.replace(old, new, 1)
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        path = os.path.join(d, "m.c")
+        with open(path, "w") as f:
+            f.write(new_src)
+        mutant = oracle.Oracle(oracle.compile_source(path, os.path.join(d, "libm.so")))
+        failed = []
+        for pin in pins.ALL_PINS:
+            try:
+                pin(mutant)
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(pin.__name__)
+        assert failed, f"no pin caught the planted mistake '{name}'"
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
