@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD mixer core on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+ssd_conv_fwd (causal conv + SiLU + dt softplus) then ssd_chunk_scan_fwd
+(chunked scan, groups, D skip, z gate, final state), at the Mini-K3 mixer
+shape B=5, L=8192, H=32, P=64, N=64, G=8, bf16 inputs, fp32 state and y.
+Inputs are resident in HBM before the timed region; two input sets alternate
+so no step runs out of the 256 MB last-level cache.
+
+Prints ONE JSON line: value = head-tokens (B*L*H) per second over the whole
+step; "roofline" = the scan kernel's algorithmic bytes / its average duration
+(HIP events around each launch on the launch stream) against 8 TB/s;
+"cpu_baseline" = the fp64 oracle (conv + scan) timed on this host.  The other
+workloads (packed documents, the large layer, the decode step) are reported
+under "extra".
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD scan tokens/sec (B×L×H/s) and % HBM roofline at 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+
+
+def scan_bytes(wl, docs=False, h0=False):
+    """Algorithmic bytes of one ssd_chunk_scan_fwd: every input read once, every output written once."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok = wl.B * wl.L
+    b = tok * wl.H * wl.P * es            # x
+    b += 2 * tok * wl.G * wl.N * es       # B, C
+    b += tok * wl.H * 4                   # dt (fp32)
+    b += tok * wl.H * wl.P * es if wl.gate else 0   # z
+    b += tok * wl.H * wl.P * 4            # y (fp32)
+    st = wl.B * wl.H * wl.P * wl.N * 4
+    b += st                               # final state
+    b += st if h0 else 0                  # initial state
+    b += tok * 4 if docs else 0           # doc ids
+    return b
+
+
+def conv_bytes(wl, docs=False):
+    """Algorithmic bytes of one ssd_conv_fwd: raw in, conv out, dt_raw in, dt out (fp32)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok = wl.B * wl.L
+    b = 2 * tok * wl.conv_dim * es + tok * wl.H * es + tok * wl.H * 4
+    b += tok * 4 if docs else 0
+    return b
+
+
+def step_bytes(wl):
+    """Algorithmic bytes of one ssd_step: state and conv buffer read + written, row inputs, y."""
+    es = 2 if wl.dtype == "bf16" else 4
+    b = 2 * wl.B * wl.H * wl.P * wl.N * 4
+    b += 2 * wl.B * 3 * wl.conv_dim * es
+    b += wl.B * wl.conv_dim * es + wl.B * wl.H * es + (wl.B * wl.H * wl.P * es if wl.gate else 0)
+    b += wl.B * wl.H * wl.P * 4
+    return b
+
+
+class Timer:
+    """Sums HIP-event intervals recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def around(self, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.append((s, e))
+        return out
+
+    def mean_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+
+
+def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0):
+    dev = "cuda"
+    HP, GN = wl.H * wl.P, wl.G * wl.N
+    prm = synth.params(wl, seed, device=dev)
+    sets = []
+    for k in range(2):
+        raw = synth.raw_inputs(wl, seed + k, device=dev)
+        ids = synth.doc_ids(wl, seed + k).to(dev) if docs else None
+        sets.append((raw, ids))
+    xbc = torch.empty(wl.B, wl.L, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
+    dt = torch.empty(wl.B, wl.L, wl.H, dtype=torch.float32, device=dev)
+    y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
+    fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
+    t_conv, t_scan = Timer(torch), Timer(torch)
+
+    def one(i, timed):
+        raw, ids = sets[i % 2]
+        conv = lambda: ssd.ssd_conv_fwd(raw["xbc_raw"], prm["conv_w"], H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                        dt_raw=raw["dt_raw"], dt_bias=prm["dt_bias"], doc_ids=ids,
+                                        xbc_out=xbc, dt_out=dt)
+        scan = lambda: ssd.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, prm["A"],
+                                              H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=prm["D"], z=raw["z"],
+                                              doc_ids=ids, init_state=raw["h0"] if h0 else None,
+                                              final_state=fs, y=y)
+        if timed:
+            t_conv.around(conv)
+            t_scan.around(scan)
+        else:
+            conv()
+            scan()
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        one(i, True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sb, cb = scan_bytes(wl, docs, h0), conv_bytes(wl, docs)
+    scan_ms, conv_ms = t_scan.mean_ms(), t_conv.mean_ms()
+    return {
+        "ms_per_step": ms,
+        "value": wl.B * wl.L * wl.H / (ms * 1e-3),
+        "scan_us": scan_ms * 1e3, "conv_us": conv_ms * 1e3,
+        "scan_bytes": sb, "conv_bytes": cb,
+        "scan_GBs": sb / (scan_ms * 1e-3) / 1e9, "conv_GBs": cb / (conv_ms * 1e-3) / 1e9,
+        "scan_head_tokens_per_s": wl.B * wl.L * wl.H / (scan_ms * 1e-3),
+    }
+
+
+def decode_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
+    dev = "cuda"
+    prm = synth.params(wl, seed, device=dev)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    ssm = torch.randn(wl.B, wl.H, wl.P, wl.N, generator=g, device=dev) * 0.1
+    conv = torch.randn(wl.B, 3, wl.conv_dim, generator=g, device=dev).to(wl.torch_dtype)
+    ins = [synth.step_inputs(wl, s, seed, device=dev) for s in range(2)]
+    y = torch.empty(wl.B, wl.H * wl.P, dtype=torch.float32, device=dev)
+    t_step = Timer(torch)
+
+    def one(i, timed):
+        st = ins[i % 2]
+        f = lambda: ssd.ssd_step(st["xbc_raw"], st["dt_raw"], prm["conv_w"], prm["A"], conv, ssm, H=wl.H, P=wl.P,
+                                 N=wl.N, G=wl.G, z=st["z"], dt_bias=prm["dt_bias"], D=prm["D"], y=y)
+        t_step.around(f) if timed else f()
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        one(i, True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kb = step_bytes(wl)
+    k_ms = t_step.mean_ms()
+    return {"ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "step_us": k_ms * 1e3, "step_bytes": kb,
+            "step_GBs": kb / (k_ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(synth, wl, rows):
+    """The fp64 oracle (conv + scan, as it stands) on `rows` batch rows of the workload."""
+    import oracle
+    prm = synth.params(wl, 0)
+    raw = synth.raw_inputs(wl, 0, B=rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.forward(raw["xbc_raw"], prm["conv_w"], None, raw["dt_raw"], prm["dt_bias"], prm["A"], prm["D"], raw["z"],
+                   H=wl.H, P=wl.P, N=wl.N, G=wl.G, round_bf16=True)
+    sec = time.perf_counter() - t0
+    return {"value": rows * wl.L * wl.H / sec, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {wl.B} batch rows of the {wl.name} workload (L={wl.L}, all {wl.H} heads), "
+                      f"conv + scan in fp64, {sec:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=5)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (hardware-counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this build runs on one GPU only (the scan shards by batch row and "
+              "head with no exchange; multi-GPU runs are not part of it)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_state_space_14_amd as ssd
+    import synth
+
+    ssd.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    wl = synth.WORKLOADS["mini_k3_bf16"]
+    main_r = prefill_bench(ssd, synth, torch, wl, args.steps, args.warmup)
+
+    extras = []
+    if not args.no_extras:
+        pk = synth.WORKLOADS["mini_k3_packed"]
+        r = prefill_bench(ssd, synth, torch, pk, args.steps, args.warmup, docs=True)
+        extras.append({"workload": pk.name, **{k: r[k] for k in ("value", "ms_per_step", "scan_us", "conv_us",
+                                                                  "scan_GBs", "conv_GBs")},
+                       "scan_frac": r["scan_GBs"] / HBM_PEAK_GBS, "unit": "head-tokens/s"})
+        ll = synth.WORKLOADS["large_layer_bf16"]
+        r = prefill_bench(ssd, synth, torch, ll, max(5, args.steps // 2), args.warmup, h0=True)
+        extras.append({"workload": ll.name, **{k: r[k] for k in ("value", "ms_per_step", "scan_us", "conv_us",
+                                                                  "scan_GBs", "conv_GBs")},
+                       "scan_frac": r["scan_GBs"] / HBM_PEAK_GBS, "unit": "head-tokens/s"})
+        dw = synth.WORKLOADS["decode_fp32"]
+        r = decode_bench(ssd, synth, torch, dw, max(20, args.steps * 2), args.warmup)
+        extras.append({"workload": dw.name + " (ssd_step)", **r, "step_frac": r["step_GBs"] / HBM_PEAK_GBS,
+                       "unit": "head-tokens/s (B*H per step)"})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, wl, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": main_r["value"],
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "H": wl.H, "P": wl.P, "N": wl.N, "G": wl.G,
+                   "chunk": 64, "conv_k": 4, "gate": True, "step": "ssd_conv_fwd + ssd_chunk_scan_fwd",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "ssd_scan_kernel", "achieved": main_r["scan_GBs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": main_r["scan_GBs"] / HBM_PEAK_GBS,
+                     "traffic": None, "launch_us": main_r["scan_us"], "algorithmic_bytes": main_r["scan_bytes"]},
+        "kernels": {"scan_us": main_r["scan_us"], "conv_us": main_r["conv_us"], "scan_GBs": main_r["scan_GBs"],
+                    "conv_GBs": main_r["conv_GBs"], "conv_frac": main_r["conv_GBs"] / HBM_PEAK_GBS,
+                    "scan_head_tokens_per_s": main_r["scan_head_tokens_per_s"]},
+        "cpu_baseline": cpu,
+        "extra": extras,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

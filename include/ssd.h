@@ -1,0 +1,208 @@
+/*
+ * ssd.h -- C ABI of libssd.so, the gfx950 (MI355X) Mamba-2 SSD mixer core.
+ *
+ * Three operations, each one HIP kernel launch on the caller's stream:
+ *
+ *   ssd_conv_fwd        causal depthwise conv (k = 4) + SiLU over the
+ *                       [x | B | C] columns, and dt = softplus(dt_raw + dt_bias)
+ *   ssd_chunk_scan_fwd  the SSD selective scan in chunks of 64 tokens, with
+ *                       B/C groups, document resets, initial/final state, the
+ *                       D skip and the y * silu(z) gate
+ *   ssd_step            one decode token per sequence: conv from a rolling
+ *                       buffer, state update, output and gate
+ *
+ * The operation (per batch row b and head h, token t, head h in group
+ * g = h / (H/G)):
+ *     a_t = exp(dt_t * A_h)
+ *     h_t = a_t * h_{t-1} + dt_t * B_t x_t^T            (h_t is N x P)
+ *     y_t = (C_t^T h_t + D_h * x_t) * silu(z_t)          (h_t after token t)
+ * is the Mamba-2 SSD layer whose tensors the Codestral-Mamba weight port
+ * lists (builderforce-memory-engine diff, codestral_mamba.ts header: in_proj
+ * rows [z | x | B | C | dt], conv1d weight [conv_dim, 1, d_conv] with
+ * conv_dim = d_inner + 2*n_groups*d_state, per-head A_log, D and dt_bias,
+ * A = -exp(A_log), gate norm(y * silu(z))), in the mixer shape of the
+ * Mini-K3-1H-mamba2-n64-g8 card ("Architecture": 32 heads x 64 channels,
+ * state 64, 8 B/C groups, conv kernel 4).  dt_bias goes inside the softplus
+ * (falcon_mamba.ts header).  Document ids reset both the conv history and
+ * the recurrent state (Mini-K3-1H card, "Checkpoint and training").  State
+ * is caller-owned, read at entry and written at exit, and a step is the
+ * forward at length 1 with the state carried (mojolearn.Mamba3Block docs,
+ * forward() and step()).  Chunk size 64 follows the same mojolearn page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All pointers are DEVICE pointers, allocated and owned by the caller,
+ *   and must stay valid until the work queued on `stream` has finished.
+ *   The library allocates nothing, frees nothing, keeps no pointer and
+ *   never synchronises.  `stream` is a hipStream_t (NULL = default stream).
+ * - Activation tensors are [B][L][row] with rows `*_row_stride` ELEMENTS
+ *   apart (stride >= row width) and batch rows L * stride elements apart.
+ *   The innermost dimension is contiguous.
+ * - dtype (ssd_dtype_t) is the storage type of the activation tensors
+ *   marked "T".  Parameters (conv_w, conv_b, dt_bias, A, D), dt after the
+ *   prologue, y and the SSM state are always fp32.  Other dtypes are
+ *   refused by name, never converted.
+ * - Column layouts: x and z are head-major [h][p] (H*P wide); B and C are
+ *   group-major [g][n] (G*N wide); the conv tensors are [x | B | C]
+ *   (conv_dim = H*P + 2*G*N wide).  The SSM state is [B][H][P][N] with n
+ *   fastest (entry (p, n) holds h[n][p] of the equations).  The conv state
+ *   is [B][K-1][conv_dim]: the last K-1 raw input rows, oldest first.
+ * - Document ids (int32 [B][L], optional): a new document starts at t > 0
+ *   exactly where doc[b][t] != doc[b][t-1].  t = 0 always continues the
+ *   carried state; a caller starting a fresh document passes NULL (zero)
+ *   states for it.
+ * - Supported sizes: P = 64, N in {16, 32, 64, 128}, K = 4, chunk = 64,
+ *   G divides H, B >= 1, L >= 0 (L = 0 is a no-op apart from copying the
+ *   states through), any L (a partial last chunk is handled).
+ * - Alignment: every tensor base must be 16-byte aligned, and row strides
+ *   of T tensors must be multiples of 16 bytes (8 bf16 or 4 fp32 elements).
+ * - Errors: arguments are validated on the host before anything is
+ *   launched and device memory is never touched on failure.  The return
+ *   value is an ssd_status_t; ssd_last_error() gives a message naming the
+ *   argument and its value(s) (thread-local, valid until the next call on
+ *   that thread).  A failed launch returns SSD_ERR_HIP with the HIP error
+ *   string.  Inputs are not scanned for NaN/Inf.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Activation after the depthwise conv: SiLU (the Mamba-2 default) or none. */
+typedef enum { SSD_ACT_SILU = 0, SSD_ACT_NONE = 1 } ssd_act_t;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                  */
+    SSD_ERR_BAD_SHAPE = 2,    /* negative/zero size, H % G != 0, stride < row */
+    SSD_ERR_UNSUPPORTED = 3,  /* P, N, K, chunk or dtype outside the set above */
+    SSD_ERR_ALIGNMENT = 4,    /* base pointer or row stride breaks 16 B loads */
+    SSD_ERR_WORKSPACE = 5,    /* workspace smaller than the size query says  */
+    SSD_ERR_HIP = 6           /* the kernel launch failed                     */
+} ssd_status_t;
+
+/* Message of the last failing call on this thread ("" after a success). */
+const char *ssd_last_error(void);
+/* Name of a status code ("SSD_OK", "SSD_ERR_BAD_SHAPE", ...). */
+const char *ssd_status_string(int status);
+/* SSD_ABI_VERSION of the loaded library. */
+int ssd_version(void);
+
+/*
+ * ssd_conv_fwd -- causal depthwise conv + activation, and the dt prologue.
+ *
+ *   xbc_out[b,t,c] = act(conv_b[c] + sum_{k<K} conv_w[c][k] * src(b, t-K+1+k, c))
+ *   dt_out[b,t,h]  = softplus(dt_raw[b,t,h] + dt_bias[h])
+ *
+ * src(b, tau, c) is xbc_raw[b,tau,c] if tau >= 0 and tau lies in t's
+ * document; conv_state_in[b][K-1+tau][c] if tau < 0 and t is still in the
+ * row's first document; else 0.  conv_w[c][K-1] multiplies the current
+ * token (the port pages store the upstream [conv_dim,1,d_conv] weight with
+ * the tap axis reversed; this is the un-reversed, upstream order).
+ *
+ *   xbc_raw        T  [B][L][conv_dim], row stride xbc_raw_row_stride
+ *   conv_w         f32 [conv_dim][K]
+ *   conv_b         f32 [conv_dim] or NULL (zero bias)
+ *   dt_raw         T  [B][L][H], row stride dt_raw_row_stride, or NULL (no dt output)
+ *   dt_bias        f32 [H] or NULL (zero)
+ *   doc_ids        i32 [B][L] or NULL (one document per row)
+ *   conv_state_in  T  [B][K-1][conv_dim] or NULL (zero history)
+ *   conv_state_out T  [B][K-1][conv_dim] or NULL; may equal conv_state_in
+ *                  (in place).  Holds the K-1 raw rows the next call's first
+ *                  token reads, judged from the last token's document.
+ *   act            ssd_act_t
+ *   xbc_out        T  [B][L][conv_dim], row stride xbc_out_row_stride; must not
+ *                  overlap xbc_raw (the halo rows are re-read)
+ *   dt_out         f32 [B][L][H] contiguous; required iff dt_raw != NULL
+ * Values are computed in fp32 and rounded to T (round to nearest even).
+ */
+int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
+                 const void *xbc_raw, int64_t xbc_raw_row_stride,
+                 const float *conv_w, const float *conv_b,
+                 const void *dt_raw, int64_t dt_raw_row_stride,
+                 const float *dt_bias, const int32_t *doc_ids,
+                 const void *conv_state_in, void *conv_state_out, int act,
+                 void *xbc_out, int64_t xbc_out_row_stride, float *dt_out,
+                 void *stream);
+
+/*
+ * ssd_chunk_scan_fwd -- the SSD selective scan, chunk = 64.
+ *
+ * Computes y (and the final state) of the recurrence above for every
+ * (b, h).  Inside a chunk the dual (quadratic) form is used; chunk states
+ * are passed strictly in chunk order with the state kept on chip in fp32,
+ * so a prefill split at a multiple of 64 tokens with the state carried is
+ * bitwise identical to one call.
+ *
+ *   x       T   [B][L][H*P]  row stride x_row_stride
+ *   Bm, Cm  T   [B][L][G*N]  row strides B_row_stride, C_row_stride
+ *               (x, Bm, Cm may be column slices of one ssd_conv_fwd output)
+ *   dt      f32 [B][L][H]    row stride dt_row_stride; dt_softplus = 0: dt is
+ *               already activated (>= 0); 1: dt := softplus(dt + dt_bias)
+ *   dt_bias f32 [H] or NULL (only read when dt_softplus = 1)
+ *   A       f32 [H], A <= 0 (the caller computes A = -exp(A_log))
+ *   D       f32 [H] or NULL (no skip)
+ *   z       T   [B][L][H*P] row stride z_row_stride, or NULL (no gate)
+ *   doc_ids i32 [B][L] or NULL
+ *   init_state  f32 [B][H][P][N] or NULL (zero)
+ *   final_state f32 [B][H][P][N] or NULL; may equal init_state (in place)
+ *   y       f32 [B][L][H*P]  row stride y_row_stride; must not overlap inputs
+ *   workspace, workspace_bytes: scratch of ssd_chunk_scan_workspace_size()
+ *               bytes (the current design needs none: NULL, 0 is accepted)
+ */
+int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                       const void *x, int64_t x_row_stride,
+                       const void *Bm, int64_t B_row_stride,
+                       const void *Cm, int64_t C_row_stride,
+                       const float *dt, int64_t dt_row_stride,
+                       int dt_softplus, const float *dt_bias,
+                       const float *A, const float *D,
+                       const void *z, int64_t z_row_stride,
+                       const int32_t *doc_ids,
+                       const float *init_state, float *final_state,
+                       float *y, int64_t y_row_stride,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace ssd_chunk_scan_fwd needs for these sizes (0 today). */
+size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
+
+/*
+ * ssd_step -- one decode token for each of B sequences.
+ *
+ * window = [conv_state[b][0..K-2], xbc_raw[b]]; xbc = act(conv over window),
+ * rounded to T; conv_state shifts by one row (the new raw row enters last);
+ * dt = softplus(dt_raw + dt_bias); then one token of the recurrence and the
+ * gate.  This is ssd_conv_fwd + ssd_chunk_scan_fwd at L = 1 with both
+ * states carried, so it continues a prefill's conv_state_out/final_state
+ * buffers as they are.
+ *
+ *   xbc_raw    T   [B][conv_dim]     dt_raw T [B][H]     z T [B][H*P] or NULL
+ *   conv_w     f32 [conv_dim][K]     conv_b f32 [conv_dim] or NULL
+ *   dt_bias    f32 [H] or NULL       A f32 [H]           D f32 [H] or NULL
+ *   conv_state T   [B][K-1][conv_dim], read and updated in place
+ *   ssm_state  f32 [B][H][P][N],     read and updated in place
+ *   y          f32 [B][H*P]
+ * One workgroup serves one sequence, so B should be >= the CU count (256)
+ * for full-device bandwidth.  Deterministic and batch-invariant: a row's
+ * result does not depend on B or on the other rows.
+ */
+int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
+             const void *xbc_raw, const void *dt_raw, const void *z,
+             const float *conv_w, const float *conv_b, const float *dt_bias,
+             const float *A, const float *D,
+             void *conv_state, float *ssm_state, int act, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,230 @@
+"""Mamba-2 SSD mixer core on MI355X (gfx950): Python binding of libssd.so.
+
+The three entry points mirror the C ABI in include/ssd.h one to one:
+
+    ssd_conv_fwd        causal depthwise conv (k=4) + SiLU, dt = softplus(dt + dt_bias)
+    ssd_chunk_scan_fwd  chunked (64) SSD scan with groups, documents, states, D skip, z gate
+    ssd_step            one decode token per sequence
+
+This module only marshals torch tensors (device pointers, row strides, the
+current HIP stream) into the library; every step of the computation runs in
+the HIP kernels.  There is no fallback: if libssd.so is not built, or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
+           "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_ACT_SILU, SSD_ACT_NONE = 0, 1
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    """A non-zero ssd_status_t; .status holds the code."""
+
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m selective_state_space_14_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    I, P, I64, SZ = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [I]
+    lib.ssd_version.restype = I
+    lib.ssd_version.argtypes = []
+    lib.ssd_conv_fwd.restype = I
+    lib.ssd_conv_fwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I, P, I64, P, P]
+    lib.ssd_chunk_scan_fwd.restype = I
+    lib.ssd_chunk_scan_fwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P,
+                                       I64, P, P, P, P, I64, P, SZ, P]
+    lib.ssd_chunk_scan_workspace_size.restype = SZ
+    lib.ssd_chunk_scan_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.ssd_step.restype = I
+    lib.ssd_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise SSDError(status, lib.ssd_status_string(status).decode(), lib.ssd_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"{name}: dtype {t.dtype} is not supported (float32 or bfloat16; other types are refused, "
+                    "not converted)")
+
+
+def _ptr(t, name, dtype=None, device=True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _rows(t, name, B, L, width):
+    """Validate a [B, L, width] view with a contiguous inner dim; return its row stride."""
+    if t is None:
+        return 0
+    if t.dim() != 3 or t.shape[0] != B or t.shape[1] != L or t.shape[2] != width:
+        raise ValueError(f"{name}: expected shape [{B}, {L}, {width}], got {list(t.shape)}")
+    if t.stride(2) != 1 and width > 1:
+        raise ValueError(f"{name}: the innermost dimension must be contiguous")
+    rs = t.stride(1)
+    if B > 1 and L > 0 and t.stride(0) != L * rs:
+        raise ValueError(f"{name}: batch rows must be L * row_stride elements apart")
+    return rs
+
+
+def _contig(t, name, shape):
+    if t is None:
+        return
+    if list(t.shape) != list(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor of shape {list(shape)}, got {list(t.shape)}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssd_conv_fwd(xbc_raw, conv_w, *, H, P, N, G, K=4, conv_b=None, dt_raw=None, dt_bias=None, doc_ids=None,
+                 conv_state_in=None, conv_state_out=None, act=SSD_ACT_SILU, xbc_out=None, dt_out=None, stream=None):
+    """Causal depthwise conv + activation over xbc_raw [B, L, conv_dim] and dt = softplus(dt_raw + dt_bias).
+
+    Returns (xbc_out [B, L, conv_dim] in xbc_raw's dtype, dt_out [B, L, H] fp32 or None)."""
+    lib = load()
+    B, L = xbc_raw.shape[0], xbc_raw.shape[1]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    rs_in = _rows(xbc_raw, "xbc_raw", B, L, C)
+    if xbc_out is None:
+        xbc_out = torch.empty((B, L, C), dtype=xbc_raw.dtype, device=xbc_raw.device)
+    rs_out = _rows(xbc_out, "xbc_out", B, L, C)
+    rs_dt = 0
+    if dt_raw is not None:
+        rs_dt = _rows(dt_raw, "dt_raw", B, L, H)
+        if dt_out is None:
+            dt_out = torch.empty((B, L, H), dtype=torch.float32, device=xbc_raw.device)
+        _contig(dt_out, "dt_out", (B, L, H))
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    _contig(conv_state_in, "conv_state_in", (B, K - 1, C))
+    _contig(conv_state_out, "conv_state_out", (B, K - 1, C))
+    st = lib.ssd_conv_fwd(
+        B, L, H, P, N, G, K, dtype,
+        _ptr(xbc_raw, "xbc_raw"), rs_in,
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(conv_b, "conv_b", torch.float32),
+        _ptr(dt_raw, "dt_raw", xbc_raw.dtype), rs_dt,
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(conv_state_in, "conv_state_in", xbc_raw.dtype), _ptr(conv_state_out, "conv_state_out", xbc_raw.dtype),
+        int(act), _ptr(xbc_out, "xbc_out", xbc_raw.dtype), rs_out,
+        _ptr(dt_out, "dt_out", torch.float32), _stream(stream))
+    _check(st)
+    return xbc_out, dt_out
+
+
+def ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
+    return int(load().ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype))
+
+
+def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=None, init_state=None,
+                       final_state=None, y=None, dt_softplus=False, dt_bias=None, chunk=64, workspace=None,
+                       stream=None):
+    """SSD scan.  x [B,L,H*P], Bm/Cm [B,L,G*N] (same dtype), dt [B,L,H] fp32, A [H] fp32.
+
+    Returns y [B, L, H*P] fp32 (and writes final_state if given)."""
+    lib = load()
+    B, L = x.shape[0], x.shape[1]
+    dtype = _dtype_code(x, "x")
+    rs_x = _rows(x, "x", B, L, H * P)
+    rs_b = _rows(Bm, "Bm", B, L, G * N)
+    rs_c = _rows(Cm, "Cm", B, L, G * N)
+    rs_dt = _rows(dt, "dt", B, L, H)
+    rs_z = _rows(z, "z", B, L, H * P)
+    if y is None:
+        y = torch.empty((B, L, H * P), dtype=torch.float32, device=x.device)
+    rs_y = _rows(y, "y", B, L, H * P)
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    _contig(init_state, "init_state", (B, H, P, N))
+    _contig(final_state, "final_state", (B, H, P, N))
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_fwd(
+        B, L, H, P, N, G, chunk, dtype,
+        _ptr(x, "x"), rs_x, _ptr(Bm, "Bm", x.dtype), rs_b, _ptr(Cm, "Cm", x.dtype), rs_c,
+        _ptr(dt, "dt", torch.float32), rs_dt, int(bool(dt_softplus)), _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
+        _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
+        _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
+    _check(st)
+    return y
+
+
+def ssd_step(xbc_raw, dt_raw, conv_w, A, conv_state, ssm_state, *, H, P, N, G, K=4, z=None, conv_b=None,
+             dt_bias=None, D=None, act=SSD_ACT_SILU, y=None, stream=None):
+    """One decode token.  xbc_raw [B, conv_dim], dt_raw [B, H] (same dtype), conv_state [B, K-1, conv_dim]
+    (same dtype) and ssm_state [B, H, P, N] fp32 are updated in place.  Returns y [B, H*P] fp32."""
+    lib = load()
+    B = xbc_raw.shape[0]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    _contig(xbc_raw, "xbc_raw", (B, C))
+    _contig(dt_raw, "dt_raw", (B, H))
+    _contig(z, "z", (B, H * P))
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(conv_state, "conv_state", (B, K - 1, C))
+    _contig(ssm_state, "ssm_state", (B, H, P, N))
+    if y is None:
+        y = torch.empty((B, H * P), dtype=torch.float32, device=xbc_raw.device)
+    _contig(y, "y", (B, H * P))
+    st = lib.ssd_step(
+        B, H, P, N, G, K, dtype,
+        _ptr(xbc_raw, "xbc_raw"), _ptr(dt_raw, "dt_raw", xbc_raw.dtype), _ptr(z, "z", xbc_raw.dtype),
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(conv_b, "conv_b", torch.float32),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
+        _ptr(conv_state, "conv_state", xbc_raw.dtype), _ptr(ssm_state, "ssm_state", torch.float32), int(act),
+        _ptr(y, "y", torch.float32), _stream(stream))
+    _check(st)
+    return y

@@ -1,0 +1,270 @@
+// api.cpp -- the C ABI of libssd.so (declared in include/ssd.h): argument
+// validation with messages that name the offending argument and its values,
+// then one launch on the caller's stream.  Nothing here touches device
+// memory or calls HIP before validation has passed.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SSD_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(int dtype) { return dtype == SSD_F32 ? 4 : 2; }
+
+// Shared size checks; returns SSD_OK or a failure with the message set.
+int check_dims(const char* fn, int B, int L, int H, int P, int N, int G, int K, int dtype) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dtype=%d is not supported (only SSD_F32=0 and SSD_BF16=1; "
+                    "fp16, fp64 and other types are refused, not converted)", fn, dtype);
+    if (B < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: B=%d must be >= 0", fn, B);
+    if (L < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: L=%d must be >= 0", fn, L);
+    if (H <= 0) return fail(SSD_ERR_BAD_SHAPE, "%s: H=%d must be > 0", fn, H);
+    if (G <= 0) return fail(SSD_ERR_BAD_SHAPE, "%s: G=%d must be > 0", fn, G);
+    if (H % G != 0) return fail(SSD_ERR_BAD_SHAPE, "%s: H=%d is not divisible by G=%d", fn, H, G);
+    if (P != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: P=%d is not supported (head dim must be 64)", fn, P);
+    if (N != 16 && N != 32 && N != 64 && N != 128)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: N=%d is not supported (state dim must be 16, 32, 64 or 128)", fn, N);
+    if (K != 4) return fail(SSD_ERR_UNSUPPORTED, "%s: K=%d is not supported (conv kernel must be 4)", fn, K);
+    const long long total_heads = (long long)B * H;
+    if (total_heads > 0x7fffffffLL)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: B*H=%lld is too large", fn, total_heads);
+    return SSD_OK;
+}
+
+int check_tensor(const char* fn, const char* name, const void* p, int64_t stride, int64_t width, int es,
+                 bool required) {
+    if (!p) {
+        if (required) return fail(SSD_ERR_NULL_ARG, "%s: %s is NULL", fn, name);
+        return SSD_OK;
+    }
+    if (stride < width)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: %s row stride %lld is smaller than the row width %lld", fn, name,
+                    (long long)stride, (long long)width);
+    if (!aligned16(p))
+        return fail(SSD_ERR_ALIGNMENT, "%s: %s=%p is not 16-byte aligned", fn, name, p);
+    if ((stride * es) % 16 != 0)
+        return fail(SSD_ERR_ALIGNMENT, "%s: %s row stride %lld elements is not a multiple of 16 bytes", fn, name,
+                    (long long)stride);
+    return SSD_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, bool required, bool need16) {
+    if (!p) return required ? fail(SSD_ERR_NULL_ARG, "%s: %s is NULL", fn, name) : SSD_OK;
+    if (need16 && !aligned16(p)) return fail(SSD_ERR_ALIGNMENT, "%s: %s=%p is not 16-byte aligned", fn, name, p);
+    if (!need16 && (reinterpret_cast<uintptr_t>(p) & 3u))
+        return fail(SSD_ERR_ALIGNMENT, "%s: %s=%p is not 4-byte aligned", fn, name, p);
+    return SSD_OK;
+}
+
+#define TRY(expr)                     \
+    do {                              \
+        int _s = (expr);              \
+        if (_s != SSD_OK) return _s;  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_last_error(void) { return g_err; }
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG";
+        case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+        case SSD_ERR_ALIGNMENT: return "SSD_ERR_ALIGNMENT";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+int ssd_version(void) { return SSD_ABI_VERSION; }
+
+int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
+                 const void* xbc_raw, int64_t xbc_raw_row_stride,
+                 const float* conv_w, const float* conv_b,
+                 const void* dt_raw, int64_t dt_raw_row_stride,
+                 const float* dt_bias, const int32_t* doc_ids,
+                 const void* conv_state_in, void* conv_state_out, int act,
+                 void* xbc_out, int64_t xbc_out_row_stride, float* dt_out,
+                 void* stream) {
+    const char* fn = "ssd_conv_fwd";
+    TRY(check_dims(fn, B, L, H, P, N, G, K, dtype));
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    const int64_t C = (int64_t)H * P + 2LL * G * N;
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "xbc_raw", xbc_raw, xbc_raw_row_stride, C, es, work));
+    TRY(check_tensor(fn, "xbc_out", xbc_out, xbc_out_row_stride, C, es, work));
+    TRY(check_ptr(fn, "conv_w", conv_w, true, true));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    if (dt_raw) {
+        if (dt_raw_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: dt_raw row stride %lld is smaller than H=%d", fn,
+                        (long long)dt_raw_row_stride, H);
+        TRY(check_ptr(fn, "dt_raw", dt_raw, true, false));
+        TRY(check_ptr(fn, "dt_out", dt_out, true, false));
+    } else if (dt_out) {
+        return fail(SSD_ERR_NULL_ARG, "%s: dt_out is given but dt_raw is NULL", fn);
+    }
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    TRY(check_ptr(fn, "conv_state_in", conv_state_in, false, true));
+    TRY(check_ptr(fn, "conv_state_out", conv_state_out, false, true));
+    if (work && xbc_out == xbc_raw)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: xbc_out must not alias xbc_raw (halo rows are re-read)", fn);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        // nothing to convolve; the carried state passes through unchanged
+        if (conv_state_out && B > 0)
+            return hip_status(fn, ssd::launch_copy16(conv_state_in, conv_state_out, (size_t)B * 3 * C * es / 16, s));
+        return ok();
+    }
+    ssd::ConvArgs a;
+    a.B = B; a.L = L; a.C = (int)C; a.H = H; a.dtype = dtype; a.act = act;
+    a.raw = xbc_raw; a.raw_stride = xbc_raw_row_stride;
+    a.w = conv_w; a.bias = conv_b;
+    a.dt_raw = dt_raw; a.dt_stride = dt_raw_row_stride; a.dt_bias = dt_bias;
+    a.doc = doc_ids;
+    a.state_in = conv_state_in; a.state_out = conv_state_out;
+    a.out = xbc_out; a.out_stride = xbc_out_row_stride;
+    a.dt_out = dt_out;
+    return hip_status(fn, ssd::launch_conv(a, s));
+}
+
+size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
+    (void)B; (void)L; (void)H; (void)P; (void)N; (void)G; (void)dtype;
+    return 0;
+}
+
+int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                       const void* x, int64_t x_row_stride,
+                       const void* Bm, int64_t B_row_stride,
+                       const void* Cm, int64_t C_row_stride,
+                       const float* dt, int64_t dt_row_stride,
+                       int dt_softplus, const float* dt_bias,
+                       const float* A, const float* D,
+                       const void* z, int64_t z_row_stride,
+                       const int32_t* doc_ids,
+                       const float* init_state, float* final_state,
+                       float* y, int64_t y_row_stride,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_chunk_scan_fwd";
+    TRY(check_dims(fn, B, L, H, P, N, G, 4, dtype));
+    if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
+    if (dt_softplus != 0 && dt_softplus != 1)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dt_softplus=%d must be 0 or 1", fn, dt_softplus);
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "x", x, x_row_stride, (int64_t)H * P, es, work));
+    TRY(check_tensor(fn, "Bm", Bm, B_row_stride, (int64_t)G * N, es, work));
+    TRY(check_tensor(fn, "Cm", Cm, C_row_stride, (int64_t)G * N, es, work));
+    TRY(check_tensor(fn, "z", z, z_row_stride, (int64_t)H * P, es, false));
+    TRY(check_tensor(fn, "y", y, y_row_stride, (int64_t)H * P, 4, work));
+    if (work) {
+        if (!dt) return fail(SSD_ERR_NULL_ARG, "%s: dt is NULL", fn);
+        if (dt_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: dt row stride %lld is smaller than H=%d", fn, (long long)dt_row_stride, H);
+    }
+    TRY(check_ptr(fn, "dt", dt, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, B > 0, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    TRY(check_ptr(fn, "init_state", init_state, false, true));
+    TRY(check_ptr(fn, "final_state", final_state, false, true));
+    const size_t need = ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype);
+    if (workspace_bytes < need)
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(SSD_ERR_NULL_ARG, "%s: workspace is NULL", fn);
+    if (work && y == final_state)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: y must not alias final_state", fn);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        if (final_state && B > 0)
+            return hip_status(fn, ssd::launch_copy16(init_state, final_state, (size_t)B * H * P * N * 4 / 16, s));
+        return ok();
+    }
+    ssd::ScanArgs a;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.x = x; a.x_stride = x_row_stride;
+    a.Bm = Bm; a.B_stride = B_row_stride;
+    a.Cm = Cm; a.C_stride = C_row_stride;
+    a.dt = dt; a.dt_stride = dt_row_stride;
+    a.dt_softplus = dt_softplus; a.dt_bias = dt_bias;
+    a.A = A; a.D = D;
+    a.z = z; a.z_stride = z_row_stride;
+    a.doc = doc_ids;
+    a.init_state = init_state; a.final_state = final_state;
+    a.y = y; a.y_stride = y_row_stride;
+    (void)workspace;
+    return hip_status(fn, ssd::launch_scan(a, s));
+}
+
+int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
+             const void* xbc_raw, const void* dt_raw, const void* z,
+             const float* conv_w, const float* conv_b, const float* dt_bias,
+             const float* A, const float* D,
+             void* conv_state, float* ssm_state, int act, float* y, void* stream) {
+    const char* fn = "ssd_step";
+    TRY(check_dims(fn, B, 1, H, P, N, G, K, dtype));
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    const bool work = B > 0;
+    const int64_t C = (int64_t)H * P + 2LL * G * N;
+    TRY(check_ptr(fn, "xbc_raw", xbc_raw, work, true));
+    TRY(check_ptr(fn, "dt_raw", dt_raw, work, false));
+    TRY(check_ptr(fn, "z", z, false, false));
+    TRY(check_ptr(fn, "conv_w", conv_w, work, true));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, work, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "conv_state", conv_state, work, true));
+    TRY(check_ptr(fn, "ssm_state", ssm_state, work, true));
+    TRY(check_ptr(fn, "y", y, work, false));
+    const size_t lds = ssd::step_lds_bytes(H, P, N, G);
+    if (lds > 64 * 1024)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: conv_dim=%lld plus 2*H=%d floats exceed the 64 KiB LDS budget", fn,
+                    (long long)C, 2 * H);
+    if (!work) return ok();
+    ssd::StepArgs a;
+    a.B = B; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype; a.act = act;
+    a.xbc_raw = xbc_raw; a.dt_raw = dt_raw; a.z = z;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.dt_bias = dt_bias; a.A = A; a.D = D;
+    a.conv_state = conv_state; a.ssm_state = ssm_state; a.y = y;
+    return hip_status(fn, ssd::launch_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+// conv.hip -- ssd_conv_fwd: causal depthwise conv (k = 4) + activation over
+// the [x | B | C] columns, and dt = softplus(dt_raw + dt_bias), on gfx950.
+//
+// Layout of the work: one 64-lane wave per block; lane l owns 16 bytes of
+// channels (8 bf16 or 4 fp32) and walks a tile of kTile consecutive tokens
+// with the last three raw rows in registers, so every raw row is read once
+// (plus a 3-row halo per tile) and every output row written once, in 1 KiB
+// coalesced row segments.  Rows are loaded kBatch at a time before use to
+// keep several 16-byte loads in flight per lane.  An extra column of blocks
+// (blockIdx.x == number of channel blocks) computes dt for the same tokens.
+//
+// Document isolation (Mini-K3-1H card, "Checkpoint and training": the conv
+// history resets at every document boundary): when token t starts a new
+// document, the three history registers are zeroed before t is convolved,
+// so no value from an earlier document reaches t or any later token by any
+// arithmetic path.  The carried conv state only ever sits in the history
+// registers of tile 0, so it reaches exactly the tokens before the row's
+// first boundary.
+//
+// Tap order: conv_w[c][3] multiplies the current token (the un-reversed form
+// of the [conv_dim, 1, d_conv] weight listed by the Codestral-Mamba port).
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kConvThreads = 64;
+constexpr int kTile = 32;     // tokens per block
+constexpr int kBatch = 8;     // rows loaded before use
+
+template <typename T> struct CV;
+template <> struct CV<float> {
+    static constexpr int n = 4;
+    __device__ static void unpack(uint4 v, float* o) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+    __device__ static uint4 pack(const float* o) {
+        return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+    }
+    __device__ static float scalar(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
+};
+template <> struct CV<uint16_t> {
+    static constexpr int n = 8;
+    __device__ static void unpack(uint4 v, float* o) {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+    __device__ static uint4 pack(const float* o) {
+        return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                          pack_bf16x2(o[6], o[7]));
+    }
+    __device__ static float scalar(const void* p, size_t i) { return bf16_to_f32(static_cast<const uint16_t*>(p)[i]); }
+};
+
+__device__ __forceinline__ bool is_boundary(const int32_t* doc, int t) {
+    return doc != nullptr && t > 0 && doc[t] != doc[t - 1];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
+    constexpr int VEC = CV<T>::n;
+    const int C = a.C, L = a.L;
+    const int b = blockIdx.z;
+    const int t0 = blockIdx.y * kTile;
+    const int t1 = min(t0 + kTile, L);
+    const int ncb = (C / VEC + kConvThreads - 1) / kConvThreads;
+    const int32_t* doc = a.doc ? a.doc + (size_t)b * L : nullptr;
+
+    if ((int)blockIdx.x == ncb) {
+        // ---- dt = softplus(dt_raw + dt_bias) for the tile's tokens
+        if (a.dt_raw == nullptr) return;
+        const int H = a.H;
+        for (int i = threadIdx.x; i < (t1 - t0) * H; i += kConvThreads) {
+            const int t = t0 + i / H, h = i % H;
+            const float r = CV<T>::scalar(a.dt_raw, ((size_t)b * L + t) * a.dt_stride + h);
+            a.dt_out[((size_t)b * L + t) * H + h] = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
+        }
+        return;
+    }
+
+    const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * VEC;
+    if (c0 >= C) return;
+    const T* raw = static_cast<const T*>(a.raw) + (size_t)b * L * a.raw_stride + c0;
+    T* out = static_cast<T*>(a.out) + (size_t)b * L * a.out_stride + c0;
+
+    float w[4][VEC], bias[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)(c0 + e) * 4);
+        w[0][e] = wv.x; w[1][e] = wv.y; w[2][e] = wv.z; w[3][e] = wv.w;
+        bias[e] = a.bias ? a.bias[c0 + e] : 0.0f;
+    }
+
+    // history registers: h3 = tap t-3, h2 = t-2, h1 = t-1
+    float h3[VEC], h2[VEC], h1[VEC];
+    if (t0 == 0) {
+        const T* st = a.state_in ? static_cast<const T*>(a.state_in) + (size_t)b * 3 * C + c0 : nullptr;
+        if (st) {
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(st), h3);
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(st + C), h2);
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(st + 2 * C), h1);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = h1[e] = 0.0f;
+        }
+    } else {
+        // t0 >= kTile >= 3: the halo rows exist; boundaries inside the halo cut older taps
+        CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(t0 - 3) * a.raw_stride), h3);
+        CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(t0 - 2) * a.raw_stride), h2);
+        CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(t0 - 1) * a.raw_stride), h1);
+        if (is_boundary(doc, t0 - 2)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) h3[e] = 0.0f;
+        }
+        if (is_boundary(doc, t0 - 1)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = 0.0f;
+        }
+    }
+
+    for (int tb = t0; tb < t1; tb += kBatch) {
+        uint4 rows[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (tb + u < t1) rows[u] = *reinterpret_cast<const uint4*>(raw + (size_t)(tb + u) * a.raw_stride);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int t = tb + u;
+            if (t >= t1) break;
+            float cur[VEC], o[VEC];
+            CV<T>::unpack(rows[u], cur);
+            if (is_boundary(doc, t)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = h1[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float v = bias[e];
+                v = fmaf(w[0][e], h3[e], v);
+                v = fmaf(w[1][e], h2[e], v);
+                v = fmaf(w[2][e], h1[e], v);
+                v = fmaf(w[3][e], cur[e], v);
+                if (a.act == 0) v = v / (1.0f + expf(-v));
+                o[e] = v;
+                h3[e] = h2[e];
+                h2[e] = h1[e];
+                h1[e] = cur[e];
+            }
+            *reinterpret_cast<uint4*>(out + (size_t)t * a.out_stride) = CV<T>::pack(o);
+        }
+    }
+
+    // ---- conv state after the call (tile 0 owns it: it alone read state_in)
+    if (t0 == 0 && a.state_out != nullptr) {
+        float s0[VEC], s1[VEC], s2[VEC];
+        if (t1 == L) {
+            // this lane convolved the last token: its history registers are the state
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) { s0[e] = h3[e]; s1[e] = h2[e]; s2[e] = h1[e]; }
+        } else {
+            // L > kTile >= 3: the last three raw rows, cut at boundaries inside them
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(L - 3) * a.raw_stride), s0);
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(L - 2) * a.raw_stride), s1);
+            CV<T>::unpack(*reinterpret_cast<const uint4*>(raw + (size_t)(L - 1) * a.raw_stride), s2);
+            if (is_boundary(doc, L - 2)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s0[e] = 0.0f;
+            }
+            if (is_boundary(doc, L - 1)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s0[e] = s1[e] = 0.0f;
+            }
+        }
+        T* so = static_cast<T*>(a.state_out) + (size_t)b * 3 * C + c0;
+        *reinterpret_cast<uint4*>(so) = CV<T>::pack(s0);
+        *reinterpret_cast<uint4*>(so + C) = CV<T>::pack(s1);
+        *reinterpret_cast<uint4*>(so + 2 * C) = CV<T>::pack(s2);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.L == 0) {
+        // nothing to convolve; a requested state_out is the (possibly absent) state_in
+        return hipSuccess;
+    }
+    const int vec = a.dtype == 0 ? 4 : 8;
+    const int ncb = (a.C / vec + kConvThreads - 1) / kConvThreads;
+    dim3 grid(ncb + 1, (a.L + kTile - 1) / kTile, a.B);
+    if (a.dtype == 0)
+        hipLaunchKernelGGL(ssd_conv_kernel<float>, grid, dim3(kConvThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(ssd_conv_kernel<uint16_t>, grid, dim3(kConvThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ssd
+
+namespace ssd {
+
+namespace {
+__global__ void copy16_kernel(const uint4* src, uint4* dst, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : make_uint4(0, 0, 0, 0);
+}
+}  // namespace
+
+hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream) {
+    if (n == 0 || src == dst) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(copy16_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), n);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,107 @@
+// ssd_device.hpp -- device-side helpers shared by the gfx950 kernels:
+// bf16 <-> fp32 conversion, fast transcendental wrappers, 16x16 MFMA tile
+// wrappers and the fragment layout they share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16
+// bf16 is the top half of an fp32 bit pattern.  Widening is exact (a shift);
+// narrowing rounds to nearest even.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+// Two fp32 -> packed pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- math
+// exp2 on the hardware unit (v_exp_f32); inputs here are <= 0 or moderate.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// silu(v) = v * sigmoid(v) = v / (1 + 2^(-v log2 e)).
+__device__ __forceinline__ float silu_f(float v) { return v * fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
+// softplus(v) = max(v, 0) + log(1 + e^-|v|), with the accurate libm routines.
+__device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
+
+// ---------------------------------------------------------------- MFMA tiles
+// All contractions are built from 16x16 output tiles.  Fragment layout, for
+// lane l = 16*q + i (q = l / 16, i = l % 16):
+//   * an operand fragment holds 4 consecutive K indices 4q..4q+3 of a 16-wide
+//     K block, at row/column index i;
+//   * an accumulator tile holds rows 4q..4q+3 of column i.
+// Hence an accumulator tile is, unchanged, an operand fragment whose K index
+// is the tile's row index.  A bf16 MFMA (16x16x32) consumes two K blocks at
+// once: elements 0..3 of both operands carry block 0, elements 4..7 block 1;
+// the fp32 MFMA (16x16x4) consumes one element per instruction.  Only the
+// pairing of A and B elements matters for the sum over K, so this fixed
+// assignment of K indices to (lane group, element) is valid for both.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct FragBF { uint32_t a, b; };   // 4 bf16: K = 4q+0,1 in a; 4q+2,3 in b
+
+__device__ __forceinline__ f32x4 mma_bf16(f32x4 acc, FragBF a0, FragBF a1, FragBF b0, FragBF b1) {
+    union { uint32_t u[4]; bf16x8 v; } A, B;
+    A.u[0] = a0.a; A.u[1] = a0.b; A.u[2] = a1.a; A.u[3] = a1.b;
+    B.u[0] = b0.a; B.u[1] = b0.b; B.u[2] = b1.a; B.u[3] = b1.b;
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, B.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma_f32(f32x4 acc, float4 a, float4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ FragBF frag_from_f32(f32x4 v) {
+    FragBF f;
+    f.a = pack_bf16x2(v[0], v[1]);
+    f.b = pack_bf16x2(v[2], v[3]);
+    return f;
+}
+
+// ---------------------------------------------------------------- wave scan
+// One step of an inclusive segmented scan across a wave64 with DPP moves:
+// (value, segment-start flag, last segment start index).  Lanes whose source
+// is outside the move (or whose row is masked off) combine with the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void segscan_step(float& v, int& f, int& s) {
+    const float vu = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+    const int fu = __builtin_amdgcn_update_dpp(0, f, CTRL, ROWS, 0xF, false);
+    const int su = __builtin_amdgcn_update_dpp(-1, s, CTRL, ROWS, 0xF, false);
+    v = f ? v : v + vu;
+    f = f | fu;
+    s = max(s, su);
+}
+// v: per-lane value; f: 1 where a segment starts at this lane; s: lane index
+// where f, else -1.  On return v is the sum from the lane's segment start (or
+// lane 0) to the lane, s the last segment start at or before the lane (-1 if
+// none).  Kogge-Stone within 16-lane rows (row_shr 1, 2, 4, 8), then the
+// row_bcast 15 / 31 moves carry row totals across rows.
+__device__ __forceinline__ void wave_segscan(float& v, int f, int& s) {
+    segscan_step<0x111, 0xF>(v, f, s);
+    segscan_step<0x112, 0xF>(v, f, s);
+    segscan_step<0x114, 0xF>(v, f, s);
+    segscan_step<0x118, 0xF>(v, f, s);
+    segscan_step<0x142, 0xA>(v, f, s);
+    segscan_step<0x143, 0xC>(v, f, s);
+}
+
+}  // namespace ssd

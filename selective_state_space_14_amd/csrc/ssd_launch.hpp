@@ -1,0 +1,55 @@
+// ssd_launch.hpp -- host-side argument blocks and launchers of the kernels.
+// Arguments are already validated by api.cpp; sizes are in elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct ConvArgs {
+    int B, L, C, H, dtype, act;
+    const void* raw; int64_t raw_stride;
+    const float* w; const float* bias;
+    const void* dt_raw; int64_t dt_stride;
+    const float* dt_bias;
+    const int32_t* doc;
+    const void* state_in; void* state_out;
+    void* out; int64_t out_stride;
+    float* dt_out;
+};
+
+struct ScanArgs {
+    int B, L, H, P, N, G, dtype;
+    const void* x; int64_t x_stride;
+    const void* Bm; int64_t B_stride;
+    const void* Cm; int64_t C_stride;
+    const float* dt; int64_t dt_stride;
+    int dt_softplus; const float* dt_bias;
+    const float* A; const float* D;
+    const void* z; int64_t z_stride;
+    const int32_t* doc;
+    const float* init_state; float* final_state;
+    float* y; int64_t y_stride;
+};
+
+struct StepArgs {
+    int B, H, P, N, G, dtype, act;
+    const void* xbc_raw; const void* dt_raw; const void* z;
+    const float* conv_w; const float* conv_b; const float* dt_bias;
+    const float* A; const float* D;
+    void* conv_state; float* ssm_state; float* y;
+};
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+// Copies n 16-byte words src -> dst (src == nullptr: zero fill); used for the
+// L = 0 state pass-through without a memset node.
+hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream);
+
+size_t scan_lds_bytes(int N, int dtype);
+size_t step_lds_bytes(int H, int P, int N, int G);
+
+}  // namespace ssd

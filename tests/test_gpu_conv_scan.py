@@ -1,0 +1,311 @@
+"""GPU parity of ssd_conv_fwd and ssd_chunk_scan_fwd against the fp64 oracle,
+through the C ABI (the ctypes binding), on seeded synthetic inputs.
+
+Small cases span several chunks/tiles and ragged tails; the full-size
+workloads are checked on whole sampled batch rows (rows are independent)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import helpers as hp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def small_wl(dtype="bf16", H=4, N=32, G=2, L=200, B=2, **kw):
+    return synth.Workload("small_" + dtype, B, L, H, 64, N, G, dtype, **kw)
+
+
+# ----------------------------------------------------------------------------- conv
+def conv_magnitude(raw, w, bias, ids, state):
+    """|bias| + sum_k |w x| per output, with the same document/state masking (oracle conv of |.|, no act)."""
+    ab = lambda t: None if t is None else hp.np64(t).__abs__()
+    mag, _, _ = oracle.conv(ab(raw), ab(w), ab(bias), doc_ids=ids, state_in=ab(state), act=1)
+    return mag
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("docs,state,act,bias", [
+    (False, False, 0, False), (True, False, 0, True), (False, True, 1, True), (True, True, 0, False),
+])
+def test_conv_parity_small(gpu_lib, dtype, docs, state, act, bias):
+    wl = small_wl(dtype, L=203, docs=docs)            # 7 token tiles, ragged tail
+    _say(f"conv small {dtype} docs={docs} state={state} act={act} bias={bias}")
+    prm = synth.params(wl, 1, conv_bias=bias)
+    raw = synth.raw_inputs(wl, 1)
+    ids = synth.doc_ids(wl, 1, mean_len=24.0) if docs else None
+    C, K = wl.conv_dim, 4
+    st_in = (torch.randn(wl.B, K - 1, C, generator=torch.Generator().manual_seed(5)).to(wl.torch_dtype)
+             if state else None)
+    ref, dref, sref = oracle.conv(raw["xbc_raw"], prm["conv_w"], prm["conv_b"], raw["dt_raw"], prm["dt_bias"], ids,
+                                  st_in, act=act, want_state=True)
+    g = lambda t: None if t is None else t.to(DEV)
+    st_out = torch.empty(wl.B, K - 1, C, dtype=wl.torch_dtype, device=DEV)
+    out, dt = gpu_lib.ssd_conv_fwd(g(raw["xbc_raw"]), g(prm["conv_w"]), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                   conv_b=g(prm["conv_b"]), dt_raw=g(raw["dt_raw"]), dt_bias=g(prm["dt_bias"]),
+                                   doc_ids=g(ids), conv_state_in=g(st_in), conv_state_out=st_out, act=act)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        mag = conv_magnitude(raw["xbc_raw"], prm["conv_w"], prm["conv_b"], ids, st_in)
+        hp.assert_within_ulp(out, ref, "xbc_out", mag)
+    else:
+        hp.assert_fp32(out, ref, "xbc_out")
+    hp.assert_fp32(dt, dref, "dt_out")
+    # the conv state holds raw rows: exact
+    np.testing.assert_array_equal(hp.np64(st_out), sref)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 31, 32, 33])
+def test_conv_short_and_in_place_state(gpu_lib, L):
+    wl = small_wl("bf16", L=L, docs=True, B=3)
+    _say(f"conv short L={L}")
+    prm = synth.params(wl, 2, conv_bias=True)
+    raw = synth.raw_inputs(wl, 2)
+    ids = torch.zeros(wl.B, L, dtype=torch.int32)
+    if L > 1:
+        ids[1, 1:] = 1          # boundary at t = 1 in row 1
+        ids[2, L - 1:] = 1      # boundary at the last token in row 2
+    st = torch.randn(wl.B, 3, wl.conv_dim, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    ref, _, sref = oracle.conv(raw["xbc_raw"], prm["conv_w"], prm["conv_b"], None, None, ids, st, want_state=True)
+    st_dev = st.to(DEV)
+    out, _ = gpu_lib.ssd_conv_fwd(raw["xbc_raw"].to(DEV), prm["conv_w"].to(DEV), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                  conv_b=prm["conv_b"].to(DEV), doc_ids=ids.to(DEV), conv_state_in=st_dev,
+                                  conv_state_out=st_dev)
+    torch.cuda.synchronize()
+    hp.assert_within_ulp(out, ref, "xbc_out", conv_magnitude(raw["xbc_raw"], prm["conv_w"], prm["conv_b"], ids, st))
+    np.testing.assert_array_equal(hp.np64(st_dev), sref)
+
+
+def test_conv_full_mini_k3_sampled(gpu_lib):
+    wl = synth.WORKLOADS["mini_k3_packed"]
+    _say("conv full mini_k3_packed")
+    prm = synth.params(wl, 0)
+    raw = synth.raw_inputs(wl, 0)
+    ids = synth.doc_ids(wl, 0)
+    out, dt = gpu_lib.ssd_conv_fwd(raw["xbc_raw"].to(DEV), prm["conv_w"].to(DEV), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                   dt_raw=raw["dt_raw"].to(DEV), dt_bias=prm["dt_bias"].to(DEV), doc_ids=ids.to(DEV))
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        ref, dref, _ = oracle.conv(raw["xbc_raw"][b:b + 1], prm["conv_w"], None, raw["dt_raw"][b:b + 1],
+                                   prm["dt_bias"], ids[b:b + 1])
+        mag = conv_magnitude(raw["xbc_raw"][b:b + 1], prm["conv_w"], None, ids[b:b + 1], None)
+        hp.assert_within_ulp(out[b:b + 1], ref, f"xbc_out row {b}", mag)
+        hp.assert_fp32(dt[b:b + 1], dref, f"dt row {b}")
+
+
+# ----------------------------------------------------------------------------- scan
+def run_scan(gpu_lib, wl, inp, prm, ids=None, final=True, dt_softplus=True):
+    g = lambda t: None if t is None else t.to(DEV)
+    fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=DEV) if final else None
+    dt = inp["dt_raw"].float()
+    y = gpu_lib.ssd_chunk_scan_fwd(g(inp["x"]), g(inp["Bm"]), g(inp["Cm"]), g(dt), g(prm["A"]), H=wl.H, P=wl.P,
+                                   N=wl.N, G=wl.G, D=g(prm["D"]), z=g(inp["z"]), doc_ids=g(ids),
+                                   init_state=g(inp["h0"]), final_state=fs, dt_softplus=dt_softplus,
+                                   dt_bias=g(prm["dt_bias"]))
+    torch.cuda.synchronize()
+    return y, fs
+
+
+def oracle_scan(wl, inp, prm, ids=None):
+    return oracle.scan(inp["x"], inp["Bm"], inp["Cm"], inp["dt_raw"].float(), prm["A"], prm["D"], inp["z"], ids,
+                       inp["h0"], H=wl.H, P=wl.P, N=wl.N, G=wl.G, dt_softplus=True, dt_bias=prm["dt_bias"],
+                       want_state=True)
+
+
+def test_scan_tiny_fp32_workload(gpu_lib):
+    """B=1, L=256, H=4, P=64, N=16, G=1, fp32, no conv, no gate, zero h0 (the tiny fp32 workload)."""
+    wl = synth.WORKLOADS["tiny_fp32"]
+    _say("scan tiny_fp32")
+    prm = synth.params(wl, 0)
+    inp = synth.scan_inputs(wl, 0)
+    y, fs = run_scan(gpu_lib, wl, inp, prm)
+    yr, fr = oracle_scan(wl, inp, prm)
+    hp.assert_fp32(y, yr, "y")
+    hp.assert_fp32(fs, fr, "final_state")
+
+
+SCAN_CASES = [
+    # dtype, N, G, H, L, docs, h0, gate
+    ("f32", 16, 1, 4, 1, False, False, False),
+    ("f32", 32, 2, 4, 130, True, True, True),
+    ("f32", 64, 1, 2, 64, False, True, True),
+    ("f32", 128, 2, 2, 200, True, True, True),
+    ("bf16", 16, 2, 4, 200, True, True, True),
+    ("bf16", 32, 1, 2, 63, False, True, False),
+    ("bf16", 64, 8, 8, 257, True, True, True),
+    ("bf16", 64, 2, 4, 65, False, False, True),
+    ("bf16", 128, 4, 8, 333, True, True, True),
+    ("bf16", 128, 1, 2, 1, False, True, True),
+]
+
+
+@pytest.mark.parametrize("dtype,N,G,H,L,docs,h0,gate", SCAN_CASES)
+def test_scan_parity_small(gpu_lib, dtype, N, G, H, L, docs, h0, gate):
+    wl = small_wl(dtype, H=H, N=N, G=G, L=L, B=2, docs=docs, h0=h0, gate=gate)
+    _say(f"scan small {dtype} N={N} G={G} H={H} L={L} docs={docs} h0={h0} gate={gate}")
+    prm = synth.params(wl, 3)
+    inp = synth.scan_inputs(wl, 3)
+    ids = synth.doc_ids(wl, 3, mean_len=40.0) if docs else None
+    y, fs = run_scan(gpu_lib, wl, inp, prm, ids)
+    yr, fr = oracle_scan(wl, inp, prm, ids)
+    check = hp.assert_fp32 if dtype == "f32" else hp.assert_bf16
+    check(y, yr, "y")
+    check(fs, fr, "final_state")
+
+
+def test_scan_adversarial_boundaries(gpu_lib):
+    """Boundaries at t % 64 in {0, 1, 63}, documents of length 1-3, back-to-back boundaries."""
+    wl = small_wl("bf16", H=4, N=64, G=2, L=320, B=2, docs=True, h0=True, gate=True)
+    _say("scan adversarial boundaries")
+    prm = synth.params(wl, 4)
+    inp = synth.scan_inputs(wl, 4)
+    ids = torch.zeros(wl.B, wl.L, dtype=torch.int32)
+    cuts = [1, 2, 3, 63, 64, 65, 66, 68, 127, 128, 129, 191, 192, 255, 256, 257, 258, 300, 319]
+    for c in cuts:
+        ids[0, c:] += 1
+    for c in [64, 128, 129, 130, 131, 192, 256]:
+        ids[1, c:] += 1
+    y, fs = run_scan(gpu_lib, wl, inp, prm, ids)
+    yr, fr = oracle_scan(wl, inp, prm, ids)
+    hp.assert_bf16(y, yr, "y")
+    hp.assert_bf16(fs, fr, "final_state")
+
+
+def test_scan_empty_sequence_passes_state_through(gpu_lib):
+    wl = small_wl("f32", H=4, N=16, G=1, L=0, B=2, h0=True)
+    h0 = torch.randn(wl.B, wl.H, wl.P, wl.N, generator=torch.Generator().manual_seed(1)).to(DEV)
+    fs = torch.full_like(h0, 7.0)
+    x = torch.empty(wl.B, 0, wl.H * wl.P, device=DEV)
+    bm = torch.empty(wl.B, 0, wl.G * wl.N, device=DEV)
+    dt = torch.empty(wl.B, 0, wl.H, device=DEV)
+    A = -torch.ones(wl.H, device=DEV)
+    gpu_lib.ssd_chunk_scan_fwd(x, bm, bm, dt, A, H=wl.H, P=wl.P, N=wl.N, G=wl.G, init_state=h0, final_state=fs)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, h0)
+    gpu_lib.ssd_chunk_scan_fwd(x, bm, bm, dt, A, H=wl.H, P=wl.P, N=wl.N, G=wl.G, final_state=fs)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fs) == 0
+
+
+# ----------------------------------------------------------------------------- full workloads
+def gpu_forward(gpu_lib, wl, raw, prm, ids=None, conv_state=None, h0=None, final=True):
+    g = lambda t: None if t is None else t.to(DEV)
+    HP, GN = wl.H * wl.P, wl.G * wl.N
+    cs_out = torch.empty(raw["xbc_raw"].shape[0], 3, wl.conv_dim, dtype=wl.torch_dtype, device=DEV)
+    xbc, dt = gpu_lib.ssd_conv_fwd(g(raw["xbc_raw"]), g(prm["conv_w"]), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                   conv_b=g(prm["conv_b"]), dt_raw=g(raw["dt_raw"]), dt_bias=g(prm["dt_bias"]),
+                                   doc_ids=g(ids), conv_state_in=g(conv_state), conv_state_out=cs_out)
+    B = xbc.shape[0]
+    fs = torch.empty(B, wl.H, wl.P, wl.N, dtype=torch.float32, device=DEV) if final else None
+    y = gpu_lib.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, g(prm["A"]),
+                                   H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=g(prm["D"]), z=g(raw["z"]), doc_ids=g(ids),
+                                   init_state=g(h0), final_state=fs)
+    torch.cuda.synchronize()
+    return y, fs, cs_out, xbc
+
+
+@pytest.mark.parametrize("name", ["mini_k3_bf16", "mini_k3_packed", "large_layer_bf16"])
+def test_full_workload_sampled_rows(gpu_lib, name):
+    wl = synth.WORKLOADS[name]
+    _say(f"full workload {name}")
+    prm = synth.params(wl, 0)
+    raw = synth.raw_inputs(wl, 0, device=DEV)
+    ids = synth.doc_ids(wl, 0) if wl.docs else None
+    y, fs, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids, h0=raw["h0"])
+    for b in (0, wl.B - 1):
+        sl = slice(b, b + 1)
+        yr, fr, _, xr, _ = oracle.forward(raw["xbc_raw"][sl].cpu(), prm["conv_w"], None, raw["dt_raw"][sl].cpu(),
+                                          prm["dt_bias"], prm["A"], prm["D"], raw["z"][sl].cpu(), H=wl.H, P=wl.P,
+                                          N=wl.N, G=wl.G, doc_ids=None if ids is None else ids[sl],
+                                          init_state=None if raw["h0"] is None else raw["h0"][sl].cpu(),
+                                          round_bf16=True)
+        err = hp.assert_pipeline(y[sl], yr, xr[..., :wl.H * wl.P], raw["z"][sl].cpu(), prm["D"], wl.H, wl.P,
+                                 f"{name} y row {b}")
+        errs = hp.assert_bf16(fs[sl], fr, f"{name} final_state row {b}")
+        _say(f"  row {b}: max|dy|={err:.3e} max|dstate|={errs:.3e} rms(y)={hp.rms(yr):.3e}")
+
+
+def test_doc_isolation_bitwise(gpu_lib):
+    """Replacing every input of the earlier documents of a row (x100 magnitudes, other dt) leaves every
+    output bit of the later documents, and the final state, unchanged (+0 and -0 equal)."""
+    wl = synth.WORKLOADS["mini_k3_packed"].with_(L=2048, B=3)
+    _say("doc isolation bitwise")
+    prm = synth.params(wl, 1)
+    raw = synth.raw_inputs(wl, 1)
+    ids = torch.zeros(wl.B, wl.L, dtype=torch.int32)
+    splits = {0: [64, 65, 700, 701, 1023, 1024, 1025, 1500], 1: [1, 2, 3, 127, 128, 1900], 2: [63, 64, 2047]}
+    for b, cuts in splits.items():
+        for c in cuts:
+            ids[b, c:] += 1
+    base, fbase, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids)
+    gen = torch.Generator().manual_seed(11)
+    for b, cuts in splits.items():
+        for k in (cuts[0], cuts[len(cuts) // 2], cuts[-1]):
+            pert = {n: (None if v is None else v.clone()) for n, v in raw.items()}
+            noise = torch.randn(k, wl.conv_dim, generator=gen) * 100.0
+            pert["xbc_raw"][b, :k] = noise.to(wl.torch_dtype)
+            pert["dt_raw"][b, :k] = (torch.randn(k, wl.H, generator=gen) * 3.0).to(wl.torch_dtype)
+            pert["z"][b, :k] = (torch.randn(k, wl.H * wl.P, generator=gen) * 100.0).to(wl.torch_dtype)
+            y, fs, _, _ = gpu_forward(gpu_lib, wl, pert, prm, ids)
+            later = base[b, k:], y[b, k:]
+            assert torch.equal(later[0], later[1]), f"row {b}: outputs after boundary {k} changed"
+            assert torch.equal(fbase[b], fs[b]), f"row {b}: final state changed (boundary {k})"
+            assert not torch.equal(base[b, :k], y[b, :k])
+            for other in range(wl.B):
+                if other != b:
+                    assert torch.equal(base[other], y[other])
+
+
+def test_packed_vs_separate_documents(gpu_lib):
+    """Packed documents vs each document launched alone: within 0.03125 (the chunk grid differs)."""
+    wl = synth.WORKLOADS["mini_k3_packed"].with_(L=1500, B=1)
+    _say("packed vs separate")
+    prm = synth.params(wl, 2)
+    raw = synth.raw_inputs(wl, 2)
+    ids = synth.doc_ids(wl, 2, mean_len=300.0)
+    y, fs, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids)
+    idv = ids[0].tolist()
+    starts = [0] + [t for t in range(1, wl.L) if idv[t] != idv[t - 1]] + [wl.L]
+    assert len(starts) > 3
+    for s, e in zip(starts[:-1], starts[1:]):
+        sub = {n: (None if v is None else v[:, s:e].contiguous()) for n, v in raw.items() if n != "h0"}
+        ys, fss, _, _ = gpu_forward(gpu_lib, wl.with_(L=e - s), sub, prm)
+        hp.assert_bf16(y[:, s:e], ys, f"doc [{s},{e})")
+    hp.assert_bf16(fs, fss, "final state of the last document")
+
+
+@pytest.mark.parametrize("cut", [64, 512, 1984])
+def test_split_prefill_bitwise(gpu_lib, cut):
+    """A prefill split at a multiple of 64 with the conv and SSM states carried == one call, bit for bit."""
+    wl = synth.WORKLOADS["large_layer_bf16"].with_(L=2048, B=2)
+    _say(f"split prefill at {cut}")
+    prm = synth.params(wl, 5)
+    raw = synth.raw_inputs(wl, 5, device=DEV)
+    y, fs, cs, _ = gpu_forward(gpu_lib, wl, raw, prm, h0=raw["h0"])
+    a = {n: (None if v is None or n == "h0" else v[:, :cut].contiguous()) for n, v in raw.items()}
+    c = {n: (None if v is None or n == "h0" else v[:, cut:].contiguous()) for n, v in raw.items()}
+    ya, fa, csa, _ = gpu_forward(gpu_lib, wl.with_(L=cut), a, prm, h0=raw["h0"])
+    yc, fc, csc, _ = gpu_forward(gpu_lib, wl.with_(L=wl.L - cut), c, prm, conv_state=csa, h0=fa)
+    assert torch.equal(torch.cat([ya, yc], 1), y)
+    assert torch.equal(fc, fs)
+    assert torch.equal(csc, cs)
+
+
+def test_scan_deterministic(gpu_lib):
+    wl = synth.WORKLOADS["mini_k3_packed"].with_(L=1024)
+    prm = synth.params(wl, 6)
+    raw = synth.raw_inputs(wl, 6, device=DEV)
+    ids = synth.doc_ids(wl, 6, L=1024, mean_len=200.0)
+    y1, f1, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids)
+    y2, f2, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
