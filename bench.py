@@ -96,6 +96,9 @@ def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, se
         raw = synth.raw_inputs(wl, seed + k, device=dev)
         ids = synth.doc_ids(wl, seed + k).to(dev) if docs else None
         sets.append((raw, ids))
+    ws_bytes = ssd.ssd_chunk_scan_workspace_size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G,
+                                                 ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     xbc = torch.empty(wl.B, wl.L, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
     dt = torch.empty(wl.B, wl.L, wl.H, dtype=torch.float32, device=dev)
     y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
@@ -110,7 +113,7 @@ def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, se
         scan = lambda: ssd.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, prm["A"],
                                               H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=prm["D"], z=raw["z"],
                                               doc_ids=ids, init_state=raw["h0"] if h0 else None,
-                                              final_state=fs, y=y)
+                                              final_state=fs, y=y, workspace=ws)
         if timed:
             t_conv.around(conv)
             t_scan.around(scan)
@@ -137,6 +140,7 @@ def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, se
         "scan_bytes": sb, "conv_bytes": cb,
         "scan_GBs": sb / (scan_ms * 1e-3) / 1e9, "conv_GBs": cb / (conv_ms * 1e-3) / 1e9,
         "scan_head_tokens_per_s": wl.B * wl.L * wl.H / (scan_ms * 1e-3),
+        "scan_workspace_bytes": ws_bytes,
     }
 
 
@@ -268,7 +272,8 @@ def main():
                      "traffic": None, "launch_us": main_r["scan_us"], "algorithmic_bytes": main_r["scan_bytes"]},
         "kernels": {"scan_us": main_r["scan_us"], "conv_us": main_r["conv_us"], "scan_GBs": main_r["scan_GBs"],
                     "conv_GBs": main_r["conv_GBs"], "conv_frac": main_r["conv_GBs"] / HBM_PEAK_GBS,
-                    "scan_head_tokens_per_s": main_r["scan_head_tokens_per_s"]},
+                    "scan_head_tokens_per_s": main_r["scan_head_tokens_per_s"],
+                    "scan_workspace_bytes": main_r["scan_workspace_bytes"]},
         "cpu_baseline": cpu,
         "extra": extras,
     }

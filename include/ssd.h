@@ -138,10 +138,17 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
  * ssd_chunk_scan_fwd -- the SSD selective scan, chunk = 64.
  *
  * Computes y (and the final state) of the recurrence above for every
- * (b, h).  Inside a chunk the dual (quadratic) form is used; chunk states
- * are passed strictly in chunk order with the state kept on chip in fp32,
- * so a prefill split at a multiple of 64 tokens with the state carried is
- * bitwise identical to one call.
+ * (b, h).  Inside a chunk the dual (quadratic) form is used.
+ *
+ * Without a workspace (NULL, 0) chunk states are passed strictly in chunk
+ * order with the state kept on chip in fp32, so a prefill split at a
+ * multiple of 64 tokens with the state carried is bitwise identical to one
+ * call.  With a workspace of ssd_chunk_scan_workspace_size() bytes the
+ * sequence may additionally be cut into superchunks scanned in parallel:
+ * a first pass stores each superchunk's local end state and total decay in
+ * the workspace and the main pass folds them in (the state passing of the
+ * SSD paper's chunked algorithm, one level up).  Results then agree with the
+ * sequential pass to fp32 rounding, not bitwise.
  *
  *   x       T   [B][L][H*P]  row stride x_row_stride
  *   Bm, Cm  T   [B][L][G*N]  row strides B_row_stride, C_row_stride
@@ -156,8 +163,12 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
  *   init_state  f32 [B][H][P][N] or NULL (zero)
  *   final_state f32 [B][H][P][N] or NULL; may equal init_state (in place)
  *   y       f32 [B][L][H*P]  row stride y_row_stride; must not overlap inputs
- *   workspace, workspace_bytes: scratch of ssd_chunk_scan_workspace_size()
- *               bytes (the current design needs none: NULL, 0 is accepted)
+ *   workspace, workspace_bytes: NULL, 0 (sequential pass) or device scratch
+ *               of at least ssd_chunk_scan_workspace_size() bytes, 16-byte
+ *               aligned, owned by the caller and not read before it is
+ *               written; SSD_ERR_WORKSPACE if too small or misaligned.
+ *               Concurrent calls must not share one workspace.
+ * Row strides are in elements, >= the row width and <= 4194304.
  */
 int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
                        const void *x, int64_t x_row_stride,
@@ -172,7 +183,8 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
                        float *y, int64_t y_row_stride,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace ssd_chunk_scan_fwd needs for these sizes (0 today). */
+/* Bytes of workspace that let ssd_chunk_scan_fwd split the sequence for
+ * these sizes; 0 when no split pays (then the workspace is ignored). */
 size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
 
 /*

@@ -162,8 +162,9 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
 }
 
 size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
-    (void)B; (void)L; (void)H; (void)P; (void)N; (void)G; (void)dtype;
-    return 0;
+    (void)G; (void)dtype;
+    if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0) return 0;
+    return ssd::scan_workspace_bytes(B, L, H, P, N);
 }
 
 int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
@@ -202,11 +203,19 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
     TRY(check_ptr(fn, "init_state", init_state, false, true));
     TRY(check_ptr(fn, "final_state", final_state, false, true));
+    // A workspace enables the sequence split (when these sizes call for one);
+    // without one the scan is a single sequential pass over every (b, h).
     const size_t need = ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype);
-    if (workspace_bytes < need)
+    const bool split = workspace != nullptr && need > 0;
+    if (split && workspace_bytes < need)
         return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
                     workspace_bytes, need);
-    if (need > 0 && !workspace) return fail(SSD_ERR_NULL_ARG, "%s: workspace is NULL", fn);
+    if (split && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+    if (work && (x_row_stride > (1 << 22) || B_row_stride > (1 << 22) || C_row_stride > (1 << 22) ||
+                 z_row_stride > (1 << 22) || dt_row_stride > (1 << 22) ||
+                 y_row_stride > (1 << 22)))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
     if (work && y == final_state)
         return fail(SSD_ERR_BAD_SHAPE, "%s: y must not alias final_state", fn);
 
@@ -228,7 +237,13 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     a.doc = doc_ids;
     a.init_state = init_state; a.final_state = final_state;
     a.y = y; a.y_stride = y_row_stride;
-    (void)workspace;
+    a.K = 1; a.S = ((L + 63) / 64) * 64; a.hloc = nullptr; a.dec = nullptr;
+    if (split) {
+        ssd::scan_split(B, L, H, a.K, a.S);
+        const size_t u = (size_t)B * H * (a.K - 1);
+        a.hloc = static_cast<float*>(workspace);
+        a.dec = a.hloc + u * (size_t)P * N;
+    }
     return hip_status(fn, ssd::launch_scan(a, s));
 }
 

@@ -32,6 +32,10 @@ struct ScanArgs {
     const int32_t* doc;
     const float* init_state; float* final_state;
     float* y; int64_t y_stride;
+    // sequence split: K superchunks of S tokens (S a multiple of 64); K = 1 is
+    // one sequential pass.  hloc / dec: workspace for the K-1 local states.
+    int K, S;
+    float* hloc; float* dec;
 };
 
 struct StepArgs {
@@ -44,6 +48,9 @@ struct StepArgs {
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+// Sequence split chosen for these sizes (1 = none) and its superchunk length.
+void scan_split(int B, int L, int H, int& K, int& S);
+size_t scan_workspace_bytes(int B, int L, int H, int P, int N);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 // Copies n 16-byte words src -> dst (src == nullptr: zero fill); used for the
 // L = 0 state pass-through without a memset node.

@@ -104,14 +104,23 @@ def test_conv_full_mini_k3_sampled(gpu_lib):
 
 
 # ----------------------------------------------------------------------------- scan
-def run_scan(gpu_lib, wl, inp, prm, ids=None, final=True, dt_softplus=True):
+def workspace(gpu_lib, B, L, H, P, N, G, dtype):
+    """The scan's workspace (enables the sequence split); None if these sizes do not split."""
+    n = gpu_lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, 1 if dtype == "bf16" else 0)
+    return torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+
+
+def run_scan(gpu_lib, wl, inp, prm, ids=None, final=True, dt_softplus=True, split=False):
     g = lambda t: None if t is None else t.to(DEV)
     fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=DEV) if final else None
     dt = inp["dt_raw"].float()
+    ws = workspace(gpu_lib, wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, wl.dtype) if split else None
+    if split:
+        assert ws is not None, "these sizes should take the sequence split"
     y = gpu_lib.ssd_chunk_scan_fwd(g(inp["x"]), g(inp["Bm"]), g(inp["Cm"]), g(dt), g(prm["A"]), H=wl.H, P=wl.P,
                                    N=wl.N, G=wl.G, D=g(prm["D"]), z=g(inp["z"]), doc_ids=g(ids),
                                    init_state=g(inp["h0"]), final_state=fs, dt_softplus=dt_softplus,
-                                   dt_bias=g(prm["dt_bias"]))
+                                   dt_bias=g(prm["dt_bias"]), workspace=ws)
     torch.cuda.synchronize()
     return y, fs
 
@@ -163,6 +172,33 @@ def test_scan_parity_small(gpu_lib, dtype, N, G, H, L, docs, h0, gate):
     check(fs, fr, "final_state")
 
 
+SPLIT_CASES = [
+    # dtype, N, G, H, L, docs, h0, gate   (L long enough for the sequence split)
+    ("bf16", 64, 2, 4, 2000, True, True, True),
+    ("bf16", 128, 1, 2, 1537, False, True, True),
+    ("bf16", 16, 2, 2, 4096, True, False, True),
+    ("f32", 64, 1, 2, 1100, True, True, True),
+    ("f32", 32, 2, 4, 2048, False, True, False),
+]
+
+
+@pytest.mark.parametrize("dtype,N,G,H,L,docs,h0,gate", SPLIT_CASES)
+def test_scan_split_parity(gpu_lib, dtype, N, G, H, L, docs, h0, gate):
+    """The sequence-split path (pre-pass + superchunks) against the oracle."""
+    wl = small_wl(dtype, H=H, N=N, G=G, L=L, B=2, docs=docs, h0=h0, gate=gate)
+    _say(f"scan split {dtype} N={N} G={G} H={H} L={L} docs={docs} h0={h0} gate={gate}")
+    prm = synth.params(wl, 8)
+    inp = synth.scan_inputs(wl, 8)
+    ids = synth.doc_ids(wl, 8, mean_len=300.0) if docs else None
+    y, fs = run_scan(gpu_lib, wl, inp, prm, ids, split=True)
+    yr, fr = oracle_scan(wl, inp, prm, ids)
+    check = hp.assert_fp32 if dtype == "f32" else hp.assert_bf16
+    check(y, yr, "y")
+    check(fs, fr, "final_state")
+    y1, f1 = run_scan(gpu_lib, wl, inp, prm, ids, split=False)
+    check(y, y1, "split vs single pass y")
+
+
 def test_scan_adversarial_boundaries(gpu_lib):
     """Boundaries at t % 64 in {0, 1, 63}, documents of length 1-3, back-to-back boundaries."""
     wl = small_wl("bf16", H=4, N=64, G=2, L=320, B=2, docs=True, h0=True, gate=True)
@@ -198,7 +234,7 @@ def test_scan_empty_sequence_passes_state_through(gpu_lib):
 
 
 # ----------------------------------------------------------------------------- full workloads
-def gpu_forward(gpu_lib, wl, raw, prm, ids=None, conv_state=None, h0=None, final=True):
+def gpu_forward(gpu_lib, wl, raw, prm, ids=None, conv_state=None, h0=None, final=True, split=False):
     g = lambda t: None if t is None else t.to(DEV)
     HP, GN = wl.H * wl.P, wl.G * wl.N
     cs_out = torch.empty(raw["xbc_raw"].shape[0], 3, wl.conv_dim, dtype=wl.torch_dtype, device=DEV)
@@ -207,21 +243,23 @@ def gpu_forward(gpu_lib, wl, raw, prm, ids=None, conv_state=None, h0=None, final
                                    doc_ids=g(ids), conv_state_in=g(conv_state), conv_state_out=cs_out)
     B = xbc.shape[0]
     fs = torch.empty(B, wl.H, wl.P, wl.N, dtype=torch.float32, device=DEV) if final else None
+    ws = workspace(gpu_lib, B, xbc.shape[1], wl.H, wl.P, wl.N, wl.G, wl.dtype) if split else None
     y = gpu_lib.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, g(prm["A"]),
                                    H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=g(prm["D"]), z=g(raw["z"]), doc_ids=g(ids),
-                                   init_state=g(h0), final_state=fs)
+                                   init_state=g(h0), final_state=fs, workspace=ws)
     torch.cuda.synchronize()
     return y, fs, cs_out, xbc
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["single_pass", "seq_split"])
 @pytest.mark.parametrize("name", ["mini_k3_bf16", "mini_k3_packed", "large_layer_bf16"])
-def test_full_workload_sampled_rows(gpu_lib, name):
+def test_full_workload_sampled_rows(gpu_lib, name, split):
     wl = synth.WORKLOADS[name]
-    _say(f"full workload {name}")
+    _say(f"full workload {name} split={split}")
     prm = synth.params(wl, 0)
     raw = synth.raw_inputs(wl, 0, device=DEV)
     ids = synth.doc_ids(wl, 0) if wl.docs else None
-    y, fs, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids, h0=raw["h0"])
+    y, fs, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids, h0=raw["h0"], split=split)
     for b in (0, wl.B - 1):
         sl = slice(b, b + 1)
         yr, fr, _, xr, _ = oracle.forward(raw["xbc_raw"][sl].cpu(), prm["conv_w"], None, raw["dt_raw"][sl].cpu(),
@@ -235,11 +273,12 @@ def test_full_workload_sampled_rows(gpu_lib, name):
         _say(f"  row {b}: max|dy|={err:.3e} max|dstate|={errs:.3e} rms(y)={hp.rms(yr):.3e}")
 
 
-def test_doc_isolation_bitwise(gpu_lib):
+@pytest.mark.parametrize("split", [False, True], ids=["single_pass", "seq_split"])
+def test_doc_isolation_bitwise(gpu_lib, split):
     """Replacing every input of the earlier documents of a row (x100 magnitudes, other dt) leaves every
     output bit of the later documents, and the final state, unchanged (+0 and -0 equal)."""
     wl = synth.WORKLOADS["mini_k3_packed"].with_(L=2048, B=3)
-    _say("doc isolation bitwise")
+    _say(f"doc isolation bitwise split={split}")
     prm = synth.params(wl, 1)
     raw = synth.raw_inputs(wl, 1)
     ids = torch.zeros(wl.B, wl.L, dtype=torch.int32)
@@ -247,7 +286,7 @@ def test_doc_isolation_bitwise(gpu_lib):
     for b, cuts in splits.items():
         for c in cuts:
             ids[b, c:] += 1
-    base, fbase, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids)
+    base, fbase, _, _ = gpu_forward(gpu_lib, wl, raw, prm, ids, split=split)
     gen = torch.Generator().manual_seed(11)
     for b, cuts in splits.items():
         for k in (cuts[0], cuts[len(cuts) // 2], cuts[-1]):
@@ -256,7 +295,7 @@ def test_doc_isolation_bitwise(gpu_lib):
             pert["xbc_raw"][b, :k] = noise.to(wl.torch_dtype)
             pert["dt_raw"][b, :k] = (torch.randn(k, wl.H, generator=gen) * 3.0).to(wl.torch_dtype)
             pert["z"][b, :k] = (torch.randn(k, wl.H * wl.P, generator=gen) * 100.0).to(wl.torch_dtype)
-            y, fs, _, _ = gpu_forward(gpu_lib, wl, pert, prm, ids)
+            y, fs, _, _ = gpu_forward(gpu_lib, wl, pert, prm, ids, split=split)
             later = base[b, k:], y[b, k:]
             assert torch.equal(later[0], later[1]), f"row {b}: outputs after boundary {k} changed"
             assert torch.equal(fbase[b], fs[b]), f"row {b}: final state changed (boundary {k})"
