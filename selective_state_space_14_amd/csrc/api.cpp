@@ -164,7 +164,7 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
 size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
     (void)G; (void)dtype;
     if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0) return 0;
-    return ssd::scan_workspace_bytes(B, L, H, P, N);
+    return ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
 }
 
 int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
@@ -239,7 +239,7 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     a.y = y; a.y_stride = y_row_stride;
     a.K = 1; a.S = ((L + 63) / 64) * 64; a.hloc = nullptr; a.dec = nullptr;
     if (split) {
-        ssd::scan_split(B, L, H, a.K, a.S);
+        ssd::scan_split(B, L, H, N, G, dtype, a.K, a.S);
         const size_t u = (size_t)B * H * (a.K - 1);
         a.hloc = static_cast<float*>(workspace);
         a.dec = a.hloc + u * (size_t)P * N;

@@ -34,6 +34,7 @@
 // LDS holds B (row-major and transposed), C, X^T, (w o X)^T, the M^T tiles
 // and the chunk's cs/dt/segment arrays; the next chunk's global loads are
 // issued right after staging, so they fly during the contractions.
+#include <algorithm>
 #include <type_traits>
 
 #include "ssd_device.hpp"
@@ -513,21 +514,39 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
 }
 
 // ============================================================================
-// bf16 kernel: LDS-DMA pipeline.
+// bf16 kernel: every per-chunk input is staged by LDS DMA.
 //
-// B, C and this head's X rows of a chunk stream from HBM straight into
-// row-major LDS tiles with global_load_lds (16 bytes per lane, lane-linear
-// destination), two chunk stages deep: the copy of chunk c+1 is in flight
-// while chunk c computes, and no registers or VALU are spent on staging.
-// Transposed operands (B^T for the chunk state, X^T and (w o X)^T) come from
-// the same row-major tiles through ds_read_b64_tr_b16: in each 16-lane group,
-// result lane j element e is element (j mod 4) of source lane 4e + j/4, so a
-// lane (q, m) that addresses row 4q + m/4, column 4(m mod 4) of a tile
-// receives column m, rows 4q..4q+3 -- exactly the operand fragment of the
-// transposed tile.  Two barriers per chunk; per-token scalars are double
-// buffered so wave 0 can publish chunk c+1's while others finish chunk c.
+// A workgroup owns HPW heads that share one B/C group (4 waves per head; wave
+// w -> head w / 4, channels 16 (w mod 4) .. +16) and one superchunk of one
+// batch row.  B, C and the heads' X rows of a chunk stream from HBM straight
+// into row-major LDS tiles with global_load_lds (16 bytes per lane, lane-
+// linear destination) one chunk ahead of the compute, into the other of two
+// stages.  B and C are staged once for the HPW heads and each G^T tile
+// (B C^T) is built once and turned into every head's M^T tile.  Transposed
+// operands (B^T for the chunk state, X^T and (w o X)^T) come from the same
+// row-major tiles through ds_read_b64_tr_b16: in each 16-lane group, result
+// lane j element e is element (j mod 4) of source lane 4e + j/4, so a lane
+// (q, m) that addresses row 4q + m/4, column 4(m mod 4) of a tile receives
+// column m, rows 4q..4q+3 -- the operand fragment of the transposed tile.
+// z (per wave: its 16 channels) and, for the head's lead wave, dt and the
+// document ids also arrive by DMA, into wave-private buffers refilled right
+// after they are read.
+//
+// Nothing in the chunk loop is an ordinary global load, so the compiler has
+// no reason to wait on the vector-memory counter there; the waits are explicit
+// and rely on one wave's vector-memory operations completing in issue order.
+// Per chunk c a wave issues, in this order:
+//   [lead: dt, doc ids of c+1] -- barrier A -- [B, C, X copies of c+1]
+//   -- barrier B -- [4 y stores of c] [2 z copies of c+1]
+// so at the top of chunk c+1 "its B/C/X (and dt/doc) have landed" is "at most
+// 6 newer operations are outstanding", and z of chunk c is in once at most
+// (this wave's B/C/X copies of c+1) remain.  y goes out through buffer stores
+// whose range check drops rows past the unit's end, so every chunk issues
+// exactly 4.  Barriers wait only for LDS traffic (lgkmcnt), never for the
+// copies in flight.
 // ============================================================================
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 #define SSD_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ FragBF tr_read(const unsigned char* lds_base, uint32_t byte_off) {
@@ -541,8 +560,55 @@ __device__ __forceinline__ FragBF plain_read(const unsigned char* p) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     return {v.x, v.y};
 }
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
-    __builtin_amdgcn_global_load_lds(g, (SSD_LDS void*)lds, 16, 0, 0);
+// LDS DMA: lane l's 16 (or 4) bytes at base + voff land at lds + 16 l (4 l).
+// base and lds are wave-uniform.  Written as inline assembly so the compiler
+// does not model the copy: it would otherwise wait for every copy in flight
+// before any LDS read it cannot prove disjoint.  M0 (the LDS destination) is
+// saved and restored inside the statement; one wait state separates its write
+// from the copy.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const SSD_LDS unsigned char*)p);
+}
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, const unsigned char* lds) {
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
+        : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, const unsigned char* lds) {
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
+        : "memory");
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
+// then s_barrier.  (A fence-based barrier would also wait for the copies in
+// flight.)  The memory clobber keeps the compiler from moving accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// At most n of this wave's vector-memory operations still outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 16, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 
 // XOR swizzle of 16-byte pieces inside a tile row of RB bytes: piece c of row r
@@ -561,64 +627,71 @@ struct Swz {
     }
 };
 
-template <int N, int MODE>
+template <int N, int MODE, int HPW>
 struct LdsBf {
-    static constexpr int RB = N * 2;                  // bytes per B / C row
-    static constexpr int XB = 128;                    // bytes per X row (64 channels)
-    static constexpr int TB = Q * RB;                 // B or C tile
-    static constexpr int TX = Q * XB;                 // X tile
     static constexpr bool FULL = MODE == kFull;
-    static constexpr int oB = 0, oC = TB, oX = FULL ? 2 * TB : TB;
-    static constexpr int STAGE = oX + TX;
-    // Copies run NSTAGE-1 chunks ahead; three stages where two workgroups
-    // still fit a CU's 160 KiB, else two.
-    static constexpr int NSTAGE = (3 * STAGE + (FULL ? kNumMTiles * 512 : 0) + 2560) * 2 <= 163840 ? 3 : 2;
-    static constexpr int oM = NSTAGE * STAGE;         // M^T tiles (kFull) [10][64][4] bf16
-    static constexpr int oS = oM + (FULL ? kNumMTiles * 256 * 2 : 0);   // scalars [2][5][Q] fp32
-    static constexpr int bytes = oS + 2 * 5 * Q * 4;
-    // vector-memory instructions one wave issues per chunk: the plain loads
-    // (dt, two doc ids, four z rows in kFull) and its share of the copies;
-    // the fewest over the four waves, so a wait for "at most this many newer
-    // operations outstanding" is never too lenient
+    static constexpr int NW = 4 * HPW;                // waves
+    static constexpr int RB = N * 2;                  // bytes per B / C row
+    static constexpr int XB = 128;                    // bytes per X row of one head (64 channels)
+    static constexpr int TB = Q * RB;                 // B or C tile
+    static constexpr int TX = Q * XB;                 // X tile of one head
+    static constexpr int oB = 0, oC = TB, oX = FULL ? 2 * TB : TB;   // then the HPW X tiles
+    static constexpr int STAGE = oX + HPW * TX;
+    static constexpr int MB = kNumMTiles * 512;       // one head's M^T tiles, bf16 fragments
+    static constexpr int oM = 2 * STAGE;
+    static constexpr int ZW = Q * 32;                 // one wave's z tile [Q][16] bf16
+    static constexpr int oZ = oM + (FULL ? HPW * MB : 0);
+    static constexpr int oD = oZ + (FULL ? NW * ZW : 0);   // per head: dt, doc, doc of the previous token [Q] each
+    static constexpr int oS = oD + HPW * 3 * Q * 4;
+    // per-token scalars of one chunk, floats: per head cs, dt, eo, w [Q] each;
+    // then the segment start per token [Q] (int); cs_end per head; last_seg
+    static constexpr int SC_SEG = 4 * HPW * Q;
+    static constexpr int SC_END = SC_SEG + Q;
+    static constexpr int SC_LAST = SC_END + HPW;
+    static constexpr int SCW = (SC_LAST + 1 + 3) / 4 * 4;
+    static constexpr int bytes = oS + 2 * SCW * 4;
+    // 16-byte copies per chunk: rows per instruction of a B/C tile and of an X tile
     static constexpr int RPI_B = 64 / (RB / 16);
-    static constexpr int nB_min = (Q / RPI_B) / kWaves;               // floor: waves that get fewer
-    static constexpr int VM_PER_CHUNK = 3 + (FULL ? 4 : 0) + nB_min * (FULL ? 2 : 1) + (Q / 8) / kWaves;
+    static constexpr int NI_B = Q / RPI_B;
+    static constexpr int NI_X = Q / 8;
+    static constexpr int NI_BC = NI_B * (FULL ? 2 : 1);
+    static constexpr int NI = NI_BC + HPW * NI_X;
+    static constexpr int NI_W = (NI + NW - 1) / NW;   // most copies a wave issues
+    static constexpr int NI_MIN = NI / NW;            // fewest
+    static_assert(bytes <= 163840, "LDS plan exceeds a CU");
 };
 
-// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their maximum).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-template <int N, int MODE, bool SP>
-__global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
-    using LD = LdsBf<N, MODE>;
+template <int N, int MODE, bool SP, int HPW>
+__global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
+    using LD = LdsBf<N, MODE, HPW>;
     constexpr int NT = N / 16;
     constexpr bool FULL = MODE == kFull;
+    constexpr int NW = LD::NW;
     constexpr int RB = LD::RB, XB = LD::XB;
-    constexpr int CPR_B = RB / 16, RPI_B = 64 / CPR_B;    // 16-byte pieces per B row, rows per DMA
-    constexpr int RPI_X = 64 / (XB / 16);                  // 8 rows per X DMA
+    constexpr int CPR_B = RB / 16;
     using SB = Swz<RB>;
     using SX = Swz<XB>;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float* scal = reinterpret_cast<float*>(smem + LD::oS);   // [2][5][Q]: cs, dt, seg, eo, w
+    float* scal = reinterpret_cast<float*>(smem + LD::oS);   // [2][SCW]
 
     const int L = a.L, H = a.H, G = a.G;
+    const int HQ = H / HPW;
     const int KU = FULL ? a.K : a.K - 1;
-    const int id = xcd_remap(blockIdx.x, a.B * H * KU);
-    const int h = id % H;
-    const int k = (id / H) % KU;
-    const int b = id / (H * KU);
-    const int g = h / (H / G);
+    const int id = xcd_remap(blockIdx.x, a.B * HQ * KU);
+    const int hq = id % HQ;
+    const int k = (id / HQ) % KU;
+    const int b = id / (HQ * KU);
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
+    const int hh = wave >> 2;                  // head of this wave within the workgroup
+    const int h = hq * HPW + hh;
+    const int g = (hq * HPW) / (H / G);
+    const bool lead = (wave & 3) == 0;         // computes its head's per-token scalars
     const int q4 = lane >> 4;
     const int j16 = lane & 15;
-    const int p0 = wave * 16;
+    const int p0 = (wave & 3) * 16;
     const float A2 = a.A[h] * kLog2e;
     const float Dh = a.D ? a.D[h] : 0.0f;
     const float dtb = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h] : 0.0f;
@@ -626,65 +699,91 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int tend = min(tbeg + a.S, L);
     const int tl = tend - 1;
     const bool gate = a.z != nullptr;
+    const bool docs = a.doc != nullptr;
 
-    const uint16_t* xbase = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)h * 64;
-    const uint16_t* zbase = gate ? static_cast<const uint16_t*>(a.z) + (size_t)b * L * a.z_stride + (size_t)h * 64 : xbase;
-    const int64_t zs = gate ? a.z_stride : a.x_stride;
+    // ---- global bases (uniform)
+    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)hq * HPW * 64;
+    const uint16_t* zbase = gate ? static_cast<const uint16_t*>(a.z) + (size_t)b * L * a.z_stride + (size_t)h * 64 + p0
+                                 : xhead + hh * 64 + p0;   // stand-in rows keep the operation count fixed
+    const int Zs2 = (int)(gate ? a.z_stride : a.x_stride) * 2;
     const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
     const uint16_t* Cbase = static_cast<const uint16_t*>(a.Cm) + (size_t)b * L * a.C_stride + (size_t)g * N;
     const float* dtbase = a.dt + (size_t)b * L * a.dt_stride + h;
-    const int32_t* docg = a.doc ? a.doc + (size_t)b * L : nullptr;
-    const int32_t* docsrc = docg ? docg : reinterpret_cast<const int32_t*>(a.dt) + (size_t)b * L;
-    float* yg = a.y + (size_t)b * L * a.y_stride + h * 64 + p0 + 4 * q4;
+    const int32_t* docbase = a.doc + (size_t)b * L;
+    float* ybase = a.y + (size_t)b * L * a.y_stride + h * 64;
+    const int Ds4 = (int)a.dt_stride * 4;
+    const int Ys = (int)a.y_stride;
 
-    // ---- chunk t0 -> LDS stage st (DMA) and the per-lane registers (dt, doc, z);
-    // register sets rotate with the stages (set s holds chunk c with c % NSTAGE == s)
-    constexpr int NSTAGE = LD::NSTAGE;
-    float r_dt[NSTAGE];
-    int r_d0[NSTAGE], r_d1[NSTAGE];
-    uint2 r_z[NSTAGE][4];
-    // Addresses: a uniform chunk base (t0 * stride, scalar) plus a 32-bit
-    // per-lane byte offset of row * stride (rows clamp to the unit's end).
-    const int Bs = (int)a.B_stride, Cs = (int)a.C_stride, Xs = (int)a.x_stride, Zs = (int)zs, Ds = (int)a.dt_stride;
-    auto issue_chunk = [&](int t0, int st, float& o_dt, int& o_d0, int& o_d1, uint2* o_z) {
+    unsigned char* zbuf = smem + LD::oZ + wave * LD::ZW;              // this wave's z tile
+    unsigned char* dbuf = smem + LD::oD + hh * 3 * Q * 4;             // this head's dt, doc, doc-1
+
+    // Copy slots of this wave: slot j is copy instruction wave + NW j of the
+    // chunk (B tile, then C tile, then the X tiles).  Per slot: the uniform
+    // source base and row stride, the LDS destination, and the lane's tile row
+    // and column byte offset (the swizzled piece this lane's 16 bytes land in).
+    const char* s_base[LD::NI_W];
+    int s_stride[LD::NI_W];        // bytes per row
+    uint32_t s_lds[LD::NI_W];
+    int s_row[LD::NI_W];
+    uint32_t s_col[LD::NI_W];
+    bool s_on[LD::NI_W];
+#pragma unroll
+    for (int j = 0; j < LD::NI_W; ++j) {
+        const int i = wave + NW * j;
+        s_on[j] = i < LD::NI;
+        if (i < LD::NI_B || (FULL && i < LD::NI_BC)) {
+            const bool isC = i >= LD::NI_B;
+            const int ins = isC ? i - LD::NI_B : i;
+            s_base[j] = reinterpret_cast<const char*>(isC ? Cbase : Bbase);
+            s_stride[j] = (int)(isC ? a.C_stride : a.B_stride) * 2;
+            s_lds[j] = (isC ? LD::oC : LD::oB) + ins * 1024;
+            const int r = ins * LD::RPI_B + lane / CPR_B;
+            s_row[j] = r;
+            s_col[j] = (uint32_t)(((lane % CPR_B) ^ SB::f(r)) * 16);
+        } else {
+            const int ix = s_on[j] ? i - LD::NI_BC : 0;
+            const int e = ix / LD::NI_X, ins = ix % LD::NI_X;
+            s_base[j] = reinterpret_cast<const char*>(xhead + e * 64);
+            s_stride[j] = (int)a.x_stride * 2;
+            s_lds[j] = LD::oX + e * LD::TX + ins * 1024;
+            const int r = ins * 8 + lane / (XB / 16);
+            s_row[j] = r;
+            s_col[j] = (uint32_t)(((lane % (XB / 16)) ^ SX::f(r)) * 16);
+        }
+    }
+    // B, C, X copies of the chunk at t0 into stage st; rows clamp to the unit's end
+    auto issue_tiles = [&](int t0, int st) {
         const int lim = tl - t0;
         unsigned char* base = smem + st * LD::STAGE;
-        const char* Bc = reinterpret_cast<const char*>(Bbase + (size_t)t0 * a.B_stride);
-        const char* Cc = reinterpret_cast<const char*>(Cbase + (size_t)t0 * a.C_stride);
-        const char* Xc = reinterpret_cast<const char*>(xbase + (size_t)t0 * a.x_stride);
-        // plain loads first, then (after a compiler fence) the copies, so the
-        // copies of a chunk are the newest vector-memory operations it issues
-        const int rowl = min(lane, lim);
-        o_dt = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(dtbase + (size_t)t0 * a.dt_stride) +
-                                               (uint32_t)(rowl * Ds) * 4);
-        o_d0 = docsrc[t0 + rowl];
-        o_d1 = docsrc[max(t0 + rowl - 1, 0)];
-        if (FULL) {
-            const char* Zc = reinterpret_cast<const char*>(zbase + (size_t)t0 * zs + p0 + 4 * q4);
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const int row = min(16 * ti + j16, lim);
-                o_z[ti] = *reinterpret_cast<const uint2*>(Zc + (uint32_t)(row * Zs) * 2);
+        for (int j = 0; j < LD::NI_W; ++j) {
+            if (s_on[j]) {
+                const char* src = s_base[j] + (size_t)t0 * s_stride[j];
+                dma16(src, (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j], base + s_lds[j]);
             }
         }
-        __asm__ volatile("" ::: "memory");
-        for (int ins = wave; ins < Q / RPI_B; ins += kWaves) {
-            const int r = ins * RPI_B + lane / CPR_B;            // tile row of this lane's slot
-            const int col = (((lane % CPR_B) ^ SB::f(r))) * 8;   // piece stored in that slot
-            const int row = min(r, lim);
-            dma16(Bc + (uint32_t)(row * Bs + col) * 2, base + LD::oB + ins * 1024);
-            if (FULL) dma16(Cc + (uint32_t)(row * Cs + col) * 2, base + LD::oC + ins * 1024);
+    };
+    // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
+    auto issue_scalars = [&](int t0) {
+        const int rowl = min(lane, tl - t0);
+        dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
+        if (docs) {
+            dma4(docbase, (uint32_t)(t0 + rowl) * 4, dbuf + Q * 4);
+            dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, dbuf + 2 * Q * 4);
         }
-        for (int ins = wave; ins < Q / RPI_X; ins += kWaves) {
-            const int r = ins * RPI_X + lane / (XB / 16);
-            const int col = ((lane % (XB / 16)) ^ SX::f(r)) * 8;
-            const int row = min(r, lim);
-            dma16(Xc + (uint32_t)(row * Xs + col) * 2, base + LD::oX + ins * 1024);
+    };
+    // z of this wave's 16 channels: row r of the chunk -> zbuf + 32 r
+    auto issue_z = [&](int t0) {
+        const int lim = tl - t0;
+        const char* Zc = reinterpret_cast<const char*>(zbase + (size_t)t0 * (Zs2 / 2));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = min(32 * i + (lane >> 1), lim);
+            dma16(Zc, (uint32_t)(row * Zs2) + (lane & 1) * 16, zbuf + i * 1024);
         }
-        __asm__ volatile("" ::: "memory");
     };
 
-    // ---- initial state (see the generic kernel)
+    // ---- initial state: the given one, then the superchunks before k folded in
     f32x4 Hs[NT];
     const size_t st_off = (((size_t)b * H + h) * 64 + p0 + j16) * N + 4 * q4;
 #pragma unroll
@@ -710,76 +809,75 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
                 Hs[nt][3] = dj < 0.0f ? v.w : fmaf(dj, Hs[nt][3], v.w);
             }
         }
+        // settle the state loads here, before any copy is in flight
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Hs[nt]));
     }
     float log2dec = 0.0f;
     bool reset = false;
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
-#pragma unroll
-    for (int j = 0; j < NSTAGE - 1; ++j)
-        if (j < nchunks) issue_chunk(tbeg + j * Q, j, r_dt[j], r_d0[j], r_d1[j], r_z[j]);
+    if (nchunks > 0) {
+        if (lead) issue_scalars(tbeg);
+        issue_tiles(tbeg, 0);
+        if (FULL) issue_z(tbeg);
+    }
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
-        const int st = c % NSTAGE;
+        const int st = c & 1;
+        const bool more = c + 1 < nchunks;
         const unsigned char* sB = smem + st * LD::STAGE + LD::oB;
         const unsigned char* sC = smem + st * LD::STAGE + LD::oC;
-        const unsigned char* sX = smem + st * LD::STAGE + LD::oX;
-        float* sc = scal + (c & 1) * 5 * Q;        // this chunk's scalars
-        const bool tok_ok = t0 + lane < tend;
-        float c_dt = r_dt[0];
-        int c_d0 = r_d0[0], c_d1 = r_d1[0];
-        uint2 z_cur[4] = {r_z[0][0], r_z[0][1], r_z[0][2], r_z[0][3]};
-#pragma unroll
-        for (int j = 1; j < NSTAGE; ++j)
-            if (st == j) {
-                c_dt = r_dt[j];
-                c_d0 = r_d0[j];
-                c_d1 = r_d1[j];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) z_cur[ti] = r_z[j][ti];
-            }
-        // ---- segmented cumulative sum of dt*A (log2 domain), lane = token
-        float dtl = c_dt;
-        if (SP) dtl = softplus_f(dtl + dtb);
-        if (!tok_ok) dtl = 0.0f;
-        const int bnd = (docg && tok_ok && t0 + lane > 0 && c_d0 != c_d1) ? 1 : 0;
-        float cs = dtl * A2;
-        int seg = bnd ? lane : -1;
-        wave_segscan(cs, bnd, seg);
-        const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
-        const int last_seg = __builtin_amdgcn_readlane(seg, 63);
-        const bool has_bnd = last_seg >= 0;
-        const int wseg = has_bnd ? last_seg : 0;
-        if (wave == 0) {
-            sc[lane] = cs;
-            sc[Q + lane] = dtl;
-            reinterpret_cast<int*>(sc)[2 * Q + lane] = seg < 0 ? 0 : seg;
-            sc[3 * Q + lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
-            sc[4 * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
-        }
-        // this wave's copies of chunk c have landed: only chunk c+1's operations
-        // (issued after them, NSTAGE = 3) or nothing (last chunk, NSTAGE = 2) may
-        // still be outstanding; newer stores only make the wait stricter
-        if (NSTAGE == 3 && c + 1 < nchunks)
-            wait_vmcnt<LD::VM_PER_CHUNK>();
-        else
+        const unsigned char* sX = smem + st * LD::STAGE + LD::oX + hh * LD::TX;
+        float* sc = scal + st * LD::SCW;           // this chunk's scalars
+        float* sch = sc + hh * 4 * Q;              // ... of this wave's head: cs, dt, eo, w
+
+        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed: only
+        // the y stores of chunk c-1 and the z copies of chunk c may be newer
+        if (FULL) {
+            if (c == 0) wait_vmcnt<2>();
+            else wait_vmcnt<6>();
+        } else {
             wait_vmcnt<0>();
-        __syncthreads();                 // chunk c tiles + scalars visible; chunk c-1 readers done
-        {
-            const int cn = c + NSTAGE - 1;    // chunk whose copies start now, into the stage chunk c-1 used
-            const int sn = cn % NSTAGE;
-            if (cn < nchunks) {
-#pragma unroll
-                for (int j = 0; j < NSTAGE; ++j)
-                    if (sn == j) issue_chunk(tbeg + cn * Q, j, r_dt[j], r_d0[j], r_d1[j], r_z[j]);
+        }
+        // ---- lead waves: segmented cumulative sum of dt*A (log2 domain), lane = token
+        if (lead) {
+            const bool tok_ok = t0 + lane < tend;
+            float dtl = reinterpret_cast<const float*>(dbuf)[lane];
+            const int d0 = reinterpret_cast<const int*>(dbuf)[Q + lane];
+            const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
+            lds_wait();
+            if (more) issue_scalars(t0 + Q);
+            if (SP) dtl = softplus_f(dtl + dtb);
+            if (!tok_ok) dtl = 0.0f;
+            const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
+            float cs = dtl * A2;
+            int seg = bnd ? lane : -1;
+            wave_segscan(cs, bnd, seg);
+            const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
+            const int last_seg = __builtin_amdgcn_readlane(seg, 63);
+            const int wseg = last_seg >= 0 ? last_seg : 0;
+            sch[lane] = cs;
+            sch[Q + lane] = dtl;
+            sch[2 * Q + lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
+            sch[3 * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
+            if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_SEG + lane] = seg < 0 ? 0 : seg;
+            if (lane == 0) {
+                sc[LD::SC_END + hh] = cs_end;
+                if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
             }
         }
+        lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
+        if (more) issue_tiles(t0 + Q, st ^ 1);
+        const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
+        const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
+        const bool has_bnd = last_seg >= 0;
 
         if (FULL) {
             unsigned char* sM = smem + LD::oM;
-            // ---- M^T tiles: G^T = B C^T (plain row reads), decay, mask -> bf16 fragments
-            for (int kt = wave; kt < kNumMTiles; kt += kWaves) {
+            // ---- G^T = B C^T once per tile, then each head's decay and mask -> M^T fragments
+            for (int kt = wave; kt < kNumMTiles; kt += NW) {
                 int si, ti;
                 mtile(kt, si, ti);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -795,40 +893,55 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
                     acc = mma_bf16(acc, a0, a1, b0, b1);
                 }
                 const int t = 16 * ti + j16;
-                const float cst = sc[t];
-                const int segt = reinterpret_cast<const int*>(sc)[2 * Q + t];
-                const float4 css = *reinterpret_cast<const float4*>(sc + 16 * si + 4 * q4);
-                const float4 dts = *reinterpret_cast<const float4*>(sc + Q + 16 * si + 4 * q4);
-                f32x4 m;
+                const int segt = reinterpret_cast<const int*>(sc)[LD::SC_SEG + t];
+                bool ok[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * si + 4 * q4 + r;
-                    const bool ok = (si < ti || s <= t) && (!has_bnd || s >= segt);
-                    m[r] = ok ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
+                    ok[r] = (si < ti || s <= t) && (!has_bnd || s >= segt);
                 }
-                *reinterpret_cast<FragBF*>(sM + (kt * 256 + lane * 4) * 2) = frag_from_f32(m);
+#pragma unroll
+                for (int e = 0; e < HPW; ++e) {
+                    const float* sce = sc + e * 4 * Q;
+                    const float cst = sce[t];
+                    const float4 css = *reinterpret_cast<const float4*>(sce + 16 * si + 4 * q4);
+                    const float4 dts = *reinterpret_cast<const float4*>(sce + Q + 16 * si + 4 * q4);
+                    f32x4 m;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        m[r] = ok[r] ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
+                    *reinterpret_cast<FragBF*>(sM + e * LD::MB + kt * 512 + lane * 8) = frag_from_f32(m);
+                }
             }
             FragBF hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = frag_from_f32(Hs[nt]);
-            __syncthreads();   // all M^T tiles are in LDS
+            lds_barrier();   // B: all M^T tiles are in LDS
+            // z of chunk c has landed: only this wave's copies of chunk c+1 (and,
+            // in lead waves, its dt / doc ids) may be newer
+            if (more) wait_vmcnt<LD::NI_MIN>();
+            else wait_vmcnt<0>();
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, output
-            float* yc = yg + (size_t)t0 * a.y_stride;
-            const int Ys = (int)a.y_stride;
+            const unsigned char* sMh = sM + hh * LD::MB;
+            const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                ybase + (size_t)t0 * a.y_stride, 0, (tend - t0) * Ys * 4, 0x00020000);
             // f of the transpose-read rows does not depend on the 16-row block sb
             const uint32_t xtr = SX::off(4 * q4 + j16 / 4, p0 + 4 * (j16 % 4));
+            uint2 zr[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) zr[ti] = *reinterpret_cast<const uint2*>(zbuf + (16 * ti + j16) * 32 + q4 * 8);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
                     const FragBF a0 = tr_read(sX, xtr + 16 * sb * XB);
-                    const FragBF b0 = plain_read(sM + (mtile_index(sb, ti) * 256 + lane * 4) * 2);
+                    const FragBF b0 = plain_read(sMh + mtile_index(sb, ti) * 512 + lane * 8);
                     FragBF a1 = {0u, 0u}, b1 = {0u, 0u};
                     if (sb + 1 <= ti) {
                         a1 = tr_read(sX, xtr + 16 * (sb + 1) * XB);
-                        b1 = plain_read(sM + (mtile_index(sb + 1, ti) * 256 + lane * 4) * 2);
+                        b1 = plain_read(sMh + mtile_index(sb + 1, ti) * 512 + lane * 8);
                     }
                     yd = mma_bf16(yd, a0, a1, b0, b1);
                 }
@@ -844,23 +957,22 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
                     yo = mma_bf16(yo, hf[nb], h1, c0, c1);
                 }
                 const int t = 16 * ti + j16;
-                const float eo = sc[3 * Q + t];
+                const float eo = sch[2 * Q + t];
                 const uint2 xr = *reinterpret_cast<const uint2*>(sX + SX::off(t, p0 + 4 * q4));
                 const float xs[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
-                const float zsv[4] = {bf16_lo(z_cur[ti].x), bf16_hi(z_cur[ti].x), bf16_lo(z_cur[ti].y),
-                                      bf16_hi(z_cur[ti].y)};
-                float o[4];
+                const float zsv[4] = {bf16_lo(zr[ti].x), bf16_hi(zr[ti].x), bf16_lo(zr[ti].y), bf16_hi(zr[ti].y)};
+                u32x4_t o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float v = fmaf(eo, yo[r], yd[r]);
                     v = fmaf(Dh, xs[r], v);
-                    if (gate) v *= silu_f(zsv[r]);
-                    o[r] = v;
+                    o[r] = __float_as_uint(gate ? v * silu_f(zsv[r]) : v);
                 }
-                if (t0 + t < tend)
-                    *reinterpret_cast<float4*>(reinterpret_cast<char*>(yc) + (uint32_t)(t * Ys) * 4) =
-                        make_float4(o[0], o[1], o[2], o[3]);
+                // rows past the unit's end fall outside the buffer range and are dropped
+                __builtin_amdgcn_raw_buffer_store_b128(o, yr, (uint32_t)(t * Ys + p0 + 4 * q4) * 4, 0, 0);
             }
+            lds_wait();                  // z of chunk c is read before its buffer is refilled
+            if (more) issue_z(t0 + Q);
         }
 
         // ---- chunk state S = B^T (w o X) from the row-major tiles via transpose reads
@@ -870,12 +982,14 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 const FragBF xf = tr_read(sX, xtr + 16 * sb * XB);
-                const float4 w = *reinterpret_cast<const float4*>(sc + 4 * Q + 16 * sb + 4 * q4);
+                const float4 w = *reinterpret_cast<const float4*>(sch + 3 * Q + 16 * sb + 4 * q4);
                 xw[sb].a = pack_bf16x2(w.x * bf16_lo(xf.a), w.y * bf16_hi(xf.a));
                 xw[sb].b = pack_bf16x2(w.z * bf16_lo(xf.b), w.w * bf16_hi(xf.b));
             }
         }
-        const float dec = fast_exp2(cs_end);
+        // a chunk holding a document start drops the carried state: decay 0
+        // (a multiply by exactly zero of a finite state, so the result is S)
+        const float dec = has_bnd ? 0.0f : fast_exp2(cs_end);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const uint32_t btr = SB::off(4 * q4 + j16 / 4, 16 * nt + 4 * (j16 % 4));
@@ -886,12 +1000,8 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
                 const FragBF a1 = tr_read(sB, btr + 16 * (sb + 1) * RB);
                 acc = mma_bf16(acc, a0, a1, xw[sb], xw[sb + 1]);
             }
-            if (has_bnd) {
-                Hs[nt] = acc;
-            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Hs[nt][r] = fmaf(dec, Hs[nt][r], acc[r]);
-            }
+            for (int r = 0; r < 4; ++r) Hs[nt][r] = fmaf(dec, Hs[nt][r], acc[r]);
         }
         if (!FULL) {
             log2dec += cs_end;
@@ -912,27 +1022,42 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             *reinterpret_cast<float4*>(hl + 16 * nt) = make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-        if (tid == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+        if (lead && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
     }
 }
 
-template <int N, int MODE, bool SP>
-hipError_t launch_scan_bf16_sp(const ScanArgs& a, int units, hipStream_t stream) {
-    const size_t lds = LdsBf<N, MODE>::bytes;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, MODE, SP>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+template <int N, int MODE, bool SP, int HPW>
+hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, MODE, SP, HPW>);
+    const size_t lds = LdsBf<N, MODE, HPW>::bytes;
+    static bool checked = false;
+    if (!checked) {
+        // The kernel's explicit vector-memory waits count only its own copies,
+        // stores and loads: register spills would add uncounted operations.
+        hipFuncAttributes fa;
+        hipError_t e = hipFuncGetAttributes(&fa, fn);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        if (fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, MODE, SP>), dim3(units), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, MODE, SP, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
 }
-template <int N, int MODE>
+template <int N, int MODE, int HPW>
 hipError_t launch_scan_bf16_mode(const ScanArgs& a, int units, hipStream_t stream) {
-    return a.dt_softplus ? launch_scan_bf16_sp<N, MODE, true>(a, units, stream)
-                         : launch_scan_bf16_sp<N, MODE, false>(a, units, stream);
+    return a.dt_softplus ? launch_scan_bf16_k<N, MODE, true, HPW>(a, units, stream)
+                         : launch_scan_bf16_k<N, MODE, false, HPW>(a, units, stream);
+}
+template <int N, int HPW>
+hipError_t launch_scan_bf16(const ScanArgs& a, hipStream_t stream) {
+    const int units = a.B * (a.H / HPW);
+    if (a.K > 1) {
+        hipError_t e = launch_scan_bf16_mode<N, kStateOnly, HPW>(a, units * (a.K - 1), stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_scan_bf16_mode<N, kFull, HPW>(a, units * a.K, stream);
 }
 
 template <typename T, int N, int MODE>
@@ -949,16 +1074,72 @@ hipError_t launch_scan_mode(const ScanArgs& a, int units, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- bf16 plan: heads per workgroup, then the sequence split.
+constexpr int kCUs = 256;
+constexpr size_t kLdsPerCU = 163840;
+constexpr int kMaxWavesPerCU = 32;
+
+template <int N>
+size_t bf16_lds_n(int hpw, bool full) {
+    if (full) {
+        switch (hpw) {
+            case 1: return LdsBf<N, kFull, 1>::bytes;
+            case 2: return LdsBf<N, kFull, 2>::bytes;
+            case 4: return N <= 64 ? LdsBf<N, kFull, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
+        }
+    } else {
+        switch (hpw) {
+            case 1: return LdsBf<N, kStateOnly, 1>::bytes;
+            case 2: return LdsBf<N, kStateOnly, 2>::bytes;
+            case 4: return N <= 64 ? LdsBf<N, kStateOnly, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
+        }
+    }
+    return kLdsPerCU + 1;
+}
+size_t bf16_lds(int N, int hpw, bool full) {
+    switch (N) {
+        case 16: return bf16_lds_n<16>(hpw, full);
+        case 32: return bf16_lds_n<32>(hpw, full);
+        case 64: return bf16_lds_n<64>(hpw, full);
+        case 128: return bf16_lds_n<128>(hpw, full);
+    }
+    return kLdsPerCU + 1;
+}
+// workgroups of 4 hpw waves that fit one CU by LDS
+int bf16_wgs_per_cu(int N, int hpw, bool full) {
+    const size_t bytes = bf16_lds(N, hpw, full);
+    if (bytes > kLdsPerCU) return 0;
+    return (int)std::min<size_t>(kLdsPerCU / bytes, (size_t)(kMaxWavesPerCU / (4 * hpw)));
+}
+// Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a
+// group and gives the most waves per CU.
+int bf16_hpw(int N, int H, int G) {
+    const int hg = H / G;
+    int best = 1, best_waves = 0;
+    for (int hpw : {4, 2, 1}) {
+        if (hg % hpw) continue;
+        const int waves = bf16_wgs_per_cu(N, hpw, true) * 4 * hpw;
+        if (waves > best_waves) { best_waves = waves; best = hpw; }
+    }
+    return best;
+}
+
 template <typename T, int N>
 hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
-    const int bh = a.B * a.H;
-    constexpr bool bf = !std::is_same<T, float>::value;
-    if (a.K > 1) {
-        hipError_t e = bf ? launch_scan_bf16_mode<N, kStateOnly>(a, bh * (a.K - 1), stream)
-                          : launch_scan_mode<T, N, kStateOnly>(a, bh * (a.K - 1), stream);
-        if (e != hipSuccess) return e;
+    if constexpr (!std::is_same<T, float>::value) {
+        switch (bf16_hpw(N, a.H, a.G)) {
+            case 4: return launch_scan_bf16<N, (N <= 64 ? 4 : 2)>(a, stream);
+            case 2: return launch_scan_bf16<N, 2>(a, stream);
+            default: return launch_scan_bf16<N, 1>(a, stream);
+        }
+    } else {
+        const int bh = a.B * a.H;
+        if (a.K > 1) {
+            hipError_t e = launch_scan_mode<T, N, kStateOnly>(a, bh * (a.K - 1), stream);
+            if (e != hipSuccess) return e;
+        }
+        return launch_scan_mode<T, N, kFull>(a, bh * a.K, stream);
     }
-    return bf ? launch_scan_bf16_mode<N, kFull>(a, bh * a.K, stream) : launch_scan_mode<T, N, kFull>(a, bh * a.K, stream);
 }
 
 template <typename T>
@@ -974,35 +1155,43 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t scan_lds_bytes(int N, int dtype) {
-    switch (N) {
-        case 16: return dtype == 0 ? Lds<float, 16, kFull>::bytes : Lds<uint16_t, 16, kFull>::bytes;
-        case 32: return dtype == 0 ? Lds<float, 32, kFull>::bytes : Lds<uint16_t, 32, kFull>::bytes;
-        case 64: return dtype == 0 ? Lds<float, 64, kFull>::bytes : Lds<uint16_t, 64, kFull>::bytes;
-        case 128: return dtype == 0 ? Lds<float, 128, kFull>::bytes : Lds<uint16_t, 128, kFull>::bytes;
-    }
-    return 0;
-}
-
-// Sequence split: enough (b, h, superchunk) units to give every CU several
-// workgroups, with superchunks of at least 8 chunks.  K = 1 when the (b, h)
-// pairs alone already fill the device.
-void scan_split(int B, int L, int H, int& K, int& S) {
-    constexpr long kTargetUnits = 1024;   // 4 workgroups per CU on 256 CUs
-    constexpr int kMinChunks = 8;
-    const long bh = (long)B * H;
+// Sequence split.  fp32: enough (b, h, superchunk) units to give every CU
+// several workgroups, with superchunks of at least 8 chunks.  bf16: the K
+// (at most 8) that minimises the critical path in chunk steps -- rounds of
+// resident workgroups times chunks per superchunk -- counting the state-only
+// pre-pass at 0.4 of a full chunk step.
+void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S) {
     const int nch = (L + Q - 1) / Q;
+    if (nch <= 1) { K = 1; S = Q * std::max(nch, 1); return; }
     int k = 1;
-    while (bh * k < kTargetUnits && nch / (2 * k) >= kMinChunks) k *= 2;
+    if (dtype == 0) {   // fp32
+        constexpr long kTargetUnits = 1024;   // 4 workgroups per CU on 256 CUs
+        constexpr int kMinChunks = 8;
+        const long bh = (long)B * H;
+        while (bh * k < kTargetUnits && nch / (2 * k) >= kMinChunks) k *= 2;
+    } else {
+        const int hpw = bf16_hpw(N, H, G);
+        const long units = (long)B * (H / hpw);
+        const long slots = (long)kCUs * std::max(bf16_wgs_per_cu(N, hpw, true), 1);
+        const long slots_pre = (long)kCUs * std::max(bf16_wgs_per_cu(N, hpw, false), 1);
+        double best = 1e300;
+        for (int kk = 1; kk <= 8 && kk <= nch; ++kk) {
+            const int per = (nch + kk - 1) / kk;
+            const int kr = (nch + per - 1) / per;      // superchunks actually used
+            if (kr != kk) continue;
+            double cost = (double)((units * kk + slots - 1) / slots) * per;
+            if (kk > 1) cost += 0.4 * (double)((units * (kk - 1) + slots_pre - 1) / slots_pre) * per;
+            if (cost < best - 1e-9) { best = cost; k = kk; }
+        }
+    }
     const int per = (nch + k - 1) / k;           // chunks per superchunk
     K = (nch + per - 1) / per;
     S = per * Q;
-    if (K < 1) { K = 1; S = Q; }
 }
 
-size_t scan_workspace_bytes(int B, int L, int H, int P, int N) {
+size_t scan_workspace_bytes(int B, int L, int H, int P, int N, int G, int dtype) {
     int K, S;
-    scan_split(B, L, H, K, S);
+    scan_split(B, L, H, N, G, dtype, K, S);
     if (K <= 1) return 0;
     const size_t u = (size_t)B * H * (K - 1);
     return u * (size_t)P * N * sizeof(float) + ((u * sizeof(float) + 255) / 256) * 256;

@@ -49,14 +49,13 @@ struct StepArgs {
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // Sequence split chosen for these sizes (1 = none) and its superchunk length.
-void scan_split(int B, int L, int H, int& K, int& S);
-size_t scan_workspace_bytes(int B, int L, int H, int P, int N);
+void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S);
+size_t scan_workspace_bytes(int B, int L, int H, int P, int N, int G, int dtype);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 // Copies n 16-byte words src -> dst (src == nullptr: zero fill); used for the
 // L = 0 state pass-through without a memset node.
 hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream);
 
-size_t scan_lds_bytes(int N, int dtype);
 size_t step_lds_bytes(int H, int P, int N, int G);
 
 }  // namespace ssd
