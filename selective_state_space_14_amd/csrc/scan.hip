@@ -627,22 +627,28 @@ struct Swz {
     }
 };
 
-template <int N, int MODE, int HPW>
+// NS: pipeline stages.  The full pass uses two (its LDS is spoken for); the
+// state-only pass, which reads only B, X and dt, can run deeper and keeps each
+// chunk's dt / doc ids inside its stage.
+template <int N, int MODE, int HPW, int NS = 2>
 struct LdsBf {
     static constexpr bool FULL = MODE == kFull;
+    static_assert(!FULL || NS == 2, "the full pass is two-stage");
     static constexpr int NW = 4 * HPW;                // waves
     static constexpr int RB = N * 2;                  // bytes per B / C row
     static constexpr int XB = 128;                    // bytes per X row of one head (64 channels)
     static constexpr int TB = Q * RB;                 // B or C tile
     static constexpr int TX = Q * XB;                 // X tile of one head
     static constexpr int oB = 0, oC = TB, oX = FULL ? 2 * TB : TB;   // then the HPW X tiles
-    static constexpr int STAGE = oX + HPW * TX;
+    static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q] each
+    static constexpr int oDS = oX + HPW * TX;         // dt / doc inside a stage (state-only pass)
+    static constexpr int STAGE = oDS + (FULL ? 0 : DB);
     static constexpr int MB = kNumMTiles * 512;       // one head's M^T tiles, bf16 fragments
-    static constexpr int oM = 2 * STAGE;
+    static constexpr int oM = NS * STAGE;
     static constexpr int ZW = Q * 32;                 // one wave's z tile [Q][16] bf16
     static constexpr int oZ = oM + (FULL ? HPW * MB : 0);
-    static constexpr int oD = oZ + (FULL ? NW * ZW : 0);   // per head: dt, doc, doc of the previous token [Q] each
-    static constexpr int oS = oD + HPW * 3 * Q * 4;
+    static constexpr int oD = oZ + (FULL ? NW * ZW : 0);   // dt / doc of the full pass (one buffer)
+    static constexpr int oS = oD + (FULL ? DB : 0);
     // per-token scalars of one chunk, floats: per head cs, dt, eo, w [Q] each;
     // then the segment start per token [Q] (int); cs_end per head; last_seg
     static constexpr int SC_SEG = 4 * HPW * Q;
@@ -658,12 +664,12 @@ struct LdsBf {
     static constexpr int NI = NI_BC + HPW * NI_X;
     static constexpr int NI_W = (NI + NW - 1) / NW;   // most copies a wave issues
     static constexpr int NI_MIN = NI / NW;            // fewest
-    static_assert(bytes <= 163840, "LDS plan exceeds a CU");
 };
 
-template <int N, int MODE, bool SP, int HPW>
+template <int N, int MODE, bool SP, int HPW, int NS>
 __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
-    using LD = LdsBf<N, MODE, HPW>;
+    using LD = LdsBf<N, MODE, HPW, NS>;
+    static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
     constexpr int NT = N / 16;
     constexpr bool FULL = MODE == kFull;
     constexpr int NW = LD::NW;
@@ -715,7 +721,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int Ys = (int)a.y_stride;
 
     unsigned char* zbuf = smem + LD::oZ + wave * LD::ZW;              // this wave's z tile
-    unsigned char* dbuf = smem + LD::oD + hh * 3 * Q * 4;             // this head's dt, doc, doc-1
+    // this head's dt, doc, doc-1 of a chunk: one buffer (full pass) or one per stage
+    auto dbuf_of = [&](int st) -> unsigned char* {
+        return FULL ? smem + LD::oD + hh * 3 * Q * 4 : smem + st * LD::STAGE + LD::oDS + hh * 3 * Q * 4;
+    };
 
     // Copy slots of this wave: slot j is copy instruction wave + NW j of the
     // chunk (B tile, then C tile, then the X tiles).  Per slot: the uniform
@@ -764,7 +773,8 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         }
     };
     // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
-    auto issue_scalars = [&](int t0) {
+    auto issue_scalars = [&](int t0, int st) {
+        unsigned char* dbuf = dbuf_of(st);
         const int rowl = min(lane, tl - t0);
         dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
         if (docs) {
@@ -817,38 +827,50 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     bool reset = false;
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
-    if (nchunks > 0) {
-        if (lead) issue_scalars(tbeg);
-        issue_tiles(tbeg, 0);
-        if (FULL) issue_z(tbeg);
+    // chunks 0 .. NS-2 in flight before the loop, in the loop's issue order
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+        if (j < nchunks) {
+            if (lead) issue_scalars(tbeg + j * Q, j);
+            issue_tiles(tbeg + j * Q, j);
+        }
     }
+    if (FULL && nchunks > 0) issue_z(tbeg);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
-        const int st = c & 1;
+        const int st = NS == 2 ? (c & 1) : c % NS;
+        const int cn = c + NS - 1;                 // chunk whose copies this iteration issues
+        const int sn = NS == 2 ? (st ^ 1) : cn % NS;
         const bool more = c + 1 < nchunks;
         const unsigned char* sB = smem + st * LD::STAGE + LD::oB;
         const unsigned char* sC = smem + st * LD::STAGE + LD::oC;
         const unsigned char* sX = smem + st * LD::STAGE + LD::oX + hh * LD::TX;
-        float* sc = scal + st * LD::SCW;           // this chunk's scalars
+        float* sc = scal + (c & 1) * LD::SCW;      // this chunk's scalars
         float* sch = sc + hh * 4 * Q;              // ... of this wave's head: cs, dt, eo, w
 
-        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed: only
-        // the y stores of chunk c-1 and the z copies of chunk c may be newer
+        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed.  Full
+        // pass: only the y stores of chunk c-1 and the z copies of chunk c may be
+        // newer.  State-only pass: only the copies of chunks c+1 .. c+NS-2 (at
+        // least this wave's share of the tiles of each) may be newer.
         if (FULL) {
             if (c == 0) wait_vmcnt<2>();
             else wait_vmcnt<6>();
         } else {
-            wait_vmcnt<0>();
+            if (c + NS - 2 < nchunks) wait_vmcnt<(NS - 2) * LD::NI_MIN>();
+            else wait_vmcnt<0>();
         }
         // ---- lead waves: segmented cumulative sum of dt*A (log2 domain), lane = token
         if (lead) {
             const bool tok_ok = t0 + lane < tend;
+            const unsigned char* dbuf = dbuf_of(st);
             float dtl = reinterpret_cast<const float*>(dbuf)[lane];
             const int d0 = reinterpret_cast<const int*>(dbuf)[Q + lane];
             const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
             lds_wait();
-            if (more) issue_scalars(t0 + Q);
+            // the full pass refills its single buffer; the state-only pass fills
+            // the stage of chunk c-1, whose dt / doc ids only this wave read
+            if (cn < nchunks) issue_scalars(t0 + (NS - 1) * Q, sn);
             if (SP) dtl = softplus_f(dtl + dtb);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
@@ -869,7 +891,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             }
         }
         lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
-        if (more) issue_tiles(t0 + Q, st ^ 1);
+        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn);
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
@@ -1026,10 +1048,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     }
 }
 
-template <int N, int MODE, bool SP, int HPW>
+template <int N, int MODE, bool SP, int HPW, int NS>
 hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, MODE, SP, HPW>);
-    const size_t lds = LdsBf<N, MODE, HPW>::bytes;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, MODE, SP, HPW, NS>);
+    const size_t lds = LdsBf<N, MODE, HPW, NS>::bytes;
     static bool checked = false;
     if (!checked) {
         // The kernel's explicit vector-memory waits count only its own copies,
@@ -1042,22 +1064,29 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
         if (e != hipSuccess) return e;
         checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, MODE, SP, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, MODE, SP, HPW, NS>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
 }
-template <int N, int MODE, int HPW>
+template <int N, int MODE, int HPW, int NS>
 hipError_t launch_scan_bf16_mode(const ScanArgs& a, int units, hipStream_t stream) {
-    return a.dt_softplus ? launch_scan_bf16_k<N, MODE, true, HPW>(a, units, stream)
-                         : launch_scan_bf16_k<N, MODE, false, HPW>(a, units, stream);
+    return a.dt_softplus ? launch_scan_bf16_k<N, MODE, true, HPW, NS>(a, units, stream)
+                         : launch_scan_bf16_k<N, MODE, false, HPW, NS>(a, units, stream);
+}
+// the state-only pre-pass: PRE_HPW heads per workgroup, kPreStages stages
+constexpr int kPreStages = 3;
+template <int N, int PRE_HPW>
+hipError_t launch_scan_bf16_pre(const ScanArgs& a, hipStream_t stream) {
+    return launch_scan_bf16_mode<N, kStateOnly, PRE_HPW, kPreStages>(a, a.B * (a.H / PRE_HPW) * (a.K - 1), stream);
 }
 template <int N, int HPW>
-hipError_t launch_scan_bf16(const ScanArgs& a, hipStream_t stream) {
-    const int units = a.B * (a.H / HPW);
+hipError_t launch_scan_bf16(const ScanArgs& a, int pre_hpw, hipStream_t stream) {
     if (a.K > 1) {
-        hipError_t e = launch_scan_bf16_mode<N, kStateOnly, HPW>(a, units * (a.K - 1), stream);
+        hipError_t e = pre_hpw == 4 ? launch_scan_bf16_pre<N, (N <= 64 ? 4 : 2)>(a, stream)
+                     : pre_hpw == 2 ? launch_scan_bf16_pre<N, 2>(a, stream)
+                                    : launch_scan_bf16_pre<N, 1>(a, stream);
         if (e != hipSuccess) return e;
     }
-    return launch_scan_bf16_mode<N, kFull, HPW>(a, units * a.K, stream);
+    return launch_scan_bf16_mode<N, kFull, HPW, 2>(a, a.B * (a.H / HPW) * a.K, stream);
 }
 
 template <typename T, int N, int MODE>
@@ -1089,9 +1118,9 @@ size_t bf16_lds_n(int hpw, bool full) {
         }
     } else {
         switch (hpw) {
-            case 1: return LdsBf<N, kStateOnly, 1>::bytes;
-            case 2: return LdsBf<N, kStateOnly, 2>::bytes;
-            case 4: return N <= 64 ? LdsBf<N, kStateOnly, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
+            case 1: return LdsBf<N, kStateOnly, 1, kPreStages>::bytes;
+            case 2: return LdsBf<N, kStateOnly, 2, kPreStages>::bytes;
+            case 4: return LdsBf<N, kStateOnly, 4, kPreStages>::bytes;
         }
     }
     return kLdsPerCU + 1;
@@ -1123,14 +1152,23 @@ int bf16_hpw(int N, int H, int G) {
     }
     return best;
 }
+// Heads per workgroup of the state-only pre-pass: the largest that divides the
+// heads of a group and keeps at least PRE_MIN_WAVES waves per CU.
+int bf16_pre_hpw(int N, int H, int G) {
+    const int hg = H / G;
+    for (int hpw : {4, 2, 1})
+        if (hg % hpw == 0 && bf16_wgs_per_cu(N, hpw, false) > 0) return hpw;
+    return 1;
+}
 
 template <typename T, int N>
 hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
     if constexpr (!std::is_same<T, float>::value) {
+        const int pre = bf16_pre_hpw(N, a.H, a.G);
         switch (bf16_hpw(N, a.H, a.G)) {
-            case 4: return launch_scan_bf16<N, (N <= 64 ? 4 : 2)>(a, stream);
-            case 2: return launch_scan_bf16<N, 2>(a, stream);
-            default: return launch_scan_bf16<N, 1>(a, stream);
+            case 4: return launch_scan_bf16<N, (N <= 64 ? 4 : 2)>(a, pre, stream);
+            case 2: return launch_scan_bf16<N, 2>(a, pre, stream);
+            default: return launch_scan_bf16<N, 1>(a, pre, stream);
         }
     } else {
         const int bh = a.B * a.H;
@@ -1173,14 +1211,16 @@ void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S) {
         const int hpw = bf16_hpw(N, H, G);
         const long units = (long)B * (H / hpw);
         const long slots = (long)kCUs * std::max(bf16_wgs_per_cu(N, hpw, true), 1);
-        const long slots_pre = (long)kCUs * std::max(bf16_wgs_per_cu(N, hpw, false), 1);
+        const int pre_hpw = bf16_pre_hpw(N, H, G);
+        const long units_pre = (long)B * (H / pre_hpw);
+        const long slots_pre = (long)kCUs * std::max(bf16_wgs_per_cu(N, pre_hpw, false), 1);
         double best = 1e300;
         for (int kk = 1; kk <= 8 && kk <= nch; ++kk) {
             const int per = (nch + kk - 1) / kk;
             const int kr = (nch + per - 1) / per;      // superchunks actually used
             if (kr != kk) continue;
             double cost = (double)((units * kk + slots - 1) / slots) * per;
-            if (kk > 1) cost += 0.4 * (double)((units * (kk - 1) + slots_pre - 1) / slots_pre) * per;
+            if (kk > 1) cost += 0.4 * (double)((units_pre * (kk - 1) + slots_pre - 1) / slots_pre) * per;
             if (cost < best - 1e-9) { best = cost; k = kk; }
         }
     }

@@ -12,8 +12,11 @@
 //      and the N/4 lanes of a row reduce C . h with a fixed xor butterfly,
 //      so the result is deterministic and independent of the batch size.
 //   y[p] = (C . h[p] + D x_p) * silu(z_p).
-// The state is 96% of the bytes (B*H*P*N*4 read + written per token); four
-// items are loaded before any is used so each thread keeps 64 B in flight.
+// The state is 96% of the bytes (B*H*P*N*4 read + written per token).  Items
+// are processed kStepUnroll at a time with the next batch's loads issued
+// before the current batch is computed (the first batch even before the conv
+// phase), so each thread keeps up to 128 B of state in flight; the item index
+// decodes into (head, p, n-quad) with shifts (P = 64, N a power of two).
 // The recurrence is the Mamba-2 SSD layer of the Codestral-Mamba port header
 // (codestral_mamba.ts); step == forward at length 1 with the state carried
 // follows mojolearn.Mamba3Block's step() description.
@@ -26,6 +29,7 @@ namespace {
 
 constexpr int kStepThreads = 1024;
 constexpr int kStepUnroll = 4;
+constexpr int kP = 64;             // head dim (the only one the library accepts)
 
 template <typename T> struct Vec16;
 template <> struct Vec16<float> { static constexpr int n = 4; };
@@ -50,7 +54,8 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     extern __shared__ float smem[];
     constexpr int VEC = Vec16<T>::n;
     constexpr int K = 4;
-    const int H = a.H, P = a.P, G = a.G;
+    constexpr int P = kP;
+    const int H = a.H, G = a.G;
     const int HP = H * P, GN = G * N, C = HP + 2 * GN;
     const int hpg = H / G;
     const int b = blockIdx.x;
@@ -58,6 +63,22 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float* xbc_s = smem;              // [C]
     float* dt_s = smem + C;           // [H]
     float* a_s = dt_s + H;            // [H]
+    int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
+
+    // state items: float4 f of this sequence is (h, p, n-quad) = (f / (P NQ), (f / NQ) % P, f % NQ)
+    constexpr int NQ = N / 4;                       // lanes per p row
+    constexpr int per_head = P * NQ;                // float4 items per head (a power of two)
+    const int total = H * per_head;
+    float4* st = reinterpret_cast<float4*>(a.ssm_state + (size_t)b * H * P * N);
+    float4 s_cur[kStepUnroll], s_nxt[kStepUnroll];
+    auto load_batch = [&](int base, float4* dst) {
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) {
+            const int f = base + u * kStepThreads + tid;
+            dst[u] = f < total ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    load_batch(0, s_cur);             // independent of the conv phase: start it now
 
     // ---- 1. conv window, activation, buffer shift
     const T* raw = static_cast<const T*>(a.xbc_raw) + (size_t)b * C;
@@ -86,7 +107,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
             v = fmaf(w.y, r1[e], v);
             v = fmaf(w.z, r2[e], v);
             v = fmaf(w.w, cur[e], v);
-            if (a.act == 0) v = v / (1.0f + expf(-v));
+            if (a.act == 0) v = silu_f(v);
             xbc_s[c] = round_to(v, (T*)nullptr);
         }
     }
@@ -95,38 +116,31 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         float dt = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
         dt_s[h] = dt;
         a_s[h] = expf(dt * a.A[h]);
+        gofs_s[h] = (h / hpg) * N;
     }
     __syncthreads();
 
     // ---- 2. state read-modify-write
-    constexpr int NQ = N / 4;                       // lanes per p row
-    const int per_head = P * NQ;                    // float4 items per head
-    const int total = H * per_head;
-    float4* st = reinterpret_cast<float4*>(a.ssm_state + (size_t)b * H * P * N);
     const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
     float* yb = a.y + (size_t)b * HP;
-    for (int base = 0; base < total; base += kStepThreads * kStepUnroll) {
-        float4 s[kStepUnroll];
-#pragma unroll
-        for (int u = 0; u < kStepUnroll; ++u) {
-            const int f = base + u * kStepThreads + tid;
-            s[u] = f < total ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    constexpr int kBatchItems = kStepThreads * kStepUnroll;
+    for (int base = 0; base < total; base += kBatchItems) {
+        if (base + kBatchItems < total) load_batch(base + kBatchItems, s_nxt);
 #pragma unroll
         for (int u = 0; u < kStepUnroll; ++u) {
             const int f = base + u * kStepThreads + tid;
             const bool live = f < total;
-            const int h = live ? f / per_head : 0;
-            const int rem = f - h * per_head;
-            const int p = rem / NQ;
-            const int nq = rem - p * NQ;
-            const int g = h / hpg;
+            // a wave's 64 items lie in one head (per_head and total are multiples of 64)
+            const int h = __builtin_amdgcn_readfirstlane(min(f, total - 1) / per_head);
+            const int p = (f / NQ) % P;
+            const int nq = f % NQ;
+            const int gofs = gofs_s[h];
             const float dt = dt_s[h], dec = a_s[h];
             const float xp = xbc_s[h * P + p];
             const float dx = dt * xp;
-            const float4 Bv = *reinterpret_cast<const float4*>(xbc_s + HP + g * N + 4 * nq);
-            const float4 Cv = *reinterpret_cast<const float4*>(xbc_s + HP + GN + g * N + 4 * nq);
-            float4 v = s[u];
+            const float4 Bv = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * nq);
+            const float4 Cv = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * nq);
+            float4 v = s_cur[u];
             v.x = fmaf(dec, v.x, dx * Bv.x);
             v.y = fmaf(dec, v.y, dx * Bv.y);
             v.z = fmaf(dec, v.z, dx * Bv.z);
@@ -146,13 +160,15 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
                 }
             }
         }
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) s_cur[u] = s_nxt[u];
     }
 }
 
 template <typename T, int N>
 hipError_t launch_step_n(const StepArgs& a, hipStream_t stream) {
     const int C = a.H * a.P + 2 * a.G * N;
-    const size_t lds = sizeof(float) * ((size_t)C + 2 * a.H);
+    const size_t lds = sizeof(float) * ((size_t)C + 3 * a.H);
     hipLaunchKernelGGL((ssd_step_kernel<T, N>), dim3(a.B), dim3(kStepThreads), lds, stream, a);
     return hipGetLastError();
 }
@@ -171,7 +187,7 @@ hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t step_lds_bytes(int H, int P, int N, int G) {
-    return sizeof(float) * ((size_t)H * P + 2 * (size_t)G * N + 2 * (size_t)H);
+    return sizeof(float) * ((size_t)H * P + 2 * (size_t)G * N + 3 * (size_t)H);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
