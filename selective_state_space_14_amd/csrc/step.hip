@@ -6,17 +6,16 @@
 //      conv buffer shifts by one row in place (same thread reads then writes
 //      each channel, so no other thread can observe a half-shifted buffer);
 //      dt = softplus(dt_raw + dt_bias) and a = exp(dt * A) per head in LDS.
-//   2. a streaming read-modify-write of the fp32 state [H][P][N]: each thread
-//      owns one float4 (4 consecutive n of one p row) per item;
+//   2. a streaming read-modify-write of the fp32 state [H][P][N], a round of
+//      rows at a time: eight lanes share a row (four float4 each for N = 128),
 //          h[p, n] = a * h[p, n] + (dt * x_p) * B_n
-//      and the N/4 lanes of a row reduce C . h with a fixed xor butterfly,
-//      so the result is deterministic and independent of the batch size.
+//      and the row's lanes reduce C . h with a fixed DPP butterfly, so the
+//      result is deterministic and independent of the batch size;
 //   y[p] = (C . h[p] + D x_p) * silu(z_p).
-// The state is 96% of the bytes (B*H*P*N*4 read + written per token).  Items
-// are processed kStepUnroll at a time with the next batch's loads issued
-// before the current batch is computed (the first batch even before the conv
-// phase), so each thread keeps up to 128 B of state in flight; the item index
-// decodes into (head, p, n-quad) with shifts (P = 64, N a power of two).
+// The state is 96% of the bytes (B*H*P*N*4 read + written per token): its
+// loads and stores are nontemporal (it is touched once per token), the next
+// round's loads are issued before the current round is computed, and the
+// first round's even before the conv phase.
 // The recurrence is the Mamba-2 SSD layer of the Codestral-Mamba port header
 // (codestral_mamba.ts); step == forward at length 1 with the state carried
 // follows mojolearn.Mamba3Block's step() description.
@@ -28,7 +27,6 @@ namespace ssd {
 namespace {
 
 constexpr int kStepThreads = 1024;
-constexpr int kStepUnroll = 4;
 constexpr int kP = 64;             // head dim (the only one the library accepts)
 
 template <typename T> struct Vec16;
@@ -49,6 +47,24 @@ __device__ __forceinline__ float round_to(float v, uint16_t*) { return __uint_as
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Sum over aligned groups of W lanes (W = 4 or 8), every lane of a group
+// receiving the group's sum: quad-permute xor 1, xor 2, then (W = 8) the
+// half-row mirror, which pairs each lane with one of the other quad.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int W>
+__device__ __forceinline__ float row_sum(float v) {
+    static_assert(W == 4 || W == 8, "group width");
+    v = dpp_add<0xB1>(v);            // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);            // quad_perm [2,3,0,1]
+    if (W == 8) v = dpp_add<0x141>(v);   // row_half_mirror
+    return v;
+}
+
 template <typename T, int N>
 __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     extern __shared__ float smem[];
@@ -65,20 +81,28 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float* a_s = dt_s + H;            // [H]
     int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
 
-    // state items: float4 f of this sequence is (h, p, n-quad) = (f / (P NQ), (f / NQ) % P, f % NQ)
-    constexpr int NQ = N / 4;                       // lanes per p row
-    constexpr int per_head = P * NQ;                // float4 items per head (a power of two)
-    const int total = H * per_head;
-    float4* st = reinterpret_cast<float4*>(a.ssm_state + (size_t)b * H * P * N);
-    float4 s_cur[kStepUnroll], s_nxt[kStepUnroll];
-    auto load_batch = [&](int base, float4* dst) {
+    // ---- state rows: row = h * P + p holds NQ float4 (n fastest).  LPR lanes
+    // share a row, lane q of a row holds float4 q + LPR j (j < FPL), so every
+    // load instruction reads whole 128-byte row segments; a wave covers RPW
+    // consecutive rows (one head) per round, the workgroup RPR rows.
+    constexpr int NQ = N / 4;
+    constexpr int LPR = NQ < 8 ? NQ : 8;
+    constexpr int FPL = NQ / LPR;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RPR = RPW * (kStepThreads / 64);
+    const int nrows = H * P;                         // a multiple of 64, so rounds cover whole waves
+    const int wave = tid >> 6, lane = tid & 63;
+    const int q = lane % LPR;
+    f4v* st = reinterpret_cast<f4v*>(a.ssm_state + (size_t)b * H * P * N);
+    f4v s_cur[FPL], s_nxt[FPL];
+    auto row_of = [&](int r) { return r * RPR + wave * RPW + lane / LPR; };
+    auto load_round = [&](int r, f4v* dst) {
+        const int row = row_of(r);
 #pragma unroll
-        for (int u = 0; u < kStepUnroll; ++u) {
-            const int f = base + u * kStepThreads + tid;
-            dst[u] = f < total ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int j = 0; j < FPL; ++j)
+            dst[j] = row < nrows ? __builtin_nontemporal_load(st + (size_t)row * NQ + q + j * LPR) : f4v{0.f, 0.f, 0.f, 0.f};
     };
-    load_batch(0, s_cur);             // independent of the conv phase: start it now
+    load_round(0, s_cur);             // independent of the conv phase: start it now
 
     // ---- 1. conv window, activation, buffer shift
     const T* raw = static_cast<const T*>(a.xbc_raw) + (size_t)b * C;
@@ -120,48 +144,47 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     }
     __syncthreads();
 
-    // ---- 2. state read-modify-write
+    // ---- 2. state read-modify-write, one round of RPR rows at a time; the
+    // next round's loads are issued before the current round is computed
     const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
     float* yb = a.y + (size_t)b * HP;
-    constexpr int kBatchItems = kStepThreads * kStepUnroll;
-    for (int base = 0; base < total; base += kBatchItems) {
-        if (base + kBatchItems < total) load_batch(base + kBatchItems, s_nxt);
-#pragma unroll
-        for (int u = 0; u < kStepUnroll; ++u) {
-            const int f = base + u * kStepThreads + tid;
-            const bool live = f < total;
-            // a wave's 64 items lie in one head (per_head and total are multiples of 64)
-            const int h = __builtin_amdgcn_readfirstlane(min(f, total - 1) / per_head);
-            const int p = (f / NQ) % P;
-            const int nq = f % NQ;
+    const int nrounds = (nrows + RPR - 1) / RPR;
+    for (int r = 0; r < nrounds; ++r) {
+        if (r + 1 < nrounds) load_round(r + 1, s_nxt);
+        const int row = row_of(r);
+        if (row < nrows) {                           // uniform over the wave
+            const int h = __builtin_amdgcn_readfirstlane(row / P);
+            const int p = row % P;
             const int gofs = gofs_s[h];
-            const float dt = dt_s[h], dec = a_s[h];
+            const float dec = a_s[h];
             const float xp = xbc_s[h * P + p];
-            const float dx = dt * xp;
-            const float4 Bv = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * nq);
-            const float4 Cv = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * nq);
-            float4 v = s_cur[u];
-            v.x = fmaf(dec, v.x, dx * Bv.x);
-            v.y = fmaf(dec, v.y, dx * Bv.y);
-            v.z = fmaf(dec, v.z, dx * Bv.z);
-            v.w = fmaf(dec, v.w, dx * Bv.w);
-            float part = Cv.x * v.x;
-            part = fmaf(Cv.y, v.y, part);
-            part = fmaf(Cv.z, v.z, part);
-            part = fmaf(Cv.w, v.w, part);
+            const float dx = dt_s[h] * xp;
+            float part = 0.0f;
 #pragma unroll
-            for (int off = 1; off < NQ; off <<= 1) part += __shfl_xor(part, off, NQ);
-            if (live) {
-                st[f] = v;
-                if (nq == 0) {
-                    float yv = part + (a.D ? a.D[h] : 0.0f) * xp;
-                    if (zb) yv *= silu_f(load1(zb + h * P + p));
-                    yb[h * P + p] = yv;
-                }
+            for (int j = 0; j < FPL; ++j) {
+                const float4 Bv = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * (q + j * LPR));
+                const float4 Cv = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * (q + j * LPR));
+                f4v v = s_cur[j];
+                v.x = fmaf(dec, v.x, dx * Bv.x);
+                v.y = fmaf(dec, v.y, dx * Bv.y);
+                v.z = fmaf(dec, v.z, dx * Bv.z);
+                v.w = fmaf(dec, v.w, dx * Bv.w);
+                part = fmaf(Cv.x, v.x, part);
+                part = fmaf(Cv.y, v.y, part);
+                part = fmaf(Cv.z, v.z, part);
+                part = fmaf(Cv.w, v.w, part);
+                __builtin_nontemporal_store(v, st + (size_t)row * NQ + q + j * LPR);
+            }
+            // sum over the LPR lanes of the row (a fixed order: deterministic)
+            part = row_sum<LPR>(part);
+            if (q == 0) {
+                float yv = part + (a.D ? a.D[h] : 0.0f) * xp;
+                if (zb) yv *= silu_f(load1(zb + h * P + p));
+                yb[h * P + p] = yv;
             }
         }
 #pragma unroll
-        for (int u = 0; u < kStepUnroll; ++u) s_cur[u] = s_nxt[u];
+        for (int j = 0; j < FPL; ++j) s_cur[j] = s_nxt[j];
     }
 }
 
