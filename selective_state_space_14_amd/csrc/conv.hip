@@ -123,11 +123,17 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
         }
     }
 
+    // raw rows are read once (the halo aside): nontemporal loads keep them from
+    // displacing the conv output the scan reads next
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
     for (int tb = t0; tb < t1; tb += kBatch) {
         uint4 rows[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            if (tb + u < t1) rows[u] = *reinterpret_cast<const uint4*>(raw + (size_t)(tb + u) * a.raw_stride);
+            if (tb + u < t1) {
+                const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(raw + (size_t)(tb + u) * a.raw_stride));
+                rows[u] = make_uint4(q.x, q.y, q.z, q.w);
+            }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int t = tb + u;

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float* dt_s = smem + C;           // [H]
     float* a_s = dt_s + H;            // [H]
     int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
+    float* z_s = a_s + 2 * H;                         // [H*P]: the gate input (when given)
 
     // ---- state rows: row = h * P + p holds NQ float4 (n fastest).  LPR lanes
     // share a row, lane q of a row holds float4 q + LPR j (j < FPL), so every
@@ -142,11 +143,14 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         a_s[h] = expf(dt * a.A[h]);
         gofs_s[h] = (h / hpg) * N;
     }
+    const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
+    if (zb) {
+        for (int i = tid; i < HP; i += kStepThreads) z_s[i] = load1(zb + i);
+    }
     __syncthreads();
 
     // ---- 2. state read-modify-write, one round of RPR rows at a time; the
     // next round's loads are issued before the current round is computed
-    const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
     float* yb = a.y + (size_t)b * HP;
     const int nrounds = (nrows + RPR - 1) / RPR;
     for (int r = 0; r < nrounds; ++r) {
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
             part = row_sum<LPR>(part);
             if (q == 0) {
                 float yv = part + (a.D ? a.D[h] : 0.0f) * xp;
-                if (zb) yv *= silu_f(load1(zb + h * P + p));
+                if (zb) yv *= silu_f(z_s[h * P + p]);
                 yb[h * P + p] = yv;
             }
         }
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
 template <typename T, int N>
 hipError_t launch_step_n(const StepArgs& a, hipStream_t stream) {
     const int C = a.H * a.P + 2 * a.G * N;
-    const size_t lds = sizeof(float) * ((size_t)C + 3 * a.H);
+    const size_t lds = sizeof(float) * ((size_t)C + 3 * a.H + (size_t)a.H * a.P);
     hipLaunchKernelGGL((ssd_step_kernel<T, N>), dim3(a.B), dim3(kStepThreads), lds, stream, a);
     return hipGetLastError();
 }
@@ -210,7 +214,7 @@ hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t step_lds_bytes(int H, int P, int N, int G) {
-    return sizeof(float) * ((size_t)H * P + 2 * (size_t)G * N + 3 * (size_t)H);
+    return sizeof(float) * (2 * (size_t)H * P + 2 * (size_t)G * N + 3 * (size_t)H);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
