@@ -206,8 +206,8 @@ size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, i
  * One workgroup serves one sequence, so B should be >= the CU count (256)
  * for full-device bandwidth.  Deterministic and batch-invariant: a row's
  * result does not depend on B or on the other rows.  The conv row, the gate
- * row and three per-head values are staged in LDS: sizes with
- * conv_dim + H*P + 3*H > 16384 floats are refused (SSD_ERR_UNSUPPORTED).
+ * row and four per-head values are staged in LDS: sizes with
+ * conv_dim + H*P + 4*H > 16384 floats are refused (SSD_ERR_UNSUPPORTED).
  */
 int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
              const void *xbc_raw, const void *dt_raw, const void *z,

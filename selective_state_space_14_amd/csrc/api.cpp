@@ -271,8 +271,8 @@ int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
     TRY(check_ptr(fn, "y", y, work, false));
     const size_t lds = ssd::step_lds_bytes(H, P, N, G);
     if (lds > 64 * 1024)
-        return fail(SSD_ERR_UNSUPPORTED, "%s: conv_dim=%lld plus H*P=%d plus 3*H=%d floats exceed the 64 KiB LDS budget",
-                    fn, (long long)C, H * P, 3 * H);
+        return fail(SSD_ERR_UNSUPPORTED, "%s: conv_dim=%lld plus H*P=%d plus 4*H=%d floats exceed the 64 KiB LDS budget",
+                    fn, (long long)C, H * P, 4 * H);
     if (!work) return ok();
     ssd::StepArgs a;
     a.B = B; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype; a.act = act;

@@ -5,11 +5,10 @@
 // channels (8 bf16 or 4 fp32) and walks a tile of kTile consecutive tokens
 // with the last three raw rows in registers, so every raw row is read once
 // (plus a 3-row halo per tile) and every output row written once, in 1 KiB
-// coalesced row segments.  Rows are loaded kBatch at a time before use to
-// keep several 16-byte loads in flight per lane.  SiLU uses the hardware
-// exp2 and reciprocal (a few fp32 ulp, far inside one bf16 ulp).  An extra
-// column of blocks (blockIdx.x == number of channel blocks) computes dt for
-// the same tokens.
+// coalesced row segments.  A ring of kBatch rows is kept loading ahead of
+// the row being convolved.  SiLU uses the hardware exp2 and reciprocal (a
+// few fp32 ulp, far inside one bf16 ulp).  An extra column of blocks
+// (blockIdx.x == number of channel blocks) computes dt for the same tokens.
 //
 // Document isolation (Mini-K3-1H card, "Checkpoint and training": the conv
 // history resets at every document boundary): when token t starts a new
@@ -83,6 +82,15 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
         return;
     }
 
+    // document starts inside the tile as a bit mask (bit i: token t0 + i starts
+    // a document), one doc-id pair per lane; built before any lane leaves
+    uint64_t starts = 0;
+    if (doc) {
+        const int tt = min(t0 + (int)threadIdx.x, t1 - 1);
+        const bool s_here = t0 + (int)threadIdx.x < t1 && tt > 0 && doc[tt] != doc[tt - 1];
+        starts = __ballot(s_here);
+    }
+
     const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * VEC;
     if (c0 >= C) return;
     const T* raw = static_cast<const T*>(a.raw) + (size_t)b * L * a.raw_stride + c0;
@@ -124,41 +132,53 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
     }
 
     // raw rows are read once (the halo aside): nontemporal loads keep them from
-    // displacing the conv output the scan reads next
+    // displacing the conv output the scan reads next.
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    for (int tb = t0; tb < t1; tb += kBatch) {
+    auto load_row = [&](int t) {
+        const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(raw + (size_t)t * a.raw_stride));
+        return make_uint4(q.x, q.y, q.z, q.w);
+    };
+    auto conv_row = [&](const uint4& rv, int t) {
+        float cur[VEC], o[VEC];
+        CV<T>::unpack(rv, cur);
+        if ((starts >> (t - t0)) & 1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = h1[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float v = bias[e];
+            v = fmaf(w[0][e], h3[e], v);
+            v = fmaf(w[1][e], h2[e], v);
+            v = fmaf(w[2][e], h1[e], v);
+            v = fmaf(w[3][e], cur[e], v);
+            if (a.act == 0) v = silu_f(v);
+            o[e] = v;
+            h3[e] = h2[e];
+            h2[e] = h1[e];
+            h1[e] = cur[e];
+        }
+        *reinterpret_cast<uint4*>(out + (size_t)t * a.out_stride) = CV<T>::pack(o);
+    };
+    if (t1 - t0 == kTile) {
+        // a ring of kBatch row slots kept full: slot u, once consumed, is
+        // refilled with the row kBatch further on (every load and store is
+        // unconditional, so kBatch loads stay in flight through the tile)
         uint4 rows[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            if (tb + u < t1) {
-                const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(raw + (size_t)(tb + u) * a.raw_stride));
-                rows[u] = make_uint4(q.x, q.y, q.z, q.w);
-            }
+        for (int u = 0; u < kBatch; ++u) rows[u] = load_row(t0 + u);
+        for (int tb = t0; tb < t1 - kBatch; tb += kBatch) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int t = tb + u;
-            if (t >= t1) break;
-            float cur[VEC], o[VEC];
-            CV<T>::unpack(rows[u], cur);
-            if (is_boundary(doc, t)) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = h1[e] = 0.0f;
+            for (int u = 0; u < kBatch; ++u) {
+                const uint4 rv = rows[u];
+                rows[u] = load_row(tb + kBatch + u);
+                conv_row(rv, tb + u);
             }
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float v = bias[e];
-                v = fmaf(w[0][e], h3[e], v);
-                v = fmaf(w[1][e], h2[e], v);
-                v = fmaf(w[2][e], h1[e], v);
-                v = fmaf(w[3][e], cur[e], v);
-                if (a.act == 0) v = silu_f(v);
-                o[e] = v;
-                h3[e] = h2[e];
-                h2[e] = h1[e];
-                h1[e] = cur[e];
-            }
-            *reinterpret_cast<uint4*>(out + (size_t)t * a.out_stride) = CV<T>::pack(o);
         }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) conv_row(rows[u], t1 - kBatch + u);
+    } else {
+        for (int t = t0; t < t1; ++t) conv_row(load_row(t), t);
     }
 
     // ---- conv state after the call (tile 0 owns it: it alone read state_in)

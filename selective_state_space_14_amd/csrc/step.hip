@@ -48,6 +48,7 @@ __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Sum over aligned groups of W lanes (W = 4 or 8), every lane of a group
 // receiving the group's sum: quad-permute xor 1, xor 2, then (W = 8) the
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float* dt_s = smem + C;           // [H]
     float* a_s = dt_s + H;            // [H]
     int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
-    float* z_s = a_s + 2 * H;                         // [H*P]: the gate input (when given)
+    float* d_s = a_s + 2 * H;                         // [H]: D (0 when absent)
+    float* z_s = d_s + H;                             // [H*P]: the gate input (when given)
 
     // ---- state rows: row = h * P + p holds NQ float4 (n fastest).  LPR lanes
     // share a row, lane q of a row holds float4 q + LPR j (j < FPL), so every
@@ -94,14 +96,21 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     const int nrows = H * P;                         // a multiple of 64, so rounds cover whole waves
     const int wave = tid >> 6, lane = tid & 63;
     const int q = lane % LPR;
-    f4v* st = reinterpret_cast<f4v*>(a.ssm_state + (size_t)b * H * P * N);
+    // The state goes through range-checked buffer loads and stores with the
+    // nontemporal bit: rows past the end read 0 and their stores are dropped,
+    // so the loop has no branches around memory operations and the compiler
+    // counts the loads in flight exactly.
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        a.ssm_state + (size_t)b * H * P * N, 0, nrows * NQ * 16, 0x00020000);
+    constexpr int kNT = 2;                           // cache policy: nontemporal
     f4v s_cur[FPL], s_nxt[FPL];
     auto row_of = [&](int r) { return r * RPR + wave * RPW + lane / LPR; };
+    auto off_of = [&](int row, int j) { return (uint32_t)((row * NQ + q + j * LPR) * 16); };
     auto load_round = [&](int r, f4v* dst) {
         const int row = row_of(r);
 #pragma unroll
         for (int j = 0; j < FPL; ++j)
-            dst[j] = row < nrows ? __builtin_nontemporal_load(st + (size_t)row * NQ + q + j * LPR) : f4v{0.f, 0.f, 0.f, 0.f};
+            dst[j] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(sr, off_of(row, j), 0, kNT));
     };
     load_round(0, s_cur);             // independent of the conv phase: start it now
 
@@ -142,6 +151,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         dt_s[h] = dt;
         a_s[h] = expf(dt * a.A[h]);
         gofs_s[h] = (h / hpg) * N;
+        d_s[h] = a.D ? a.D[h] : 0.0f;
     }
     const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
     if (zb) {
@@ -151,42 +161,55 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
 
     // ---- 2. state read-modify-write, one round of RPR rows at a time; the
     // next round's loads are issued before the current round is computed
-    float* yb = a.y + (size_t)b * HP;
+    // y through a range-checked buffer store: lanes other than a row's first
+    // aim past the range and are dropped, so the store is never skipped
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)b * HP, 0, HP * 4, 0x00020000);
     const int nrounds = (nrows + RPR - 1) / RPR;
+    // B and C of this lane's n-quads for the current group, reloaded only when
+    // the group changes (never, for one group)
+    float4 Bq[FPL], Cq[FPL];
+    int cur_gofs = -1;
     for (int r = 0; r < nrounds; ++r) {
-        if (r + 1 < nrounds) load_round(r + 1, s_nxt);
+        load_round(r + 1, s_nxt);                    // past the last round: out of range, reads 0
         const int row = row_of(r);
-        if (row < nrows) {                           // uniform over the wave
-            const int h = __builtin_amdgcn_readfirstlane(row / P);
-            const int p = row % P;
-            const int gofs = gofs_s[h];
-            const float dec = a_s[h];
-            const float xp = xbc_s[h * P + p];
-            const float dx = dt_s[h] * xp;
-            float part = 0.0f;
+        // a wave's rows lie in one head; a wave past the end computes on zeros
+        // and its stores fall outside the ranges
+        const int hrow = min(row, nrows - 1);
+        const int h = __builtin_amdgcn_readfirstlane(hrow / P);
+        const int p = hrow % P;
+        const int gofs = gofs_s[h];
+        if (gofs != cur_gofs) {                     // uniform: gofs is per head
+            cur_gofs = gofs;
 #pragma unroll
             for (int j = 0; j < FPL; ++j) {
-                const float4 Bv = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * (q + j * LPR));
-                const float4 Cv = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * (q + j * LPR));
-                f4v v = s_cur[j];
-                v.x = fmaf(dec, v.x, dx * Bv.x);
-                v.y = fmaf(dec, v.y, dx * Bv.y);
-                v.z = fmaf(dec, v.z, dx * Bv.z);
-                v.w = fmaf(dec, v.w, dx * Bv.w);
-                part = fmaf(Cv.x, v.x, part);
-                part = fmaf(Cv.y, v.y, part);
-                part = fmaf(Cv.z, v.z, part);
-                part = fmaf(Cv.w, v.w, part);
-                __builtin_nontemporal_store(v, st + (size_t)row * NQ + q + j * LPR);
-            }
-            // sum over the LPR lanes of the row (a fixed order: deterministic)
-            part = row_sum<LPR>(part);
-            if (q == 0) {
-                float yv = part + (a.D ? a.D[h] : 0.0f) * xp;
-                if (zb) yv *= silu_f(z_s[h * P + p]);
-                yb[h * P + p] = yv;
+                Bq[j] = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * (q + j * LPR));
+                Cq[j] = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * (q + j * LPR));
             }
         }
+        const float dec = a_s[h];
+        const float xp = xbc_s[h * P + p];
+        const float dx = dt_s[h] * xp;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FPL; ++j) {
+            const float4 Bv = Bq[j], Cv = Cq[j];
+            f4v v = s_cur[j];
+            v.x = fmaf(dec, v.x, dx * Bv.x);
+            v.y = fmaf(dec, v.y, dx * Bv.y);
+            v.z = fmaf(dec, v.z, dx * Bv.z);
+            v.w = fmaf(dec, v.w, dx * Bv.w);
+            part = fmaf(Cv.x, v.x, part);
+            part = fmaf(Cv.y, v.y, part);
+            part = fmaf(Cv.z, v.z, part);
+            part = fmaf(Cv.w, v.w, part);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr, off_of(row, j), 0, kNT);
+        }
+        // sum over the LPR lanes of the row (a fixed order: deterministic)
+        part = row_sum<LPR>(part);
+        float yv = fmaf(d_s[h], xp, part);
+        if (zb) yv *= silu_f(z_s[h * P + p]);
+        const bool first = q == 0 && row < nrows;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yr, first ? (uint32_t)(h * P + p) * 4 : 0x7fffffffu, 0, 0);
 #pragma unroll
         for (int j = 0; j < FPL; ++j) s_cur[j] = s_nxt[j];
     }
@@ -195,7 +218,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
 template <typename T, int N>
 hipError_t launch_step_n(const StepArgs& a, hipStream_t stream) {
     const int C = a.H * a.P + 2 * a.G * N;
-    const size_t lds = sizeof(float) * ((size_t)C + 3 * a.H + (size_t)a.H * a.P);
+    const size_t lds = sizeof(float) * ((size_t)C + 4 * a.H + (size_t)a.H * a.P);
     hipLaunchKernelGGL((ssd_step_kernel<T, N>), dim3(a.B), dim3(kStepThreads), lds, stream, a);
     return hipGetLastError();
 }
@@ -214,7 +237,7 @@ hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t step_lds_bytes(int H, int P, int N, int G) {
-    return sizeof(float) * (2 * (size_t)H * P + 2 * (size_t)G * N + 3 * (size_t)H);
+    return sizeof(float) * (2 * (size_t)H * P + 2 * (size_t)G * N + 4 * (size_t)H);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
