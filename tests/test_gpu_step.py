@@ -48,6 +48,10 @@ def oracle_single_pass(wl, prm, raw, steps, seed, rows, device):
     ("f32", 128, 1, 8, 200, 24),
     ("f32", 16, 2, 4, 64, 10),
     ("bf16", 64, 2, 8, 130, 12),
+    # H*P rows that leave the last round of the step's state sweep partly empty
+    ("f32", 64, 1, 3, 100, 8),
+    ("bf16", 128, 1, 1, 70, 6),
+    ("f32", 16, 1, 1, 65, 5),
 ])
 def test_prefill_then_steps_small(gpu_lib, dtype, N, G, H, L, steps):
     wl = synth.Workload("dec_" + dtype, 3, L, H, 64, N, G, dtype, steps=steps)
