@@ -5,35 +5,38 @@
 // evaluated in chunks of Q = 64 tokens with the dual (quadratic) form inside
 // a chunk and the state passed between chunks (chunk size 64: the
 // mojolearn.Mamba3Block description; the layer itself: the Codestral-Mamba
-// port header and the Mini-K3-1H card).
-//
-// Work decomposition: one workgroup = one (b, h) = 4 waves; wave w owns the
-// 16 head channels p in [16w, 16w+16) for the whole sequence and keeps their
-// slice of the fp32 state H (N x 16) in registers.  Chunks are walked strictly
-// in order, so the state never leaves the chip and a prefill split at a
-// multiple of 64 tokens reproduces one call bit for bit.  Per chunk c with
-// tokens t, s in [0, 64) (cs = log2-domain cumulative sum of dt A, restarted
-// at every document start inside the chunk):
-//   G^T[s,t]  = B_s . C_t                       (MFMA, K = N; 10 lower tiles,
-//                                                 split over the 4 waves)
+// port header and the Mini-K3-1H card).  Per chunk c with tokens t, s in
+// [0, 64) (cs = log2-domain cumulative sum of dt A, restarted at every
+// document start inside the chunk):
+//   G^T[s,t]  = B_s . C_t                       (MFMA, K = N; 10 lower tiles)
 //   M^T[s,t]  = G^T[s,t] 2^(cs_t - cs_s) dt_s    for seg(t) <= s <= t, else 0
 //   Ydiag^T   = X^T M^T                          (MFMA, K = s)
-//   Yoff^T    = H_prev^T C^T                     (MFMA, K = N; H split into
-//                                                 bf16 hi + lo parts)
+//   Yoff^T    = H_prev^T C^T                     (MFMA, K = N)
 //   S         = B^T (w o X),  w_s = 2^(cs_end - cs_s) dt_s on the last segment
 //   y_t       = Ydiag + [t in a carried segment] 2^(cs_t) Yoff + D x_t, gated
 //   H         = chunk holds a boundary ? S : 2^(cs_end) H_prev + S
-// Every document mask is a select, never a multiply, so tokens of a later
-// document are bit-for-bit independent of (finite) earlier-document inputs.
-// The pairwise decay is built from the difference cs_t - cs_s (the two sums
-// alone can reach hundreds in magnitude within a chunk).
+// Every document mask is a select (or a multiply by exactly zero of a finite
+// value), so tokens of a later document are bit-for-bit independent of
+// (finite) earlier-document inputs.  The pairwise decay is built from the
+// difference cs_t - cs_s (the two sums alone can reach hundreds in magnitude
+// within a chunk).
+//
+// Kernels:
+//   ssd_scan_kernel<float, N, MODE>  fp32 inputs: one (b, h) per workgroup,
+//       register-prefetch staging, fp32 MFMA; MODE kStateOnly is its pre-pass.
+//   ssd_scan_bf16_kernel<N, SP, HPW> bf16 inputs: HPW heads of one B/C group
+//       per workgroup, every per-chunk input staged by LDS DMA, bf16 MFMA.
+//   ssd_scan_state_kernel<...>       bf16 state-only pre-pass of the split.
+// Sequence split: with a workspace, each sequence may be cut into K
+// superchunks; a state-only pre-pass stores each superchunk's local end state
+// and total decay, and the full pass folds the preceding ones into its
+// starting state.  Without a workspace the chunks are walked strictly in
+// order, so a prefill split at a multiple of 64 tokens reproduces one call
+// bit for bit.
 //
 // All contractions are 16x16 MFMA tiles whose accumulator layout doubles as
 // the next contraction's operand layout (see ssd_device.hpp), so G^T feeds
 // the Y contraction and H feeds the C.H contraction without any shuffle.
-// LDS holds B (row-major and transposed), C, X^T, (w o X)^T, the M^T tiles
-// and the chunk's cs/dt/segment arrays; the next chunk's global loads are
-// issued right after staging, so they fly during the contractions.
 #include <algorithm>
 #include <type_traits>
 
@@ -607,8 +610,19 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // At most n of this wave's vector-memory operations still outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 16, "vmcnt range");
+    static_assert(n >= 0 && n < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+// The same for a wave-uniform n in [0, 31] (larger n waits for 31): a chain of
+// scalar compares picks the immediate.
+template <int LO = 0>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+    if constexpr (LO == 31) {
+        wait_vmcnt<31>();
+    } else {
+        if (n <= LO) wait_vmcnt<LO>();
+        else wait_vmcnt_n<LO + 1>(n);
+    }
 }
 
 // XOR swizzle of 16-byte pieces inside a tile row of RB bytes: piece c of row r
@@ -627,28 +641,25 @@ struct Swz {
     }
 };
 
-// NS: pipeline stages.  The full pass uses two (its LDS is spoken for); the
-// state-only pass, which reads only B, X and dt, can run deeper and keeps each
-// chunk's dt / doc ids inside its stage.
-template <int N, int MODE, int HPW, int NS = 2>
+// LDS plan of the full pass: two stages of B, C and the heads' X tiles, the
+// heads' M^T fragments, each wave's z tile, the heads' dt / doc ids (one
+// buffer), and two buffers of per-token scalars.
+template <int N, int HPW>
 struct LdsBf {
-    static constexpr bool FULL = MODE == kFull;
-    static_assert(!FULL || NS == 2, "the full pass is two-stage");
     static constexpr int NW = 4 * HPW;                // waves
     static constexpr int RB = N * 2;                  // bytes per B / C row
     static constexpr int XB = 128;                    // bytes per X row of one head (64 channels)
     static constexpr int TB = Q * RB;                 // B or C tile
     static constexpr int TX = Q * XB;                 // X tile of one head
-    static constexpr int oB = 0, oC = TB, oX = FULL ? 2 * TB : TB;   // then the HPW X tiles
+    static constexpr int oB = 0, oC = TB, oX = 2 * TB;   // then the HPW X tiles
     static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q] each
-    static constexpr int oDS = oX + HPW * TX;         // dt / doc inside a stage (state-only pass)
-    static constexpr int STAGE = oDS + (FULL ? 0 : DB);
+    static constexpr int STAGE = oX + HPW * TX;
     static constexpr int MB = kNumMTiles * 512;       // one head's M^T tiles, bf16 fragments
-    static constexpr int oM = NS * STAGE;
+    static constexpr int oM = 2 * STAGE;
     static constexpr int ZW = Q * 32;                 // one wave's z tile [Q][16] bf16
-    static constexpr int oZ = oM + (FULL ? HPW * MB : 0);
-    static constexpr int oD = oZ + (FULL ? NW * ZW : 0);   // dt / doc of the full pass (one buffer)
-    static constexpr int oS = oD + (FULL ? DB : 0);
+    static constexpr int oZ = oM + HPW * MB;
+    static constexpr int oD = oZ + NW * ZW;           // dt / doc ids
+    static constexpr int oS = oD + DB;
     // per-token scalars of one chunk, floats: per head cs, dt, eo, w [Q] each;
     // then the segment start per token [Q] (int); cs_end per head; last_seg
     static constexpr int SC_SEG = 4 * HPW * Q;
@@ -660,18 +671,17 @@ struct LdsBf {
     static constexpr int RPI_B = 64 / (RB / 16);
     static constexpr int NI_B = Q / RPI_B;
     static constexpr int NI_X = Q / 8;
-    static constexpr int NI_BC = NI_B * (FULL ? 2 : 1);
+    static constexpr int NI_BC = 2 * NI_B;
     static constexpr int NI = NI_BC + HPW * NI_X;
     static constexpr int NI_W = (NI + NW - 1) / NW;   // most copies a wave issues
     static constexpr int NI_MIN = NI / NW;            // fewest
 };
 
-template <int N, int MODE, bool SP, int HPW, int NS>
+template <int N, bool SP, int HPW>
 __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
-    using LD = LdsBf<N, MODE, HPW, NS>;
+    using LD = LdsBf<N, HPW>;
     static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
     constexpr int NT = N / 16;
-    constexpr bool FULL = MODE == kFull;
     constexpr int NW = LD::NW;
     constexpr int RB = LD::RB, XB = LD::XB;
     constexpr int CPR_B = RB / 16;
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
 
     const int L = a.L, H = a.H, G = a.G;
     const int HQ = H / HPW;
-    const int KU = FULL ? a.K : a.K - 1;
+    const int KU = a.K;
     const int id = xcd_remap(blockIdx.x, a.B * HQ * KU);
     const int hq = id % HQ;
     const int k = (id / HQ) % KU;
@@ -721,10 +731,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int Ys = (int)a.y_stride;
 
     unsigned char* zbuf = smem + LD::oZ + wave * LD::ZW;              // this wave's z tile
-    // this head's dt, doc, doc-1 of a chunk: one buffer (full pass) or one per stage
-    auto dbuf_of = [&](int st) -> unsigned char* {
-        return FULL ? smem + LD::oD + hh * 3 * Q * 4 : smem + st * LD::STAGE + LD::oDS + hh * 3 * Q * 4;
-    };
+    unsigned char* dbuf = smem + LD::oD + hh * 3 * Q * 4;             // this head's dt, doc, doc-1
 
     // Copy slots of this wave: slot j is copy instruction wave + NW j of the
     // chunk (B tile, then C tile, then the X tiles).  Per slot: the uniform
@@ -740,7 +747,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     for (int j = 0; j < LD::NI_W; ++j) {
         const int i = wave + NW * j;
         s_on[j] = i < LD::NI;
-        if (i < LD::NI_B || (FULL && i < LD::NI_BC)) {
+        if (i < LD::NI_BC) {
             const bool isC = i >= LD::NI_B;
             const int ins = isC ? i - LD::NI_B : i;
             s_base[j] = reinterpret_cast<const char*>(isC ? Cbase : Bbase);
@@ -760,6 +767,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             s_col[j] = (uint32_t)(((lane % (XB / 16)) ^ SX::f(r)) * 16);
         }
     }
+    // vector-memory operations this wave issues per chunk for the tiles, and
+    // (lead waves) for dt / doc ids: the exact counts its waits are built from
+    const int n_tiles = (LD::NI - wave + NW - 1) / NW;
+    const int n_scal = lead ? (docs ? 3 : 1) : 0;
     // B, C, X copies of the chunk at t0 into stage st; rows clamp to the unit's end
     auto issue_tiles = [&](int t0, int st) {
         const int lim = tl - t0;
@@ -773,8 +784,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         }
     };
     // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
-    auto issue_scalars = [&](int t0, int st) {
-        unsigned char* dbuf = dbuf_of(st);
+    auto issue_scalars = [&](int t0) {
         const int rowl = min(lane, tl - t0);
         dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
         if (docs) {
@@ -798,50 +808,40 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const size_t st_off = (((size_t)b * H + h) * 64 + p0 + j16) * N + 4 * q4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) Hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (FULL) {
-        if (a.init_state) {
+    if (a.init_state) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float4 v = *reinterpret_cast<const float4*>(a.init_state + st_off + 16 * nt);
-                Hs[nt] = f32x4{v.x, v.y, v.z, v.w};
-            }
+        for (int nt = 0; nt < NT; ++nt) {
+            const float4 v = *reinterpret_cast<const float4*>(a.init_state + st_off + 16 * nt);
+            Hs[nt] = f32x4{v.x, v.y, v.z, v.w};
         }
-        for (int j = 0; j < k; ++j) {
-            const size_t u = ((size_t)b * H + h) * (a.K - 1) + j;
-            const float dj = a.dec[u];
-            const float* hl = a.hloc + u * 64 * N + (size_t)(p0 + j16) * N + 4 * q4;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float4 v = *reinterpret_cast<const float4*>(hl + 16 * nt);
-                Hs[nt][0] = dj < 0.0f ? v.x : fmaf(dj, Hs[nt][0], v.x);
-                Hs[nt][1] = dj < 0.0f ? v.y : fmaf(dj, Hs[nt][1], v.y);
-                Hs[nt][2] = dj < 0.0f ? v.z : fmaf(dj, Hs[nt][2], v.z);
-                Hs[nt][3] = dj < 0.0f ? v.w : fmaf(dj, Hs[nt][3], v.w);
-            }
-        }
-        // settle the state loads here, before any copy is in flight
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Hs[nt]));
     }
-    float log2dec = 0.0f;
-    bool reset = false;
+    for (int j = 0; j < k; ++j) {
+        const size_t u = ((size_t)b * H + h) * (a.K - 1) + j;
+        const float dj = a.dec[u];
+        const float* hl = a.hloc + u * 64 * N + (size_t)(p0 + j16) * N + 4 * q4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float4 v = *reinterpret_cast<const float4*>(hl + 16 * nt);
+            Hs[nt][0] = dj < 0.0f ? v.x : fmaf(dj, Hs[nt][0], v.x);
+            Hs[nt][1] = dj < 0.0f ? v.y : fmaf(dj, Hs[nt][1], v.y);
+            Hs[nt][2] = dj < 0.0f ? v.z : fmaf(dj, Hs[nt][2], v.z);
+            Hs[nt][3] = dj < 0.0f ? v.w : fmaf(dj, Hs[nt][3], v.w);
+        }
+    }
+    // settle the state loads here, before any copy is in flight
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Hs[nt]));
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
-    // chunks 0 .. NS-2 in flight before the loop, in the loop's issue order
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) {
-        if (j < nchunks) {
-            if (lead) issue_scalars(tbeg + j * Q, j);
-            issue_tiles(tbeg + j * Q, j);
-        }
+    if (nchunks > 0) {
+        if (lead) issue_scalars(tbeg);
+        issue_tiles(tbeg, 0);
+        issue_z(tbeg);
     }
-    if (FULL && nchunks > 0) issue_z(tbeg);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
-        const int st = NS == 2 ? (c & 1) : c % NS;
-        const int cn = c + NS - 1;                 // chunk whose copies this iteration issues
-        const int sn = NS == 2 ? (st ^ 1) : cn % NS;
+        const int st = c & 1;
         const bool more = c + 1 < nchunks;
         const unsigned char* sB = smem + st * LD::STAGE + LD::oB;
         const unsigned char* sC = smem + st * LD::STAGE + LD::oC;
@@ -849,28 +849,18 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         float* sc = scal + (c & 1) * LD::SCW;      // this chunk's scalars
         float* sch = sc + hh * 4 * Q;              // ... of this wave's head: cs, dt, eo, w
 
-        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed.  Full
-        // pass: only the y stores of chunk c-1 and the z copies of chunk c may be
-        // newer.  State-only pass: only the copies of chunks c+1 .. c+NS-2 (at
-        // least this wave's share of the tiles of each) may be newer.
-        if (FULL) {
-            if (c == 0) wait_vmcnt<2>();
-            else wait_vmcnt<6>();
-        } else {
-            if (c + NS - 2 < nchunks) wait_vmcnt<(NS - 2) * LD::NI_MIN>();
-            else wait_vmcnt<0>();
-        }
+        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed: only
+        // the y stores of chunk c-1 and the z copies of chunk c may be newer
+        if (c == 0) wait_vmcnt<2>();
+        else wait_vmcnt<6>();
         // ---- lead waves: segmented cumulative sum of dt*A (log2 domain), lane = token
         if (lead) {
             const bool tok_ok = t0 + lane < tend;
-            const unsigned char* dbuf = dbuf_of(st);
             float dtl = reinterpret_cast<const float*>(dbuf)[lane];
             const int d0 = reinterpret_cast<const int*>(dbuf)[Q + lane];
             const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
             lds_wait();
-            // the full pass refills its single buffer; the state-only pass fills
-            // the stage of chunk c-1, whose dt / doc ids only this wave read
-            if (cn < nchunks) issue_scalars(t0 + (NS - 1) * Q, sn);
+            if (more) issue_scalars(t0 + Q);
             if (SP) dtl = softplus_f(dtl + dtb);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
@@ -891,12 +881,12 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             }
         }
         lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
-        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn);
+        if (more) issue_tiles(t0 + Q, st ^ 1);
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
 
-        if (FULL) {
+        {
             unsigned char* sM = smem + LD::oM;
             // ---- G^T = B C^T once per tile, then each head's decay and mask -> M^T fragments
             for (int kt = wave; kt < kNumMTiles; kt += NW) {
@@ -941,7 +931,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             lds_barrier();   // B: all M^T tiles are in LDS
             // z of chunk c has landed: only this wave's copies of chunk c+1 (and,
             // in lead waves, its dt / doc ids) may be newer
-            if (more) wait_vmcnt<LD::NI_MIN>();
+            if (more) wait_vmcnt_n(n_tiles + n_scal);
             else wait_vmcnt<0>();
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, output
@@ -1025,33 +1015,263 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) Hs[nt][r] = fmaf(dec, Hs[nt][r], acc[r]);
         }
-        if (!FULL) {
-            log2dec += cs_end;
-            reset = reset || has_bnd;
-        }
     }
 
-    if (FULL) {
-        if (a.final_state && k == a.K - 1) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                *reinterpret_cast<float4*>(a.final_state + st_off + 16 * nt) =
-                    make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-        }
-    } else {
-        const size_t u = ((size_t)b * H + h) * (a.K - 1) + k;
-        float* hl = a.hloc + u * 64 * N + (size_t)(p0 + j16) * N + 4 * q4;
+    if (a.final_state && k == a.K - 1) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            *reinterpret_cast<float4*>(hl + 16 * nt) = make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-        if (lead && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+            *reinterpret_cast<float4*>(a.final_state + st_off + 16 * nt) =
+                make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
     }
 }
 
-template <int N, int MODE, bool SP, int HPW, int NS>
+// ============================================================================
+// bf16 state-only pre-pass of the sequence split.
+//
+// For superchunk k < K-1 of (b, head group) it runs the chunk-state recurrence
+// from a zero state over the superchunk and stores the local end state (hloc)
+// and the total decay (dec; negative if a document starts inside, i.e. the
+// carried state is dropped there).  Only B, X, dt and the doc ids are read.
+// A workgroup covers HPW heads of one B/C group with 4 / PB waves per head; a
+// wave owns PB 16-channel blocks, so each B^T fragment it reads from LDS feeds
+// PB MFMAs and the per-wave overheads (copy issue, waits) are shared by PB
+// blocks.  Copies run NS - 1 chunks ahead through an NS-stage LDS ring; each
+// stage also holds the chunk's dt and doc ids for the heads' lead waves.
+// ============================================================================
+template <int N, int HPW, int PB, int NS>
+struct LdsPre {
+    static constexpr int WPH = 4 / PB;                // waves per head
+    static constexpr int NW = WPH * HPW;              // waves
+    static constexpr int RB = N * 2, XB = 128;        // bytes per B row, per X row of one head
+    static constexpr int TB = Q * RB, TX = Q * XB;
+    static constexpr int oB = 0, oX = TB;             // B tile, then the HPW X tiles
+    static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q]
+    static constexpr int oD = oX + HPW * TX;
+    static constexpr int STAGE = oD + DB;
+    static constexpr int oS = NS * STAGE;
+    // scalars of one chunk (floats): per head w [Q]; cs_end per head; last_seg
+    static constexpr int SC_END = HPW * Q;
+    static constexpr int SC_LAST = SC_END + HPW;
+    static constexpr int SCW = (SC_LAST + 1 + 3) / 4 * 4;
+    static constexpr int bytes = oS + 2 * SCW * 4;
+    static constexpr int RPI_B = 64 / (RB / 16);      // B rows per 1 KiB copy
+    static constexpr int NI_B = Q / RPI_B;
+    static constexpr int NI_X = Q / 8;
+    static constexpr int NI = NI_B + HPW * NI_X;      // copies per chunk
+    static constexpr int NI_W = (NI + NW - 1) / NW;
+};
+
+template <int N, bool SP, int HPW, int PB, int NS>
+__global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(ScanArgs a) {
+    using LD = LdsPre<N, HPW, PB, NS>;
+    static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
+    constexpr int NT = N / 16;
+    constexpr int NW = LD::NW, WPH = LD::WPH;
+    constexpr int RB = LD::RB, XB = LD::XB;
+    constexpr int CPR_B = RB / 16;
+    using SB = Swz<RB>;
+    using SX = Swz<XB>;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* scal = reinterpret_cast<float*>(smem + LD::oS);   // [2][SCW]
+
+    const int L = a.L, H = a.H, G = a.G;
+    const int HQ = H / HPW;
+    const int KU = a.K - 1;
+    const int id = xcd_remap(blockIdx.x, a.B * HQ * KU);
+    const int hq = id % HQ;
+    const int k = (id / HQ) % KU;
+    const int b = id / (HQ * KU);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int hh = wave / WPH;                 // head of this wave within the workgroup
+    const int h = hq * HPW + hh;
+    const int g = (hq * HPW) / (H / G);
+    const bool lead = wave % WPH == 0;         // computes its head's per-token weights
+    const int q4 = lane >> 4;
+    const int j16 = lane & 15;
+    const int p0 = (wave % WPH) * 16 * PB;     // first channel of this wave's blocks
+    const float A2 = a.A[h] * kLog2e;
+    const float dtb = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h] : 0.0f;
+    const int tbeg = k * a.S;
+    const int tend = min(tbeg + a.S, L);
+    const int tl = tend - 1;
+    const bool docs = a.doc != nullptr;
+
+    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)hq * HPW * 64;
+    const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
+    const float* dtbase = a.dt + (size_t)b * L * a.dt_stride + h;
+    const int32_t* docbase = a.doc + (size_t)b * L;
+    const int Ds4 = (int)a.dt_stride * 4;
+
+    // copy slots of this wave: copy wave + NW j of the chunk (B tile, then X tiles)
+    const char* s_base[LD::NI_W];
+    int s_stride[LD::NI_W];
+    uint32_t s_lds[LD::NI_W];
+    int s_row[LD::NI_W];
+    uint32_t s_col[LD::NI_W];
+    bool s_on[LD::NI_W];
+#pragma unroll
+    for (int j = 0; j < LD::NI_W; ++j) {
+        const int i = wave + NW * j;
+        s_on[j] = i < LD::NI;
+        if (i < LD::NI_B) {
+            s_base[j] = reinterpret_cast<const char*>(Bbase);
+            s_stride[j] = (int)a.B_stride * 2;
+            s_lds[j] = LD::oB + i * 1024;
+            const int r = i * LD::RPI_B + lane / CPR_B;
+            s_row[j] = r;
+            s_col[j] = (uint32_t)(((lane % CPR_B) ^ SB::f(r)) * 16);
+        } else {
+            const int ix = s_on[j] ? i - LD::NI_B : 0;
+            const int e = ix / LD::NI_X, ins = ix % LD::NI_X;
+            s_base[j] = reinterpret_cast<const char*>(xhead + e * 64);
+            s_stride[j] = (int)a.x_stride * 2;
+            s_lds[j] = LD::oX + e * LD::TX + ins * 1024;
+            const int r = ins * 8 + lane / (XB / 16);
+            s_row[j] = r;
+            s_col[j] = (uint32_t)(((lane % (XB / 16)) ^ SX::f(r)) * 16);
+        }
+    }
+    const int n_tiles = (LD::NI - wave + NW - 1) / NW;
+    const int n_scal = lead ? (docs ? 3 : 1) : 0;
+    auto issue_tiles = [&](int t0, int st) {
+        const int lim = tl - t0;
+        unsigned char* base = smem + st * LD::STAGE;
+#pragma unroll
+        for (int j = 0; j < LD::NI_W; ++j) {
+            if (s_on[j]) {
+                const char* src = s_base[j] + (size_t)t0 * s_stride[j];
+                dma16(src, (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j], base + s_lds[j]);
+            }
+        }
+    };
+    auto dbuf_of = [&](int st) -> unsigned char* { return smem + st * LD::STAGE + LD::oD + hh * 3 * Q * 4; };
+    auto issue_scalars = [&](int t0, int st) {
+        unsigned char* dbuf = dbuf_of(st);
+        const int rowl = min(lane, tl - t0);
+        dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
+        if (docs) {
+            dma4(docbase, (uint32_t)(t0 + rowl) * 4, dbuf + Q * 4);
+            dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, dbuf + 2 * Q * 4);
+        }
+    };
+
+    f32x4 Hs[PB][NT];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) Hs[pb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float log2dec = 0.0f;
+    bool reset = false;
+
+    const int nchunks = (tend - tbeg + Q - 1) / Q;
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+        if (j < nchunks) {
+            if (lead) issue_scalars(tbeg + j * Q, j);
+            issue_tiles(tbeg + j * Q, j);
+        }
+    }
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = tbeg + c * Q;
+        const int st = NS == 2 ? (c & 1) : c % NS;
+        const int cn = c + NS - 1;
+        const int sn = NS == 2 ? (st ^ 1) : cn % NS;
+        const unsigned char* sB = smem + st * LD::STAGE + LD::oB;
+        const unsigned char* sX = smem + st * LD::STAGE + LD::oX + hh * LD::TX;
+        float* sc = scal + (c & 1) * LD::SCW;
+        // chunk c's copies have landed: only this wave's copies for chunks
+        // c+1 .. c+NS-2 (dt / doc ids, then tiles, of each) may be newer
+        if (c + NS - 2 < nchunks) wait_vmcnt_n((NS - 2) * (n_tiles + n_scal));
+        else wait_vmcnt<0>();
+        // ---- lead waves: segmented cumulative sum of dt*A (log2 domain) and the
+        // chunk-state weights w_s = 2^(cs_end - cs_s) dt_s on the last segment
+        if (lead) {
+            const bool tok_ok = t0 + lane < tend;
+            const unsigned char* dbuf = dbuf_of(st);
+            float dtl = reinterpret_cast<const float*>(dbuf)[lane];
+            const int d0 = reinterpret_cast<const int*>(dbuf)[Q + lane];
+            const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
+            lds_wait();
+            if (cn < nchunks) issue_scalars(t0 + (NS - 1) * Q, sn);
+            if (SP) dtl = softplus_f(dtl + dtb);
+            if (!tok_ok) dtl = 0.0f;
+            const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
+            float cs = dtl * A2;
+            int seg = bnd ? lane : -1;
+            wave_segscan(cs, bnd, seg);
+            const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
+            const int last_seg = __builtin_amdgcn_readlane(seg, 63);
+            const int wseg = last_seg >= 0 ? last_seg : 0;
+            sc[hh * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
+            if (lane == 0) {
+                sc[LD::SC_END + hh] = cs_end;
+                if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
+            }
+        }
+        lds_barrier();                   // chunk c tiles + weights visible; chunk c-1 readers done
+        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn);
+        const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
+        const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
+        const bool has_bnd = last_seg >= 0;
+
+        // ---- (w o X)^T fragments of this wave's blocks via transpose reads
+        FragBF xw[PB][4];
+        const float* wv = sc + hh * Q;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            const float4 w = *reinterpret_cast<const float4*>(wv + 16 * sb + 4 * q4);
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const uint32_t xtr = SX::off(4 * q4 + j16 / 4, p0 + 16 * pb + 4 * (j16 % 4));
+                const FragBF xf = tr_read(sX, xtr + 16 * sb * XB);
+                xw[pb][sb].a = pack_bf16x2(w.x * bf16_lo(xf.a), w.y * bf16_hi(xf.a));
+                xw[pb][sb].b = pack_bf16x2(w.z * bf16_lo(xf.b), w.w * bf16_hi(xf.b));
+            }
+        }
+        // ---- S = B^T (w o X) per block; H = dec H + S (dec = 0 past a document start)
+        const float dec = has_bnd ? 0.0f : fast_exp2(cs_end);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint32_t btr = SB::off(4 * q4 + j16 / 4, 16 * nt + 4 * (j16 % 4));
+            f32x4 acc[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < 4; sb += 2) {
+                const FragBF a0 = tr_read(sB, btr + 16 * sb * RB);
+                const FragBF a1 = tr_read(sB, btr + 16 * (sb + 1) * RB);
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) acc[pb] = mma_bf16(acc[pb], a0, a1, xw[pb][sb], xw[pb][sb + 1]);
+            }
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Hs[pb][nt][r] = fmaf(dec, Hs[pb][nt][r], acc[pb][r]);
+        }
+        log2dec += cs_end;
+        reset = reset || has_bnd;
+    }
+
+    const size_t u = ((size_t)b * H + h) * (a.K - 1) + k;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+        float* hl = a.hloc + u * 64 * N + (size_t)(p0 + 16 * pb + j16) * N + 4 * q4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            *reinterpret_cast<float4*>(hl + 16 * nt) =
+                make_float4(Hs[pb][nt][0], Hs[pb][nt][1], Hs[pb][nt][2], Hs[pb][nt][3]);
+    }
+    if (lead && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+}
+
+template <int N, bool SP, int HPW>
 hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, MODE, SP, HPW, NS>);
-    const size_t lds = LdsBf<N, MODE, HPW, NS>::bytes;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW>);
+    const size_t lds = LdsBf<N, HPW>::bytes;
     static bool checked = false;
     if (!checked) {
         // The kernel's explicit vector-memory waits count only its own copies,
@@ -1064,29 +1284,51 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
         if (e != hipSuccess) return e;
         checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, MODE, SP, HPW, NS>), dim3(units), dim3(256 * HPW), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
 }
-template <int N, int MODE, int HPW, int NS>
-hipError_t launch_scan_bf16_mode(const ScanArgs& a, int units, hipStream_t stream) {
-    return a.dt_softplus ? launch_scan_bf16_k<N, MODE, true, HPW, NS>(a, units, stream)
-                         : launch_scan_bf16_k<N, MODE, false, HPW, NS>(a, units, stream);
+template <int N, int HPW>
+hipError_t launch_scan_bf16_full(const ScanArgs& a, int units, hipStream_t stream) {
+    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW>(a, units, stream)
+                         : launch_scan_bf16_k<N, false, HPW>(a, units, stream);
 }
-// the state-only pre-pass: PRE_HPW heads per workgroup, kPreStages stages
+// the state-only pre-pass: PRE_HPW heads per workgroup, kPrePB channel blocks
+// per wave, kPreStages stages
 constexpr int kPreStages = 3;
+constexpr int kPrePB = 2;
+template <int N, bool SP, int PRE_HPW>
+hipError_t launch_scan_state_k(const ScanArgs& a, hipStream_t stream) {
+    using LD = LdsPre<N, PRE_HPW, kPrePB, kPreStages>;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_state_kernel<N, SP, PRE_HPW, kPrePB, kPreStages>);
+    static bool checked = false;
+    if (!checked) {
+        hipFuncAttributes fa;                   // see launch_scan_bf16_k: no scratch allowed
+        hipError_t e = hipFuncGetAttributes(&fa, fn);
+        if (e != hipSuccess) return e;
+        if (fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LD::bytes);
+        if (e != hipSuccess) return e;
+        checked = true;
+    }
+    const int units = a.B * (a.H / PRE_HPW) * (a.K - 1);
+    hipLaunchKernelGGL((ssd_scan_state_kernel<N, SP, PRE_HPW, kPrePB, kPreStages>), dim3(units), dim3(64 * LD::NW),
+                       LD::bytes, stream, a);
+    return hipGetLastError();
+}
 template <int N, int PRE_HPW>
 hipError_t launch_scan_bf16_pre(const ScanArgs& a, hipStream_t stream) {
-    return launch_scan_bf16_mode<N, kStateOnly, PRE_HPW, kPreStages>(a, a.B * (a.H / PRE_HPW) * (a.K - 1), stream);
+    return a.dt_softplus ? launch_scan_state_k<N, true, PRE_HPW>(a, stream)
+                         : launch_scan_state_k<N, false, PRE_HPW>(a, stream);
 }
 template <int N, int HPW>
 hipError_t launch_scan_bf16(const ScanArgs& a, int pre_hpw, hipStream_t stream) {
     if (a.K > 1) {
-        hipError_t e = pre_hpw == 4 ? launch_scan_bf16_pre<N, (N <= 64 ? 4 : 2)>(a, stream)
+        hipError_t e = pre_hpw == 4 ? launch_scan_bf16_pre<N, 4>(a, stream)
                      : pre_hpw == 2 ? launch_scan_bf16_pre<N, 2>(a, stream)
                                     : launch_scan_bf16_pre<N, 1>(a, stream);
         if (e != hipSuccess) return e;
     }
-    return launch_scan_bf16_mode<N, kFull, HPW, 2>(a, a.B * (a.H / HPW) * a.K, stream);
+    return launch_scan_bf16_full<N, HPW>(a, a.B * (a.H / HPW) * a.K, stream);
 }
 
 template <typename T, int N, int MODE>
@@ -1112,15 +1354,15 @@ template <int N>
 size_t bf16_lds_n(int hpw, bool full) {
     if (full) {
         switch (hpw) {
-            case 1: return LdsBf<N, kFull, 1>::bytes;
-            case 2: return LdsBf<N, kFull, 2>::bytes;
-            case 4: return N <= 64 ? LdsBf<N, kFull, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
+            case 1: return LdsBf<N, 1>::bytes;
+            case 2: return LdsBf<N, 2>::bytes;
+            case 4: return N <= 64 ? LdsBf<N, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
         }
     } else {
         switch (hpw) {
-            case 1: return LdsBf<N, kStateOnly, 1, kPreStages>::bytes;
-            case 2: return LdsBf<N, kStateOnly, 2, kPreStages>::bytes;
-            case 4: return LdsBf<N, kStateOnly, 4, kPreStages>::bytes;
+            case 1: return LdsPre<N, 1, kPrePB, kPreStages>::bytes;
+            case 2: return LdsPre<N, 2, kPrePB, kPreStages>::bytes;
+            case 4: return LdsPre<N, 4, kPrePB, kPreStages>::bytes;
         }
     }
     return kLdsPerCU + 1;
@@ -1138,7 +1380,8 @@ size_t bf16_lds(int N, int hpw, bool full) {
 int bf16_wgs_per_cu(int N, int hpw, bool full) {
     const size_t bytes = bf16_lds(N, hpw, full);
     if (bytes > kLdsPerCU) return 0;
-    return (int)std::min<size_t>(kLdsPerCU / bytes, (size_t)(kMaxWavesPerCU / (4 * hpw)));
+    const int waves = full ? 4 * hpw : 4 * hpw / kPrePB;
+    return (int)std::min<size_t>(kLdsPerCU / bytes, (size_t)(kMaxWavesPerCU / waves));
 }
 // Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a
 // group and gives the most waves per CU.
