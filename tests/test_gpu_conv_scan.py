@@ -155,6 +155,10 @@ SCAN_CASES = [
     ("bf16", 64, 2, 4, 65, False, False, True),
     ("bf16", 128, 4, 8, 333, True, True, True),
     ("bf16", 128, 1, 2, 1, False, True, True),
+    # four heads per B/C group: the widest workgroups the plan picks
+    ("bf16", 16, 1, 4, 190, True, True, True),
+    ("bf16", 32, 2, 8, 129, False, True, True),
+    ("bf16", 128, 1, 4, 100, True, False, True),
 ]
 
 
@@ -179,6 +183,10 @@ SPLIT_CASES = [
     ("bf16", 16, 2, 2, 4096, True, False, True),
     ("f32", 64, 1, 2, 1100, True, True, True),
     ("f32", 32, 2, 4, 2048, False, True, False),
+    # four heads per group: the pre-pass with four heads per workgroup
+    ("bf16", 128, 1, 4, 3000, True, True, True),
+    ("bf16", 32, 1, 4, 2500, False, False, True),
+    ("bf16", 16, 2, 8, 1800, True, True, False),
 ]
 
 
