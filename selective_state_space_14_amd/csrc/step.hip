@@ -13,9 +13,9 @@
 //      result is deterministic and independent of the batch size;
 //   y[p] = (C . h[p] + D x_p) * silu(z_p).
 // The state is 96% of the bytes (B*H*P*N*4 read + written per token): its
-// loads and stores are nontemporal (it is touched once per token), the next
-// round's loads are issued before the current round is computed, and the
-// first round's even before the conv phase.
+// loads and stores are nontemporal (it is touched once per token), loads run
+// two rounds ahead of the round being computed, and the first two rounds'
+// loads are issued even before the conv phase.
 // The recurrence is the Mamba-2 SSD layer of the Codestral-Mamba port header
 // (codestral_mamba.ts); step == forward at length 1 with the state carried
 // follows mojolearn.Mamba3Block's step() description.
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         a.ssm_state + (size_t)b * H * P * N, 0, nrows * NQ * 16, 0x00020000);
     constexpr int kNT = 2;                           // cache policy: nontemporal
-    f4v s_cur[FPL], s_nxt[FPL];
+    f4v s_cur[FPL], s_nxt[FPL], s_nx2[FPL];     // rounds r, r+1, r+2
     auto row_of = [&](int r) { return r * RPR + wave * RPW + lane / LPR; };
     auto off_of = [&](int row, int j) { return (uint32_t)((row * NQ + q + j * LPR) * 16); };
     auto load_round = [&](int r, f4v* dst) {
@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
             dst[j] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(sr, off_of(row, j), 0, kNT));
     };
     load_round(0, s_cur);             // independent of the conv phase: start it now
+    load_round(1, s_nxt);
 
     // ---- 1. conv window, activation, buffer shift
     const T* raw = static_cast<const T*>(a.xbc_raw) + (size_t)b * C;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float4 Bq[FPL], Cq[FPL];
     int cur_gofs = -1;
     for (int r = 0; r < nrounds; ++r) {
-        load_round(r + 1, s_nxt);                    // past the last round: out of range, reads 0
+        load_round(r + 2, s_nx2);                    // past the last round: out of range, reads 0
         const int row = row_of(r);
         // a wave's rows lie in one head; a wave past the end computes on zeros
         // and its stores fall outside the ranges
@@ -211,7 +212,10 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         const bool first = q == 0 && row < nrows;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yr, first ? (uint32_t)(h * P + p) * 4 : 0x7fffffffu, 0, 0);
 #pragma unroll
-        for (int j = 0; j < FPL; ++j) s_cur[j] = s_nxt[j];
+        for (int j = 0; j < FPL; ++j) {
+            s_cur[j] = s_nxt[j];
+            s_nxt[j] = s_nx2[j];
+        }
     }
 }
 
