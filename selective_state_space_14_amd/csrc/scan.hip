@@ -815,17 +815,31 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             Hs[nt] = f32x4{v.x, v.y, v.z, v.w};
         }
     }
-    for (int j = 0; j < k; ++j) {
-        const size_t u = ((size_t)b * H + h) * (a.K - 1) + j;
-        const float dj = a.dec[u];
-        const float* hl = a.hloc + u * 64 * N + (size_t)(p0 + j16) * N + 4 * q4;
+    // the preceding superchunks' local states, folded in order; their loads
+    // are issued FOLD at a time so the fold costs ceil(k / FOLD) latencies
+    constexpr int FOLD = 16 / NT < 4 ? 16 / NT : 4;
+    for (int j0 = 0; j0 < k; j0 += FOLD) {
+        float dj[FOLD];
+        float4 v[FOLD][NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const float4 v = *reinterpret_cast<const float4*>(hl + 16 * nt);
-            Hs[nt][0] = dj < 0.0f ? v.x : fmaf(dj, Hs[nt][0], v.x);
-            Hs[nt][1] = dj < 0.0f ? v.y : fmaf(dj, Hs[nt][1], v.y);
-            Hs[nt][2] = dj < 0.0f ? v.z : fmaf(dj, Hs[nt][2], v.z);
-            Hs[nt][3] = dj < 0.0f ? v.w : fmaf(dj, Hs[nt][3], v.w);
+        for (int i = 0; i < FOLD; ++i) {
+            const size_t u = ((size_t)b * H + h) * (a.K - 1) + min(j0 + i, k - 1);
+            dj[i] = a.dec[u];
+            const float* hl = a.hloc + u * 64 * N + (size_t)(p0 + j16) * N + 4 * q4;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) v[i][nt] = *reinterpret_cast<const float4*>(hl + 16 * nt);
+        }
+#pragma unroll
+        for (int i = 0; i < FOLD; ++i) {
+            if (j0 + i < k) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    Hs[nt][0] = dj[i] < 0.0f ? v[i][nt].x : fmaf(dj[i], Hs[nt][0], v[i][nt].x);
+                    Hs[nt][1] = dj[i] < 0.0f ? v[i][nt].y : fmaf(dj[i], Hs[nt][1], v[i][nt].y);
+                    Hs[nt][2] = dj[i] < 0.0f ? v[i][nt].z : fmaf(dj[i], Hs[nt][2], v[i][nt].z);
+                    Hs[nt][3] = dj[i] < 0.0f ? v[i][nt].w : fmaf(dj[i], Hs[nt][3], v[i][nt].w);
+                }
+            }
         }
     }
     // settle the state loads here, before any copy is in flight
