@@ -1,13 +1,15 @@
 /*
  * ssd.h -- C ABI of libssd.so, the gfx950 (MI355X) Mamba-2 SSD mixer core.
  *
- * Three operations, each one HIP kernel launch on the caller's stream:
+ * Four operations, each one or two HIP kernel launches on the caller's stream:
  *
  *   ssd_conv_fwd        causal depthwise conv (k = 4) + SiLU over the
  *                       [x | B | C] columns, and dt = softplus(dt_raw + dt_bias)
  *   ssd_chunk_scan_fwd  the SSD selective scan in chunks of 64 tokens, with
  *                       B/C groups, document resets, initial/final state, the
  *                       D skip and the y * silu(z) gate
+ *   ssd_mixer_fwd       both of the above in one pass: the scan reads the raw
+ *                       columns and convolves each chunk on chip
  *   ssd_step            one decode token per sequence: conv from a rolling
  *                       buffer, state update, output and gate
  *
@@ -148,7 +150,9 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
  * a first pass stores each superchunk's local end state and total decay in
  * the workspace and the main pass folds them in (the state passing of the
  * SSD paper's chunked algorithm, one level up).  Results then agree with the
- * sequential pass to fp32 rounding, not bitwise.
+ * sequential pass to fp32 rounding, not bitwise.  The first pass also copies
+ * init_state into the workspace and the main pass reads only that copy, so
+ * final_state may alias init_state on either path.
  *
  *   x       T   [B][L][H*P]  row stride x_row_stride
  *   Bm, Cm  T   [B][L][G*N]  row strides B_row_stride, C_row_stride
@@ -186,6 +190,59 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
 /* Bytes of workspace that let ssd_chunk_scan_fwd split the sequence for
  * these sizes; 0 when no split pays (then the workspace is ignored). */
 size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
+
+/*
+ * ssd_mixer_fwd -- the conv prologue and the scan in one pass.
+ *
+ * Computes what ssd_conv_fwd followed by ssd_chunk_scan_fwd computes -- the
+ * conv (k = 4) + act over the raw [x | B | C] columns, dt = softplus(dt_raw +
+ * dt_bias), the scan with groups, documents and states, the D skip and the
+ * gate -- without writing the convolved columns or dt to memory (the fused
+ * conv-in-scan prologue; the Codestral-Mamba port header for the in_proj row
+ * layout and the conv weight).  For bf16 the scan kernels read the raw tiles
+ * and convolve each chunk in LDS with the same fp32 arithmetic as
+ * ssd_conv_fwd, so y, final_state and conv_state_out are bit-identical to
+ * the two-call composition (ssd_chunk_scan_fwd with dt_softplus = 0 on
+ * ssd_conv_fwd's outputs) given the same workspace choice.  For fp32 the two
+ * kernels run back to back through the workspace.
+ *
+ *   xbc_raw      T  [B][L][conv_dim], row stride xbc_raw_row_stride
+ *   conv_w       f32 [conv_dim][K], conv_b f32 [conv_dim] or NULL; act as in
+ *                ssd_conv_fwd
+ *   dt_raw       T  [B][L][H], row stride dt_raw_row_stride (even for bf16:
+ *                read in 4-byte words; base 4-byte aligned)
+ *   dt_bias      f32 [H] or NULL; A, D, z, doc_ids, init_state, final_state
+ *                and y as in ssd_chunk_scan_fwd (final_state may equal
+ *                init_state)
+ *   conv_state_in, conv_state_out  T [B][K-1][conv_dim] or NULL, as in
+ *                ssd_conv_fwd, except that they must not overlap
+ *                (SSD_ERR_BAD_SHAPE): several workgroups read the incoming
+ *                B/C history while another writes the outgoing one
+ *   workspace    bf16: NULL, 0 (sequential pass) or at least
+ *                ssd_mixer_workspace_size() bytes (the sequence split, as in
+ *                ssd_chunk_scan_fwd).  fp32: required, at least
+ *                ssd_mixer_workspace_size() bytes (the conv output and dt are
+ *                staged there, then the split state).  16-byte aligned,
+ *                owned by the caller, not shared by concurrent calls.
+ * Row strides are in elements, >= the row width and <= 4194304.  L = 0
+ * copies both carried states through.
+ */
+int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, int dtype,
+                  const void *xbc_raw, int64_t xbc_raw_row_stride,
+                  const float *conv_w, const float *conv_b,
+                  const void *dt_raw, int64_t dt_raw_row_stride, const float *dt_bias,
+                  const float *A, const float *D,
+                  const void *z, int64_t z_row_stride,
+                  const int32_t *doc_ids,
+                  const void *conv_state_in, void *conv_state_out,
+                  const float *init_state, float *final_state,
+                  int act, float *y, int64_t y_row_stride,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace ssd_mixer_fwd uses for these sizes (bf16: the split
+ * state, 0 when no split pays; fp32: the staged conv output and dt, plus the
+ * split state). */
+size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
 
 /*
  * ssd_step -- one decode token for each of B sequences.

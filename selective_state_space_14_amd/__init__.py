@@ -1,9 +1,10 @@
 """Mamba-2 SSD mixer core on MI355X (gfx950): Python binding of libssd.so.
 
-The three entry points mirror the C ABI in include/ssd.h one to one:
+The entry points mirror the C ABI in include/ssd.h one to one:
 
     ssd_conv_fwd        causal depthwise conv (k=4) + SiLU, dt = softplus(dt + dt_bias)
     ssd_chunk_scan_fwd  chunked (64) SSD scan with groups, documents, states, D skip, z gate
+    ssd_mixer_fwd       both in one pass (the scan convolves the raw columns on chip)
     ssd_step            one decode token per sequence
 
 This module only marshals torch tensors (device pointers, row strides, the
@@ -18,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
+__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_step",
+           "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size",
            "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -60,6 +62,11 @@ def load() -> ctypes.CDLL:
                                        I64, P, P, P, P, I64, P, SZ, P]
     lib.ssd_chunk_scan_workspace_size.restype = SZ
     lib.ssd_chunk_scan_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.ssd_mixer_fwd.restype = I
+    lib.ssd_mixer_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I64, P, P, P, P, P,
+                                  I, P, I64, P, SZ, P]
+    lib.ssd_mixer_workspace_size.restype = SZ
+    lib.ssd_mixer_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.ssd_step.restype = I
     lib.ssd_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P]
     _lib = lib
@@ -194,6 +201,52 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=
         _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
         _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
         _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
+    _check(st)
+    return y
+
+
+def ssd_mixer_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
+    return int(load().ssd_mixer_workspace_size(B, L, H, P, N, G, dtype))
+
+
+def ssd_mixer_fwd(xbc_raw, dt_raw, conv_w, A, *, H, P, N, G, K=4, conv_b=None, dt_bias=None, D=None, z=None,
+                  doc_ids=None, conv_state_in=None, conv_state_out=None, init_state=None, final_state=None,
+                  act=SSD_ACT_SILU, y=None, chunk=64, workspace=None, stream=None):
+    """Conv prologue + scan in one pass.  xbc_raw [B, L, conv_dim], dt_raw [B, L, H] (same dtype),
+    conv_w [conv_dim, K] fp32, A [H] fp32; the rest as in ssd_conv_fwd / ssd_chunk_scan_fwd.
+
+    Returns y [B, L, H*P] fp32 (and writes final_state / conv_state_out if given)."""
+    lib = load()
+    B, L = xbc_raw.shape[0], xbc_raw.shape[1]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    rs_in = _rows(xbc_raw, "xbc_raw", B, L, C)
+    rs_dt = _rows(dt_raw, "dt_raw", B, L, H)
+    rs_z = _rows(z, "z", B, L, H * P)
+    if y is None:
+        y = torch.empty((B, L, H * P), dtype=torch.float32, device=xbc_raw.device)
+    rs_y = _rows(y, "y", B, L, H * P)
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    _contig(conv_state_in, "conv_state_in", (B, K - 1, C))
+    _contig(conv_state_out, "conv_state_out", (B, K - 1, C))
+    _contig(init_state, "init_state", (B, H, P, N))
+    _contig(final_state, "final_state", (B, H, P, N))
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_mixer_fwd(
+        B, L, H, P, N, G, K, chunk, dtype,
+        _ptr(xbc_raw, "xbc_raw"), rs_in,
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(conv_b, "conv_b", torch.float32),
+        _ptr(dt_raw, "dt_raw", xbc_raw.dtype), rs_dt, _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
+        _ptr(z, "z", xbc_raw.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(conv_state_in, "conv_state_in", xbc_raw.dtype), _ptr(conv_state_out, "conv_state_out", xbc_raw.dtype),
+        _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
+        int(act), _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
     _check(st)
     return y
 

@@ -35,6 +35,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int esize(int dtype) { return dtype == SSD_F32 ? 4 : 2; }
 
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
 // Shared size checks; returns SSD_OK or a failure with the message set.
 int check_dims(const char* fn, int B, int L, int H, int P, int N, int G, int K, int dtype) {
     if (dtype != SSD_F32 && dtype != SSD_BF16)
@@ -225,7 +227,7 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
             return hip_status(fn, ssd::launch_copy16(init_state, final_state, (size_t)B * H * P * N * 4 / 16, s));
         return ok();
     }
-    ssd::ScanArgs a;
+    ssd::ScanArgs a{};
     a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
     a.x = x; a.x_stride = x_row_stride;
     a.Bm = Bm; a.B_stride = B_row_stride;
@@ -237,12 +239,149 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     a.doc = doc_ids;
     a.init_state = init_state; a.final_state = final_state;
     a.y = y; a.y_stride = y_row_stride;
-    a.K = 1; a.S = ((L + 63) / 64) * 64; a.hloc = nullptr; a.dec = nullptr;
+    a.K = 1; a.S = ((L + 63) / 64) * 64; a.hloc = nullptr; a.dec = nullptr; a.h0 = nullptr;
     if (split) {
         ssd::scan_split(B, L, H, N, G, dtype, a.K, a.S);
         const size_t u = (size_t)B * H * (a.K - 1);
         a.hloc = static_cast<float*>(workspace);
         a.dec = a.hloc + u * (size_t)P * N;
+        if (init_state) a.h0 = a.dec + ((u * sizeof(float) + 255) / 256) * 256 / sizeof(float);
+    }
+    return hip_status(fn, ssd::launch_scan(a, s));
+}
+
+size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
+    if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0) return 0;
+    const size_t scan = ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
+    if (dtype != SSD_F32) return scan;
+    // fp32: the conv output [B][L][conv_dim] and dt [B][L][H] are staged first
+    const size_t C = (size_t)H * P + 2 * (size_t)G * N;
+    return round256((size_t)B * L * C * 4) + round256((size_t)B * L * H * 4) + scan;
+}
+
+int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, int dtype,
+                  const void* xbc_raw, int64_t xbc_raw_row_stride,
+                  const float* conv_w, const float* conv_b,
+                  const void* dt_raw, int64_t dt_raw_row_stride, const float* dt_bias,
+                  const float* A, const float* D,
+                  const void* z, int64_t z_row_stride,
+                  const int32_t* doc_ids,
+                  const void* conv_state_in, void* conv_state_out,
+                  const float* init_state, float* final_state,
+                  int act, float* y, int64_t y_row_stride,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_mixer_fwd";
+    TRY(check_dims(fn, B, L, H, P, N, G, K, dtype));
+    if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    const int64_t C = (int64_t)H * P + 2LL * G * N;
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "xbc_raw", xbc_raw, xbc_raw_row_stride, C, es, work));
+    TRY(check_tensor(fn, "z", z, z_row_stride, (int64_t)H * P, es, false));
+    TRY(check_tensor(fn, "y", y, y_row_stride, (int64_t)H * P, 4, work));
+    if (work) {
+        if (!dt_raw) return fail(SSD_ERR_NULL_ARG, "%s: dt_raw is NULL", fn);
+        if (dt_raw_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: dt_raw row stride %lld is smaller than H=%d", fn,
+                        (long long)dt_raw_row_stride, H);
+        if (dtype == SSD_BF16 && (dt_raw_row_stride & 1))
+            return fail(SSD_ERR_ALIGNMENT, "%s: dt_raw row stride %lld must be even for bf16 (4-byte reads)", fn,
+                        (long long)dt_raw_row_stride);
+    }
+    TRY(check_ptr(fn, "dt_raw", dt_raw, false, false));
+    TRY(check_ptr(fn, "conv_w", conv_w, work, true));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, B > 0, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    TRY(check_ptr(fn, "conv_state_in", conv_state_in, false, true));
+    TRY(check_ptr(fn, "conv_state_out", conv_state_out, false, true));
+    TRY(check_ptr(fn, "init_state", init_state, false, true));
+    TRY(check_ptr(fn, "final_state", final_state, false, true));
+    if (conv_state_in && conv_state_out) {
+        const uintptr_t i0 = reinterpret_cast<uintptr_t>(conv_state_in), o0 = reinterpret_cast<uintptr_t>(conv_state_out);
+        const uintptr_t n = (uintptr_t)B * 3 * (uintptr_t)C * es;
+        if (i0 < o0 + n && o0 < i0 + n)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: conv_state_out must not overlap conv_state_in (several workgroups "
+                        "read the incoming B/C history while others write the outgoing one)", fn);
+    }
+    if (work && (xbc_raw_row_stride > (1 << 22) || z_row_stride > (1 << 22) || dt_raw_row_stride > (1 << 22) ||
+                 y_row_stride > (1 << 22)))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
+    if (work && y == final_state)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: y must not alias final_state", fn);
+    const size_t need = ssd_mixer_workspace_size(B, L, H, P, N, G, dtype);
+    const bool split = workspace != nullptr && need > 0;
+    if (work && dtype == SSD_F32 && workspace == nullptr)
+        return fail(SSD_ERR_WORKSPACE, "%s: fp32 needs a workspace of ssd_mixer_workspace_size()=%zu bytes (the "
+                    "conv output is staged there)", fn, need);
+    if (split && workspace_bytes < need)
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace_bytes, need);
+    if (split && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        // nothing to scan; both carried states pass through unchanged
+        if (B > 0 && conv_state_out) {
+            hipError_t e = ssd::launch_copy16(conv_state_in, conv_state_out, (size_t)B * 3 * C * es / 16, s);
+            if (e != hipSuccess) return hip_status(fn, e);
+        }
+        if (B > 0 && final_state)
+            return hip_status(fn, ssd::launch_copy16(init_state, final_state, (size_t)B * H * P * N * 4 / 16, s));
+        return ok();
+    }
+
+    ssd::ScanArgs a{};
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.A = A; a.D = D;
+    a.z = z; a.z_stride = z_row_stride;
+    a.doc = doc_ids;
+    a.init_state = init_state; a.final_state = final_state;
+    a.y = y; a.y_stride = y_row_stride;
+    a.dt_bias = dt_bias;
+    a.K = 1; a.S = ((L + 63) / 64) * 64;
+    char* ws = static_cast<char*>(workspace);
+    if (dtype == SSD_F32) {
+        // conv into the workspace, then the scan over it
+        float* xbc = reinterpret_cast<float*>(ws);
+        float* dtw = reinterpret_cast<float*>(ws + round256((size_t)B * L * C * 4));
+        ws += round256((size_t)B * L * C * 4) + round256((size_t)B * L * H * 4);
+        ssd::ConvArgs c;
+        c.B = B; c.L = L; c.C = (int)C; c.H = H; c.dtype = dtype; c.act = act;
+        c.raw = xbc_raw; c.raw_stride = xbc_raw_row_stride;
+        c.w = conv_w; c.bias = conv_b;
+        c.dt_raw = dt_raw; c.dt_stride = dt_raw_row_stride; c.dt_bias = dt_bias;
+        c.doc = doc_ids;
+        c.state_in = conv_state_in; c.state_out = conv_state_out;
+        c.out = xbc; c.out_stride = C;
+        c.dt_out = dtw;
+        hipError_t e = ssd::launch_conv(c, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+        a.x = xbc; a.x_stride = C;
+        a.Bm = xbc + (size_t)H * P; a.B_stride = C;
+        a.Cm = xbc + (size_t)H * P + (size_t)G * N; a.C_stride = C;
+        a.dt = dtw; a.dt_stride = H; a.dt_softplus = 0;
+    } else {
+        const char* raw = static_cast<const char*>(xbc_raw);
+        a.x = raw; a.x_stride = xbc_raw_row_stride;
+        a.Bm = raw + (size_t)H * P * es; a.B_stride = xbc_raw_row_stride;
+        a.Cm = raw + ((size_t)H * P + (size_t)G * N) * es; a.C_stride = xbc_raw_row_stride;
+        a.dt16 = static_cast<const uint16_t*>(dt_raw); a.dt16_stride = dt_raw_row_stride; a.dt_softplus = 1;
+        a.conv = 1; a.act = act;
+        a.conv_w = conv_w; a.conv_b = conv_b;
+        a.cstate_in = conv_state_in; a.cstate_out = conv_state_out;
+    }
+    if (ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype) > 0 && workspace != nullptr) {
+        ssd::scan_split(B, L, H, N, G, dtype, a.K, a.S);
+        const size_t u = (size_t)B * H * (a.K - 1);
+        a.hloc = reinterpret_cast<float*>(ws);
+        a.dec = a.hloc + u * (size_t)P * N;
+        if (init_state) a.h0 = a.dec + ((u * sizeof(float) + 255) / 256) * 256 / sizeof(float);
     }
     return hip_status(fn, ssd::launch_scan(a, s));
 }

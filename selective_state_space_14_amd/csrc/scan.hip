@@ -288,10 +288,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) Hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (FULL) {
-        if (a.init_state) {
+        const float* h_init = a.K > 1 ? a.h0 : a.init_state;
+        if (h_init) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const float4 v = *reinterpret_cast<const float4*>(a.init_state + st_off + 16 * nt);
+                const float4 v = *reinterpret_cast<const float4*>(h_init + st_off + 16 * nt);
                 Hs[nt] = f32x4{v.x, v.y, v.z, v.w};
             }
         }
@@ -513,6 +514,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
         for (int nt = 0; nt < NT; ++nt)
             *reinterpret_cast<float4*>(hl + 16 * nt) = make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
         if (tid == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+        if (k == 0 && a.h0) {
+            // the main pass reads this copy instead of init_state
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<float4*>(a.h0 + st_off + 16 * nt) =
+                    *reinterpret_cast<const float4*>(a.init_state + st_off + 16 * nt);
+        }
     }
 }
 
@@ -641,6 +649,68 @@ struct Swz {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Fused conv prologue (CV kernels): a chunk's raw B (and C) and X tiles are
+// convolved (k = 4) and activated in place in LDS before any contraction reads
+// them.  A lane owns one 4-byte word (two channels) of the tile rows; waves
+// are grouped WPS to a row segment of R consecutive rows, which the lane walks
+// in order with the three previous raw rows in registers.  The arithmetic (the
+// fp32 fma chain bias + w0 x(t-3) + w1 x(t-2) + w2 x(t-1) + w3 x(t), SiLU,
+// rounding to bf16) and the document handling (history zeroed where a
+// document starts, halo rows cut at starts inside them) are those of
+// ssd_conv_fwd, so the contractions see bit-identical operands.
+template <int N, int HPW, bool WITH_C, int NW>
+struct ConvMap {
+    static constexpr int NWB = (WITH_C ? 2 : 1) * (N / 2);   // B (and C) words per row
+    static constexpr int WD = NWB + 32 * HPW;                 // words per row, X last
+    static constexpr int WPS = (WD + 63) / 64;                // waves per row segment
+    static constexpr int RS = NW / WPS;                       // row segments
+    static constexpr int R = (Q + RS - 1) / RS;               // rows per segment
+};
+
+// One lane's conv word inside a stage, swizzled like the copies: row r of the
+// word's tile sits at (tp + r * rb) ^ (f(r) << 4), f(r) = (r >> rl_sh) & cpr_m
+// (tp = tile offset | 16-byte piece << 4 | byte in the piece; the tile offset
+// is a multiple of rb, so the xor only touches the piece bits).
+struct ConvWord {
+    uint32_t tp;
+    int rb, rl_sh, cpr_m;
+};
+__device__ __forceinline__ ConvWord conv_word(uint32_t tile, int rb, int wb) {
+    const int rl = rb >= 256 ? 1 : 256 / rb;
+    return {tile | (uint32_t)((wb >> 2) << 4) | (uint32_t)((wb & 3) * 4), rb,
+            rl == 1 ? 0 : (rl == 2 ? 1 : (rl == 4 ? 2 : 3)), rb / 16 - 1};
+}
+// RBU > 0: every lane's tile rows are RBU bytes, so the swizzle is wave-uniform
+// and only tp is per lane.
+template <int RBU>
+__device__ __forceinline__ uint32_t conv_off(const ConvWord& w, int r) {
+    if constexpr (RBU > 0) {
+        constexpr int rl = RBU >= 256 ? 1 : 256 / RBU;
+        constexpr int sh = rl == 1 ? 0 : (rl == 2 ? 1 : (rl == 4 ? 2 : 3));
+        return (w.tp + (uint32_t)(r * RBU)) ^ ((uint32_t)((r >> sh) & (RBU / 16 - 1)) << 4);
+    } else {
+        return (w.tp + (uint32_t)(r * w.rb)) ^ ((uint32_t)((r >> w.rl_sh) & w.cpr_m) << 4);
+    }
+}
+// Conv of one row for the word's two channels: history v3 (t-3), v2, v1 and
+// the current raw word; returns the packed bf16 pair.
+__device__ __forceinline__ uint32_t conv_pair(const float (&w)[2][4], const float (&cb)[2], uint32_t v3,
+                                              uint32_t v2, uint32_t v1, uint32_t cur, bool silu) {
+    float o[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const auto el = [&](uint32_t v) { return e ? bf16_hi(v) : bf16_lo(v); };
+        float v = cb[e];
+        v = fmaf(w[e][0], el(v3), v);
+        v = fmaf(w[e][1], el(v2), v);
+        v = fmaf(w[e][2], el(v1), v);
+        v = fmaf(w[e][3], el(cur), v);
+        o[e] = silu ? silu_f(v) : v;
+    }
+    return pack_bf16x2(o[0], o[1]);
+}
+
 // LDS plan of the full pass: two stages of B, C and the heads' X tiles, the
 // heads' M^T fragments, each wave's z tile, the heads' dt / doc ids (one
 // buffer), and two buffers of per-token scalars.
@@ -665,7 +735,10 @@ struct LdsBf {
     static constexpr int SC_SEG = 4 * HPW * Q;
     static constexpr int SC_END = SC_SEG + Q;
     static constexpr int SC_LAST = SC_END + HPW;
-    static constexpr int SCW = (SC_LAST + 1 + 3) / 4 * 4;
+    // fused conv: document starts of the chunk (64-bit mask), and of the two
+    // tokens before it (bit 0: t0 - 1, bit 1: t0 - 2)
+    static constexpr int SC_ST = SC_LAST + 1;
+    static constexpr int SCW = (SC_ST + 3 + 3) / 4 * 4;
     static constexpr int bytes = oS + 2 * SCW * 4;
     // 16-byte copies per chunk: rows per instruction of a B/C tile and of an X tile
     static constexpr int RPI_B = 64 / (RB / 16);
@@ -677,10 +750,11 @@ struct LdsBf {
     static constexpr int NI_MIN = NI / NW;            // fewest
 };
 
-template <int N, bool SP, int HPW>
+template <int N, bool SP, int HPW, bool CV>
 __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     using LD = LdsBf<N, HPW>;
     static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
+    static_assert(SP || !CV, "the fused conv takes raw dt through the softplus");
     constexpr int NT = N / 16;
     constexpr int NW = LD::NW;
     constexpr int RB = LD::RB, XB = LD::XB;
@@ -724,10 +798,12 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int Zs2 = (int)(gate ? a.z_stride : a.x_stride) * 2;
     const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
     const uint16_t* Cbase = static_cast<const uint16_t*>(a.Cm) + (size_t)b * L * a.C_stride + (size_t)g * N;
-    const float* dtbase = a.dt + (size_t)b * L * a.dt_stride + h;
+    // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * L * a.dt16_stride + (h & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * L * a.dt_stride + h);
     const int32_t* docbase = a.doc + (size_t)b * L;
     float* ybase = a.y + (size_t)b * L * a.y_stride + h * 64;
-    const int Ds4 = (int)a.dt_stride * 4;
+    const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
     const int Ys = (int)a.y_stride;
 
     unsigned char* zbuf = smem + LD::oZ + wave * LD::ZW;              // this wave's z tile
@@ -786,7 +862,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
     auto issue_scalars = [&](int t0) {
         const int rowl = min(lane, tl - t0);
-        dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
+        dma4(static_cast<const char*>(dtbase) + (size_t)t0 * Ds4, (uint32_t)(rowl * Ds4), dbuf);
         if (docs) {
             dma4(docbase, (uint32_t)(t0 + rowl) * 4, dbuf + Q * 4);
             dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, dbuf + 2 * Q * 4);
@@ -808,10 +884,11 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const size_t st_off = (((size_t)b * H + h) * 64 + p0 + j16) * N + 4 * q4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) Hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.init_state) {
+    const float* h_init = a.K > 1 ? a.h0 : a.init_state;   // split: the pre-pass's copy
+    if (h_init) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float4 v = *reinterpret_cast<const float4*>(a.init_state + st_off + 16 * nt);
+            const float4 v = *reinterpret_cast<const float4*>(h_init + st_off + 16 * nt);
             Hs[nt] = f32x4{v.x, v.y, v.z, v.w};
         }
     }
@@ -846,6 +923,102 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Hs[nt]));
 
+    // ---- fused conv: this lane's word, its weights, and the raw halo rows of
+    // the first chunk (the conv state at t = 0, else the three rows before)
+    using CM = ConvMap<N, HPW, true, NW>;
+    static_assert(!CV || (CM::RS >= 1 && CM::R >= 3 && (CM::RS - 1) * CM::R < Q), "conv row segments");
+    const int cseg = wave / CM::WPS;
+    const int cwi = (wave % CM::WPS) * 64 + lane;
+    const bool c_on = CV && cseg < CM::RS && cwi < CM::WD;
+    const int CD = H * 64 + 2 * G * N;              // conv_dim
+    constexpr int RBU = RB == XB ? RB : 0;        // B/C and X rows alike: wave-uniform swizzle
+    // the lane's word: its tile in a stage, its channel, its raw column in global memory
+    auto conv_lane = [&](int wi, ConvWord& w, int& ch, const uint16_t*& src, int64_t& stride) {
+        if (wi < N) {
+            const bool isC = wi >= N / 2;
+            const int wb = isC ? wi - N / 2 : wi;
+            w = conv_word(isC ? LD::oC : LD::oB, RB, wb);
+            ch = H * 64 + (isC ? G * N : 0) + g * N + 2 * wb;
+            src = (isC ? Cbase : Bbase) + 2 * wb;
+            stride = isC ? a.C_stride : a.B_stride;
+        } else {
+            const int e = (wi - N) / 32, wb = (wi - N) % 32;
+            w = conv_word(LD::oX + e * LD::TX, XB, wb);
+            ch = (hq * HPW + e) * 64 + 2 * wb;
+            src = xhead + e * 64 + 2 * wb;
+            stride = a.x_stride;
+        }
+    };
+    ConvWord cw{};
+    float cwt[2][4] = {}, cbias[2] = {};
+    uint32_t hw3 = 0, hw2 = 0, hw1 = 0;            // raw rows t0-3, t0-2, t0-1 (segment 0)
+    int pbits = 0;                                 // lead of head 0: starts at t0-1 (bit 0), t0-2 (bit 1)
+    // the B/C columns of the conv state are written by the group's first workgroup
+    const bool bc_owner = (hq * HPW) % (H / G) == 0;
+    if constexpr (CV) {
+        int ch;
+        const uint16_t* src;
+        int64_t cstride;
+        conv_lane(min(cwi, CM::WD - 1), cw, ch, src, cstride);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float4 wv = *reinterpret_cast<const float4*>(a.conv_w + (size_t)(ch + e) * 4);
+            cwt[e][0] = wv.x; cwt[e][1] = wv.y; cwt[e][2] = wv.z; cwt[e][3] = wv.w;
+            cbias[e] = a.conv_b ? a.conv_b[ch + e] : 0.0f;
+        }
+        if (tbeg == 0) {
+            if (a.cstate_in) {
+                const uint16_t* si = static_cast<const uint16_t*>(a.cstate_in) + (size_t)b * 3 * CD + ch;
+                hw3 = *reinterpret_cast<const uint32_t*>(si);
+                hw2 = *reinterpret_cast<const uint32_t*>(si + CD);
+                hw1 = *reinterpret_cast<const uint32_t*>(si + 2 * CD);
+            }
+        } else {   // tbeg >= 64
+            hw3 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 3) * cstride);
+            hw2 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 2) * cstride);
+            hw1 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 1) * cstride);
+            if (docs) {
+                const int d1 = docbase[tbeg - 1], d2 = docbase[tbeg - 2], d3 = docbase[tbeg - 3];
+                pbits = (d1 != d2 ? 1 : 0) | (d2 != d3 ? 2 : 0);
+            }
+        }
+        pbits = __builtin_amdgcn_readfirstlane(pbits);
+        // ---- conv state after the call: the raw rows L-3 .. L-1 (rows before 0
+        // from the incoming conv state), cut at document starts inside them.
+        // Inputs only, so the last superchunk writes it up front (the caller's
+        // conv state buffers do not overlap).
+        const bool own = cwi < N ? bc_owner : true;
+        if (a.cstate_out && k == a.K - 1 && c_on && cseg == 0 && own) {
+            uint32_t sv[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int u = L - 3 + i;
+                if (u >= 0) {
+                    sv[i] = *reinterpret_cast<const uint32_t*>(src + (size_t)u * cstride);
+                } else {
+                    sv[i] = a.cstate_in ? *reinterpret_cast<const uint32_t*>(
+                                              static_cast<const uint16_t*>(a.cstate_in) + (size_t)b * 3 * CD +
+                                              (size_t)(3 + u) * CD + ch)
+                                        : 0u;
+                }
+            }
+            if (docs) {
+                if (L >= 3 && docbase[L - 2] != docbase[L - 3]) sv[0] = 0;            // a start at L-2
+                if (L >= 2 && docbase[L - 1] != docbase[L - 2]) sv[0] = sv[1] = 0;    // a start at L-1
+            }
+            uint16_t* so = static_cast<uint16_t*>(a.cstate_out) + (size_t)b * 3 * CD + ch;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) *reinterpret_cast<uint32_t*>(so + (size_t)i * CD) = sv[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            asm volatile("" : "+v"(cbias[e]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cwt[e][j]));
+        }
+        asm volatile("" : "+v"(hw3), "+v"(hw2), "+v"(hw1));
+    }
+
     const int nchunks = (tend - tbeg + Q - 1) / Q;
     if (nchunks > 0) {
         if (lead) issue_scalars(tbeg);
@@ -875,9 +1048,23 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
             lds_wait();
             if (more) issue_scalars(t0 + Q);
+            if (CV) {
+                const uint32_t wd = __float_as_uint(dtl);
+                dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
+            }
             if (SP) dtl = softplus_f(dtl + dtb);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
+            if (CV) {
+                const uint64_t m = __ballot(bnd);
+                if (hh == 0 && lane == 0) {
+                    int* sci = reinterpret_cast<int*>(sc);
+                    sci[LD::SC_ST] = (int)(uint32_t)m;
+                    sci[LD::SC_ST + 1] = (int)(uint32_t)(m >> 32);
+                    sci[LD::SC_ST + 2] = pbits;
+                }
+                pbits = (int)(m >> 63) | (int)((m >> 61) & 2);   // for the next chunk
+            }
             float cs = dtl * A2;
             int seg = bnd ? lane : -1;
             wave_segscan(cs, bnd, seg);
@@ -899,6 +1086,43 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
+
+        if constexpr (CV) {
+            // ---- conv + activation of the chunk's raw B, C and X tiles, in place
+            unsigned char* stg = smem + st * LD::STAGE;
+            const int* sci = reinterpret_cast<const int*>(sc);
+            const uint64_t smask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sci[LD::SC_ST + 1]) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane(sci[LD::SC_ST]);
+            const int r0 = cseg * CM::R;
+            auto ldw = [&](int r) { return *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r)); };
+            uint32_t v3 = 0, v2 = 0, v1 = 0;
+            int pb = 0;
+            if (c_on) {
+                if (cseg == 0) {
+                    v3 = hw3; v2 = hw2; v1 = hw1;
+                    pb = __builtin_amdgcn_readfirstlane(sci[LD::SC_ST + 2]);
+                    if (more) { hw3 = ldw(Q - 3); hw2 = ldw(Q - 2); hw1 = ldw(Q - 1); }   // next chunk's halo
+                } else {
+                    v3 = ldw(r0 - 3); v2 = ldw(r0 - 2); v1 = ldw(r0 - 1);
+                    pb = (int)((smask >> (r0 - 1)) & 1) | (int)(((smask >> (r0 - 2)) & 1) << 1);
+                }
+            }
+            lds_barrier();               // C: every raw halo row is read before any row is overwritten
+            if (c_on) {
+                if (pb & 1) { v3 = 0; v2 = 0; }   // a document starts at r0 - 1
+                if (pb & 2) v3 = 0;               // ... at r0 - 2
+                const bool silu = a.act == 0;
+#pragma unroll 1
+                for (int r = r0; r < min(r0 + CM::R, Q); ++r) {
+                    const uint32_t cur = ldw(r);
+                    if ((smask >> r) & 1) { v3 = 0; v2 = 0; v1 = 0; }
+                    *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r)) =
+                        conv_pair(cwt, cbias, v3, v2, v1, cur, silu);
+                    v3 = v2; v2 = v1; v1 = cur;
+                }
+            }
+            lds_barrier();               // D: the convolved tiles are visible
+        }
 
         {
             unsigned char* sM = smem + LD::oM;
@@ -1037,6 +1261,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             *reinterpret_cast<float4*>(a.final_state + st_off + 16 * nt) =
                 make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
     }
+
 }
 
 // ============================================================================
@@ -1066,7 +1291,8 @@ struct LdsPre {
     // scalars of one chunk (floats): per head w [Q]; cs_end per head; last_seg
     static constexpr int SC_END = HPW * Q;
     static constexpr int SC_LAST = SC_END + HPW;
-    static constexpr int SCW = (SC_LAST + 1 + 3) / 4 * 4;
+    static constexpr int SC_ST = SC_LAST + 1;         // fused conv: document starts, as in LdsBf
+    static constexpr int SCW = (SC_ST + 3 + 3) / 4 * 4;
     static constexpr int bytes = oS + 2 * SCW * 4;
     static constexpr int RPI_B = 64 / (RB / 16);      // B rows per 1 KiB copy
     static constexpr int NI_B = Q / RPI_B;
@@ -1075,10 +1301,11 @@ struct LdsPre {
     static constexpr int NI_W = (NI + NW - 1) / NW;
 };
 
-template <int N, bool SP, int HPW, int PB, int NS>
+template <int N, bool SP, int HPW, int PB, int NS, bool CV>
 __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(ScanArgs a) {
     using LD = LdsPre<N, HPW, PB, NS>;
     static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
+    static_assert(SP || !CV, "the fused conv takes raw dt through the softplus");
     constexpr int NT = N / 16;
     constexpr int NW = LD::NW, WPH = LD::WPH;
     constexpr int RB = LD::RB, XB = LD::XB;
@@ -1115,9 +1342,11 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
 
     const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)hq * HPW * 64;
     const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
-    const float* dtbase = a.dt + (size_t)b * L * a.dt_stride + h;
+    // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * L * a.dt16_stride + (h & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * L * a.dt_stride + h);
     const int32_t* docbase = a.doc + (size_t)b * L;
-    const int Ds4 = (int)a.dt_stride * 4;
+    const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
 
     // copy slots of this wave: copy wave + NW j of the chunk (B tile, then X tiles)
     const char* s_base[LD::NI_W];
@@ -1165,7 +1394,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     auto issue_scalars = [&](int t0, int st) {
         unsigned char* dbuf = dbuf_of(st);
         const int rowl = min(lane, tl - t0);
-        dma4(dtbase + (size_t)t0 * a.dt_stride, (uint32_t)(rowl * Ds4), dbuf);
+        dma4(static_cast<const char*>(dtbase) + (size_t)t0 * Ds4, (uint32_t)(rowl * Ds4), dbuf);
         if (docs) {
             dma4(docbase, (uint32_t)(t0 + rowl) * 4, dbuf + Q * 4);
             dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, dbuf + 2 * Q * 4);
@@ -1179,6 +1408,67 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
         for (int nt = 0; nt < NT; ++nt) Hs[pb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float log2dec = 0.0f;
     bool reset = false;
+
+    // ---- fused conv: this lane's word (B or X), its weights, the first halo
+    using CM = ConvMap<N, HPW, false, NW>;
+    static_assert(!CV || (CM::RS >= 1 && CM::R >= 3 && (CM::RS - 1) * CM::R < Q), "conv row segments");
+    const int cseg = wave / CM::WPS;
+    const int cwi = (wave % CM::WPS) * 64 + lane;
+    const bool c_on = CV && cseg < CM::RS && cwi < CM::WD;
+    const int CD = H * 64 + 2 * G * N;              // conv_dim
+    constexpr int RBU = RB == XB ? RB : 0;
+    ConvWord cw{};
+    float cwt[2][4] = {}, cbias[2] = {};
+    uint32_t hw3 = 0, hw2 = 0, hw1 = 0;
+    int pbits = 0;
+    if constexpr (CV) {
+        const int wi = min(cwi, CM::WD - 1);
+        int ch;
+        const uint16_t* src;
+        int64_t cstride;
+        if (wi < N / 2) {
+            cw = conv_word(LD::oB, RB, wi);
+            ch = H * 64 + g * N + 2 * wi;
+            src = Bbase + 2 * wi;
+            cstride = a.B_stride;
+        } else {
+            const int e = (wi - N / 2) / 32, wb = (wi - N / 2) % 32;
+            cw = conv_word(LD::oX + e * LD::TX, XB, wb);
+            ch = (hq * HPW + e) * 64 + 2 * wb;
+            src = xhead + e * 64 + 2 * wb;
+            cstride = a.x_stride;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float4 wv = *reinterpret_cast<const float4*>(a.conv_w + (size_t)(ch + e) * 4);
+            cwt[e][0] = wv.x; cwt[e][1] = wv.y; cwt[e][2] = wv.z; cwt[e][3] = wv.w;
+            cbias[e] = a.conv_b ? a.conv_b[ch + e] : 0.0f;
+        }
+        if (tbeg == 0) {
+            if (a.cstate_in) {
+                const uint16_t* si = static_cast<const uint16_t*>(a.cstate_in) + (size_t)b * 3 * CD + ch;
+                hw3 = *reinterpret_cast<const uint32_t*>(si);
+                hw2 = *reinterpret_cast<const uint32_t*>(si + CD);
+                hw1 = *reinterpret_cast<const uint32_t*>(si + 2 * CD);
+            }
+        } else {
+            hw3 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 3) * cstride);
+            hw2 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 2) * cstride);
+            hw1 = *reinterpret_cast<const uint32_t*>(src + (size_t)(tbeg - 1) * cstride);
+            if (docs) {
+                const int d1 = docbase[tbeg - 1], d2 = docbase[tbeg - 2], d3 = docbase[tbeg - 3];
+                pbits = (d1 != d2 ? 1 : 0) | (d2 != d3 ? 2 : 0);
+            }
+        }
+        pbits = __builtin_amdgcn_readfirstlane(pbits);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            asm volatile("" : "+v"(cbias[e]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cwt[e][j]));
+        }
+        asm volatile("" : "+v"(hw3), "+v"(hw2), "+v"(hw1));
+    }
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
 #pragma unroll
@@ -1211,9 +1501,23 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
             lds_wait();
             if (cn < nchunks) issue_scalars(t0 + (NS - 1) * Q, sn);
+            if (CV) {
+                const uint32_t wd = __float_as_uint(dtl);
+                dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
+            }
             if (SP) dtl = softplus_f(dtl + dtb);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
+            if (CV) {
+                const uint64_t m = __ballot(bnd);
+                if (hh == 0 && lane == 0) {
+                    int* sci = reinterpret_cast<int*>(sc);
+                    sci[LD::SC_ST] = (int)(uint32_t)m;
+                    sci[LD::SC_ST + 1] = (int)(uint32_t)(m >> 32);
+                    sci[LD::SC_ST + 2] = pbits;
+                }
+                pbits = (int)(m >> 63) | (int)((m >> 61) & 2);   // for the next chunk
+            }
             float cs = dtl * A2;
             int seg = bnd ? lane : -1;
             wave_segscan(cs, bnd, seg);
@@ -1231,6 +1535,45 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
+
+        if constexpr (CV) {
+            // ---- conv + activation of the chunk's raw B and X tiles, in place
+            // (the same pass as the main kernel's, without C)
+            unsigned char* stg = smem + st * LD::STAGE;
+            const int* sci = reinterpret_cast<const int*>(sc);
+            const uint64_t smask = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sci[LD::SC_ST + 1]) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane(sci[LD::SC_ST]);
+            const int r0 = cseg * CM::R;
+            const bool more = c + 1 < nchunks;
+            auto ldw = [&](int r) { return *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r)); };
+            uint32_t v3 = 0, v2 = 0, v1 = 0;
+            int pb = 0;
+            if (c_on) {
+                if (cseg == 0) {
+                    v3 = hw3; v2 = hw2; v1 = hw1;
+                    pb = __builtin_amdgcn_readfirstlane(sci[LD::SC_ST + 2]);
+                    if (more) { hw3 = ldw(Q - 3); hw2 = ldw(Q - 2); hw1 = ldw(Q - 1); }
+                } else {
+                    v3 = ldw(r0 - 3); v2 = ldw(r0 - 2); v1 = ldw(r0 - 1);
+                    pb = (int)((smask >> (r0 - 1)) & 1) | (int)(((smask >> (r0 - 2)) & 1) << 1);
+                }
+            }
+            lds_barrier();               // every raw halo row is read before any row is overwritten
+            if (c_on) {
+                if (pb & 1) { v3 = 0; v2 = 0; }
+                if (pb & 2) v3 = 0;
+                const bool silu = a.act == 0;
+#pragma unroll 1
+                for (int r = r0; r < min(r0 + CM::R, Q); ++r) {
+                    const uint32_t cur = ldw(r);
+                    if ((smask >> r) & 1) { v3 = 0; v2 = 0; v1 = 0; }
+                    *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r)) =
+                        conv_pair(cwt, cbias, v3, v2, v1, cur, silu);
+                    v3 = v2; v2 = v1; v1 = cur;
+                }
+            }
+            lds_barrier();               // the convolved tiles are visible
+        }
 
         // ---- (w o X)^T fragments of this wave's blocks via transpose reads
         FragBF xw[PB][4];
@@ -1280,11 +1623,22 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
                 make_float4(Hs[pb][nt][0], Hs[pb][nt][1], Hs[pb][nt][2], Hs[pb][nt][3]);
     }
     if (lead && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+    if (k == 0 && a.h0) {
+        // the main pass reads this copy instead of init_state
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            const size_t o = (((size_t)b * H + h) * 64 + p0 + 16 * pb + j16) * N + 4 * q4;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<float4*>(a.h0 + o + 16 * nt) =
+                    *reinterpret_cast<const float4*>(a.init_state + o + 16 * nt);
+        }
+    }
 }
 
-template <int N, bool SP, int HPW>
+template <int N, bool SP, int HPW, bool CV>
 hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW>);
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV>);
     const size_t lds = LdsBf<N, HPW>::bytes;
     static bool checked = false;
     if (!checked) {
@@ -1298,22 +1652,25 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
         if (e != hipSuccess) return e;
         checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
 }
 template <int N, int HPW>
 hipError_t launch_scan_bf16_full(const ScanArgs& a, int units, hipStream_t stream) {
-    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW>(a, units, stream)
-                         : launch_scan_bf16_k<N, false, HPW>(a, units, stream);
+    if (a.conv) return launch_scan_bf16_k<N, true, HPW, true>(a, units, stream);
+    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW, false>(a, units, stream)
+                         : launch_scan_bf16_k<N, false, HPW, false>(a, units, stream);
 }
 // the state-only pre-pass: PRE_HPW heads per workgroup, kPrePB channel blocks
-// per wave, kPreStages stages
+// per wave (one with the fused conv, whose in-LDS pass wants every wave of a
+// CU), kPreStages stages
 constexpr int kPreStages = 3;
 constexpr int kPrePB = 2;
-template <int N, bool SP, int PRE_HPW>
+template <int N, bool SP, int PRE_HPW, bool CV>
 hipError_t launch_scan_state_k(const ScanArgs& a, hipStream_t stream) {
-    using LD = LdsPre<N, PRE_HPW, kPrePB, kPreStages>;
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_state_kernel<N, SP, PRE_HPW, kPrePB, kPreStages>);
+    constexpr int PB = CV ? 1 : kPrePB;
+    using LD = LdsPre<N, PRE_HPW, PB, kPreStages>;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_state_kernel<N, SP, PRE_HPW, PB, kPreStages, CV>);
     static bool checked = false;
     if (!checked) {
         hipFuncAttributes fa;                   // see launch_scan_bf16_k: no scratch allowed
@@ -1325,14 +1682,15 @@ hipError_t launch_scan_state_k(const ScanArgs& a, hipStream_t stream) {
         checked = true;
     }
     const int units = a.B * (a.H / PRE_HPW) * (a.K - 1);
-    hipLaunchKernelGGL((ssd_scan_state_kernel<N, SP, PRE_HPW, kPrePB, kPreStages>), dim3(units), dim3(64 * LD::NW),
+    hipLaunchKernelGGL((ssd_scan_state_kernel<N, SP, PRE_HPW, PB, kPreStages, CV>), dim3(units), dim3(64 * LD::NW),
                        LD::bytes, stream, a);
     return hipGetLastError();
 }
 template <int N, int PRE_HPW>
 hipError_t launch_scan_bf16_pre(const ScanArgs& a, hipStream_t stream) {
-    return a.dt_softplus ? launch_scan_state_k<N, true, PRE_HPW>(a, stream)
-                         : launch_scan_state_k<N, false, PRE_HPW>(a, stream);
+    if (a.conv) return launch_scan_state_k<N, true, PRE_HPW, true>(a, stream);
+    return a.dt_softplus ? launch_scan_state_k<N, true, PRE_HPW, false>(a, stream)
+                         : launch_scan_state_k<N, false, PRE_HPW, false>(a, stream);
 }
 template <int N, int HPW>
 hipError_t launch_scan_bf16(const ScanArgs& a, int pre_hpw, hipStream_t stream) {
@@ -1491,7 +1849,9 @@ size_t scan_workspace_bytes(int B, int L, int H, int P, int N, int G, int dtype)
     scan_split(B, L, H, N, G, dtype, K, S);
     if (K <= 1) return 0;
     const size_t u = (size_t)B * H * (K - 1);
-    return u * (size_t)P * N * sizeof(float) + ((u * sizeof(float) + 255) / 256) * 256;
+    // hloc [u][P][N], dec [u] (padded to 256 bytes), the copy of init_state [B][H][P][N]
+    return u * (size_t)P * N * sizeof(float) + ((u * sizeof(float) + 255) / 256) * 256 +
+           (size_t)B * H * P * N * sizeof(float);
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {

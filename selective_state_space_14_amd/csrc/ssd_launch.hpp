@@ -36,6 +36,18 @@ struct ScanArgs {
     // one sequential pass.  hloc / dec: workspace for the K-1 local states.
     int K, S;
     float* hloc; float* dec;
+    // K > 1 with an initial state: the pre-pass copies init_state here and the
+    // main pass reads the copy, so final_state may alias init_state even though
+    // superchunk K-1 can finish before superchunk 0 starts.
+    float* h0;
+    // Fused conv prologue (bf16 only; the mixer entry point): x, Bm and Cm are
+    // the raw column slices of one [x | B | C] tensor (conv_dim wide) and are
+    // convolved (k = 4, weights [conv_dim][4]) and activated on chip; dt16 is
+    // the raw bf16 dt, taken through softplus(dt16 + dt_bias).  conv = 0: off.
+    int conv, act;
+    const float* conv_w; const float* conv_b;
+    const void* cstate_in; void* cstate_out;   // [B][3][conv_dim]
+    const uint16_t* dt16; int64_t dt16_stride;
 };
 
 struct StepArgs {

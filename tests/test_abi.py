@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
+    for n in ("ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size", "ssd_mixer_fwd",
+              "ssd_mixer_workspace_size",
               "ssd_last_error", "ssd_status_string", "ssd_version"):
         assert n in names
 
@@ -115,6 +116,51 @@ def test_conv_refusals(lib, over, status, needle):
     st = call_conv(lib, **over)
     assert st == status, (st, lib.ssd_last_error())
     assert needle in lib.ssd_last_error().decode()
+
+
+def call_mixer(lib, **over):
+    a = dict(B=2, L=100, H=32, P=64, N=64, G=8, K=4, chunk=64, dtype=1, raw=FAKE, rs=3072, w=FAKE, b=None,
+             dtr=FAKE, dtrs=32, dtb=None, A=FAKE, D=None, z=None, zs=0, doc=None, si=None, so=None, h0=None,
+             hf=None, act=0, y=FAKE + 0x100000, ys=2048, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return lib.ssd_mixer_fwd(a["B"], a["L"], a["H"], a["P"], a["N"], a["G"], a["K"], a["chunk"], a["dtype"],
+                             a["raw"], a["rs"], a["w"], a["b"], a["dtr"], a["dtrs"], a["dtb"], a["A"], a["D"],
+                             a["z"], a["zs"], a["doc"], a["si"], a["so"], a["h0"], a["hf"], a["act"], a["y"],
+                             a["ys"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(K=2), 3, "K=2"),
+    (dict(chunk=32), 3, "chunk=32"),
+    (dict(act=3), 3, "act=3"),
+    (dict(raw=None), 1, "xbc_raw is NULL"),
+    (dict(dtr=None), 1, "dt_raw is NULL"),
+    (dict(w=None), 1, "conv_w is NULL"),
+    (dict(A=None), 1, "A is NULL"),
+    (dict(rs=1000), 2, "xbc_raw row stride 1000"),
+    (dict(dtrs=31, H=32), 2, "dt_raw row stride 31"),
+    (dict(dtrs=33), 4, "must be even"),
+    (dict(si=FAKE, so=FAKE), 2, "must not overlap"),
+    (dict(si=FAKE, so=FAKE + 0x100), 2, "must not overlap"),
+    (dict(y=FAKE, hf=FAKE), 2, "y must not alias final_state"),
+    (dict(dtype=0, dtrs=32), 5, "fp32 needs a workspace"),
+    (dict(ys=1024), 2, "y row stride 1024"),
+])
+def test_mixer_refusals(lib, over, status, needle):
+    st = call_mixer(lib, **over)
+    assert st == status, (st, lib.ssd_last_error())
+    assert needle in lib.ssd_last_error().decode()
+
+
+def test_mixer_workspace_size(lib):
+    # bf16: the split state only (the scan's own size); fp32: plus the staged conv output and dt
+    B, L, H, P, N, G = 5, 8192, 32, 64, 64, 8
+    assert lib.ssd_mixer_workspace_size(B, L, H, P, N, G, 1) == lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, 1)
+    C = H * P + 2 * G * N
+    r = lambda n: (n + 255) // 256 * 256
+    assert (lib.ssd_mixer_workspace_size(B, L, H, P, N, G, 0) ==
+            r(B * L * C * 4) + r(B * L * H * 4) + lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, 0))
+    assert lib.ssd_mixer_workspace_size(0, L, H, P, N, G, 1) == 0
 
 
 def call_step(lib, **over):

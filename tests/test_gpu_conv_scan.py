@@ -207,6 +207,30 @@ def test_scan_split_parity(gpu_lib, dtype, N, G, H, L, docs, h0, gate):
     check(y, y1, "split vs single pass y")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scan_split_in_place_state(gpu_lib, dtype):
+    """final_state aliasing init_state with the sequence split: the main pass reads only the pre-pass's
+    copy of the initial state, so the last superchunk may finish before the first one starts."""
+    wl = small_wl(dtype, H=4, N=64, G=1, L=3000, B=2, docs=True, h0=True, gate=True)
+    _say(f"scan split in place {dtype}")
+    prm = synth.params(wl, 9)
+    inp = synth.scan_inputs(wl, 9)
+    ids = synth.doc_ids(wl, 9, mean_len=700.0)
+    st = inp["h0"].to(DEV).clone()
+    ws = workspace(gpu_lib, wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, wl.dtype)
+    assert ws is not None
+    g = lambda t: None if t is None else t.to(DEV)
+    y = gpu_lib.ssd_chunk_scan_fwd(g(inp["x"]), g(inp["Bm"]), g(inp["Cm"]), g(inp["dt_raw"].float()), g(prm["A"]),
+                                   H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=g(prm["D"]), z=g(inp["z"]), doc_ids=g(ids),
+                                   init_state=st, final_state=st, dt_softplus=True, dt_bias=g(prm["dt_bias"]),
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan(wl, inp, prm, ids)
+    check = hp.assert_fp32 if dtype == "f32" else hp.assert_bf16
+    check(y, yr, "y")
+    check(st, fr, "final_state (in place)")
+
+
 def test_scan_adversarial_boundaries(gpu_lib):
     """Boundaries at t % 64 in {0, 1, 63}, documents of length 1-3, back-to-back boundaries."""
     wl = small_wl("bf16", H=4, N=64, G=2, L=320, B=2, docs=True, h0=True, gate=True)
