@@ -9,11 +9,13 @@ Inputs are resident in HBM before the timed region; two input sets alternate
 so no step runs out of the 256 MB last-level cache.
 
 Prints ONE JSON line: value = head-tokens (B*L*H) per second over the whole
-step; "roofline" = the scan kernel's algorithmic bytes / its average duration
-(HIP events around each launch on the launch stream) against 8 TB/s;
-"cpu_baseline" = the fp64 oracle (conv + scan) timed on this host.  The other
-workloads (packed documents, the large layer, the decode step) are reported
-under "extra".
+step; "roofline" = the scan call's algorithmic bytes / its average duration
+(HIP events around each call on the launch stream) against 8 TB/s;
+"cpu_baseline" = the fp64 oracle (conv + scan) timed on this host.  Under
+"extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
+two kernels behind one call; fused: the conv computed inside the scan
+kernels), and the other workloads (packed documents, the large layer, the
+decode step).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -86,6 +88,23 @@ def conv_bytes(wl, docs=False):
     return b
 
 
+def mixer_bytes(wl, docs=False, h0=False):
+    """Algorithmic bytes of one ssd_mixer_fwd: the raw [x | B | C] columns, dt_raw and z read once, y and
+    the final state written once (the conv output and dt never reach memory)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok = wl.B * wl.L
+    b = tok * wl.conv_dim * es            # raw x | B | C
+    b += tok * wl.H * es                  # dt_raw
+    b += tok * wl.H * wl.P * es if wl.gate else 0   # z
+    b += tok * wl.H * wl.P * 4            # y (fp32)
+    st = wl.B * wl.H * wl.P * wl.N * 4
+    b += st                               # final state
+    b += st if h0 else 0                  # initial state
+    b += tok * 4 if docs else 0           # doc ids
+    b += wl.B * 3 * wl.conv_dim * es      # conv state out
+    return b
+
+
 def step_bytes(wl):
     """Algorithmic bytes of one ssd_step: state and conv buffer read + written, row inputs, y."""
     es = 2 if wl.dtype == "bf16" else 4
@@ -116,7 +135,52 @@ class Timer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
 
 
+def mixer_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0, plan="staged"):
+    """ssd_mixer_fwd as the step: plan "staged" (a workspace of ssd_mixer_workspace_size() bytes) or "fused"
+    (the scan's split workspace only)."""
+    dev = "cuda"
+    HP = wl.H * wl.P
+    prm = synth.params(wl, seed, device=dev)
+    sets = []
+    for k in range(2):
+        raw = synth.raw_inputs(wl, seed + k, device=dev)
+        ids = synth.doc_ids(wl, seed + k).to(dev) if docs else None
+        sets.append((raw, ids))
+    code = ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32
+    size = ssd.ssd_mixer_workspace_size if plan == "staged" else ssd.ssd_chunk_scan_workspace_size
+    ws_bytes = size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
+    fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
+    cs = torch.empty(wl.B, 3, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
+    t_mix = Timer(torch)
+
+    def one(i, timed):
+        raw, ids = sets[i % 2]
+        f = lambda: ssd.ssd_mixer_fwd(raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], H=wl.H, P=wl.P,
+                                      N=wl.N, G=wl.G, dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], doc_ids=ids,
+                                      conv_state_out=cs, init_state=raw["h0"] if h0 else None, final_state=fs,
+                                      y=y, workspace=ws)
+        t_mix.around(f) if timed else f()
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        one(i, True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    mb = mixer_bytes(wl, docs, h0)
+    mix_ms = t_mix.mean_ms()
+    return {"ms_per_step": ms, "value": wl.B * wl.L * wl.H / (ms * 1e-3), "mixer_us": mix_ms * 1e3,
+            "mixer_bytes": mb, "mixer_GBs": mb / (mix_ms * 1e-3) / 1e9, "mixer_workspace_bytes": ws_bytes}
+
+
 def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0):
+    """The two-call path: ssd_conv_fwd then ssd_chunk_scan_fwd."""
     dev = "cuda"
     HP, GN = wl.H * wl.P, wl.G * wl.N
     prm = synth.params(wl, seed, device=dev)
@@ -259,18 +323,29 @@ def main():
     wl = synth.WORKLOADS["mini_k3_bf16"]
     main_r = prefill_bench(ssd, synth, torch, wl, args.steps, args.warmup)
 
+    def mixer_extra(w, r, plan):
+        return {"workload": w.name, "path": f"ssd_mixer_fwd ({plan} plan)", "value": r["value"],
+                "ms_per_step": r["ms_per_step"], "mixer_us": r["mixer_us"], "mixer_GBs": r["mixer_GBs"],
+                "mixer_frac": r["mixer_GBs"] / HBM_PEAK_GBS, "unit": "head-tokens/s"}
+
+    def two_call_extra(w, r):
+        return {"workload": w.name, "path": "ssd_conv_fwd + ssd_chunk_scan_fwd",
+                **{k: r[k] for k in ("value", "ms_per_step", "scan_us", "conv_us", "scan_GBs", "conv_GBs")},
+                "scan_frac": r["scan_GBs"] / HBM_PEAK_GBS, "conv_frac": r["conv_GBs"] / HBM_PEAK_GBS,
+                "unit": "head-tokens/s"}
+
     extras = []
     if not args.no_extras:
+        for plan in ("staged", "fused"):
+            extras.append(mixer_extra(wl, mixer_bench(ssd, synth, torch, wl, args.steps, args.warmup, plan=plan),
+                                      plan))
         pk = synth.WORKLOADS["mini_k3_packed"]
-        r = prefill_bench(ssd, synth, torch, pk, args.steps, args.warmup, docs=True)
-        extras.append({"workload": pk.name, **{k: r[k] for k in ("value", "ms_per_step", "scan_us", "conv_us",
-                                                                  "scan_GBs", "conv_GBs")},
-                       "scan_frac": r["scan_GBs"] / HBM_PEAK_GBS, "unit": "head-tokens/s"})
+        extras.append(two_call_extra(pk, prefill_bench(ssd, synth, torch, pk, args.steps, args.warmup, docs=True)))
         ll = synth.WORKLOADS["large_layer_bf16"]
-        r = prefill_bench(ssd, synth, torch, ll, max(5, args.steps // 2), args.warmup, h0=True)
-        extras.append({"workload": ll.name, **{k: r[k] for k in ("value", "ms_per_step", "scan_us", "conv_us",
-                                                                  "scan_GBs", "conv_GBs")},
-                       "scan_frac": r["scan_GBs"] / HBM_PEAK_GBS, "unit": "head-tokens/s"})
+        ls = max(5, args.steps // 2)
+        extras.append(two_call_extra(ll, prefill_bench(ssd, synth, torch, ll, ls, args.warmup, h0=True)))
+        extras.append(mixer_extra(ll, mixer_bench(ssd, synth, torch, ll, ls, args.warmup, h0=True, plan="fused"),
+                                  "fused"))
         dw = synth.WORKLOADS["decode_fp32"]
         r = decode_bench(ssd, synth, torch, dw, max(20, args.steps * 2), args.warmup)
         extras.append({"workload": dw.name + " (ssd_step)", **r, "step_frac": r["step_GBs"] / HBM_PEAK_GBS,

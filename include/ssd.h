@@ -197,14 +197,21 @@ size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, i
  * Computes what ssd_conv_fwd followed by ssd_chunk_scan_fwd computes -- the
  * conv (k = 4) + act over the raw [x | B | C] columns, dt = softplus(dt_raw +
  * dt_bias), the scan with groups, documents and states, the D skip and the
- * gate -- without writing the convolved columns or dt to memory (the fused
- * conv-in-scan prologue; the Codestral-Mamba port header for the in_proj row
- * layout and the conv weight).  For bf16 the scan kernels read the raw tiles
- * and convolve each chunk in LDS with the same fp32 arithmetic as
- * ssd_conv_fwd, so y, final_state and conv_state_out are bit-identical to
- * the two-call composition (ssd_chunk_scan_fwd with dt_softplus = 0 on
- * ssd_conv_fwd's outputs) given the same workspace choice.  For fp32 the two
- * kernels run back to back through the workspace.
+ * gate (the Codestral-Mamba port header for the in_proj row layout and the
+ * conv weight).  Two plans, chosen by the workspace size:
+ *   staged  workspace_bytes >= ssd_mixer_workspace_size(): the conv kernel
+ *           writes the convolved columns and dt into the workspace and the
+ *           scan reads them, with the sequence split (the faster plan).
+ *   fused   a smaller workspace, or NULL (bf16 only): the scan kernels read
+ *           the raw tiles and convolve each chunk in LDS with the conv
+ *           kernel's fp32 arithmetic, so the convolved columns never reach
+ *           memory; the split is used when the workspace holds
+ *           ssd_chunk_scan_workspace_size() bytes.  It needs no staging
+ *           buffer but is slower on MI355X: the conv's SiLU arithmetic then
+ *           runs inside the scan kernels at one workgroup per CU.
+ * Either way y, final_state and conv_state_out are bit-identical to the
+ * two-call composition (ssd_chunk_scan_fwd with dt_softplus = 0 on
+ * ssd_conv_fwd's outputs) with the same split choice.
  *
  *   xbc_raw      T  [B][L][conv_dim], row stride xbc_raw_row_stride
  *   conv_w       f32 [conv_dim][K], conv_b f32 [conv_dim] or NULL; act as in
@@ -218,12 +225,10 @@ size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, i
  *                ssd_conv_fwd, except that they must not overlap
  *                (SSD_ERR_BAD_SHAPE): several workgroups read the incoming
  *                B/C history while another writes the outgoing one
- *   workspace    bf16: NULL, 0 (sequential pass) or at least
- *                ssd_mixer_workspace_size() bytes (the sequence split, as in
- *                ssd_chunk_scan_fwd).  fp32: required, at least
- *                ssd_mixer_workspace_size() bytes (the conv output and dt are
- *                staged there, then the split state).  16-byte aligned,
- *                owned by the caller, not shared by concurrent calls.
+ *   workspace    device scratch selecting the plan (above); fp32 requires
+ *                the staged plan (SSD_ERR_WORKSPACE otherwise).  16-byte
+ *                aligned, owned by the caller, not read before it is
+ *                written, not shared by concurrent calls.
  * Row strides are in elements, >= the row width and <= 4194304.  L = 0
  * copies both carried states through.
  */
@@ -239,9 +244,9 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
                   int act, float *y, int64_t y_row_stride,
                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace ssd_mixer_fwd uses for these sizes (bf16: the split
- * state, 0 when no split pays; fp32: the staged conv output and dt, plus the
- * split state). */
+/* Bytes of workspace of ssd_mixer_fwd's staged plan for these sizes: the
+ * conv output [B][L][conv_dim] (T) and dt [B][L][H] (fp32), each padded to
+ * 256 bytes, plus the scan's split state (ssd_chunk_scan_workspace_size()). */
 size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
 
 /*

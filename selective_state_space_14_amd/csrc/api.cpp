@@ -252,11 +252,10 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
 
 size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
     if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0) return 0;
-    const size_t scan = ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
-    if (dtype != SSD_F32) return scan;
-    // fp32: the conv output [B][L][conv_dim] and dt [B][L][H] are staged first
+    // the staged plan: the conv output [B][L][conv_dim] (T) and dt [B][L][H] (fp32), then the split state
     const size_t C = (size_t)H * P + 2 * (size_t)G * N;
-    return round256((size_t)B * L * C * 4) + round256((size_t)B * L * H * 4) + scan;
+    return round256((size_t)B * L * C * esize(dtype)) + round256((size_t)B * L * H * 4) +
+           ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
 }
 
 int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, int dtype,
@@ -313,15 +312,17 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
     if (work && y == final_state)
         return fail(SSD_ERR_BAD_SHAPE, "%s: y must not alias final_state", fn);
+    // Plan: staged (the conv kernel into the workspace, then the scan) when the workspace holds
+    // ssd_mixer_workspace_size() bytes; otherwise (bf16 only) fused, with the sequence split when the
+    // workspace holds the scan's split state.
     const size_t need = ssd_mixer_workspace_size(B, L, H, P, N, G, dtype);
-    const bool split = workspace != nullptr && need > 0;
-    if (work && dtype == SSD_F32 && workspace == nullptr)
+    const size_t need_split = ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
+    if (workspace == nullptr) workspace_bytes = 0;
+    const bool staged = work && workspace_bytes >= need;
+    if (work && dtype == SSD_F32 && !staged)
         return fail(SSD_ERR_WORKSPACE, "%s: fp32 needs a workspace of ssd_mixer_workspace_size()=%zu bytes (the "
-                    "conv output is staged there)", fn, need);
-    if (split && workspace_bytes < need)
-        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
-                    workspace_bytes, need);
-    if (split && !aligned16(workspace))
+                    "conv output is staged there), got %zu", fn, need, workspace_bytes);
+    if (workspace_bytes > 0 && !aligned16(workspace))
         return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -346,11 +347,14 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
     a.dt_bias = dt_bias;
     a.K = 1; a.S = ((L + 63) / 64) * 64;
     char* ws = static_cast<char*>(workspace);
-    if (dtype == SSD_F32) {
+    size_t ws_left = workspace_bytes;
+    if (staged) {
         // conv into the workspace, then the scan over it
-        float* xbc = reinterpret_cast<float*>(ws);
-        float* dtw = reinterpret_cast<float*>(ws + round256((size_t)B * L * C * 4));
-        ws += round256((size_t)B * L * C * 4) + round256((size_t)B * L * H * 4);
+        char* xbc = ws;
+        float* dtw = reinterpret_cast<float*>(ws + round256((size_t)B * L * C * es));
+        const size_t used = round256((size_t)B * L * C * es) + round256((size_t)B * L * H * 4);
+        ws += used;
+        ws_left -= used;
         ssd::ConvArgs c;
         c.B = B; c.L = L; c.C = (int)C; c.H = H; c.dtype = dtype; c.act = act;
         c.raw = xbc_raw; c.raw_stride = xbc_raw_row_stride;
@@ -363,8 +367,8 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         hipError_t e = ssd::launch_conv(c, s);
         if (e != hipSuccess) return hip_status(fn, e);
         a.x = xbc; a.x_stride = C;
-        a.Bm = xbc + (size_t)H * P; a.B_stride = C;
-        a.Cm = xbc + (size_t)H * P + (size_t)G * N; a.C_stride = C;
+        a.Bm = xbc + (size_t)H * P * es; a.B_stride = C;
+        a.Cm = xbc + ((size_t)H * P + (size_t)G * N) * es; a.C_stride = C;
         a.dt = dtw; a.dt_stride = H; a.dt_softplus = 0;
     } else {
         const char* raw = static_cast<const char*>(xbc_raw);
@@ -376,7 +380,7 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         a.conv_w = conv_w; a.conv_b = conv_b;
         a.cstate_in = conv_state_in; a.cstate_out = conv_state_out;
     }
-    if (ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype) > 0 && workspace != nullptr) {
+    if (need_split > 0 && ws_left >= need_split) {
         ssd::scan_split(B, L, H, N, G, dtype, a.K, a.S);
         const size_t u = (size_t)B * H * (a.K - 1);
         a.hloc = reinterpret_cast<float*>(ws);

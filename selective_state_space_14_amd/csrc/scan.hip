@@ -693,22 +693,47 @@ __device__ __forceinline__ uint32_t conv_off(const ConvWord& w, int r) {
         return (w.tp + (uint32_t)(r * w.rb)) ^ ((uint32_t)((r >> w.rl_sh) & w.cpr_m) << 4);
     }
 }
-// Conv of one row for the word's two channels: history v3 (t-3), v2, v1 and
-// the current raw word; returns the packed bf16 pair.
-__device__ __forceinline__ uint32_t conv_pair(const float (&w)[2][4], const float (&cb)[2], uint32_t v3,
-                                              uint32_t v2, uint32_t v1, uint32_t cur, bool silu) {
-    float o[2];
+// The in-place conv of one lane's word over rows [r0, r1) of a stage.  v3,
+// v2, v1: the raw words of rows r0-3 .. r0-1, already cut at document
+// starts before r0; smask bit r: row r starts a document (the history is
+// zeroed before it).  Rows are independent given the raw history, so they are
+// read four at a time ahead of the arithmetic.
+template <int RBU>
+__device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw, int r0, int r1, uint64_t smask,
+                                          uint32_t v3, uint32_t v2, uint32_t v1, const float (&w)[2][4],
+                                          const float (&cb)[2], bool silu) {
+    float h3[2] = {bf16_lo(v3), bf16_hi(v3)}, h2[2] = {bf16_lo(v2), bf16_hi(v2)},
+          h1[2] = {bf16_lo(v1), bf16_hi(v1)};
+#pragma unroll 1
+    for (int r = r0; r < r1; r += 4) {
+        uint32_t cur[4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const auto el = [&](uint32_t v) { return e ? bf16_hi(v) : bf16_lo(v); };
-        float v = cb[e];
-        v = fmaf(w[e][0], el(v3), v);
-        v = fmaf(w[e][1], el(v2), v);
-        v = fmaf(w[e][2], el(v1), v);
-        v = fmaf(w[e][3], el(cur), v);
-        o[e] = silu ? silu_f(v) : v;
+        for (int u = 0; u < 4; ++u)
+            cur[u] = r + u < r1 ? *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r + u)) : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (r + u < r1) {
+                if ((smask >> (r + u)) & 1) {
+                    h3[0] = h3[1] = h2[0] = h2[1] = h1[0] = h1[1] = 0.0f;
+                }
+                const float c[2] = {bf16_lo(cur[u]), bf16_hi(cur[u])};
+                float o[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float v = cb[e];
+                    v = fmaf(w[e][0], h3[e], v);
+                    v = fmaf(w[e][1], h2[e], v);
+                    v = fmaf(w[e][2], h1[e], v);
+                    v = fmaf(w[e][3], c[e], v);
+                    o[e] = silu ? silu_f(v) : v;
+                    h3[e] = h2[e];
+                    h2[e] = h1[e];
+                    h1[e] = c[e];
+                }
+                *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r + u)) = pack_bf16x2(o[0], o[1]);
+            }
+        }
     }
-    return pack_bf16x2(o[0], o[1]);
 }
 
 // LDS plan of the full pass: two stages of B, C and the heads' X tiles, the
@@ -1111,15 +1136,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             if (c_on) {
                 if (pb & 1) { v3 = 0; v2 = 0; }   // a document starts at r0 - 1
                 if (pb & 2) v3 = 0;               // ... at r0 - 2
-                const bool silu = a.act == 0;
-#pragma unroll 1
-                for (int r = r0; r < min(r0 + CM::R, Q); ++r) {
-                    const uint32_t cur = ldw(r);
-                    if ((smask >> r) & 1) { v3 = 0; v2 = 0; v1 = 0; }
-                    *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r)) =
-                        conv_pair(cwt, cbias, v3, v2, v1, cur, silu);
-                    v3 = v2; v2 = v1; v1 = cur;
-                }
+                conv_rows<RBU>(stg, cw, r0, min(r0 + CM::R, Q), smask, v3, v2, v1, cwt, cbias, a.act == 0);
             }
             lds_barrier();               // D: the convolved tiles are visible
         }
@@ -1562,15 +1579,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             if (c_on) {
                 if (pb & 1) { v3 = 0; v2 = 0; }
                 if (pb & 2) v3 = 0;
-                const bool silu = a.act == 0;
-#pragma unroll 1
-                for (int r = r0; r < min(r0 + CM::R, Q); ++r) {
-                    const uint32_t cur = ldw(r);
-                    if ((smask >> r) & 1) { v3 = 0; v2 = 0; v1 = 0; }
-                    *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r)) =
-                        conv_pair(cwt, cbias, v3, v2, v1, cur, silu);
-                    v3 = v2; v2 = v1; v1 = cur;
-                }
+                conv_rows<RBU>(stg, cw, r0, min(r0 + CM::R, Q), smask, v3, v2, v1, cwt, cbias, a.act == 0);
             }
             lds_barrier();               // the convolved tiles are visible
         }

@@ -144,6 +144,8 @@ def call_mixer(lib, **over):
     (dict(si=FAKE, so=FAKE + 0x100), 2, "must not overlap"),
     (dict(y=FAKE, hf=FAKE), 2, "y must not alias final_state"),
     (dict(dtype=0, dtrs=32), 5, "fp32 needs a workspace"),
+    (dict(dtype=0, dtrs=32, ws=FAKE, wsb=4096), 5, "fp32 needs a workspace"),
+    (dict(ws=MIS, wsb=4096), 4, "workspace="),
     (dict(ys=1024), 2, "y row stride 1024"),
 ])
 def test_mixer_refusals(lib, over, status, needle):
@@ -153,13 +155,14 @@ def test_mixer_refusals(lib, over, status, needle):
 
 
 def test_mixer_workspace_size(lib):
-    # bf16: the split state only (the scan's own size); fp32: plus the staged conv output and dt
+    # the staged plan: conv output (element size of the dtype) and fp32 dt, each padded to 256 bytes, then the
+    # scan's split state
     B, L, H, P, N, G = 5, 8192, 32, 64, 64, 8
-    assert lib.ssd_mixer_workspace_size(B, L, H, P, N, G, 1) == lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, 1)
     C = H * P + 2 * G * N
     r = lambda n: (n + 255) // 256 * 256
-    assert (lib.ssd_mixer_workspace_size(B, L, H, P, N, G, 0) ==
-            r(B * L * C * 4) + r(B * L * H * 4) + lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, 0))
+    for dtype, es in ((0, 4), (1, 2)):
+        assert (lib.ssd_mixer_workspace_size(B, L, H, P, N, G, dtype) ==
+                r(B * L * C * es) + r(B * L * H * 4) + lib.ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype))
     assert lib.ssd_mixer_workspace_size(0, L, H, P, N, G, 1) == 0
 
 

@@ -32,14 +32,19 @@ def _g(t):
     return None if t is None else t.to(DEV)
 
 
-def run_mixer(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=False):
-    """ssd_mixer_fwd; fp32 always takes its (required) workspace, bf16 only when split."""
+def run_mixer(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=False, plan="fused"):
+    """ssd_mixer_fwd.  plan "staged": a workspace of ssd_mixer_workspace_size() bytes (the split is then
+    always on when the sizes call for one); "fused" (bf16): no workspace, or the scan's split workspace."""
     B, L = raw["xbc_raw"].shape[:2]
+    code = 1 if wl.dtype == "bf16" else 0
     cs_out = torch.full((B, 3, wl.conv_dim), 7.0, dtype=wl.torch_dtype, device=DEV)
     fs = torch.full((B, wl.H, wl.P, wl.N), 7.0, dtype=torch.float32, device=DEV)
     ws = None
-    if split or wl.dtype == "f32":
-        n = lib.ssd_mixer_workspace_size(B, L, wl.H, wl.P, wl.N, wl.G, 1 if wl.dtype == "bf16" else 0)
+    if plan == "staged" or wl.dtype == "f32":
+        n = lib.ssd_mixer_workspace_size(B, L, wl.H, wl.P, wl.N, wl.G, code)
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+    elif split:
+        n = lib.ssd_chunk_scan_workspace_size(B, L, wl.H, wl.P, wl.N, wl.G, code)
         ws = torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
     y = lib.ssd_mixer_fwd(_g(raw["xbc_raw"]), _g(raw["dt_raw"]), _g(prm["conv_w"]), _g(prm["A"]), H=wl.H, P=wl.P,
                           N=wl.N, G=wl.G, conv_b=_g(prm.get("conv_b")), dt_bias=_g(prm["dt_bias"]), D=_g(prm["D"]),
@@ -49,7 +54,8 @@ def run_mixer(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=Fal
     return y, fs, cs_out
 
 
-def run_two_call(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=False):
+def run_two_call(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=False, plan=None):
+    split = split or plan == "staged"
     B, L = raw["xbc_raw"].shape[:2]
     HP, GN = wl.H * wl.P, wl.G * wl.N
     cs_out = torch.full((B, 3, wl.conv_dim), 7.0, dtype=wl.torch_dtype, device=DEV)
@@ -118,13 +124,16 @@ MIX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("plan", ["fused", "staged"])
 @pytest.mark.parametrize("dtype,N,G,H,L,docs,cs,h0,gate,act,bias", MIX_CASES)
-def test_mixer_small(gpu_lib, dtype, N, G, H, L, docs, cs, h0, gate, act, bias):
+def test_mixer_small(gpu_lib, dtype, N, G, H, L, docs, cs, h0, gate, act, bias, plan):
+    if dtype == "f32" and plan == "fused":
+        pytest.skip("fp32 has only the staged plan")
     wl = mix_wl(dtype, H, N, G, L, gate=gate)
-    _say(f"mixer small {dtype} N={N} G={G} H={H} L={L} docs={docs} cs={cs} h0={h0} gate={gate} act={act}")
+    _say(f"mixer small {plan} {dtype} N={N} G={G} H={H} L={L} docs={docs} cs={cs} h0={h0} gate={gate} act={act}")
     prm, raw, ids, cs_in = inputs(wl, 21, docs, cs, h0, bias, mean_len=20.0)
-    y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act)
-    y2, fs2, co2 = run_two_call(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act)
+    y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, plan=plan)
+    y2, fs2, co2 = run_two_call(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, plan=plan)
     assert torch.equal(y, y2), hp.report("mixer vs two-call y", y, y2)
     assert torch.equal(fs, fs2), hp.report("mixer vs two-call final_state", fs, fs2)
     assert torch.equal(co, co2), "mixer vs two-call conv_state_out"
@@ -144,11 +153,12 @@ SPLIT_CASES = [
 
 @pytest.mark.parametrize("dtype,N,G,H,L,docs,cs,h0", SPLIT_CASES)
 def test_mixer_split(gpu_lib, dtype, N, G, H, L, docs, cs, h0):
-    """The split path: the fused state-only pre-pass plus the fused main pass."""
+    """The split path of the fused plan (fp32: the staged plan): the state-only pre-pass plus the main pass,
+    both convolving on chip."""
     wl = mix_wl(dtype, H, N, G, L)
     _say(f"mixer split {dtype} N={N} G={G} H={H} L={L} docs={docs} cs={cs} h0={h0}")
     prm, raw, ids, cs_in = inputs(wl, 22, docs, cs, h0, True, mean_len=300.0)
-    n = gpu_lib.ssd_mixer_workspace_size(wl.B, L, H, 64, N, G, 1 if dtype == "bf16" else 0)
+    n = gpu_lib.ssd_chunk_scan_workspace_size(wl.B, L, H, 64, N, G, 1 if dtype == "bf16" else 0)
     assert n > 0
     y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], split=True)
     y2, fs2, co2 = run_two_call(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], split=True)
@@ -193,16 +203,17 @@ def test_mixer_empty_sequence_passes_states_through(gpu_lib):
     assert torch.equal(co, cs_in) and torch.equal(fs, h0)
 
 
+@pytest.mark.parametrize("plan", ["fused", "staged"])
 @pytest.mark.parametrize("name", ["mini_k3_packed", "large_layer_bf16"])
-def test_mixer_full_workload(gpu_lib, name):
+def test_mixer_full_workload(gpu_lib, name, plan):
     """The full-size workloads with the split: bit-identical to the two-call path on every output, and
     within the pipeline bound of the oracle on the first and last batch rows."""
     wl = synth.WORKLOADS[name]
-    _say(f"mixer full {name}")
+    _say(f"mixer full {name} {plan}")
     prm = synth.params(wl, 0)
     raw = synth.raw_inputs(wl, 0, device=DEV)
     ids = synth.doc_ids(wl, 0) if wl.docs else None
-    y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, None, raw["h0"], split=True)
+    y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, None, raw["h0"], split=True, plan=plan)
     y2, fs2, co2 = run_two_call(gpu_lib, wl, raw, prm, ids, None, raw["h0"], split=True)
     assert torch.equal(y, y2), hp.report("mixer vs two-call y", y, y2)
     assert torch.equal(fs, fs2) and torch.equal(co, co2)
