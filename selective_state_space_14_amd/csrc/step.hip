@@ -1,21 +1,24 @@
 // step.hip -- ssd_step: one decode token per sequence on gfx950.
 //
 // Per sequence b (one workgroup of 1024 threads):
-//   1. conv window [conv_state rows 0..K-2, new raw row] -> act -> rounded to
-//      the storage dtype (as a prefill would store it) -> fp32 in LDS; the
-//      conv buffer shifts by one row in place (same thread reads then writes
-//      each channel, so no other thread can observe a half-shifted buffer);
-//      dt = softplus(dt_raw + dt_bias) and a = exp(dt * A) per head in LDS.
+//   1. the B and C columns: conv window [conv_state rows 0..K-2, new raw
+//      row] -> act -> rounded to the storage dtype (as a prefill would store
+//      it) -> fp32 in LDS, the conv buffer shifting by one row in place (the
+//      thread that reads a channel's rows writes them); dt = softplus(dt_raw +
+//      dt_bias) and a = exp(dt * A) per head in LDS.
 //   2. a streaming read-modify-write of the fp32 state [H][P][N], a round of
-//      rows at a time: eight lanes share a row (four float4 each for N = 128),
+//      rows at a time: eight lanes share a row (four float4 each for N = 128);
+//      row h*P + p also convolves x channel h*P + p (its inputs loaded one
+//      round ahead) and shifts that channel's buffer rows, then
 //          h[p, n] = a * h[p, n] + (dt * x_p) * B_n
 //      and the row's lanes reduce C . h with a fixed DPP butterfly, so the
 //      result is deterministic and independent of the batch size;
 //   y[p] = (C . h[p] + D x_p) * silu(z_p).
 // The state is 96% of the bytes (B*H*P*N*4 read + written per token): its
 // loads and stores are nontemporal (it is touched once per token), loads run
-// two rounds ahead of the round being computed, and the first two rounds'
-// loads are issued even before the conv phase.
+// one round ahead of the round being computed (deeper prefetch measured no
+// faster: 64 KB per round and CU already covers the latency), and the first
+// round's loads are issued even before the B/C conv phase.
 // The recurrence is the Mamba-2 SSD layer of the Codestral-Mamba port header
 // (codestral_mamba.ts); step == forward at length 1 with the state carried
 // follows mojolearn.Mamba3Block's step() description.
@@ -46,6 +49,8 @@ __device__ __forceinline__ float round_to(float v, float*) { return v; }
 __device__ __forceinline__ float round_to(float v, uint16_t*) { return __uint_as_float(f32_to_bf16_bits(v) << 16); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -82,7 +87,6 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float* a_s = dt_s + H;            // [H]
     int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
     float* d_s = a_s + 2 * H;                         // [H]: D (0 when absent)
-    float* z_s = d_s + H;                             // [H*P]: the gate input (when given)
 
     // ---- state rows: row = h * P + p holds NQ float4 (n fastest).  LPR lanes
     // share a row, lane q of a row holds float4 q + LPR j (j < FPL), so every
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         a.ssm_state + (size_t)b * H * P * N, 0, nrows * NQ * 16, 0x00020000);
     constexpr int kNT = 2;                           // cache policy: nontemporal
-    f4v s_cur[FPL], s_nxt[FPL], s_nx2[FPL];     // rounds r, r+1, r+2
+    f4v s_cur[FPL], s_nxt[FPL];       // rounds r, r+1
     auto row_of = [&](int r) { return r * RPR + wave * RPW + lane / LPR; };
     auto off_of = [&](int row, int j) { return (uint32_t)((row * NQ + q + j * LPR) * 16); };
     auto load_round = [&](int r, f4v* dst) {
@@ -113,12 +117,13 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
             dst[j] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(sr, off_of(row, j), 0, kNT));
     };
     load_round(0, s_cur);             // independent of the conv phase: start it now
-    load_round(1, s_nxt);
 
-    // ---- 1. conv window, activation, buffer shift
+    // ---- 1. the B and C columns: conv window, activation, buffer shift, to
+    // LDS (every state row reads them); dt, the decay, D per head.  The x
+    // columns are convolved inside the state loop by the rows they feed.
     const T* raw = static_cast<const T*>(a.xbc_raw) + (size_t)b * C;
     T* cst = static_cast<T*>(a.conv_state) + (size_t)b * (K - 1) * C;
-    for (int c0 = tid * VEC; c0 < C; c0 += kStepThreads * VEC) {
+    for (int c0 = HP + tid * VEC; c0 < C; c0 += kStepThreads * VEC) {
         // the three carried rows and the new row, as raw 16-byte words
         const uint4 q0 = *reinterpret_cast<const uint4*>(cst + c0);
         const uint4 q1 = *reinterpret_cast<const uint4*>(cst + C + c0);
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const int c = c0 + e;
-            float4 w = *reinterpret_cast<const float4*>(a.conv_w + (size_t)c * K);
+            const float4 w = *reinterpret_cast<const float4*>(a.conv_w + (size_t)c * K);
             float v = a.conv_b ? a.conv_b[c] : 0.0f;
             v = fmaf(w.x, r0[e], v);
             v = fmaf(w.y, r1[e], v);
@@ -154,10 +159,28 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         gofs_s[h] = (h / hpg) * N;
         d_s[h] = a.D ? a.D[h] : 0.0f;
     }
+
+    // ---- per-row x inputs, loaded one round ahead of their use: row h*P + p
+    // is x channel h*P + p, so a row's lanes convolve their own channel (all
+    // of them, from the same addresses) and its first lane shifts the buffer.
     const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
-    if (zb) {
-        for (int i = tid; i < HP; i += kStepThreads) z_s[i] = load1(zb + i);
-    }
+    struct XIn {
+        T q0, q1, q2, qr;     // carried rows and the new raw value (bits as stored)
+        float4 w;
+        float bias, z;
+    };
+    auto load_x = [&](int r, XIn& o) {
+        const int ch = min(row_of(r), nrows - 1);    // the row's x channel, clamped past the end
+        o.q0 = cst[ch];
+        o.q1 = cst[C + ch];
+        o.q2 = cst[2 * C + ch];
+        o.qr = raw[ch];
+        o.w = *reinterpret_cast<const float4*>(a.conv_w + (size_t)ch * K);
+        o.bias = a.conv_b ? a.conv_b[ch] : 0.0f;
+        o.z = zb ? load1(zb + ch) : 0.0f;
+    };
+    XIn x_cur, x_nxt;
+    load_x(0, x_cur);
     __syncthreads();
 
     // ---- 2. state read-modify-write, one round of RPR rows at a time; the
@@ -171,10 +194,11 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     float4 Bq[FPL], Cq[FPL];
     int cur_gofs = -1;
     for (int r = 0; r < nrounds; ++r) {
-        load_round(r + 2, s_nx2);                    // past the last round: out of range, reads 0
+        load_round(r + 1, s_nxt);                    // past the last round: out of range, reads 0
+        load_x(r + 1, x_nxt);
         const int row = row_of(r);
-        // a wave's rows lie in one head; a wave past the end computes on zeros
-        // and its stores fall outside the ranges
+        // a wave's rows lie in one head; a wave past the end computes on clamped
+        // rows and its stores fall outside the ranges or are skipped
         const int hrow = min(row, nrows - 1);
         const int h = __builtin_amdgcn_readfirstlane(hrow / P);
         const int p = hrow % P;
@@ -187,8 +211,23 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
                 Cq[j] = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * (q + j * LPR));
             }
         }
+        // the row's x channel: conv window, activation, rounded to T as a prefill stores it
+        float xp;
+        {
+            float v = x_cur.bias;
+            v = fmaf(x_cur.w.x, to_f32(x_cur.q0), v);
+            v = fmaf(x_cur.w.y, to_f32(x_cur.q1), v);
+            v = fmaf(x_cur.w.z, to_f32(x_cur.q2), v);
+            v = fmaf(x_cur.w.w, to_f32(x_cur.qr), v);
+            if (a.act == 0) v = silu_f(v);
+            xp = round_to(v, (T*)nullptr);
+        }
+        if (q == 0 && row < nrows) {                 // shift the channel's buffer rows
+            cst[row] = x_cur.q1;
+            cst[C + row] = x_cur.q2;
+            cst[2 * C + row] = x_cur.qr;
+        }
         const float dec = a_s[h];
-        const float xp = xbc_s[h * P + p];
         const float dx = dt_s[h] * xp;
         float part = 0.0f;
 #pragma unroll
@@ -208,14 +247,14 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
         // sum over the LPR lanes of the row (a fixed order: deterministic)
         part = row_sum<LPR>(part);
         float yv = fmaf(d_s[h], xp, part);
-        if (zb) yv *= silu_f(z_s[h * P + p]);
+        if (zb) yv *= silu_f(x_cur.z);
         const bool first = q == 0 && row < nrows;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yr, first ? (uint32_t)(h * P + p) * 4 : 0x7fffffffu, 0, 0);
 #pragma unroll
         for (int j = 0; j < FPL; ++j) {
             s_cur[j] = s_nxt[j];
-            s_nxt[j] = s_nx2[j];
         }
+        x_cur = x_nxt;
     }
 }
 
