@@ -1,7 +1,7 @@
 /*
  * ssd.h -- C ABI of libssd.so, the gfx950 (MI355X) Mamba-2 SSD mixer core.
  *
- * Four operations, each one or two HIP kernel launches on the caller's stream:
+ * Five operations, each a few HIP kernel launches on the caller's stream:
  *
  *   ssd_conv_fwd        causal depthwise conv (k = 4) + SiLU over the
  *                       [x | B | C] columns, and dt = softplus(dt_raw + dt_bias)
@@ -10,6 +10,9 @@
  *                       D skip and the y * silu(z) gate
  *   ssd_mixer_fwd       both of the above in one pass: the scan reads the raw
  *                       columns and convolves each chunk on chip
+ *   ssd_resume_fwd      decode tokens appended to the working chunk and
+ *                       rescanned with the forward kernels: bit-identical to
+ *                       the forward
  *   ssd_step            one decode token per sequence: conv from a rolling
  *                       buffer, state update, output and gate
  *
@@ -248,6 +251,49 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
  * conv output [B][L][conv_dim] (T) and dt [B][L][H] (fp32), each padded to
  * 256 bytes, plus the scan's split state (ssd_chunk_scan_workspace_size()). */
 size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
+
+/*
+ * ssd_resume_fwd -- append n tokens to each sequence's working chunk and
+ * return their outputs exactly as the sequential forward computes them.
+ *
+ * The working chunk is the tokens after a sequence's last multiple of 64
+ * (pos of them, the same for every sequence).  Decoding resumes it (the
+ * mojolearn.Mamba3Block step() description: decoding resumes the working
+ * chunk, so step and forward continue a prefill bit for bit): the new tokens
+ * are convolved by the conv kernel into rows pos .. pos+n-1 of the working
+ * chunk, and the scan kernel reruns the chunk's rows 0 .. pos+n-1 from the
+ * state at the chunk's start.  A token's output depends only on the chunk's
+ * rows up to it, so y is bit-identical (up to the sign of zero) to
+ * ssd_conv_fwd + ssd_chunk_scan_fwd without a workspace over the whole
+ * sequence, and so is the state each time a chunk completes.  A step costs a
+ * rerun of the working chunk; ssd_step is the cheaper recurrent step.
+ *
+ *   pos, n       0 <= pos <= 63, n >= 1, pos + n <= 64
+ *   xbc_raw      T [B][n][conv_dim], dt_raw T [B][n][H], z T [B][n][H*P] or
+ *                NULL, all contiguous: the new tokens' raw inputs
+ *   conv_w, conv_b, dt_bias, A, D, act   as in ssd_conv_fwd / ssd_chunk_scan_fwd
+ *   conv_state   T [B][K-1][conv_dim], read and advanced in place
+ *   chunk_xbc    T [B][64][conv_dim], chunk_dt f32 [B][64][H], chunk_z T
+ *                [B][64][H*P] (given iff z is): the working chunk's
+ *                convolved rows, dt and gate rows; rows < pos as earlier
+ *                calls left them, rows pos .. pos+n-1 written
+ *   chunk_state  f32 [B][H][P][N]: the SSM state at the working chunk's
+ *                start; when pos + n = 64 it becomes the state at its end
+ *                (the next chunk's start, pos = 0)
+ *   chunk_y      f32 [B][64][H*P] scratch
+ *   y            f32 [B][n][H*P]: the new tokens' outputs
+ * To continue a forward over L0 tokens (a multiple of 64): chunk_state = its
+ * final_state, conv_state = its conv_state_out, pos = 0; a prefill whose
+ * length is not a multiple of 64 passes its last L mod 64 tokens through
+ * this call.  No document ids: appended tokens continue the working chunk's
+ * document.  All buffers 16-byte aligned (chunk_dt, dt_raw: 4-byte).
+ */
+int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos, int n,
+                   const void *xbc_raw, const void *dt_raw, const void *z,
+                   const float *conv_w, const float *conv_b, const float *dt_bias,
+                   const float *A, const float *D, int act,
+                   void *conv_state, void *chunk_xbc, float *chunk_dt, void *chunk_z,
+                   float *chunk_state, float *chunk_y, float *y, void *stream);
 
 /*
  * ssd_step -- one decode token for each of B sequences.

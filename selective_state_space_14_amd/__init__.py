@@ -4,7 +4,8 @@ The entry points mirror the C ABI in include/ssd.h one to one:
 
     ssd_conv_fwd        causal depthwise conv (k=4) + SiLU, dt = softplus(dt + dt_bias)
     ssd_chunk_scan_fwd  chunked (64) SSD scan with groups, documents, states, D skip, z gate
-    ssd_mixer_fwd       both in one pass (the scan convolves the raw columns on chip)
+    ssd_mixer_fwd       both in one call (staged, or the scan convolving the raw columns on chip)
+    ssd_resume_fwd      decode tokens rescanned with the working chunk: bit-identical to the forward
     ssd_step            one decode token per sequence
 
 This module only marshals torch tensors (device pointers, row strides, the
@@ -19,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_step",
+__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_resume_fwd", "ssd_step",
            "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size",
            "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
 
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
                                   I, P, I64, P, SZ, P]
     lib.ssd_mixer_workspace_size.restype = SZ
     lib.ssd_mixer_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.ssd_resume_fwd.restype = I
+    lib.ssd_resume_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
     lib.ssd_step.restype = I
     lib.ssd_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P]
     _lib = lib
@@ -247,6 +250,47 @@ def ssd_mixer_fwd(xbc_raw, dt_raw, conv_w, A, *, H, P, N, G, K=4, conv_b=None, d
         _ptr(conv_state_in, "conv_state_in", xbc_raw.dtype), _ptr(conv_state_out, "conv_state_out", xbc_raw.dtype),
         _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
         int(act), _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
+    _check(st)
+    return y
+
+
+def ssd_resume_fwd(xbc_raw, dt_raw, conv_w, A, conv_state, chunk_xbc, chunk_dt, chunk_state, chunk_y, *, pos,
+                   H, P, N, G, K=4, z=None, chunk_z=None, conv_b=None, dt_bias=None, D=None, act=SSD_ACT_SILU, y=None,
+                   stream=None):
+    """Append n = xbc_raw.shape[1] tokens to the working chunk (pos tokens already in it) and return their
+    y [B, n, H*P] fp32, bit-identical to the sequential forward.  xbc_raw [B, n, conv_dim], dt_raw [B, n, H],
+    z [B, n, H*P] (same dtype, contiguous); conv_state [B, K-1, conv_dim], chunk_xbc [B, 64, conv_dim],
+    chunk_z [B, 64, H*P] (same dtype), chunk_dt [B, 64, H], chunk_state [B, H, P, N], chunk_y [B, 64, H*P] fp32."""
+    lib = load()
+    B, n = xbc_raw.shape[0], xbc_raw.shape[1]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    _contig(xbc_raw, "xbc_raw", (B, n, C))
+    _contig(dt_raw, "dt_raw", (B, n, H))
+    _contig(z, "z", (B, n, H * P))
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(conv_state, "conv_state", (B, K - 1, C))
+    _contig(chunk_xbc, "chunk_xbc", (B, 64, C))
+    _contig(chunk_dt, "chunk_dt", (B, 64, H))
+    _contig(chunk_z, "chunk_z", (B, 64, H * P))
+    _contig(chunk_state, "chunk_state", (B, H, P, N))
+    _contig(chunk_y, "chunk_y", (B, 64, H * P))
+    if y is None:
+        y = torch.empty((B, n, H * P), dtype=torch.float32, device=xbc_raw.device)
+    _contig(y, "y", (B, n, H * P))
+    st = lib.ssd_resume_fwd(
+        B, H, P, N, G, K, dtype, int(pos), n,
+        _ptr(xbc_raw, "xbc_raw"), _ptr(dt_raw, "dt_raw", xbc_raw.dtype), _ptr(z, "z", xbc_raw.dtype),
+        _ptr(conv_w, "conv_w", torch.float32), _ptr(conv_b, "conv_b", torch.float32),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32), int(act),
+        _ptr(conv_state, "conv_state", xbc_raw.dtype), _ptr(chunk_xbc, "chunk_xbc", xbc_raw.dtype),
+        _ptr(chunk_dt, "chunk_dt", torch.float32), _ptr(chunk_z, "chunk_z", xbc_raw.dtype),
+        _ptr(chunk_state, "chunk_state", torch.float32), _ptr(chunk_y, "chunk_y", torch.float32),
+        _ptr(y, "y", torch.float32), _stream(stream))
     _check(st)
     return y
 

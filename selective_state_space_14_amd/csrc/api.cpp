@@ -153,6 +153,7 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
     }
     ssd::ConvArgs a;
     a.B = B; a.L = L; a.C = (int)C; a.H = H; a.dtype = dtype; a.act = act;
+    a.Lb_in = a.Lb_out = L;
     a.raw = xbc_raw; a.raw_stride = xbc_raw_row_stride;
     a.w = conv_w; a.bias = conv_b;
     a.dt_raw = dt_raw; a.dt_stride = dt_raw_row_stride; a.dt_bias = dt_bias;
@@ -228,7 +229,7 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
         return ok();
     }
     ssd::ScanArgs a{};
-    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype; a.Lb = L;
     a.x = x; a.x_stride = x_row_stride;
     a.Bm = Bm; a.B_stride = B_row_stride;
     a.Cm = Cm; a.C_stride = C_row_stride;
@@ -338,7 +339,7 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
     }
 
     ssd::ScanArgs a{};
-    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype; a.Lb = L;
     a.A = A; a.D = D;
     a.z = z; a.z_stride = z_row_stride;
     a.doc = doc_ids;
@@ -357,6 +358,7 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         ws_left -= used;
         ssd::ConvArgs c;
         c.B = B; c.L = L; c.C = (int)C; c.H = H; c.dtype = dtype; c.act = act;
+        c.Lb_in = c.Lb_out = L;
         c.raw = xbc_raw; c.raw_stride = xbc_raw_row_stride;
         c.w = conv_w; c.bias = conv_b;
         c.dt_raw = dt_raw; c.dt_stride = dt_raw_row_stride; c.dt_bias = dt_bias;
@@ -388,6 +390,86 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         if (init_state) a.h0 = a.dec + ((u * sizeof(float) + 255) / 256) * 256 / sizeof(float);
     }
     return hip_status(fn, ssd::launch_scan(a, s));
+}
+
+int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos, int n,
+                   const void* xbc_raw, const void* dt_raw, const void* z,
+                   const float* conv_w, const float* conv_b, const float* dt_bias,
+                   const float* A, const float* D, int act,
+                   void* conv_state, void* chunk_xbc, float* chunk_dt, void* chunk_z,
+                   float* chunk_state, float* chunk_y, float* y, void* stream) {
+    const char* fn = "ssd_resume_fwd";
+    TRY(check_dims(fn, B, 1, H, P, N, G, K, dtype));
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    if (pos < 0 || pos > 63)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: pos=%d must lie in [0, 63] (tokens already in the working chunk)", fn, pos);
+    if (n < 1 || pos + n > 64)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: n=%d must be >= 1 with pos + n = %d <= 64", fn, n, pos + n);
+    const bool work = B > 0;
+    const int64_t C = (int64_t)H * P + 2LL * G * N;
+    const int es = esize(dtype);
+    TRY(check_ptr(fn, "xbc_raw", xbc_raw, work, true));
+    TRY(check_ptr(fn, "dt_raw", dt_raw, work, false));
+    TRY(check_ptr(fn, "z", z, false, true));
+    TRY(check_ptr(fn, "conv_w", conv_w, work, true));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, work, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "conv_state", conv_state, work, true));
+    TRY(check_ptr(fn, "chunk_xbc", chunk_xbc, work, true));
+    TRY(check_ptr(fn, "chunk_dt", chunk_dt, work, false));
+    TRY(check_ptr(fn, "chunk_z", chunk_z, false, true));
+    TRY(check_ptr(fn, "chunk_state", chunk_state, work, true));
+    TRY(check_ptr(fn, "chunk_y", chunk_y, work, true));
+    TRY(check_ptr(fn, "y", y, work, true));
+    if ((z == nullptr) != (chunk_z == nullptr))
+        return fail(SSD_ERR_NULL_ARG, "%s: z and chunk_z must be given together (z=%p, chunk_z=%p)", fn, z, chunk_z);
+    if (!work) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t HP = (int64_t)H * P;
+
+    // 1. conv of the new tokens into rows pos .. pos+n-1 of the working chunk;
+    //    the rolling conv state advances in place
+    ssd::ConvArgs c;
+    c.B = B; c.L = n; c.C = (int)C; c.H = H; c.dtype = dtype; c.act = act;
+    c.Lb_in = n; c.Lb_out = 64;
+    c.raw = xbc_raw; c.raw_stride = C;
+    c.w = conv_w; c.bias = conv_b;
+    c.dt_raw = dt_raw; c.dt_stride = H; c.dt_bias = dt_bias;
+    c.doc = nullptr;
+    c.state_in = conv_state; c.state_out = conv_state;
+    c.out = static_cast<char*>(chunk_xbc) + (size_t)pos * C * es; c.out_stride = C;
+    c.dt_out = chunk_dt + (size_t)pos * H;
+    hipError_t e = ssd::launch_conv(c, s);
+    if (e != hipSuccess) return hip_status(fn, e);
+    // 2. the gate rows
+    if (z) {
+        e = ssd::launch_copy_rows(z, HP * es, n * HP * es, static_cast<char*>(chunk_z) + (size_t)pos * HP * es,
+                                  HP * es, 64 * HP * es, B, n, (int)(HP * es), s);
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+    // 3. the scan over the working chunk from its starting state, as the
+    //    sequential forward runs this chunk; a full chunk replaces the state
+    ssd::ScanArgs a{};
+    a.B = B; a.L = pos + n; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype; a.Lb = 64;
+    const char* xb = static_cast<const char*>(chunk_xbc);
+    a.x = xb; a.x_stride = C;
+    a.Bm = xb + (size_t)HP * es; a.B_stride = C;
+    a.Cm = xb + ((size_t)HP + (size_t)G * N) * es; a.C_stride = C;
+    a.dt = chunk_dt; a.dt_stride = H; a.dt_softplus = 0;
+    a.A = A; a.D = D;
+    a.z = chunk_z; a.z_stride = HP;
+    a.doc = nullptr;
+    a.init_state = chunk_state; a.final_state = pos + n == 64 ? chunk_state : nullptr;
+    a.y = chunk_y; a.y_stride = HP;
+    a.K = 1; a.S = 64;
+    e = ssd::launch_scan(a, s);
+    if (e != hipSuccess) return hip_status(fn, e);
+    // 4. the new tokens' outputs
+    return hip_status(fn, ssd::launch_copy_rows(chunk_y + (size_t)pos * HP, HP * 4, 64 * HP * 4, y, HP * 4,
+                                                n * HP * 4, B, n, (int)(HP * 4), s));
 }
 
 int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,

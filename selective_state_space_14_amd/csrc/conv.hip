@@ -20,6 +20,8 @@
 //
 // Tap order: conv_w[c][3] multiplies the current token (the un-reversed form
 // of the [conv_dim, 1, d_conv] weight listed by the Codestral-Mamba port).
+#include <algorithm>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
     const int t0 = blockIdx.y * kTile;
     const int t1 = min(t0 + kTile, L);
     const int ncb = (C / VEC + kConvThreads - 1) / kConvThreads;
-    const int32_t* doc = a.doc ? a.doc + (size_t)b * L : nullptr;
+    const int32_t* doc = a.doc ? a.doc + (size_t)b * a.Lb_in : nullptr;
 
     if ((int)blockIdx.x == ncb) {
         // ---- dt = softplus(dt_raw + dt_bias) for the tile's tokens
@@ -76,8 +78,8 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
         const int H = a.H;
         for (int i = threadIdx.x; i < (t1 - t0) * H; i += kConvThreads) {
             const int t = t0 + i / H, h = i % H;
-            const float r = CV<T>::scalar(a.dt_raw, ((size_t)b * L + t) * a.dt_stride + h);
-            a.dt_out[((size_t)b * L + t) * H + h] = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
+            const float r = CV<T>::scalar(a.dt_raw, ((size_t)b * a.Lb_in + t) * a.dt_stride + h);
+            a.dt_out[((size_t)b * a.Lb_out + t) * H + h] = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
         }
         return;
     }
@@ -93,8 +95,8 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
 
     const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * VEC;
     if (c0 >= C) return;
-    const T* raw = static_cast<const T*>(a.raw) + (size_t)b * L * a.raw_stride + c0;
-    T* out = static_cast<T*>(a.out) + (size_t)b * L * a.out_stride + c0;
+    const T* raw = static_cast<const T*>(a.raw) + (size_t)b * a.Lb_in * a.raw_stride + c0;
+    T* out = static_cast<T*>(a.out) + (size_t)b * a.Lb_out * a.out_stride + c0;
 
     float w[4][VEC], bias[VEC];
 #pragma unroll
@@ -237,11 +239,35 @@ __global__ void copy16_kernel(const uint4* src, uint4* dst, size_t n) {
 }
 }  // namespace
 
+__global__ void copy_rows_kernel(const char* src, int64_t srs, int64_t sbs, char* dst, int64_t drs, int64_t dbs,
+                                 int rows, int row_words) {
+    const int b = blockIdx.y;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (int64_t)rows * row_words;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i / row_words), w = (int)(i % row_words);
+        *reinterpret_cast<uint4*>(dst + b * dbs + r * drs + 16 * w) =
+            *reinterpret_cast<const uint4*>(src + b * sbs + r * srs + 16 * w);
+    }
+}
+
 hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream) {
     if (n == 0 || src == dst) return hipSuccess;
     const unsigned blocks = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(copy16_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
                        static_cast<uint4*>(dst), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* src, int64_t src_row_stride, int64_t src_batch_stride, void* dst,
+                            int64_t dst_row_stride, int64_t dst_batch_stride, int B, int rows, int row_bytes,
+                            hipStream_t stream) {
+    if (B == 0 || rows == 0 || row_bytes == 0) return hipSuccess;
+    const int row_words = row_bytes / 16;
+    const long total = (long)rows * row_words;
+    const unsigned bx = (unsigned)std::min<long>((total + 255) / 256, 1024);
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(bx, B), dim3(256), 0, stream, static_cast<const char*>(src),
+                       src_row_stride, src_batch_stride, static_cast<char*>(dst), dst_row_stride, dst_batch_stride,
+                       rows, row_words);
     return hipGetLastError();
 }
 

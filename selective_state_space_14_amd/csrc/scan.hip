@@ -217,17 +217,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
 
     // Row bases (uniform) and per-lane element offsets; a chunk's loads are
     // base + t0 * stride (scalar) + lane offset, rows clamped only in the tail.
-    const E* xbase = static_cast<const E*>(a.x) + (size_t)b * L * a.x_stride;
-    const E* zbase = gate ? static_cast<const E*>(a.z) + (size_t)b * L * a.z_stride : xbase;
+    const E* xbase = static_cast<const E*>(a.x) + (size_t)b * a.Lb * a.x_stride;
+    const E* zbase = gate ? static_cast<const E*>(a.z) + (size_t)b * a.Lb * a.z_stride : xbase;
     const int64_t zs = gate ? a.z_stride : a.x_stride;
-    const E* Bbase = static_cast<const E*>(a.Bm) + (size_t)b * L * a.B_stride;
-    const E* Cbase = static_cast<const E*>(a.Cm) + (size_t)b * L * a.C_stride;
-    const float* dtbase = a.dt + (size_t)b * L * a.dt_stride;
-    const int32_t* docg = a.doc ? a.doc + (size_t)b * L : nullptr;
+    const E* Bbase = static_cast<const E*>(a.Bm) + (size_t)b * a.Lb * a.B_stride;
+    const E* Cbase = static_cast<const E*>(a.Cm) + (size_t)b * a.Lb * a.C_stride;
+    const float* dtbase = a.dt + (size_t)b * a.Lb * a.dt_stride;
+    const int32_t* docg = a.doc ? a.doc + (size_t)b * a.Lb : nullptr;
     // absent doc ids: load (unused) in-bounds words of dt instead, keeping loads unconditional
     const int32_t* docsrc = docg ? docg : reinterpret_cast<const int32_t*>(dtbase);
     const int xcol = h * 64 + p0 + 4 * q4;
-    float* yg = a.y + (size_t)b * L * a.y_stride + xcol;
+    float* yg = a.y + (size_t)b * a.Lb * a.y_stride + xcol;
 
     // Loads: a uniform chunk base (t0 * stride, scalar) plus a 32-bit per-lane
     // byte offset fixed for the whole unit; only a chunk that runs past the
@@ -817,17 +817,17 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const bool docs = a.doc != nullptr;
 
     // ---- global bases (uniform)
-    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)hq * HPW * 64;
-    const uint16_t* zbase = gate ? static_cast<const uint16_t*>(a.z) + (size_t)b * L * a.z_stride + (size_t)h * 64 + p0
+    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * a.Lb * a.x_stride + (size_t)hq * HPW * 64;
+    const uint16_t* zbase = gate ? static_cast<const uint16_t*>(a.z) + (size_t)b * a.Lb * a.z_stride + (size_t)h * 64 + p0
                                  : xhead + hh * 64 + p0;   // stand-in rows keep the operation count fixed
     const int Zs2 = (int)(gate ? a.z_stride : a.x_stride) * 2;
-    const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
-    const uint16_t* Cbase = static_cast<const uint16_t*>(a.Cm) + (size_t)b * L * a.C_stride + (size_t)g * N;
+    const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * a.Lb * a.B_stride + (size_t)g * N;
+    const uint16_t* Cbase = static_cast<const uint16_t*>(a.Cm) + (size_t)b * a.Lb * a.C_stride + (size_t)g * N;
     // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
-    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * L * a.dt16_stride + (h & ~1))
-                            : static_cast<const void*>(a.dt + (size_t)b * L * a.dt_stride + h);
-    const int32_t* docbase = a.doc + (size_t)b * L;
-    float* ybase = a.y + (size_t)b * L * a.y_stride + h * 64;
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h);
+    const int32_t* docbase = a.doc + (size_t)b * a.Lb;
+    float* ybase = a.y + (size_t)b * a.Lb * a.y_stride + h * 64;
     const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
     const int Ys = (int)a.y_stride;
 
@@ -1357,12 +1357,12 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     const int tl = tend - 1;
     const bool docs = a.doc != nullptr;
 
-    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * L * a.x_stride + (size_t)hq * HPW * 64;
-    const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * L * a.B_stride + (size_t)g * N;
+    const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * a.Lb * a.x_stride + (size_t)hq * HPW * 64;
+    const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * a.Lb * a.B_stride + (size_t)g * N;
     // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
-    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * L * a.dt16_stride + (h & ~1))
-                            : static_cast<const void*>(a.dt + (size_t)b * L * a.dt_stride + h);
-    const int32_t* docbase = a.doc + (size_t)b * L;
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h);
+    const int32_t* docbase = a.doc + (size_t)b * a.Lb;
     const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
 
     // copy slots of this wave: copy wave + NW j of the chunk (B tile, then X tiles)

@@ -10,6 +10,9 @@ namespace ssd {
 
 struct ConvArgs {
     int B, L, C, H, dtype, act;
+    // rows between batch rows: of raw, dt_raw and doc (Lb_in), of out and
+    // dt_out (Lb_out); both >= L, and L for the public calls
+    int Lb_in, Lb_out;
     const void* raw; int64_t raw_stride;
     const float* w; const float* bias;
     const void* dt_raw; int64_t dt_stride;
@@ -22,6 +25,7 @@ struct ConvArgs {
 
 struct ScanArgs {
     int B, L, H, P, N, G, dtype;
+    int Lb;   // rows between batch rows of every [B][L][...] tensor (>= L; L for the public calls)
     const void* x; int64_t x_stride;
     const void* Bm; int64_t B_stride;
     const void* Cm; int64_t C_stride;
@@ -67,6 +71,11 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 // Copies n 16-byte words src -> dst (src == nullptr: zero fill); used for the
 // L = 0 state pass-through without a memset node.
 hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream);
+// Copies rows of row_bytes (a multiple of 16) for B batch rows x `rows` rows:
+// src/dst row r of batch b at base + b * batch_stride + r * row_stride (bytes).
+hipError_t launch_copy_rows(const void* src, int64_t src_row_stride, int64_t src_batch_stride, void* dst,
+                            int64_t dst_row_stride, int64_t dst_batch_stride, int B, int rows, int row_bytes,
+                            hipStream_t stream);
 
 size_t step_lds_bytes(int H, int P, int N, int G);
 
