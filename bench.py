@@ -14,8 +14,8 @@ step; "roofline" = the scan call's algorithmic bytes / its average duration
 "cpu_baseline" = the fp64 oracle (conv + scan) timed on this host.  Under
 "extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
 two kernels behind one call; fused: the conv computed inside the scan
-kernels), and the other workloads (packed documents, the large layer, the
-decode step).
+kernels), the other workloads (packed documents, the large layer, the decode
+step), and the chunk-resume decode (ssd_resume_fwd) on the decode workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -269,6 +269,43 @@ def decode_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
             "step_GBs": kb / (k_ms * 1e-3) / 1e9}
 
 
+def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
+    """ssd_resume_fwd one token at a time over one full working chunk (64 steps, pos 0..63): the decode that
+    continues the forward bit for bit.  Returns the mean per step."""
+    dev = "cuda"
+    prm = synth.params(wl, seed, device=dev)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    B, C, HP = wl.B, wl.conv_dim, wl.H * wl.P
+    state = torch.randn(B, wl.H, wl.P, wl.N, generator=g, device=dev) * 0.1
+    conv = torch.randn(B, 3, C, generator=g, device=dev).to(wl.torch_dtype)
+    cx = torch.zeros(B, 64, C, dtype=wl.torch_dtype, device=dev)
+    cdt = torch.zeros(B, 64, wl.H, dtype=torch.float32, device=dev)
+    cz = torch.zeros(B, 64, HP, dtype=wl.torch_dtype, device=dev)
+    cy = torch.empty(B, 64, HP, dtype=torch.float32, device=dev)
+    y = torch.empty(B, 1, HP, dtype=torch.float32, device=dev)
+    ins = [synth.step_inputs(wl, s, seed, device=dev) for s in range(2)]
+    ins = [{k: v[:, None].contiguous() for k, v in st.items()} for st in ins]
+
+    def one(pos):
+        st = ins[pos % 2]
+        ssd.ssd_resume_fwd(st["xbc_raw"], st["dt_raw"], prm["conv_w"], prm["A"], conv, cx, cdt, state, cy, pos=pos,
+                           H=wl.H, P=wl.P, N=wl.N, G=wl.G, z=st["z"], chunk_z=cz, dt_bias=prm["dt_bias"], D=prm["D"],
+                           y=y)
+
+    for i in range(warmup):
+        one(i % 64)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for pos in range(64):
+        one(pos)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / 64
+    return {"workload": wl.name + " (ssd_resume_fwd, one token per call, mean over a 64-token chunk)",
+            "ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "unit": "head-tokens/s (B*H per step)"}
+
+
 def cpu_baseline(synth, wl, rows):
     """The fp64 oracle (conv + scan, as it stands) on `rows` batch rows of the workload."""
     import oracle
@@ -350,6 +387,7 @@ def main():
         r = decode_bench(ssd, synth, torch, dw, max(20, args.steps * 2), args.warmup)
         extras.append({"workload": dw.name + " (ssd_step)", **r, "step_frac": r["step_GBs"] / HBM_PEAK_GBS,
                        "unit": "head-tokens/s (B*H per step)"})
+        extras.append(resume_bench(ssd, synth, torch, dw, args.warmup))
 
     cpu = None
     if not args.no_cpu_baseline:
