@@ -30,7 +30,7 @@ def np64(t):
 
 
 def rms(a):
-    a = np.asarray(a, np.float64)
+    a = np64(a)
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
 
 
