@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Mamba-2 SSD mixer core (conv, scan, decode step).
+"""fp64 CPU oracle for the Mamba-2 SSD mixer core (conv, scan, decode step) and the Mamba-1 S6 scan.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  It
@@ -93,6 +93,8 @@ class Oracle:
         lib.oracle_scan.restype = i
         lib.oracle_scan.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, i, _dp, _dp, _dp, _dp, _ip,
                                     _dp, _dp, _dp]
+        lib.oracle_s6.restype = i
+        lib.oracle_s6.argtypes = [i, i, i, i, _dp, _dp, i, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _dp, _dp]
         lib.oracle_step.restype = i
         lib.oracle_step.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                     i, i, _dp]
@@ -160,6 +162,33 @@ class Oracle:
                                    a_p, dd_p, z_p, d_p, h0_p, _out(fs), _out(y))
         if rc != 0:
             raise ValueError("oracle_scan rejected its arguments")
+        return y, fs
+
+    def s6(self, x, dt, A, Bm, Cm, D=None, z=None, doc_ids=None, init_state=None, *, dt_softplus: bool = False,
+           dt_bias=None, want_state: bool = False):
+        """Sequential fp64 Mamba-1 selective scan.  x, dt, z [B,L,D]; A [D,N]; Bm, Cm [B,L,N].
+
+        Returns (y [B,L,D], final_state [B,D,N] or None)."""
+        x_c, x_p = _in(x)
+        Bsz, L, Dn = x_c.shape
+        a_c, a_p = _in(A)
+        N = a_c.shape[1]
+        if a_c.shape != (Dn, N):
+            raise ValueError("oracle.s6: A must be [D, N]")
+        dt_c, dt_p = _in(dt, (Bsz, L, Dn))
+        b_c, b_p = _in(Bm, (Bsz, L, N))
+        c_c, c_p = _in(Cm, (Bsz, L, N))
+        dd_c, dd_p = _in(D, (Dn,) if D is not None else None)
+        db_c, db_p = _in(dt_bias, (Dn,) if dt_bias is not None else None)
+        z_c, z_p = _in(z, (Bsz, L, Dn) if z is not None else None)
+        d_c, d_p = _ids(doc_ids, (Bsz, L))
+        h0_c, h0_p = _in(init_state, (Bsz, Dn, N) if init_state is not None else None)
+        y = np.empty((Bsz, L, Dn), np.float64)
+        fs = np.empty((Bsz, Dn, N), np.float64) if want_state else None
+        rc = self._lib.oracle_s6(Bsz, L, Dn, N, x_p, dt_p, int(bool(dt_softplus)), db_p, a_p, b_p, c_p, dd_p, z_p,
+                                 d_p, h0_p, _out(fs), _out(y))
+        if rc != 0:
+            raise ValueError("oracle_s6 rejected its arguments")
         return y, fs
 
     def step(self, raw, dt_raw, z, w, bias, dt_bias, A, D, conv_state, ssm_state, *, H, P, N, G,
@@ -238,3 +267,7 @@ def step(*a, **k):
 
 def forward(*a, **k):
     return default().forward(*a, **k)
+
+
+def s6(*a, **k):
+    return default().s6(*a, **k)

@@ -16,6 +16,11 @@ shared with the oracle's C code or with the HIP library.
   ``dt_s x_s B_s^T`` (``np.cumsum``), and ``y_t = C_t . S_t + D x_t``.
 * ``conv_reference`` -- a causal depthwise conv without documents or carried
   state, via ``np.convolve`` (a library routine the oracle does not use).
+* ``s6_quadratic_form`` -- the Mamba-1 selective scan written out the same
+  way: for each channel d and state index n the whole sequence at once,
+  ``h_t[n] = sum_s Lmask_dn[t, s] dt_s B_s[n] x_s + decay_dn[t] h0[n]`` with
+  ``Lmask_dn[t, s] = exp(A[d, n] sum_{r=s+1..t} dt_r)`` inside a document,
+  then ``y_t = C_t . h_t + D x_t`` and the gate.
 """
 from __future__ import annotations
 
@@ -117,3 +122,40 @@ def conv_reference(raw, w, bias=None, act_silu=True):
     if act_silu:
         out = out / (1.0 + np.exp(-out))
     return out
+
+
+def s6_quadratic_form(x, dt, A, Bm, Cm, D=None, z=None, doc_ids=None, init_state=None):
+    """Y and the final state of the Mamba-1 selective scan via materialised per-(d, n) decay matrices.
+
+    x, dt [B,L,D] (dt already activated), A [D,N], Bm, Cm [B,L,N], init_state [B,D,N].
+    """
+    x = np.asarray(x, np.float64)
+    Bsz, L, Dn = x.shape
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    N = A.shape[1]
+    Bm = np.asarray(Bm, np.float64)
+    Cm = np.asarray(Cm, np.float64)
+    y = np.zeros((Bsz, L, Dn))
+    fin = np.zeros((Bsz, Dn, N))
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(Bsz):
+        seg = _segments(None if doc_ids is None else doc_ids[b], L)
+        mask = causal & (seg[:, None] == seg[None, :])
+        first = seg == 0                                    # tokens that still see the initial state
+        for d in range(Dn):
+            T = np.cumsum(dt[b, :, d])                      # sum_{r <= t} dt_r
+            for n in range(N):
+                # Lmask[t, s] = exp(A (T_t - T_s)) for s <= t in one document
+                E = np.where(mask, np.exp(A[d, n] * (T[:, None] - T[None, :])), 0.0)
+                h = E @ (dt[b, :, d] * Bm[b, :, n] * x[b, :, d])
+                if init_state is not None:
+                    h = h + np.where(first, np.exp(A[d, n] * T), 0.0) * init_state[b, d, n]
+                y[b, :, d] += Cm[b, :, n] * h
+                fin[b, d, n] = h[-1] if L else (0.0 if init_state is None else init_state[b, d, n])
+            if D is not None:
+                y[b, :, d] += D[d] * x[b, :, d]
+            if z is not None:
+                zz = np.asarray(z, np.float64)[b, :, d]
+                y[b, :, d] *= zz / (1.0 + np.exp(-zz))
+    return y, fin

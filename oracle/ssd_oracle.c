@@ -52,6 +52,18 @@
  *   conv state      [B][K-1][conv_dim] (raw rows, oldest first)
  *   head h uses group h / (H/G).
  *
+ *  - The Mamba-1 selective scan (S6), per (batch row, channel d), with a
+ *    per-channel diagonal state of d_state entries (oracle_s6):
+ *        a_t[d,n] = exp(dt_t[d] * A[d][n])
+ *        h_t[d,n] = a_t[d,n] * h_{t-1}[d,n] + dt_t[d] * B_t[n] * x_t[d]
+ *        y_t[d]   = sum_n C_t[n] h_t[d,n] + D[d] * x_t[d]
+ *    falcon_mamba.ts header: x_proj rows [dt, B, C] give one B and one C per
+ *    token, shared by every channel; dt_proj (a linear with a bias) gives dt
+ *    per channel and the bias goes inside the softplus; A [d_inner, d_state]
+ *    = -exp(A_log), which selective_scan.ts computes as -exp(clamp(A_log,
+ *    -10, 5)).  The oracle takes A itself.  Gate, documents and states as
+ *    above.
+ *
  * Every routine below is a straight loop in the notation above.  The
  * per-token helpers conv_channel() and ssm_token() are shared by the prefill
  * routines and the step so that a prefill followed by steps runs the very
@@ -275,4 +287,48 @@ int oracle_step(int B, int H, int P, int N, int G, int K,
     free(xbc);
     free(yp);
     return 0;
+}
+
+/*
+ * Sequential Mamba-1 selective scan (S6) over [B, L] for all channels.
+ *   x, dt, z, y [B][L][D]; Bm, Cm [B][L][N]; A [D][N]; D_skip [D];
+ *   init_state, final_state [B][D][N].
+ * dt_softplus != 0: dt holds raw values and dt := softplus(dt + dt_bias).
+ * D_skip, z, doc, init_state, final_state, dt_bias may be NULL.
+ */
+int oracle_s6(int B, int L, int D, int N,
+              const double *x, const double *dt, int dt_softplus, const double *dt_bias,
+              const double *A, const double *Bm, const double *Cm, const double *D_skip,
+              const double *z, const int32_t *doc, const double *init_state, double *final_state,
+              double *y) {
+    if (B < 0 || L < 0 || D <= 0 || N <= 0 || !A) return -1;
+    if (L > 0 && (!x || !dt || !Bm || !Cm || !y)) return -1;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int d = 0; d < D; ++d) {
+            double *h = (double *)calloc((size_t)N, sizeof(double));
+            if (!h) { bad = 1; continue; }
+            if (init_state) memcpy(h, init_state + ((size_t)b * D + d) * N, sizeof(double) * (size_t)N);
+            const double *Ad = A + (size_t)d * N;
+            for (int t = 0; t < L; ++t) {
+                size_t row = (size_t)b * L + t;
+                if (doc && t > 0 && doc[row] != doc[row - 1]) memset(h, 0, sizeof(double) * (size_t)N);
+                double dtv = dt[row * D + d];
+                if (dt_softplus) dtv = softplus(dtv + (dt_bias ? dt_bias[d] : 0.0));
+                const double xv = x[row * D + d];
+                const double *Bt = Bm + row * N, *Ct = Cm + row * N;
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    h[n] = exp(dtv * Ad[n]) * h[n] + dtv * Bt[n] * xv;
+                    acc += Ct[n] * h[n];
+                }
+                double v = acc + (D_skip ? D_skip[d] : 0.0) * xv;
+                if (z) v *= silu(z[row * D + d]);
+                y[row * D + d] = v;
+            }
+            if (final_state) memcpy(final_state + ((size_t)b * D + d) * N, h, sizeof(double) * (size_t)N);
+            free(h);
+        }
+    return bad ? -1 : 0;
 }

@@ -301,9 +301,93 @@ def pin_dt_softplus_inside(o, seed=12):
     np.testing.assert_allclose(y1, y2, rtol=1e-13, atol=1e-14)
 
 
+# ----------------------------------------------------------------------------- Mamba-1 S6
+def _tiny_s6_case(seed, *, B=2, L=29, D=5, N=4, docs=False, h0=False, gate=False, Dskip=True):
+    r = _rng(seed)
+    case = dict(
+        x=r.standard_normal((B, L, D)),
+        dt=np.log1p(np.exp(r.standard_normal((B, L, D)) + r.uniform(-4, -1, D))),
+        A=-np.exp(r.uniform(-1.0, math.log(16), (D, N))),
+        Bm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        Cm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        D=r.standard_normal(D) if Dskip else None,
+        z=r.standard_normal((B, L, D)) if gate else None,
+        doc_ids=None,
+        init_state=r.standard_normal((B, D, N)) * 0.3 if h0 else None,
+    )
+    if docs:
+        ids = np.zeros((B, L), np.int32)
+        for b in range(B):
+            for c in sorted(r.choice(np.arange(1, L), size=3, replace=False)):
+                ids[b, c:] += 1
+        ids[0, 4:] += 1
+        ids[0, 5:] += 1                                   # a length-1 document
+        case["doc_ids"] = ids
+    return case
+
+
+def pin_s6_quadratic_form(o, seed=20):
+    """S6 recurrence == per-(d, n) materialised decay-matrix form, with D skip, gate, documents and a carried
+    initial state (per-n decay rates, so a decay taken from the wrong state index is caught)."""
+    for variant in (dict(), dict(docs=True), dict(h0=True, gate=True), dict(docs=True, h0=True, gate=True),
+                    dict(D=1, N=7), dict(N=1, h0=True)):
+        case = _tiny_s6_case(seed, **variant)
+        y, fs = o.s6(**case, want_state=True)
+        yq, fq = cf.s6_quadratic_form(**case)
+        np.testing.assert_allclose(y, yq, rtol=1e-11, atol=1e-12, err_msg=str(variant))
+        np.testing.assert_allclose(fs, fq, rtol=1e-11, atol=1e-12, err_msg=str(variant))
+
+
+def pin_s6_equals_ssd(o, seed=21):
+    """With A[d, n] equal to its head's A for every n and dt equal across a head's P channels, the S6 scan is
+    the SSD scan with one group (both run through their own oracle routines)."""
+    B, L, H, P, N = 2, 33, 3, 4, 5
+    case, dims = _tiny_scan_case(seed, B=B, L=L, H=H, P=P, N=N, G=1, docs=True, h0=True, gate=True)
+    y_ssd, f_ssd = o.scan(**case, **dims, want_state=True)
+    dt6 = np.repeat(case["dt"], P, axis=2)                # [B, L, H*P]
+    A6 = np.repeat(case["A"], P)[:, None] * np.ones((1, N))
+    h06 = case["init_state"].reshape(B, H * P, N)         # [B][H][P][N] -> channels h*P + p
+    y6, f6 = o.s6(case["x"], dt6, A6, case["Bm"], case["Cm"], np.repeat(case["D"], P), case["z"],
+                  case["doc_ids"], h06, want_state=True)
+    np.testing.assert_allclose(y6, y_ssd, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f6.reshape(B, H, P, N), f_ssd, rtol=1e-12, atol=1e-13)
+
+
+def pin_s6_zero_decay_and_carry(o, seed=22):
+    """A = 0: the state is a running sum (np.cumsum); a prefill split anywhere with the state carried equals one
+    pass bit for bit; raw dt with its bias through the softplus equals dt activated with numpy's logaddexp."""
+    case = _tiny_s6_case(seed, Dskip=True)
+    case["A"] = np.zeros_like(case["A"])
+    y, _ = o.s6(**case)
+    hsum = np.cumsum(case["dt"][..., None] * case["Bm"][:, :, None, :] * case["x"][..., None], axis=1)
+    expect = (hsum * case["Cm"][:, :, None, :]).sum(-1) + case["D"] * case["x"]
+    np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-12)
+    case = _tiny_s6_case(seed + 1, docs=True, h0=True, gate=True)
+    y, f = o.s6(**case, want_state=True)
+    for cut in (1, 13, 28):
+        sl = lambda v, a, b: None if v is None else v[:, a:b]
+        ya, fa = o.s6(case["x"][:, :cut], case["dt"][:, :cut], case["A"], case["Bm"][:, :cut], case["Cm"][:, :cut],
+                      case["D"], sl(case["z"], 0, cut), sl(case["doc_ids"], 0, cut), case["init_state"],
+                      want_state=True)
+        ids_c = sl(case["doc_ids"], cut, None)
+        # the second call's t = 0 continues its state: a cut on a document start passes a zero state
+        yc, fc = o.s6(case["x"][:, cut:], case["dt"][:, cut:], case["A"], case["Bm"][:, cut:], case["Cm"][:, cut:],
+                      case["D"], sl(case["z"], cut, None), ids_c,
+                      np.where((case["doc_ids"][:, cut] != case["doc_ids"][:, cut - 1])[:, None, None], 0.0, fa),
+                      want_state=True)
+        np.testing.assert_array_equal(np.concatenate([ya, yc], 1), y)
+        np.testing.assert_array_equal(fc, f)
+    r = _rng(seed + 2)
+    raw = r.standard_normal(case["dt"].shape)
+    bias = r.uniform(-4, -1, case["x"].shape[2])
+    y1, _ = o.s6(**{**case, "dt": raw}, dt_softplus=True, dt_bias=bias)
+    y2, _ = o.s6(**{**case, "dt": np.logaddexp(0.0, raw + bias)})
+    np.testing.assert_allclose(y1, y2, rtol=1e-13, atol=1e-14)
+
+
 ALL_PINS = [
     pin_hand_vectors, pin_quadratic_form, pin_zero_decay, pin_softplus_silu_bf16, pin_conv_library,
     pin_conv_impulse, pin_conv_documents, pin_conv_state_carry, pin_packed_equals_separate,
     pin_split_equals_single, pin_step_equals_prefill, pin_linearity_and_decay_only, pin_groups_and_batch,
-    pin_dt_softplus_inside,
+    pin_dt_softplus_inside, pin_s6_quadratic_form, pin_s6_equals_ssd, pin_s6_zero_decay_and_carry,
 ]

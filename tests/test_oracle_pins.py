@@ -52,6 +52,15 @@ MUTATIONS = [
     ("conv_state_shift", "memcpy(cs + (size_t)k * C, cs + (size_t)(k + 1) * C", "memcpy(cs + (size_t)(k + 1) * C, cs + (size_t)k * C"),
     ("step_no_round", "xbc[c] = round_bf16 ? oracle_round_bf16(v) : v;", "xbc[c] = v;"),
     ("round_truncates", "double r = rint(v / q) * q;", "double r = trunc(v / q) * q;"),
+    # the Mamba-1 S6 scan
+    ("s6_decay_one_rate", "h[n] = exp(dtv * Ad[n]) * h[n]", "h[n] = exp(dtv * Ad[0]) * h[n]"),
+    ("s6_A_transposed", "h[n] = exp(dtv * Ad[n]) * h[n]", "h[n] = exp(dtv * A[(size_t)n * D + d]) * h[n]"),
+    ("s6_dropped_dt_on_input", "+ dtv * Bt[n] * xv;", "+ Bt[n] * xv;"),
+    ("s6_read_with_B", "acc += Ct[n] * h[n];", "acc += Bt[n] * h[n];"),
+    ("s6_dropped_skip", "double v = acc + (D_skip ? D_skip[d] : 0.0) * xv;", "double v = acc;"),
+    ("s6_no_doc_reset", "if (doc && t > 0 && doc[row] != doc[row - 1]) memset(h", "if (0) memset(h"),
+    ("s6_bias_outside", "dtv = softplus(dtv + (dt_bias ? dt_bias[d] : 0.0));",
+     "dtv = softplus(dtv) + (dt_bias ? dt_bias[d] : 0.0);"),
 ]
 
 
