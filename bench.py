@@ -15,7 +15,8 @@ step; "roofline" = the scan call's algorithmic bytes / its average duration
 "extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
 two kernels behind one call; fused: the conv computed inside the scan
 kernels), the other workloads (packed documents, the large layer, the decode
-step), and the chunk-resume decode (ssd_resume_fwd) on the decode workload.
+step), the chunk-resume decode (ssd_resume_fwd) on the decode workload, and
+the Mamba-1 selective scan (ssd_s6_scan_fwd) priced against the VALU rate.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -306,6 +307,61 @@ def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
             "ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "unit": "head-tokens/s (B*H per step)"}
 
 
+# fp32 VALU lane-instructions per second of MI355X (157.3 TFLOP/s counts an fma as two flops) and the cost of
+# one S6 state update in full-rate issue slots: exp2 (a transcendental, quarter rate: 4 slots), dt*A, dt*x*B,
+# the fma into h and the fma into y (4 slots).
+VALU_LANE_OPS = 157.3e12 / 2
+S6_SLOTS_PER_UPDATE = 8
+
+
+def s6_bytes(wl, h0=False, docs=False):
+    """Algorithmic bytes of one ssd_s6_scan_fwd: x, dt, z (T) and B, C rows read once, y (fp32) and the final
+    state written once."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok, Dn = wl.B * wl.L, wl.H * wl.P
+    b = tok * Dn * (2 + (1 if wl.gate else 0)) * es + 2 * tok * wl.N * es + tok * Dn * 4
+    st = wl.B * Dn * wl.N * 4
+    return b + st + (st if h0 else 0) + (tok * 4 if docs else 0)
+
+
+def s6_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
+    """ssd_s6_scan_fwd (the Mamba-1 selective scan) with its split workspace; the value is channel-tokens
+    (B*L*D) per second, and the kernel is priced against the VALU issue rate (bound "alu")."""
+    dev = "cuda"
+    Dn = wl.H * wl.P
+    prm = synth.s6_params(wl, seed, device=dev)
+    sets = [synth.s6_inputs(wl, seed + k, device=dev) for k in range(2)]
+    ws_bytes = ssd.ssd_s6_workspace_size(wl.B, wl.L, Dn, wl.N, ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty(wl.B, wl.L, Dn, dtype=torch.float32, device=dev)
+    fs = torch.empty(wl.B, Dn, wl.N, dtype=torch.float32, device=dev)
+    t = Timer(torch)
+
+    def one(i, timed):
+        a = sets[i % 2]
+        f = lambda: ssd.ssd_s6_scan_fwd(a["x"], a["dt_raw"], prm["A"], a["Bm"], a["Cm"], D_skip=prm["D_skip"],
+                                        z=a["z"], final_state=fs, y=y, dt_softplus=True, dt_bias=prm["dt_bias"],
+                                        workspace=ws)
+        t.around(f) if timed else f()
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        one(i, True)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    upd = wl.B * wl.L * Dn * wl.N
+    peak = VALU_LANE_OPS / S6_SLOTS_PER_UPDATE
+    nb = s6_bytes(wl)
+    return {"workload": wl.name + " (ssd_s6_scan_fwd: B=%d L=%d D=%d N=%d)" % (wl.B, wl.L, Dn, wl.N),
+            "ms_per_step": ms, "value": wl.B * wl.L * Dn / (ms * 1e-3), "unit": "channel-tokens/s (B*L*D)",
+            "roofline": {"bound": "alu", "achieved": upd / (ms * 1e-3) / 1e12, "peak": peak / 1e12,
+                         "unit": "T state-updates/s", "frac": upd / (ms * 1e-3) / peak},
+            "hbm_GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nb, "workspace_bytes": ws_bytes}
+
+
 def cpu_baseline(synth, wl, rows):
     """The fp64 oracle (conv + scan, as it stands) on `rows` batch rows of the workload."""
     import oracle
@@ -388,6 +444,7 @@ def main():
         extras.append({"workload": dw.name + " (ssd_step)", **r, "step_frac": r["step_GBs"] / HBM_PEAK_GBS,
                        "unit": "head-tokens/s (B*H per step)"})
         extras.append(resume_bench(ssd, synth, torch, dw, args.warmup))
+        extras.append(s6_bench(ssd, synth, torch, synth.WORKLOADS["s6_bf16"], args.steps, args.warmup))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,7 +1,7 @@
 /*
  * ssd.h -- C ABI of libssd.so, the gfx950 (MI355X) Mamba-2 SSD mixer core.
  *
- * Five operations, each a few HIP kernel launches on the caller's stream:
+ * Six operations, each a few HIP kernel launches on the caller's stream:
  *
  *   ssd_conv_fwd        causal depthwise conv (k = 4) + SiLU over the
  *                       [x | B | C] columns, and dt = softplus(dt_raw + dt_bias)
@@ -15,6 +15,8 @@
  *                       the forward
  *   ssd_step            one decode token per sequence: conv from a rolling
  *                       buffer, state update, output and gate
+ *   ssd_s6_scan_fwd     the Mamba-1 selective scan (S6): a per-channel
+ *                       diagonal state, B and C shared by the channels
  *
  * The operation (per batch row b and head h, token t, head h in group
  * g = h / (H/G)):
@@ -322,6 +324,63 @@ int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
              const float *conv_w, const float *conv_b, const float *dt_bias,
              const float *A, const float *D,
              void *conv_state, float *ssm_state, int act, float *y, void *stream);
+
+/*
+ * ssd_s6_scan_fwd -- the Mamba-1 selective scan (S6).
+ *
+ * Per batch row b and channel d (D channels), with a state of N entries:
+ *     a_t[d][n] = exp(dt_t[d] * A[d][n])
+ *     h_t[d][n] = a_t[d][n] * h_{t-1}[d][n] + dt_t[d] * B_t[n] * x_t[d]
+ *     y_t[d]    = (sum_n C_t[n] h_t[d][n] + D_skip[d] * x_t[d]) * silu(z_t[d])
+ * (builderforce-memory-engine diff, falcon_mamba.ts header: x_proj rows
+ * [dt, B, C] give one B and one C per token for all channels, dt_proj gives
+ * dt per channel with its bias inside the softplus, A_log is [d_inner,
+ * d_state] and A = -exp(A_log)).  Document ids, states and the gate follow
+ * the conventions above; the state is [B][D][N] with n fastest.  The decay
+ * differs per (d, n), so the scan runs token by token (no chunked matrix
+ * form); with a workspace of ssd_s6_workspace_size() bytes the sequence is
+ * cut into superchunks scanned in parallel, a first pass storing each one's
+ * local end state and sum of dt, and the main pass folding them in (results
+ * agree with the sequential pass to fp32 rounding, not bitwise; final_state
+ * may equal init_state either way).  exp and softplus use the hardware exp2 /
+ * log2 (a few ulp); softplus(v) for v below about -17 reads as 0.
+ *
+ *   x, dt   T   [B][L][D]   row strides x_row_stride, dt_row_stride;
+ *               dt_softplus = 0: dt is already activated; 1: dt :=
+ *               softplus(dt + dt_bias)
+ *   dt_bias f32 [D] or NULL (read only when dt_softplus = 1)
+ *   A       f32 [D][N], A <= 0 (the caller computes A = -exp(A_log))
+ *   Bm, Cm  T   [B][L][N]   row strides B_row_stride, C_row_stride (column
+ *               slices of the x_proj output are fine)
+ *   D_skip  f32 [D] or NULL; z T [B][L][D] or NULL; doc_ids i32 [B][L] or NULL
+ *   init_state, final_state  f32 [B][D][N] or NULL
+ *   y       f32 [B][L][D]   row stride y_row_stride; must not overlap inputs
+ *   workspace, workspace_bytes: NULL, 0 (one sequential pass per channel)
+ *               or device scratch of at least ssd_s6_workspace_size()
+ *               bytes, 16-byte aligned, caller-owned, not shared by
+ *               concurrent calls
+ * Supported: N in {8, 16, 32}, any D >= 1, B, L >= 0.  Tensor bases 16-byte
+ * aligned and T row strides multiples of 16 bytes, as above; row strides in
+ * elements, >= the row width and <= 4194304.
+ */
+int ssd_s6_scan_fwd(int B, int L, int D, int N, int dtype,
+                    const void *x, int64_t x_row_stride,
+                    const void *dt, int64_t dt_row_stride,
+                    int dt_softplus, const float *dt_bias,
+                    const float *A,
+                    const void *Bm, int64_t B_row_stride,
+                    const void *Cm, int64_t C_row_stride,
+                    const float *D_skip,
+                    const void *z, int64_t z_row_stride,
+                    const int32_t *doc_ids,
+                    const float *init_state, float *final_state,
+                    float *y, int64_t y_row_stride,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace that let ssd_s6_scan_fwd split the sequence for these
+ * sizes: hloc [B][D][K-1][N] and sdt [B][D][K-1] (fp32) and a copy of the
+ * initial state; 0 when no split pays. */
+size_t ssd_s6_workspace_size(int B, int L, int D, int N, int dtype);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@ The entry points mirror the C ABI in include/ssd.h one to one:
     ssd_mixer_fwd       both in one call (staged, or the scan convolving the raw columns on chip)
     ssd_resume_fwd      decode tokens rescanned with the working chunk: bit-identical to the forward
     ssd_step            one decode token per sequence
+    ssd_s6_scan_fwd     the Mamba-1 selective scan (per-channel diagonal state)
 
 This module only marshals torch tensors (device pointers, row strides, the
 current HIP stream) into the library; every step of the computation runs in
@@ -21,7 +22,7 @@ import os
 import torch
 
 __all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_resume_fwd", "ssd_step",
-           "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size",
+           "ssd_s6_scan_fwd", "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size", "ssd_s6_workspace_size",
            "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -72,6 +73,11 @@ def load() -> ctypes.CDLL:
     lib.ssd_resume_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
     lib.ssd_step.restype = I
     lib.ssd_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P]
+    lib.ssd_s6_scan_fwd.restype = I
+    lib.ssd_s6_scan_fwd.argtypes = [I, I, I, I, I, P, I64, P, I64, I, P, P, P, I64, P, I64, P, P, I64, P, P, P,
+                                    P, I64, P, SZ, P]
+    lib.ssd_s6_workspace_size.restype = SZ
+    lib.ssd_s6_workspace_size.argtypes = [I, I, I, I, I]
     _lib = lib
     return lib
 
@@ -323,5 +329,45 @@ def ssd_step(xbc_raw, dt_raw, conv_w, A, conv_state, ssm_state, *, H, P, N, G, K
         _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
         _ptr(conv_state, "conv_state", xbc_raw.dtype), _ptr(ssm_state, "ssm_state", torch.float32), int(act),
         _ptr(y, "y", torch.float32), _stream(stream))
+    _check(st)
+    return y
+
+
+def ssd_s6_workspace_size(B, L, D, N, dtype=SSD_BF16) -> int:
+    return int(load().ssd_s6_workspace_size(B, L, D, N, dtype))
+
+
+def ssd_s6_scan_fwd(x, dt, A, Bm, Cm, *, D_skip=None, z=None, doc_ids=None, init_state=None, final_state=None,
+                    y=None, dt_softplus=False, dt_bias=None, workspace=None, stream=None):
+    """Mamba-1 selective scan.  x, dt [B, L, D] and Bm, Cm [B, L, N] (one dtype), A [D, N] fp32.
+
+    Returns y [B, L, D] fp32 (and writes final_state [B, D, N] if given)."""
+    lib = load()
+    B, L, Dn = x.shape
+    N = A.shape[1] if A.dim() == 2 else 0
+    dtype = _dtype_code(x, "x")
+    rs_x = _rows(x, "x", B, L, Dn)
+    rs_dt = _rows(dt, "dt", B, L, Dn)
+    rs_b = _rows(Bm, "Bm", B, L, N)
+    rs_c = _rows(Cm, "Cm", B, L, N)
+    rs_z = _rows(z, "z", B, L, Dn)
+    if y is None:
+        y = torch.empty((B, L, Dn), dtype=torch.float32, device=x.device)
+    rs_y = _rows(y, "y", B, L, Dn)
+    _contig(A, "A", (Dn, N))
+    _contig(D_skip, "D_skip", (Dn,))
+    _contig(dt_bias, "dt_bias", (Dn,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    _contig(init_state, "init_state", (B, Dn, N))
+    _contig(final_state, "final_state", (B, Dn, N))
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_s6_scan_fwd(
+        B, L, Dn, N, dtype,
+        _ptr(x, "x"), rs_x, _ptr(dt, "dt", x.dtype), rs_dt, int(bool(dt_softplus)),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32),
+        _ptr(Bm, "Bm", x.dtype), rs_b, _ptr(Cm, "Cm", x.dtype), rs_c, _ptr(D_skip, "D_skip", torch.float32),
+        _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
+        _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
     _check(st)
     return y

@@ -472,6 +472,95 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
                                                 n * HP * 4, B, n, (int)(HP * 4), s));
 }
 
+size_t ssd_s6_workspace_size(int B, int L, int D, int N, int dtype) {
+    (void)dtype;
+    if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+    return ssd::s6_workspace_bytes(B, L, D, N);
+}
+
+int ssd_s6_scan_fwd(int B, int L, int D, int N, int dtype,
+                    const void* x, int64_t x_row_stride,
+                    const void* dt, int64_t dt_row_stride,
+                    int dt_softplus, const float* dt_bias,
+                    const float* A,
+                    const void* Bm, int64_t B_row_stride,
+                    const void* Cm, int64_t C_row_stride,
+                    const float* D_skip,
+                    const void* z, int64_t z_row_stride,
+                    const int32_t* doc_ids,
+                    const float* init_state, float* final_state,
+                    float* y, int64_t y_row_stride,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_s6_scan_fwd";
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dtype=%d is not supported (only SSD_F32=0 and SSD_BF16=1; "
+                    "fp16, fp64 and other types are refused, not converted)", fn, dtype);
+    if (B < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: B=%d must be >= 0", fn, B);
+    if (L < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: L=%d must be >= 0", fn, L);
+    if (D <= 0) return fail(SSD_ERR_BAD_SHAPE, "%s: D=%d must be > 0", fn, D);
+    if (N != 8 && N != 16 && N != 32)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: N=%d is not supported (state dim must be 8, 16 or 32)", fn, N);
+    if ((long long)B * D > 0x7fffffffLL || (long long)B * L > 0x7fffffffLL)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: B*D or B*L is too large", fn);
+    if (dt_softplus != 0 && dt_softplus != 1)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dt_softplus=%d must be 0 or 1", fn, dt_softplus);
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "x", x, x_row_stride, D, es, work));
+    TRY(check_tensor(fn, "dt", dt, dt_row_stride, D, es, work));
+    TRY(check_tensor(fn, "Bm", Bm, B_row_stride, N, es, work));
+    TRY(check_tensor(fn, "Cm", Cm, C_row_stride, N, es, work));
+    TRY(check_tensor(fn, "z", z, z_row_stride, D, es, false));
+    TRY(check_tensor(fn, "y", y, y_row_stride, D, 4, work));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, B > 0, false));
+    TRY(check_ptr(fn, "D_skip", D_skip, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    TRY(check_ptr(fn, "init_state", init_state, false, true));
+    TRY(check_ptr(fn, "final_state", final_state, false, true));
+    if (work && (x_row_stride > (1 << 22) || dt_row_stride > (1 << 22) || B_row_stride > (1 << 22) ||
+                 C_row_stride > (1 << 22) || z_row_stride > (1 << 22) || y_row_stride > (1 << 22)))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
+    const size_t need = ssd_s6_workspace_size(B, L, D, N, dtype);
+    const bool split = workspace != nullptr && need > 0;
+    if (split && workspace_bytes < need)
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace_bytes, need);
+    if (split && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+    if (work && y == final_state)
+        return fail(SSD_ERR_BAD_SHAPE, "%s: y must not alias final_state", fn);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        if (final_state && B > 0)
+            return hip_status(fn, ssd::launch_copy16(init_state, final_state, (size_t)B * D * N * 4 / 16, s));
+        return ok();
+    }
+    ssd::S6Args a{};
+    a.B = B; a.L = L; a.D = D; a.N = N; a.dtype = dtype;
+    a.x = x; a.x_stride = x_row_stride;
+    a.dt = dt; a.dt_stride = dt_row_stride;
+    a.dt_softplus = dt_softplus; a.dt_bias = dt_bias;
+    a.A = A;
+    a.Bm = Bm; a.B_stride = B_row_stride;
+    a.Cm = Cm; a.C_stride = C_row_stride;
+    a.D_skip = D_skip;
+    a.z = z; a.z_stride = z_row_stride;
+    a.doc = doc_ids;
+    a.init_state = init_state; a.final_state = final_state;
+    a.y = y; a.y_stride = y_row_stride;
+    a.K = 1; a.S = L;
+    if (split) {
+        ssd::s6_split(B, L, D, a.K, a.S);
+        const size_t u = (size_t)B * D * (a.K - 1);
+        a.hloc = static_cast<float*>(workspace);
+        a.sdt = a.hloc + u * (size_t)N;
+        if (init_state) a.h0 = a.sdt + round256(u * sizeof(float)) / sizeof(float);
+    }
+    return hip_status(fn, ssd::launch_s6(a, s));
+}
+
 int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
              const void* xbc_raw, const void* dt_raw, const void* z,
              const float* conv_w, const float* conv_b, const float* dt_bias,

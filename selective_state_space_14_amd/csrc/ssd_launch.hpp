@@ -62,6 +62,27 @@ struct StepArgs {
     void* conv_state; float* ssm_state; float* y;
 };
 
+// Mamba-1 selective scan: per (b, d) a diagonal state of N entries with
+// decay exp(dt A[d][n]); B and C are shared by all channels of a token.
+struct S6Args {
+    int B, L, D, N, dtype;
+    const void* x; int64_t x_stride;     // [B][L][D] (dtype)
+    const void* dt; int64_t dt_stride;   // [B][L][D] (dtype)
+    int dt_softplus; const float* dt_bias;
+    const float* A;                      // [D][N]
+    const void* Bm; int64_t B_stride;    // [B][L][N] (dtype), rows 16-byte aligned
+    const void* Cm; int64_t C_stride;
+    const float* D_skip;                 // [D] or null
+    const void* z; int64_t z_stride;     // [B][L][D] (dtype) or null
+    const int32_t* doc;                  // [B][L] or null
+    const float* init_state; float* final_state;   // [B][D][N]
+    float* y; int64_t y_stride;          // [B][L][D] fp32
+    // sequence split (K superchunks of S tokens); workspace for K > 1:
+    // hloc [B][D][K-1][N], sdt [B][D][K-1], h0 [B][D][N] (init_state copy)
+    int K, S;
+    float* hloc; float* sdt; float* h0;
+};
+
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // Sequence split chosen for these sizes (1 = none) and its superchunk length.
@@ -78,5 +99,9 @@ hipError_t launch_copy_rows(const void* src, int64_t src_row_stride, int64_t src
                             hipStream_t stream);
 
 size_t step_lds_bytes(int H, int P, int N, int G);
+
+hipError_t launch_s6(const S6Args& a, hipStream_t stream);
+void s6_split(int B, int L, int D, int& K, int& S);
+size_t s6_workspace_bytes(int B, int L, int D, int N);
 
 }  // namespace ssd

@@ -17,6 +17,10 @@ paragraph; chunk 64 from the mojolearn.Mamba3Block description):
   large_layer_bf16   B=4,   L=4096, H=128, P=64, N=128, G=8, bf16, h0 carried in
   decode_fp32        B=256, H=64,   P=64,  N=128, G=1, fp32, 4096-token prefill
                      then single-token steps
+  s6_bf16            the Mamba-1 selective scan (S6) on the same token batch:
+                     B=5, L=8192, D=H*P=2048 channels, state N=16 (the Mamba
+                     block default of the nanochat hybrid-blocks page,
+                     "Mamba-Specific Parameters"), bf16, gate
 
 Distributions: raw x columns ~ N(0,1); raw B and C columns ~ N(0, 1/N)
 (variance); dt_raw ~ N(0,1); dt_bias ~ U(-4,-1); A = -exp(U(log 1, log 16));
@@ -73,6 +77,7 @@ WORKLOADS = {
     "mini_k3_packed": Workload("mini_k3_packed", 5, 8192, 32, 64, 64, 8, "bf16", docs=True),
     "large_layer_bf16": Workload("large_layer_bf16", 4, 4096, 128, 64, 128, 8, "bf16", h0=True),
     "decode_fp32": Workload("decode_fp32", 256, 4096, 64, 64, 128, 1, "f32", steps=1024),
+    "s6_bf16": Workload("s6_bf16", 5, 8192, 32, 64, 16, 1, "bf16", conv=False),
 }
 
 
@@ -181,4 +186,35 @@ def step_inputs(wl: Workload, step: int, seed: int = 0, device="cpu", B: int | N
         "xbc_raw": torch.cat([x, bm, cm], dim=1).to(dt),
         "dt_raw": _normal((B, wl.H), 1.0, seed, wl, f"step{step}/dt", device).to(dt),
         "z": _normal((B, HP), 1.0, seed, wl, f"step{step}/z", device).to(dt) if wl.gate else None,
+    }
+
+
+def s6_params(wl: Workload, seed: int = 0, device="cpu") -> dict:
+    """Mamba-1 (S6) parameters over D = H*P channels, fp32: A [D, N] = -exp(A_log) with
+    A_log ~ U(log 1, log 16) per (d, n), D skip [D] ~ N(0,1), dt_bias [D] ~ U(-4,-1)."""
+    Dn = wl.H * wl.P
+    A_log = _uniform((Dn, wl.N), 0.0, math.log(16.0), seed, wl, "s6/A_log", device)
+    return {
+        "A": -torch.exp(A_log),
+        "D_skip": _normal((Dn,), 1.0, seed, wl, "s6/D", device),
+        "dt_bias": _uniform((Dn,), -4.0, -1.0, seed, wl, "s6/dt_bias", device),
+    }
+
+
+def s6_inputs(wl: Workload, seed: int = 0, device="cpu", L: int | None = None, B: int | None = None) -> dict:
+    """Mamba-1 scan inputs in the workload's dtype: x [B,L,D] ~ N(0,1), dt_raw [B,L,D] ~ N(0,1)
+    (before softplus(dt + dt_bias)), Bm/Cm [B,L,N] ~ N(0,1/N), z [B,L,D] ~ N(0,1) if gated, and
+    h0 [B,D,N] ~ N(0,0.1) fp32 if carried."""
+    L = wl.L if L is None else L
+    B = wl.B if B is None else B
+    Dn = wl.H * wl.P
+    sB = 1.0 / math.sqrt(wl.N)
+    dt = wl.torch_dtype
+    return {
+        "x": _normal((B, L, Dn), 1.0, seed, wl, "s6/x", device).to(dt),
+        "dt_raw": _normal((B, L, Dn), 1.0, seed, wl, "s6/dt", device).to(dt),
+        "Bm": _normal((B, L, wl.N), sB, seed, wl, "s6/B", device).to(dt),
+        "Cm": _normal((B, L, wl.N), sB, seed, wl, "s6/C", device).to(dt),
+        "z": _normal((B, L, Dn), 1.0, seed, wl, "s6/z", device).to(dt) if wl.gate else None,
+        "h0": _normal((B, Dn, wl.N), math.sqrt(0.1), seed, wl, "s6/h0", device) if wl.h0 else None,
     }

@@ -23,13 +23,13 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size", "ssd_mixer_fwd",
-              "ssd_mixer_workspace_size",
+              "ssd_mixer_workspace_size", "ssd_resume_fwd", "ssd_s6_scan_fwd", "ssd_s6_workspace_size",
               "ssd_last_error", "ssd_status_string", "ssd_version"):
         assert n in names
 
@@ -214,3 +214,64 @@ def test_python_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         ssd.ssd_chunk_scan_fwd(x, bm, bm, torch.zeros(1, 4, 1), torch.zeros(1), H=1, P=64, N=16, G=1,
                                y=torch.zeros(1, 4, 64))
+
+
+def s6_args(**over):
+    a = dict(B=2, L=128, D=512, N=16, dtype=1, x=FAKE, xs=512, dt=FAKE, dts=512, sp=1, db=None, A=FAKE,
+             Bm=FAKE, bs=16, Cm=FAKE, cs=16, Dk=None, z=None, zs=0, doc=None, h0=None, hf=None, y=FAKE, ys=512,
+             ws=None, wsb=0, stream=None)
+    a.update(over)
+    return a
+
+
+def call_s6(lib, a):
+    f = lib.ssd_s6_scan_fwd
+    I, P, I64, SZ = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    f.restype = I
+    f.argtypes = [I, I, I, I, I, P, I64, P, I64, I, P, P, P, I64, P, I64, P, P, I64, P, P, P, P, I64, P, SZ, P]
+    return f(a["B"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["xs"], a["dt"], a["dts"], a["sp"], a["db"],
+             a["A"], a["Bm"], a["bs"], a["Cm"], a["cs"], a["Dk"], a["z"], a["zs"], a["doc"], a["h0"], a["hf"],
+             a["y"], a["ys"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(N=64), 3, "N=64 is not supported"),
+    (dict(N=4), 3, "N=4"),
+    (dict(dtype=3), 3, "dtype=3"),
+    (dict(D=0), 2, "D=0"),
+    (dict(B=-2), 2, "B=-2"),
+    (dict(L=-1), 2, "L=-1"),
+    (dict(x=None), 1, "x is NULL"),
+    (dict(dt=None), 1, "dt is NULL"),
+    (dict(A=None), 1, "A is NULL"),
+    (dict(Bm=None), 1, "Bm is NULL"),
+    (dict(y=None), 1, "y is NULL"),
+    (dict(xs=500), 2, "x row stride 500"),
+    (dict(bs=12), 2, "Bm row stride 12"),
+    (dict(Cm=MIS), 4, "Cm=.*not 16-byte aligned"),
+    (dict(cs=20), 4, "Cm row stride 20 elements"),
+    (dict(z=FAKE, zs=100), 2, "z row stride 100"),
+    (dict(h0=MIS), 4, "init_state"),
+    (dict(sp=2), 3, "dt_softplus=2"),
+    (dict(hf=FAKE), 2, "y must not alias final_state"),
+    (dict(L=8192, ws=FAKE, wsb=64), 5, "workspace_bytes=64"),
+    (dict(L=8192, ws=MIS, wsb=1 << 40), 4, "workspace=.*not 16-byte aligned"),
+])
+def test_s6_refusals(lib, over, status, needle):
+    st = call_s6(lib, s6_args(**over))
+    assert st == status, (st, lib.ssd_last_error())
+    assert re.search(needle, lib.ssd_last_error().decode()), lib.ssd_last_error()
+
+
+def test_s6_workspace_size(lib):
+    f = lib.ssd_s6_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int] * 5
+    assert f(0, 8192, 2048, 16, 1) == 0
+    assert f(5, 0, 2048, 16, 1) == 0
+    # a short sequence is not split (one superchunk per 64 tokens at most)
+    assert f(5, 64, 2048, 16, 1) == 0
+    n = f(5, 8192, 2048, 16, 1)
+    assert n > 0 and n % 4 == 0
+    # hloc + sdt grow with N only through hloc; the initial-state copy is B*D*N floats
+    assert f(5, 8192, 2048, 32, 1) > n
