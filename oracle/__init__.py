@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the Mamba-2 SSD mixer core (conv, scan, decode step) and the Mamba-1 S6 scan.
+"""fp64 CPU oracle for the Mamba-2 SSD mixer core (conv, scan, decode step, and their backward) and the
+Mamba-1 S6 scan.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  It
@@ -95,6 +96,12 @@ class Oracle:
                                     _dp, _dp, _dp]
         lib.oracle_s6.restype = i
         lib.oracle_s6.argtypes = [i, i, i, i, _dp, _dp, i, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _dp, _dp]
+        lib.oracle_scan_bwd.restype = i
+        lib.oracle_scan_bwd.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, i, _dp, _dp, _dp, _dp, _ip, _dp,
+                                        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.oracle_conv_bwd.restype = i
+        lib.oracle_conv_bwd.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _ip, i, _dp, _dp, _dp, _dp, _dp,
+                                        _dp, _dp]
         lib.oracle_step.restype = i
         lib.oracle_step.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                     i, i, _dp]
@@ -218,6 +225,79 @@ class Oracle:
             raise ValueError("oracle_step rejected its arguments")
         return y
 
+    def scan_bwd(self, x, Bm, Cm, dt, A, gy, D=None, z=None, doc_ids=None, *, H, P, N, G,
+                 dt_softplus: bool = False, dt_bias=None):
+        """Backward (VJP) of the zero-state scan for dLoss/dy = gy [B,L,H*P].
+
+        Returns a dict: x, Bm, Cm [B,L,*], dt [B,L,H] (w.r.t. the dt input), A [H], and D [H], z [B,L,H*P],
+        dt_bias [H] where those inputs are given."""
+        x_c, x_p = _in(x)
+        Bsz, L = x_c.shape[0], x_c.shape[1]
+        if x_c.shape != (Bsz, L, H * P):
+            raise ValueError("oracle.scan_bwd: x must be [B, L, H*P]")
+        b_c, b_p = _in(Bm, (Bsz, L, G * N))
+        c_c, c_p = _in(Cm, (Bsz, L, G * N))
+        dt_c, dt_p = _in(dt, (Bsz, L, H))
+        db_c, db_p = _in(dt_bias, (H,) if dt_bias is not None else None)
+        a_c, a_p = _in(A, (H,))
+        dd_c, dd_p = _in(D, (H,) if D is not None else None)
+        z_c, z_p = _in(z, (Bsz, L, H * P) if z is not None else None)
+        d_c, d_p = _ids(doc_ids, (Bsz, L))
+        g_c, g_p = _in(gy, (Bsz, L, H * P))
+        g = {"x": np.empty((Bsz, L, H * P)), "Bm": np.empty((Bsz, L, G * N)), "Cm": np.empty((Bsz, L, G * N)),
+             "dt": np.empty((Bsz, L, H)), "A": np.empty(H), "D": np.empty(H) if D is not None else None,
+             "z": np.empty((Bsz, L, H * P)) if z is not None else None,
+             "dt_bias": np.empty(H) if dt_softplus else None}
+        rc = self._lib.oracle_scan_bwd(Bsz, L, H, P, N, G, x_p, b_p, c_p, dt_p, int(bool(dt_softplus)), db_p, a_p,
+                                       dd_p, z_p, d_p, g_p, _out(g["x"]), _out(g["Bm"]), _out(g["Cm"]),
+                                       _out(g["dt"]), _out(g["dt_bias"]), _out(g["A"]), _out(g["D"]), _out(g["z"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected its arguments")
+        return {k: v for k, v in g.items() if v is not None}
+
+    def conv_bwd(self, raw, w, dout, bias=None, dt_raw=None, dt_bias=None, ddt=None, doc_ids=None, act: int = 0):
+        """Backward of the zero-state conv (+ act) and of dt = softplus(dt_raw + dt_bias).
+
+        Returns a dict: raw [B,L,C], w [C,K], and bias [C], dt_raw [B,L,H], dt_bias [H] where given."""
+        raw_c, raw_p = _in(raw)
+        Bsz, L, C = raw_c.shape
+        w_c, w_p = _in(w)
+        K = w_c.shape[1]
+        if w_c.shape != (C, K):
+            raise ValueError("oracle.conv_bwd: w must be [conv_dim, K]")
+        b_c, b_p = _in(bias, (C,))
+        go_c, go_p = _in(dout, (Bsz, L, C))
+        dr_c, dr_p = _in(dt_raw)
+        H = 0 if dr_c is None else dr_c.shape[2]
+        db_c, db_p = _in(dt_bias, (H,) if dt_bias is not None else None)
+        gdt_c, gdt_p = _in(ddt, (Bsz, L, H) if ddt is not None else None)
+        d_c, d_p = _ids(doc_ids, (Bsz, L))
+        g = {"raw": np.empty((Bsz, L, C)), "w": np.empty((C, K)), "bias": np.empty(C) if bias is not None else None,
+             "dt_raw": np.empty((Bsz, L, H)) if ddt is not None else None,
+             "dt_bias": np.empty(H) if ddt is not None and dt_bias is not None else None}
+        rc = self._lib.oracle_conv_bwd(Bsz, L, C, K, H, raw_p, w_p, b_p, dr_p, db_p, d_p, int(act), go_p, gdt_p,
+                                       _out(g["raw"]), _out(g["w"]), _out(g["bias"]), _out(g["dt_raw"]),
+                                       _out(g["dt_bias"]))
+        if rc != 0:
+            raise ValueError("oracle_conv_bwd rejected its arguments")
+        return {k: v for k, v in g.items() if v is not None}
+
+    def mixer_bwd(self, raw, w, bias, dt_raw, dt_bias, A, D, z, gy, *, H, P, N, G, doc_ids=None, act: int = 0,
+                  round_bf16: bool = False):
+        """Backward of forward() (conv then scan) for a zero-state prefill: conv, then scan_bwd on the conv's
+        outputs, then conv_bwd.  Returns a dict: raw, w, bias, dt_raw, dt_bias, A, D, z (where given)."""
+        xbc, dt, _ = self.conv(raw, w, bias, dt_raw, dt_bias, doc_ids, None, act=act, round_bf16=round_bf16)
+        HP, GN = H * P, G * N
+        gs = self.scan_bwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, A, gy, D, z, doc_ids,
+                           H=H, P=P, N=N, G=G)
+        dxbc = np.concatenate([gs["x"], gs["Bm"], gs["Cm"]], axis=2)
+        gc = self.conv_bwd(raw, w, dxbc, bias, dt_raw, dt_bias, gs["dt"], doc_ids, act=act)
+        out = {"raw": gc["raw"], "w": gc["w"], "dt_raw": gc["dt_raw"], "A": gs["A"]}
+        for k, src in (("bias", gc), ("dt_bias", gc), ("D", gs), ("z", gs)):
+            if k in src:
+                out[k] = src[k]
+        return out
+
     def forward(self, raw, w, bias, dt_raw, dt_bias, A, D, z, *, H, P, N, G, doc_ids=None,
                 conv_state_in=None, init_state=None, act: int = 0, round_bf16: bool = False):
         """Conv prologue then scan (the mixer core end to end).
@@ -271,3 +351,15 @@ def forward(*a, **k):
 
 def s6(*a, **k):
     return default().s6(*a, **k)
+
+
+def scan_bwd(*a, **k):
+    return default().scan_bwd(*a, **k)
+
+
+def conv_bwd(*a, **k):
+    return default().conv_bwd(*a, **k)
+
+
+def mixer_bwd(*a, **k):
+    return default().mixer_bwd(*a, **k)

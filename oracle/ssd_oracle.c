@@ -41,6 +41,26 @@
  *  - Caller-owned state read at entry and written at exit; a step is the
  *    same computation as a forward of length 1 with the state carried
  *    (mojolearn.Mamba3Block docs, forward() and step()).
+ *  - Backward (oracle_scan_bwd, oracle_conv_bwd): the vector-Jacobian
+ *    product of a zero-state prefill, given the gradient of the loss with
+ *    respect to y; no gradient for a carried state and no final-state
+ *    cotangent (mojolearn.Mamba3Block docs, backward()).  It is reverse-mode
+ *    differentiation of the recurrence above, token by token from the last:
+ *        dS      <- adjoint of h_t (the state after token t), from t+1
+ *        yr_t    = C_t^T h_t + D x_t,  y_t = yr_t * silu(z_t)
+ *        dz_t    = dy_t * yr_t * silu'(z_t);   dyr_t = dy_t * silu(z_t)
+ *        dD     += dyr_t . x_t;  dx_t = D dyr_t;  dC_t += h_t dyr_t
+ *        dS     += C_t dyr_t^T
+ *        dB_t   += dt_t dS x_t;  dx_t += dt_t dS^T B_t
+ *        ddt_t   = B_t^T dS x_t + A a_t <dS, h_{t-1}>;  dA += dt_t a_t <dS, h_{t-1}>
+ *        dS      = a_t dS   (0 where a document starts at t: h_{t-1} is cut)
+ *    and through dt = softplus(dt_raw + dt_bias) by sigmoid(dt_raw + dt_bias).
+ *    The conv's backward runs the chain rule through the activation and the
+ *    taps within each document.  A bf16 pipeline's rounding of the conv
+ *    output is taken as the identity (the scan's inputs are the rounded
+ *    values).  Packed documents: a loss on a later document gives exactly
+ *    zero gradient on earlier-document inputs (Mini-K3-1H card, "Checkpoint
+ *    and training").
  *
  * Layouts (all arrays fp64, contiguous):
  *   raw / conv out  [B][L][conv_dim]   columns [x (H*P, head-major) | B (G*N,
@@ -82,6 +102,9 @@ static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
 
 /* silu(v) = v * sigmoid(v). */
 static double silu(double v) { return v / (1.0 + exp(-v)); }
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+/* d silu / dv = s + v s (1 - s), s = sigmoid(v) */
+static double dsilu(double v) { double s = sigmoid(v); return s + v * s * (1.0 - s); }
 
 /* Round to the nearest bfloat16 value (8 significant bits), ties to even.
  * Used only where the contract stores a tensor in bf16 (the conv output of a
@@ -331,4 +354,190 @@ int oracle_s6(int B, int L, int D, int N,
             free(h);
         }
     return bad ? -1 : 0;
+}
+
+/*
+ * Backward of oracle_scan for a zero initial state.  gy is dLoss/dy
+ * [B][L][H*P].  Writes dx [B][L][H*P], dB and dC [B][L][G*N] (summed over
+ * the heads of a group), ddt [B][L][H] (with respect to the dt input: the
+ * raw value when dt_softplus != 0), and, if not NULL, ddt_bias, dA, dD [H]
+ * and dz [B][L][H*P].  Returns 0, or -1 on bad arguments.
+ */
+int oracle_scan_bwd(int B, int L, int H, int P, int N, int G,
+                    const double *x, const double *Bm, const double *Cm,
+                    const double *dt, int dt_softplus, const double *dt_bias,
+                    const double *A, const double *D, const double *z,
+                    const int32_t *doc, const double *gy,
+                    double *dx, double *dB, double *dC, double *ddt,
+                    double *ddt_bias, double *dA, double *dD, double *dz) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || !A) return -1;
+    if (L > 0 && (!x || !Bm || !Cm || !dt || !gy || !dx || !dB || !dC || !ddt)) return -1;
+    const int HP = H * P, GN = G * N, hpg = H / G;
+    const size_t PN = (size_t)P * N;
+    /* per (b, h) partial sums of the per-head parameters, summed over b in
+     * order afterwards */
+    double *pA = (double *)calloc((size_t)B * H * 3 + 1, sizeof(double));
+    if (!pA) return -1;
+    double *pD = pA + (size_t)B * H, *pBias = pD + (size_t)B * H;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int g = 0; g < G; ++g) {
+            double *Sall = (double *)calloc((size_t)(L + 1) * PN, sizeof(double));
+            double *dS = (double *)malloc(sizeof(double) * PN);
+            if (!Sall || !dS) { bad = 1; free(Sall); free(dS); continue; }
+            for (int t = 0; t < L; ++t) {
+                size_t row = (size_t)b * L + t;
+                for (int n = 0; n < N; ++n) {
+                    dB[row * GN + (size_t)g * N + n] = 0.0;
+                    dC[row * GN + (size_t)g * N + n] = 0.0;
+                }
+            }
+            for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+                const double Ah = A[h], Dh = D ? D[h] : 0.0, bias = dt_bias ? dt_bias[h] : 0.0;
+                /* forward: Sall[t + 1] is the state after token t */
+                for (int t = 0; t < L; ++t) {
+                    size_t row = (size_t)b * L + t;
+                    double d = dt[row * H + h];
+                    if (dt_softplus) d = softplus(d + bias);
+                    const double a = exp(d * Ah);
+                    const int reset = doc && t > 0 && doc[row] != doc[row - 1];
+                    const double *xv = x + row * HP + (size_t)h * P, *Bv = Bm + row * GN + (size_t)g * N;
+                    double *Sp = Sall + (size_t)t * PN, *Sc = Sall + (size_t)(t + 1) * PN;
+                    for (int p = 0; p < P; ++p)
+                        for (int n = 0; n < N; ++n)
+                            Sc[(size_t)p * N + n] = (reset ? 0.0 : a * Sp[(size_t)p * N + n]) + d * xv[p] * Bv[n];
+                }
+                /* reverse */
+                memset(dS, 0, sizeof(double) * PN);
+                double sA = 0.0, sD = 0.0, sBias = 0.0;
+                for (int t = L - 1; t >= 0; --t) {
+                    size_t row = (size_t)b * L + t;
+                    const double raw_dt = dt[row * H + h];
+                    const double d = dt_softplus ? softplus(raw_dt + bias) : raw_dt;
+                    const double a = exp(d * Ah);
+                    const int reset = doc && t > 0 && doc[row] != doc[row - 1];
+                    const double *xv = x + row * HP + (size_t)h * P;
+                    const double *Bv = Bm + row * GN + (size_t)g * N, *Cv = Cm + row * GN + (size_t)g * N;
+                    const double *Sc = Sall + (size_t)(t + 1) * PN, *Sp = Sall + (size_t)t * PN;
+                    double *dxv = dx + row * HP + (size_t)h * P;
+                    double *dBv = dB + row * GN + (size_t)g * N, *dCv = dC + row * GN + (size_t)g * N;
+                    /* output */
+                    for (int p = 0; p < P; ++p) {
+                        double yr = Dh * xv[p];
+                        for (int n = 0; n < N; ++n) yr += Cv[n] * Sc[(size_t)p * N + n];
+                        const double gyv = gy[row * HP + (size_t)h * P + p];
+                        double dyr = gyv;
+                        if (z) {
+                            const double zv = z[row * HP + (size_t)h * P + p];
+                            dyr = gyv * silu(zv);
+                            if (dz) dz[row * HP + (size_t)h * P + p] = gyv * yr * dsilu(zv);
+                        }
+                        sD += dyr * xv[p];
+                        dxv[p] = Dh * dyr;
+                        for (int n = 0; n < N; ++n) {
+                            dCv[n] += dyr * Sc[(size_t)p * N + n];
+                            dS[(size_t)p * N + n] += Cv[n] * dyr;
+                        }
+                    }
+                    /* through h_t = a h_{t-1} + dt B x^T */
+                    double dd = 0.0, da = 0.0;
+                    for (int p = 0; p < P; ++p)
+                        for (int n = 0; n < N; ++n) {
+                            const double g_pn = dS[(size_t)p * N + n];
+                            dBv[n] += d * g_pn * xv[p];
+                            dxv[p] += d * g_pn * Bv[n];
+                            dd += g_pn * Bv[n] * xv[p];
+                            if (!reset) da += g_pn * Sp[(size_t)p * N + n];
+                        }
+                    dd += da * a * Ah;
+                    sA += da * a * d;
+                    for (size_t i = 0; i < PN; ++i) dS[i] = reset ? 0.0 : a * dS[i];
+                    if (dt_softplus) {
+                        const double s = sigmoid(raw_dt + bias);
+                        ddt[row * H + h] = dd * s;
+                        sBias += dd * s;
+                    } else {
+                        ddt[row * H + h] = dd;
+                    }
+                }
+                pA[(size_t)b * H + h] = sA;
+                pD[(size_t)b * H + h] = sD;
+                pBias[(size_t)b * H + h] = sBias;
+            }
+            free(Sall);
+            free(dS);
+        }
+    for (int h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0, sb = 0.0;
+        for (int b = 0; b < B; ++b) {
+            sa += pA[(size_t)b * H + h];
+            sd += pD[(size_t)b * H + h];
+            sb += pBias[(size_t)b * H + h];
+        }
+        if (dA) dA[h] = sa;
+        if (dD) dD[h] = sd;
+        if (ddt_bias) ddt_bias[h] = sb;
+    }
+    free(pA);
+    return bad ? -1 : 0;
+}
+
+/*
+ * Backward of oracle_conv for a zero conv state: given dout = dLoss/d(conv
+ * output) [B][L][C] and ddt = dLoss/d(dt output) [B][L][H] (or NULL), writes
+ * draw [B][L][C], dw [C][K], dbias [C] (or NULL), and, when ddt is given,
+ * ddt_raw [B][L][H] and ddt_bias [H] (or NULL).
+ */
+int oracle_conv_bwd(int B, int L, int C, int K, int H,
+                    const double *raw, const double *w, const double *bias,
+                    const double *dt_raw, const double *dt_bias,
+                    const int32_t *doc, int act, const double *dout, const double *ddt,
+                    double *draw, double *dw, double *dbias, double *ddt_raw, double *ddt_bias) {
+    if (B < 0 || L < 0 || C <= 0 || K < 1 || K > ORACLE_MAXK || !w || !dw) return -1;
+    if (L > 0 && (!raw || !dout || !draw)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < C; ++c) {
+        double gw[ORACLE_MAXK] = {0.0};
+        double gb = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const double *raw_b = raw + (size_t)b * L * C;
+            const int32_t *doc_b = doc ? doc + (size_t)b * L : NULL;
+            for (int t = 0; t < L; ++t) draw[((size_t)b * L + t) * C + c] = 0.0;
+            for (int t = 0; t < L; ++t) {
+                const int seg = seg_start(doc_b, t);
+                double pre = bias ? bias[c] : 0.0;
+                for (int k = 0; k < K; ++k) {
+                    const int tau = t - (K - 1) + k;
+                    if (tau >= seg && tau >= 0) pre += w[(size_t)c * K + k] * raw_b[(size_t)tau * C + c];
+                }
+                const double go = dout[((size_t)b * L + t) * C + c];
+                const double gp = act == 0 ? go * dsilu(pre) : go;
+                gb += gp;
+                for (int k = 0; k < K; ++k) {
+                    const int tau = t - (K - 1) + k;
+                    if (tau >= seg && tau >= 0) {
+                        draw[((size_t)b * L + tau) * C + c] += w[(size_t)c * K + k] * gp;
+                        gw[k] += gp * raw_b[(size_t)tau * C + c];
+                    }
+                }
+            }
+        }
+        for (int k = 0; k < K; ++k) dw[(size_t)c * K + k] = gw[k];
+        if (dbias) dbias[c] = gb;
+    }
+    if (ddt && dt_raw && ddt_raw) {
+        for (int h = 0; h < H; ++h) {
+            double sb = 0.0;
+            for (int b = 0; b < B; ++b)
+                for (int t = 0; t < L; ++t) {
+                    const size_t i = ((size_t)b * L + t) * H + h;
+                    const double s = sigmoid(dt_raw[i] + (dt_bias ? dt_bias[h] : 0.0));
+                    ddt_raw[i] = ddt[i] * s;
+                    sb += ddt[i] * s;
+                }
+            if (ddt_bias) ddt_bias[h] = sb;
+        }
+    }
+    return 0;
 }

@@ -385,9 +385,152 @@ def pin_s6_zero_decay_and_carry(o, seed=22):
     np.testing.assert_allclose(y1, y2, rtol=1e-13, atol=1e-14)
 
 
+# ----------------------------------------------------------------------------- backward (VJP)
+def _fd_check(f, grad, X, seed, name, eps=1e-5, rtol=1e-6, ndir=3):
+    """<grad, V> against the central difference (f(X + eps V) - f(X - eps V)) / (2 eps) along random V.
+    f is fp64 and smooth, so the two agree to ~1e-9 relative; the bar is 1e-6 of the summed term sizes."""
+    r = _rng(seed)
+    X = np.asarray(X, np.float64)
+    for k in range(ndir):
+        V = r.standard_normal(X.shape)
+        lhs = float(np.sum(grad * V))
+        rhs = (f(X + eps * V) - f(X - eps * V)) / (2 * eps)
+        scale = float(np.sum(np.abs(grad * V))) + 1e-300
+        assert abs(lhs - rhs) <= rtol * scale, f"{name} direction {k}: <g,v>={lhs!r} fd={rhs!r} scale={scale!r}"
+
+
+def _scan_bwd_case(seed, *, softplus, **kw):
+    case, dims = _tiny_scan_case(seed, **kw)
+    r = _rng(seed + 1000)
+    case.pop("init_state")
+    if softplus:
+        case["dt"] = r.standard_normal(case["dt"].shape)
+        case["dt_bias"] = r.uniform(-4, -1, dims["H"])
+    gy = r.standard_normal(case["x"].shape)
+    return case, dims, gy
+
+
+def pin_scan_bwd_finite_differences(o, seed=30):
+    """Every gradient of the scan's backward against central differences of the forward oracle, with and
+    without documents, gate, D skip, groups and the softplus on dt."""
+    for variant in (dict(softplus=False), dict(softplus=True, docs=True, gate=True),
+                    dict(softplus=True, G=1, H=2, docs=True), dict(softplus=False, gate=True, D=False, N=1, P=2)):
+        case, dims, gy = _scan_bwd_case(seed, **variant)
+        sp = variant["softplus"]
+        g = o.scan_bwd(case["x"], case["Bm"], case["Cm"], case["dt"], case["A"], gy, case["D"], case["z"],
+                       case["doc_ids"], dt_softplus=sp, dt_bias=case.get("dt_bias"), **dims)
+        names = ["x", "Bm", "Cm", "dt", "A"] + (["D"] if case["D"] is not None else []) + \
+                (["z"] if case["z"] is not None else []) + (["dt_bias"] if sp else [])
+        for i, nm in enumerate(names):
+            def f(v, nm=nm):
+                c = dict(case)
+                c[nm] = v
+                y, _ = o.scan(c["x"], c["Bm"], c["Cm"], c["dt"], c["A"], c["D"], c["z"], c["doc_ids"],
+                              dt_softplus=sp, dt_bias=c.get("dt_bias"), **dims)
+                return float(np.sum(gy * y))
+            _fd_check(f, g[nm], case[nm], seed + 7 * i, f"{variant} d{nm}")
+
+
+def _conv_bwd_case(seed, *, B=2, L=23, C=7, K=4, H=3, docs=True):
+    r = _rng(seed)
+    case = dict(raw=r.standard_normal((B, L, C)), w=r.standard_normal((C, K)) * 0.5, bias=r.standard_normal(C),
+                dt_raw=r.standard_normal((B, L, H)), dt_bias=r.uniform(-4, -1, H), doc_ids=None)
+    if docs:
+        ids = np.zeros((B, L), np.int32)
+        for b in range(B):
+            for c in sorted(r.choice(np.arange(1, L), size=3, replace=False)):
+                ids[b, c:] += 1
+        ids[0, 9:] += 1
+        ids[0, 10:] += 1                                   # a length-1 document
+        case["doc_ids"] = ids
+    return case, r.standard_normal((B, L, C)), r.standard_normal((B, L, H))
+
+
+def pin_conv_bwd_finite_differences(o, seed=31):
+    """Every gradient of the conv's backward (SiLU and identity activations, documents) against central
+    differences of the forward conv."""
+    for act in (0, 1):
+        case, dout, ddt = _conv_bwd_case(seed + act)
+        g = o.conv_bwd(case["raw"], case["w"], dout, case["bias"], case["dt_raw"], case["dt_bias"], ddt,
+                       case["doc_ids"], act=act)
+        for i, nm in enumerate(["raw", "w", "bias", "dt_raw", "dt_bias"]):
+            def f(v, nm=nm):
+                c = dict(case)
+                c[nm] = v
+                out, dt, _ = o.conv(c["raw"], c["w"], c["bias"], c["dt_raw"], c["dt_bias"], c["doc_ids"], act=act)
+                return float(np.sum(dout * out) + np.sum(ddt * dt))
+            _fd_check(f, g[nm], case[nm], seed + 11 * i, f"act={act} d{nm}")
+
+
+def _mixer_case(seed, *, B=2, L=21, H=2, P=3, N=4, G=1, docs=True):
+    r = _rng(seed)
+    C = H * P + 2 * G * N
+    case = dict(raw=r.standard_normal((B, L, C)), w=r.standard_normal((C, 4)) * 0.5, bias=r.standard_normal(C) * 0.5,
+                dt_raw=r.standard_normal((B, L, H)), dt_bias=r.uniform(-4, -1, H), A=-np.exp(r.uniform(0, 2.7, H)),
+                D=r.standard_normal(H), z=r.standard_normal((B, L, H * P)))
+    ids = None
+    if docs:
+        ids = np.zeros((B, L), np.int32)
+        for b in range(B):
+            for c in sorted(r.choice(np.arange(1, L), size=3, replace=False)):
+                ids[b, c:] += 1
+    return case, ids, dict(H=H, P=P, N=N, G=G), r.standard_normal((B, L, H * P))
+
+
+def pin_mixer_bwd_finite_differences(o, seed=32):
+    """The composed backward (conv -> scan) against central differences of forward() end to end."""
+    case, ids, dims, gy = _mixer_case(seed)
+    g = o.mixer_bwd(*[case[k] for k in ("raw", "w", "bias", "dt_raw", "dt_bias", "A", "D", "z")], gy, doc_ids=ids,
+                    **dims)
+    keys = ("raw", "w", "bias", "dt_raw", "dt_bias", "A", "D", "z")
+    for i, nm in enumerate(keys):
+        def f(v, nm=nm):
+            c = dict(case)
+            c[nm] = v
+            y = o.forward(*[c[k] for k in keys], doc_ids=ids, **dims)[0]
+            return float(np.sum(gy * y))
+        _fd_check(f, g[nm], case[nm], seed + 13 * i, f"mixer d{nm}")
+
+
+def pin_bwd_document_isolation(o, seed=33):
+    """A loss on a later document gives exactly zero gradient on every earlier-document input (scan and
+    conv -> scan), and the per-token gradients of a packed row's document equal, bit for bit, those of the
+    document run alone."""
+    case, dims, gy = _scan_bwd_case(seed, softplus=True, docs=True, gate=True)
+    ids = case["doc_ids"]
+    for b in range(ids.shape[0]):
+        k = ids[b, -1]
+        start = int(np.argmax(ids[b] == k))
+        assert start > 0
+        gk = np.zeros_like(gy)
+        gk[b, start:] = gy[b, start:]
+        g = o.scan_bwd(case["x"], case["Bm"], case["Cm"], case["dt"], case["A"], gk, case["D"], case["z"], ids,
+                       dt_softplus=True, dt_bias=case["dt_bias"], **dims)
+        for nm in ("x", "Bm", "Cm", "dt", "z"):
+            assert np.all(g[nm][:, :start] == 0.0) and np.all(g[nm][1 - b] == 0.0), f"scan d{nm} row {b}"
+        # the same document alone
+        sl = lambda t: t[b:b + 1, start:]
+        ga = o.scan_bwd(sl(case["x"]), sl(case["Bm"]), sl(case["Cm"]), sl(case["dt"]), case["A"], sl(gy),
+                        case["D"], sl(case["z"]), None, dt_softplus=True, dt_bias=case["dt_bias"], **dims)
+        for nm in ("x", "Bm", "Cm", "dt", "z"):
+            assert np.array_equal(g[nm][b:b + 1, start:], ga[nm]), f"packed vs alone d{nm} row {b}"
+    mcase, mids, mdims, mgy = _mixer_case(seed + 1)
+    for b in range(mids.shape[0]):
+        k = mids[b, -1]
+        start = int(np.argmax(mids[b] == k))
+        gk = np.zeros_like(mgy)
+        gk[b, start:] = mgy[b, start:]
+        g = o.mixer_bwd(*[mcase[k] for k in ("raw", "w", "bias", "dt_raw", "dt_bias", "A", "D", "z")], gk,
+                        doc_ids=mids, **mdims)
+        for nm in ("raw", "dt_raw", "z"):
+            assert np.all(g[nm][:, :start] == 0.0) and np.all(g[nm][1 - b] == 0.0), f"mixer d{nm} row {b}"
+
+
 ALL_PINS = [
     pin_hand_vectors, pin_quadratic_form, pin_zero_decay, pin_softplus_silu_bf16, pin_conv_library,
     pin_conv_impulse, pin_conv_documents, pin_conv_state_carry, pin_packed_equals_separate,
     pin_split_equals_single, pin_step_equals_prefill, pin_linearity_and_decay_only, pin_groups_and_batch,
     pin_dt_softplus_inside, pin_s6_quadratic_form, pin_s6_equals_ssd, pin_s6_zero_decay_and_carry,
+    pin_scan_bwd_finite_differences, pin_conv_bwd_finite_differences, pin_mixer_bwd_finite_differences,
+    pin_bwd_document_isolation,
 ]

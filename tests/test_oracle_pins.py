@@ -61,6 +61,23 @@ MUTATIONS = [
     ("s6_no_doc_reset", "if (doc && t > 0 && doc[row] != doc[row - 1]) memset(h", "if (0) memset(h"),
     ("s6_bias_outside", "dtv = softplus(dtv + (dt_bias ? dt_bias[d] : 0.0));",
      "dtv = softplus(dtv) + (dt_bias ? dt_bias[d] : 0.0);"),
+    # the backward (VJP)
+    ("bwd_adjoint_not_decayed", "dS[i] = reset ? 0.0 : a * dS[i];", "dS[i] = reset ? 0.0 : dS[i];"),
+    ("bwd_adjoint_not_reset", "dS[i] = reset ? 0.0 : a * dS[i];", "dS[i] = a * dS[i];"),
+    ("bwd_decay_uses_new_state", "if (!reset) da += g_pn * Sp[", "if (!reset) da += g_pn * Sc["),
+    ("bwd_dB_without_dt", "dBv[n] += d * g_pn * xv[p];", "dBv[n] += g_pn * xv[p];"),
+    ("bwd_dx_without_skip", "dxv[p] = Dh * dyr;", "dxv[p] = 0.0;"),
+    ("bwd_dC_from_old_state", "dCv[n] += dyr * Sc[", "dCv[n] += dyr * Sp["),
+    ("bwd_dt_no_decay_term", "dd += da * a * Ah;", "dd += 0.0 * da;"),
+    ("bwd_dA_without_dt", "sA += da * a * d;", "sA += da * a;"),
+    ("bwd_softplus_chain_dropped", "ddt[row * H + h] = dd * s;", "ddt[row * H + h] = dd;"),
+    ("bwd_gate_derivative_as_silu", "gyv * yr * dsilu(zv)", "gyv * yr * silu(zv)"),
+    ("bwd_adjoint_misses_output", "dS[(size_t)p * N + n] += Cv[n] * dyr;", "dS[(size_t)p * N + n] += Bv[n] * dyr;"),
+    ("conv_bwd_taps_reversed", "draw[((size_t)b * L + tau) * C + c] += w[(size_t)c * K + k] * gp;",
+     "draw[((size_t)b * L + tau) * C + c] += w[(size_t)c * K + (K - 1 - k)] * gp;"),
+    ("conv_bwd_no_act_derivative", "go * dsilu(pre)", "go"),
+    ("conv_bwd_ignores_documents", "if (tau >= seg && tau >= 0) {", "if (tau >= 0) {"),
+    ("conv_bwd_dt_no_sigmoid", "ddt_raw[i] = ddt[i] * s;", "ddt_raw[i] = ddt[i];"),
 ]
 
 
