@@ -1,7 +1,7 @@
 /*
  * ssd.h -- C ABI of libssd.so, the gfx950 (MI355X) Mamba-2 SSD mixer core.
  *
- * Six operations, each a few HIP kernel launches on the caller's stream:
+ * Nine operations, each a few HIP kernel launches on the caller's stream:
  *
  *   ssd_conv_fwd        causal depthwise conv (k = 4) + SiLU over the
  *                       [x | B | C] columns, and dt = softplus(dt_raw + dt_bias)
@@ -17,6 +17,9 @@
  *                       buffer, state update, output and gate
  *   ssd_s6_scan_fwd     the Mamba-1 selective scan (S6): a per-channel
  *                       diagonal state, B and C shared by the channels
+ *   ssd_chunk_scan_bwd  backward (VJP) of the scan for a zero-state prefill
+ *   ssd_conv_bwd        backward of the conv prologue
+ *   ssd_mixer_bwd       backward of conv + scan, recomputing the forward
  *
  * The operation (per batch row b and head h, token t, head h in group
  * g = h / (H/G)):
@@ -381,6 +384,111 @@ int ssd_s6_scan_fwd(int B, int L, int D, int N, int dtype,
  * sizes: hloc [B][D][K-1][N] and sdt [B][D][K-1] (fp32) and a copy of the
  * initial state; 0 when no split pays. */
 size_t ssd_s6_workspace_size(int B, int L, int D, int N, int dtype);
+
+/*
+ * ssd_chunk_scan_bwd -- backward (vector-Jacobian product) of
+ * ssd_chunk_scan_fwd for a prefill from a zero state.
+ *
+ * Given grad_y = dLoss/dy, writes the gradients of every input of the scan.
+ * The forward is recomputed from the inputs; no earlier forward's state is
+ * used.  As the mojolearn.Mamba3Block backward() describes, there is no
+ * gradient for a carried initial state and no cotangent for the final state.
+ * Document ids cut gradients exactly as they cut the forward: a loss on a
+ * later document gives exactly zero gradient on earlier-document inputs
+ * (Mini-K3-1H card, "Checkpoint and training").  bf16 inputs are widened to
+ * fp32; all gradients are fp32.  Results are deterministic: dB and dC are
+ * summed over a group's heads in one workgroup, and dA, dD, ddt_bias through
+ * per-chunk partial sums added in a fixed order.
+ *
+ *   x, Bm, Cm, dt, dt_softplus, dt_bias, A, D, z, doc_ids   as in
+ *               ssd_chunk_scan_fwd (no init_state)
+ *   grad_y  f32 [B][L][H*P], row stride grad_y_row_stride
+ *   dx      f32 [B][L][H*P];  dB, dC f32 [B][L][G*N] (row strides in
+ *               elements, multiples of 4)
+ *   ddt     f32 [B][L][H]: with respect to the dt input (the raw value when
+ *               dt_softplus = 1)
+ *   ddt_bias f32 [H] or NULL (written when dt_softplus = 1)
+ *   dA      f32 [H]: with respect to A (the caller chains A = -exp(A_log))
+ *   dD      f32 [H] or NULL (zero when D is NULL)
+ *   dz      f32 [B][L][H*P] or NULL (only with z)
+ *   workspace, workspace_bytes: required, at least
+ *               ssd_chunk_scan_bwd_workspace_size() bytes, 16-byte aligned,
+ *               caller-owned, not shared by concurrent calls
+ * Outputs must not overlap the inputs or each other.  Supported: N in
+ * {16, 32, 64}, P = 64, chunk = 64.  L = 0 writes zero parameter gradients.
+ */
+int ssd_chunk_scan_bwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                       const void *x, int64_t x_row_stride,
+                       const void *Bm, int64_t B_row_stride,
+                       const void *Cm, int64_t C_row_stride,
+                       const float *dt, int64_t dt_row_stride,
+                       int dt_softplus, const float *dt_bias,
+                       const float *A, const float *D,
+                       const void *z, int64_t z_row_stride,
+                       const int32_t *doc_ids,
+                       const float *grad_y, int64_t grad_y_row_stride,
+                       float *dx, int64_t dx_row_stride,
+                       float *dB, int64_t dB_row_stride,
+                       float *dC, int64_t dC_row_stride,
+                       float *ddt, int64_t ddt_row_stride,
+                       float *ddt_bias, float *dA, float *dD,
+                       float *dz, int64_t dz_row_stride,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace ssd_chunk_scan_bwd needs: the state entering and the
+ * adjoint of the state leaving every chunk ([B][H][L/64][N][P] fp32 each),
+ * the chunk decays and per-chunk partial sums. */
+size_t ssd_chunk_scan_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
+
+/*
+ * ssd_conv_bwd -- backward of ssd_conv_fwd's conv + act for a zero conv
+ * state: given grad_xbc = dLoss/d(conv output) (f32 [B][L][conv_dim]),
+ * writes dxbc_raw (f32 [B][L][conv_dim]), dconv_w (f32 [conv_dim][K]) and
+ * dconv_b (f32 [conv_dim] or NULL).  Taps across a document start carry no
+ * gradient, as they carry no value forward.  The softplus of dt is not part
+ * of this call: ssd_chunk_scan_bwd with dt_softplus = 1 (or ssd_mixer_bwd)
+ * returns dt_raw's gradient.  The workspace (ssd_conv_bwd_workspace_size()
+ * bytes, required) holds per-64-token partial sums of dconv_w and dconv_b.
+ */
+int ssd_conv_bwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
+                 const void *xbc_raw, int64_t xbc_raw_row_stride,
+                 const float *conv_w, const float *conv_b, const int32_t *doc_ids, int act,
+                 const float *grad_xbc, int64_t grad_xbc_row_stride,
+                 float *dxbc_raw, int64_t dxbc_raw_row_stride,
+                 float *dconv_w, float *dconv_b,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+size_t ssd_conv_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
+
+/*
+ * ssd_mixer_bwd -- backward of ssd_mixer_fwd (conv + act, dt softplus, scan,
+ * D skip, gate) for a prefill from zero states.
+ *
+ * Recomputes the conv output and dt with the conv kernel (a bf16 pipeline's
+ * rounding of the conv output is taken as the identity in the backward),
+ * runs ssd_chunk_scan_bwd's passes on them, then the conv backward.  Writes
+ * dxbc_raw (f32 [B][L][conv_dim]), dconv_w, dconv_b, ddt_raw (f32 [B][L][H]),
+ * ddt_bias, dA, dD and dz as above.  workspace: required,
+ * ssd_mixer_bwd_workspace_size() bytes.
+ */
+int ssd_mixer_bwd(int B, int L, int H, int P, int N, int G, int K, int chunk, int dtype,
+                  const void *xbc_raw, int64_t xbc_raw_row_stride,
+                  const float *conv_w, const float *conv_b,
+                  const void *dt_raw, int64_t dt_raw_row_stride, const float *dt_bias,
+                  const float *A, const float *D,
+                  const void *z, int64_t z_row_stride,
+                  const int32_t *doc_ids, int act,
+                  const float *grad_y, int64_t grad_y_row_stride,
+                  float *dxbc_raw, int64_t dxbc_raw_row_stride,
+                  float *dconv_w, float *dconv_b,
+                  float *ddt_raw, int64_t ddt_raw_row_stride, float *ddt_bias,
+                  float *dA, float *dD,
+                  float *dz, int64_t dz_row_stride,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace of ssd_mixer_bwd: the recomputed conv output (T) and dt,
+ * the conv output's gradient (fp32), and the two backward calls' scratch. */
+size_t ssd_mixer_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,9 @@ The entry points mirror the C ABI in include/ssd.h one to one:
     ssd_resume_fwd      decode tokens rescanned with the working chunk: bit-identical to the forward
     ssd_step            one decode token per sequence
     ssd_s6_scan_fwd     the Mamba-1 selective scan (per-channel diagonal state)
+    ssd_chunk_scan_bwd  backward (VJP) of the scan for a zero-state prefill
+    ssd_conv_bwd        backward of the conv prologue
+    ssd_mixer_bwd       backward of conv + scan
 
 This module only marshals torch tensors (device pointers, row strides, the
 current HIP stream) into the library; every step of the computation runs in
@@ -23,6 +26,8 @@ import torch
 
 __all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_resume_fwd", "ssd_step",
            "ssd_s6_scan_fwd", "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size", "ssd_s6_workspace_size",
+           "ssd_chunk_scan_bwd", "ssd_conv_bwd", "ssd_mixer_bwd", "ssd_chunk_scan_bwd_workspace_size",
+           "ssd_conv_bwd_workspace_size", "ssd_mixer_bwd_workspace_size",
            "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
@@ -76,6 +81,17 @@ def load() -> ctypes.CDLL:
     lib.ssd_s6_scan_fwd.restype = I
     lib.ssd_s6_scan_fwd.argtypes = [I, I, I, I, I, P, I64, P, I64, I, P, P, P, I64, P, I64, P, P, I64, P, P, P,
                                     P, I64, P, SZ, P]
+    lib.ssd_chunk_scan_bwd.restype = I
+    lib.ssd_chunk_scan_bwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P, I64, P,
+                                       P, I64, P, I64, P, I64, P, I64, P, I64, P, P, P, P, I64, P, SZ, P]
+    lib.ssd_conv_bwd.restype = I
+    lib.ssd_conv_bwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, P, P, I, P, I64, P, I64, P, P, P, SZ, P]
+    lib.ssd_mixer_bwd.restype = I
+    lib.ssd_mixer_bwd.argtypes = [I, I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I64, P, I, P, I64, P,
+                                  I64, P, P, P, I64, P, P, P, P, I64, P, SZ, P]
+    for nm in ("ssd_chunk_scan_bwd_workspace_size", "ssd_conv_bwd_workspace_size", "ssd_mixer_bwd_workspace_size"):
+        getattr(lib, nm).restype = SZ
+        getattr(lib, nm).argtypes = [I, I, I, I, I, I, I]
     lib.ssd_s6_workspace_size.restype = SZ
     lib.ssd_s6_workspace_size.argtypes = [I, I, I, I, I]
     _lib = lib
@@ -371,3 +387,125 @@ def ssd_s6_scan_fwd(x, dt, A, Bm, Cm, *, D_skip=None, z=None, doc_ids=None, init
         _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
     _check(st)
     return y
+
+
+def ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
+    return int(load().ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype))
+
+
+def ssd_conv_bwd_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
+    return int(load().ssd_conv_bwd_workspace_size(B, L, H, P, N, G, dtype))
+
+
+def ssd_mixer_bwd_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
+    return int(load().ssd_mixer_bwd_workspace_size(B, L, H, P, N, G, dtype))
+
+
+def _ws(workspace, nbytes, device):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def ssd_chunk_scan_bwd(x, Bm, Cm, dt, A, grad_y, *, H, P, N, G, D=None, z=None, doc_ids=None, dt_softplus=False,
+                       dt_bias=None, chunk=64, workspace=None, stream=None):
+    """Backward of the zero-state scan.  Returns a dict of fp32 gradients: x, Bm, Cm, dt, A (and D, z, dt_bias
+    where those inputs are given).  A workspace is allocated here when none is passed."""
+    lib = load()
+    B, L = x.shape[0], x.shape[1]
+    dtype = _dtype_code(x, "x")
+    dev = x.device
+    rs_x = _rows(x, "x", B, L, H * P)
+    rs_b = _rows(Bm, "Bm", B, L, G * N)
+    rs_c = _rows(Cm, "Cm", B, L, G * N)
+    rs_dt = _rows(dt, "dt", B, L, H)
+    rs_z = _rows(z, "z", B, L, H * P)
+    rs_gy = _rows(grad_y, "grad_y", B, L, H * P)
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"x": torch.empty(B, L, H * P, **f32), "Bm": torch.empty(B, L, G * N, **f32),
+         "Cm": torch.empty(B, L, G * N, **f32), "dt": torch.empty(B, L, H, **f32), "A": torch.empty(H, **f32),
+         "D": torch.empty(H, **f32) if D is not None else None,
+         "z": torch.empty(B, L, H * P, **f32) if z is not None else None,
+         "dt_bias": torch.empty(H, **f32) if dt_softplus else None}
+    ws = _ws(workspace, ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype), dev)
+    nb = ws.numel() * ws.element_size()
+    st = lib.ssd_chunk_scan_bwd(
+        B, L, H, P, N, G, chunk, dtype,
+        _ptr(x, "x"), rs_x, _ptr(Bm, "Bm", x.dtype), rs_b, _ptr(Cm, "Cm", x.dtype), rs_c,
+        _ptr(dt, "dt", torch.float32), rs_dt, int(bool(dt_softplus)), _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32), _ptr(z, "z", x.dtype), rs_z,
+        _ptr(doc_ids, "doc_ids", torch.int32), _ptr(grad_y, "grad_y", torch.float32), rs_gy,
+        _ptr(g["x"], "dx"), H * P, _ptr(g["Bm"], "dB"), G * N, _ptr(g["Cm"], "dC"), G * N, _ptr(g["dt"], "ddt"), H,
+        _ptr(g["dt_bias"], "ddt_bias"), _ptr(g["A"], "dA"), _ptr(g["D"], "dD"), _ptr(g["z"], "dz"), H * P,
+        _ptr(ws, "workspace"), nb, _stream(stream))
+    _check(st)
+    return {k: v for k, v in g.items() if v is not None}
+
+
+def ssd_conv_bwd(xbc_raw, conv_w, grad_xbc, *, H, P, N, G, K=4, conv_b=None, doc_ids=None, act=SSD_ACT_SILU,
+                 workspace=None, stream=None):
+    """Backward of the zero-state conv + act.  Returns a dict: raw [B, L, conv_dim], w [conv_dim, K] (and bias)."""
+    lib = load()
+    B, L = xbc_raw.shape[0], xbc_raw.shape[1]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    dev = xbc_raw.device
+    rs_in = _rows(xbc_raw, "xbc_raw", B, L, C)
+    rs_g = _rows(grad_xbc, "grad_xbc", B, L, C)
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"raw": torch.empty(B, L, C, **f32), "w": torch.empty(C, K, **f32),
+         "bias": torch.empty(C, **f32) if conv_b is not None else None}
+    ws = _ws(workspace, ssd_conv_bwd_workspace_size(B, L, H, P, N, G, dtype), dev)
+    st = lib.ssd_conv_bwd(
+        B, L, H, P, N, G, K, dtype, _ptr(xbc_raw, "xbc_raw"), rs_in, _ptr(conv_w, "conv_w", torch.float32),
+        _ptr(conv_b, "conv_b", torch.float32), _ptr(doc_ids, "doc_ids", torch.int32), int(act),
+        _ptr(grad_xbc, "grad_xbc", torch.float32), rs_g, _ptr(g["raw"], "dxbc_raw"), C, _ptr(g["w"], "dconv_w"),
+        _ptr(g["bias"], "dconv_b"), _ptr(ws, "workspace"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st)
+    return {k: v for k, v in g.items() if v is not None}
+
+
+def ssd_mixer_bwd(xbc_raw, dt_raw, conv_w, A, grad_y, *, H, P, N, G, K=4, conv_b=None, dt_bias=None, D=None, z=None,
+                  doc_ids=None, act=SSD_ACT_SILU, chunk=64, workspace=None, stream=None):
+    """Backward of ssd_mixer_fwd for zero states.  Returns a dict of fp32 gradients: raw, w, dt_raw, A (and bias,
+    dt_bias, D, z where those inputs are given)."""
+    lib = load()
+    B, L = xbc_raw.shape[0], xbc_raw.shape[1]
+    C = H * P + 2 * G * N
+    dtype = _dtype_code(xbc_raw, "xbc_raw")
+    dev = xbc_raw.device
+    rs_in = _rows(xbc_raw, "xbc_raw", B, L, C)
+    rs_dt = _rows(dt_raw, "dt_raw", B, L, H)
+    rs_z = _rows(z, "z", B, L, H * P)
+    rs_gy = _rows(grad_y, "grad_y", B, L, H * P)
+    _contig(conv_w, "conv_w", (C, K))
+    _contig(conv_b, "conv_b", (C,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"raw": torch.empty(B, L, C, **f32), "w": torch.empty(C, K, **f32),
+         "bias": torch.empty(C, **f32) if conv_b is not None else None, "dt_raw": torch.empty(B, L, H, **f32),
+         "dt_bias": torch.empty(H, **f32) if dt_bias is not None else None, "A": torch.empty(H, **f32),
+         "D": torch.empty(H, **f32) if D is not None else None,
+         "z": torch.empty(B, L, H * P, **f32) if z is not None else None}
+    ws = _ws(workspace, ssd_mixer_bwd_workspace_size(B, L, H, P, N, G, dtype), dev)
+    st = lib.ssd_mixer_bwd(
+        B, L, H, P, N, G, K, chunk, dtype, _ptr(xbc_raw, "xbc_raw"), rs_in, _ptr(conv_w, "conv_w", torch.float32),
+        _ptr(conv_b, "conv_b", torch.float32), _ptr(dt_raw, "dt_raw", xbc_raw.dtype), rs_dt,
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
+        _ptr(z, "z", xbc_raw.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32), int(act),
+        _ptr(grad_y, "grad_y", torch.float32), rs_gy, _ptr(g["raw"], "dxbc_raw"), C, _ptr(g["w"], "dconv_w"),
+        _ptr(g["bias"], "dconv_b"), _ptr(g["dt_raw"], "ddt_raw"), H, _ptr(g["dt_bias"], "ddt_bias"),
+        _ptr(g["A"], "dA"), _ptr(g["D"], "dD"), _ptr(g["z"], "dz"), H * P, _ptr(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check(st)
+    return {k: v for k, v in g.items() if v is not None}

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["api.cpp", "conv.hip", "scan.hip", "step.hip", "s6.hip"]
+SOURCES = ["api.cpp", "conv.hip", "scan.hip", "step.hip", "s6.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -472,6 +472,313 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
                                                 n * HP * 4, B, n, (int)(HP * 4), s));
 }
 
+static int check_bwd_dims(const char* fn, int B, int L, int H, int P, int N, int G, int dtype) {
+    TRY(check_dims(fn, B, L, H, P, N, G, 4, dtype));
+    if (N > 64)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: N=%d is not supported by the backward (16, 32 or 64)", fn, N);
+    return SSD_OK;
+}
+
+size_t ssd_chunk_scan_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
+    (void)G; (void)dtype;
+    if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0) return 0;
+    return ssd::scan_bwd_workspace_bytes(B, L, H, P, N);
+}
+
+// Shared by ssd_chunk_scan_bwd and ssd_mixer_bwd: the three backward passes,
+// arguments already validated.
+static int run_scan_bwd(const char* fn, ssd::BwdArgs& a, void* workspace, hipStream_t s) {
+    const size_t nc = (size_t)(a.L + 63) / 64;
+    const size_t st = round256((size_t)a.B * a.H * nc * a.N * a.P * sizeof(float));
+    a.nc = (int)nc;
+    a.S = static_cast<float*>(workspace);
+    a.dS = a.S + st / sizeof(float);
+    a.dec = a.dS + st / sizeof(float);
+    a.part = a.dec + round256((size_t)a.B * a.H * nc * sizeof(float)) / sizeof(float);
+    return hip_status(fn, ssd::launch_scan_bwd(a, s));
+}
+
+int ssd_chunk_scan_bwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                       const void* x, int64_t x_row_stride,
+                       const void* Bm, int64_t B_row_stride,
+                       const void* Cm, int64_t C_row_stride,
+                       const float* dt, int64_t dt_row_stride,
+                       int dt_softplus, const float* dt_bias,
+                       const float* A, const float* D,
+                       const void* z, int64_t z_row_stride,
+                       const int32_t* doc_ids,
+                       const float* grad_y, int64_t grad_y_row_stride,
+                       float* dx, int64_t dx_row_stride,
+                       float* dB, int64_t dB_row_stride,
+                       float* dC, int64_t dC_row_stride,
+                       float* ddt, int64_t ddt_row_stride,
+                       float* ddt_bias, float* dA, float* dD,
+                       float* dz, int64_t dz_row_stride,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_chunk_scan_bwd";
+    TRY(check_bwd_dims(fn, B, L, H, P, N, G, dtype));
+    if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
+    if (dt_softplus != 0 && dt_softplus != 1)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: dt_softplus=%d must be 0 or 1", fn, dt_softplus);
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
+    TRY(check_tensor(fn, "x", x, x_row_stride, HP, es, work));
+    TRY(check_tensor(fn, "Bm", Bm, B_row_stride, GN, es, work));
+    TRY(check_tensor(fn, "Cm", Cm, C_row_stride, GN, es, work));
+    TRY(check_tensor(fn, "z", z, z_row_stride, HP, es, false));
+    TRY(check_tensor(fn, "grad_y", grad_y, grad_y_row_stride, HP, 4, work));
+    TRY(check_tensor(fn, "dx", dx, dx_row_stride, HP, 4, work));
+    TRY(check_tensor(fn, "dB", dB, dB_row_stride, GN, 4, work));
+    TRY(check_tensor(fn, "dC", dC, dC_row_stride, GN, 4, work));
+    TRY(check_tensor(fn, "dz", dz, dz_row_stride, HP, 4, false));
+    if (work) {
+        if (!dt) return fail(SSD_ERR_NULL_ARG, "%s: dt is NULL", fn);
+        if (dt_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: dt row stride %lld is smaller than H=%d", fn, (long long)dt_row_stride, H);
+        if (!ddt) return fail(SSD_ERR_NULL_ARG, "%s: ddt is NULL", fn);
+        if (ddt_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: ddt row stride %lld is smaller than H=%d", fn,
+                        (long long)ddt_row_stride, H);
+    }
+    if (dz && !z) return fail(SSD_ERR_NULL_ARG, "%s: dz is given but z is NULL", fn);
+    TRY(check_ptr(fn, "dt", dt, false, false));
+    TRY(check_ptr(fn, "ddt", ddt, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, B > 0, false));
+    TRY(check_ptr(fn, "dA", dA, B > 0, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "dD", dD, false, false));
+    TRY(check_ptr(fn, "ddt_bias", ddt_bias, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    if (work && (x_row_stride > (1 << 22) || B_row_stride > (1 << 22) || C_row_stride > (1 << 22) ||
+                 z_row_stride > (1 << 22) || dt_row_stride > (1 << 22) || grad_y_row_stride > (1 << 22) ||
+                 dx_row_stride > (1 << 22) || dB_row_stride > (1 << 22) || dC_row_stride > (1 << 22) ||
+                 ddt_row_stride > (1 << 22) || dz_row_stride > (1 << 22)))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
+    const size_t need = ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype);
+    if (work && (!workspace || workspace_bytes < need))
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (work && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {   // no tokens: every parameter gradient is zero
+        if (B > 0) {
+            TRY(hip_status(fn, ssd::launch_zero_f32(dA, (size_t)H, s)));
+            TRY(hip_status(fn, ssd::launch_zero_f32(dD, (size_t)H, s)));
+            TRY(hip_status(fn, ssd::launch_zero_f32(dt_softplus ? ddt_bias : nullptr, (size_t)H, s)));
+        }
+        return ok();
+    }
+    ssd::BwdArgs a{};
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.x = x; a.x_stride = x_row_stride;
+    a.Bm = Bm; a.B_stride = B_row_stride;
+    a.Cm = Cm; a.C_stride = C_row_stride;
+    a.dt = dt; a.dt_stride = dt_row_stride;
+    a.dt_softplus = dt_softplus; a.chain_from_dt = 0; a.dt_bias = dt_bias;
+    a.A = A; a.D = D;
+    a.z = z; a.z_stride = z_row_stride;
+    a.doc = doc_ids;
+    a.gy = grad_y; a.gy_stride = grad_y_row_stride;
+    a.dx = dx; a.dx_stride = dx_row_stride;
+    a.dB = dB; a.dB_stride = dB_row_stride;
+    a.dC = dC; a.dC_stride = dC_row_stride;
+    a.ddt = ddt; a.ddt_stride = ddt_row_stride;
+    a.dz = dz; a.dz_stride = dz_row_stride;
+    a.ddt_bias = dt_softplus ? ddt_bias : nullptr; a.dA = dA; a.dD = D ? dD : nullptr;
+    if (!D) TRY(hip_status(fn, ssd::launch_zero_f32(dD, (size_t)H, s)));
+    return run_scan_bwd(fn, a, workspace, s);
+}
+
+size_t ssd_conv_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
+    (void)dtype;
+    if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return 0;
+    return ssd::conv_bwd_workspace_bytes(B, L, H * P + 2 * G * N);
+}
+
+static int run_conv_bwd(const char* fn, int B, int L, int C, int dtype, const void* raw, int64_t raw_stride,
+                        const float* w, const float* bias, const int32_t* doc, int act, const float* dout,
+                        int64_t dout_stride, float* draw, int64_t draw_stride, float* dw, float* dbias,
+                        void* workspace, hipStream_t s) {
+    ssd::ConvBwdArgs c{};
+    c.B = B; c.L = L; c.C = C; c.dtype = dtype; c.act = act;
+    c.raw = raw; c.raw_stride = raw_stride;
+    c.w = w; c.bias = bias; c.doc = doc;
+    c.dout = dout; c.dout_stride = dout_stride;
+    c.draw = draw; c.draw_stride = draw_stride;
+    c.dw = dw; c.dbias = dbias;
+    c.ntc = (L + 63) / 64;
+    c.part = static_cast<float*>(workspace);
+    return hip_status(fn, ssd::launch_conv_bwd(c, s));
+}
+
+int ssd_conv_bwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
+                 const void* xbc_raw, int64_t xbc_raw_row_stride,
+                 const float* conv_w, const float* conv_b, const int32_t* doc_ids, int act,
+                 const float* grad_xbc, int64_t grad_xbc_row_stride,
+                 float* dxbc_raw, int64_t dxbc_raw_row_stride,
+                 float* dconv_w, float* dconv_b,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_conv_bwd";
+    TRY(check_dims(fn, B, L, H, P, N, G, K, dtype));
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    const int64_t C = (int64_t)H * P + 2LL * G * N;
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "xbc_raw", xbc_raw, xbc_raw_row_stride, C, es, work));
+    TRY(check_tensor(fn, "grad_xbc", grad_xbc, grad_xbc_row_stride, C, 4, work));
+    TRY(check_tensor(fn, "dxbc_raw", dxbc_raw, dxbc_raw_row_stride, C, 4, work));
+    TRY(check_ptr(fn, "conv_w", conv_w, true, true));
+    TRY(check_ptr(fn, "dconv_w", dconv_w, true, false));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    TRY(check_ptr(fn, "dconv_b", dconv_b, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    const size_t need = ssd_conv_bwd_workspace_size(B, L, H, P, N, G, dtype);
+    if (work && (!workspace || workspace_bytes < need))
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (work && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        TRY(hip_status(fn, ssd::launch_zero_f32(dconv_w, (size_t)C * 4, s)));
+        TRY(hip_status(fn, ssd::launch_zero_f32(dconv_b, (size_t)C, s)));
+        return ok();
+    }
+    return run_conv_bwd(fn, B, L, (int)C, dtype, xbc_raw, xbc_raw_row_stride, conv_w, conv_b, doc_ids, act, grad_xbc,
+                        grad_xbc_row_stride, dxbc_raw, dxbc_raw_row_stride, dconv_w, dconv_b, workspace, s);
+}
+
+size_t ssd_mixer_bwd_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
+    if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return 0;
+    const size_t C = (size_t)H * P + 2 * (size_t)G * N;
+    return round256((size_t)B * L * C * esize(dtype)) + round256((size_t)B * L * H * 4) +
+           round256((size_t)B * L * C * 4) + ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype) +
+           round256(ssd_conv_bwd_workspace_size(B, L, H, P, N, G, dtype));
+}
+
+int ssd_mixer_bwd(int B, int L, int H, int P, int N, int G, int K, int chunk, int dtype,
+                  const void* xbc_raw, int64_t xbc_raw_row_stride,
+                  const float* conv_w, const float* conv_b,
+                  const void* dt_raw, int64_t dt_raw_row_stride, const float* dt_bias,
+                  const float* A, const float* D,
+                  const void* z, int64_t z_row_stride,
+                  const int32_t* doc_ids, int act,
+                  const float* grad_y, int64_t grad_y_row_stride,
+                  float* dxbc_raw, int64_t dxbc_raw_row_stride,
+                  float* dconv_w, float* dconv_b,
+                  float* ddt_raw, int64_t ddt_raw_row_stride, float* ddt_bias,
+                  float* dA, float* dD,
+                  float* dz, int64_t dz_row_stride,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssd_mixer_bwd";
+    TRY(check_bwd_dims(fn, B, L, H, P, N, G, dtype));
+    if (K != 4) return fail(SSD_ERR_UNSUPPORTED, "%s: K=%d is not supported (conv kernel must be 4)", fn, K);
+    if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
+    if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: act=%d is not supported (SSD_ACT_SILU=0, SSD_ACT_NONE=1)", fn, act);
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, C = HP + 2 * GN;
+    const int es = esize(dtype);
+    const bool work = B > 0 && L > 0;
+    TRY(check_tensor(fn, "xbc_raw", xbc_raw, xbc_raw_row_stride, C, es, work));
+    TRY(check_tensor(fn, "z", z, z_row_stride, HP, es, false));
+    TRY(check_tensor(fn, "grad_y", grad_y, grad_y_row_stride, HP, 4, work));
+    TRY(check_tensor(fn, "dxbc_raw", dxbc_raw, dxbc_raw_row_stride, C, 4, work));
+    TRY(check_tensor(fn, "dz", dz, dz_row_stride, HP, 4, false));
+    if (work) {
+        if (!dt_raw) return fail(SSD_ERR_NULL_ARG, "%s: dt_raw is NULL", fn);
+        if (!ddt_raw) return fail(SSD_ERR_NULL_ARG, "%s: ddt_raw is NULL", fn);
+        if (dt_raw_row_stride < H || ddt_raw_row_stride < H)
+            return fail(SSD_ERR_BAD_SHAPE, "%s: dt_raw / ddt_raw row strides (%lld, %lld) are smaller than H=%d", fn,
+                        (long long)dt_raw_row_stride, (long long)ddt_raw_row_stride, H);
+    }
+    if (dz && !z) return fail(SSD_ERR_NULL_ARG, "%s: dz is given but z is NULL", fn);
+    TRY(check_ptr(fn, "dt_raw", dt_raw, false, false));
+    TRY(check_ptr(fn, "ddt_raw", ddt_raw, false, false));
+    TRY(check_ptr(fn, "conv_w", conv_w, true, true));
+    TRY(check_ptr(fn, "dconv_w", dconv_w, true, false));
+    TRY(check_ptr(fn, "conv_b", conv_b, false, false));
+    TRY(check_ptr(fn, "dconv_b", dconv_b, false, false));
+    TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));
+    TRY(check_ptr(fn, "ddt_bias", ddt_bias, false, false));
+    TRY(check_ptr(fn, "A", A, B > 0, false));
+    TRY(check_ptr(fn, "dA", dA, B > 0, false));
+    TRY(check_ptr(fn, "D", D, false, false));
+    TRY(check_ptr(fn, "dD", dD, false, false));
+    TRY(check_ptr(fn, "doc_ids", doc_ids, false, false));
+    if (work && (xbc_raw_row_stride > (1 << 22) || z_row_stride > (1 << 22) || grad_y_row_stride > (1 << 22) ||
+                 dxbc_raw_row_stride > (1 << 22) || dz_row_stride > (1 << 22) || dt_raw_row_stride > (1 << 22) ||
+                 ddt_raw_row_stride > (1 << 22)))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: row strides above 4194304 elements are not supported", fn);
+    const size_t need = ssd_mixer_bwd_workspace_size(B, L, H, P, N, G, dtype);
+    if (work && (!workspace || workspace_bytes < need))
+        return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (work && !aligned16(workspace))
+        return fail(SSD_ERR_ALIGNMENT, "%s: workspace=%p is not 16-byte aligned", fn, workspace);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        if (B > 0) {
+            TRY(hip_status(fn, ssd::launch_zero_f32(dA, (size_t)H, s)));
+            TRY(hip_status(fn, ssd::launch_zero_f32(dD, (size_t)H, s)));
+            TRY(hip_status(fn, ssd::launch_zero_f32(ddt_bias, (size_t)H, s)));
+        }
+        TRY(hip_status(fn, ssd::launch_zero_f32(dconv_w, (size_t)C * 4, s)));
+        TRY(hip_status(fn, ssd::launch_zero_f32(dconv_b, (size_t)C, s)));
+        return ok();
+    }
+    // workspace: the recomputed conv output (T) and dt, the conv output's gradient, then the passes' scratch
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    void* xbc = ws;
+    ws += round256((size_t)B * L * C * es);
+    float* dtw = reinterpret_cast<float*>(ws);
+    ws += round256((size_t)B * L * H * 4);
+    float* dxbc = reinterpret_cast<float*>(ws);
+    ws += round256((size_t)B * L * C * 4);
+    void* scan_ws = ws;
+    ws += ssd_chunk_scan_bwd_workspace_size(B, L, H, P, N, G, dtype);
+    void* conv_ws = ws;
+
+    ssd::ConvArgs cv{};
+    cv.B = B; cv.L = L; cv.C = (int)C; cv.H = H; cv.dtype = dtype; cv.act = act;
+    cv.Lb_in = cv.Lb_out = L;
+    cv.raw = xbc_raw; cv.raw_stride = xbc_raw_row_stride;
+    cv.w = conv_w; cv.bias = conv_b;
+    cv.dt_raw = dt_raw; cv.dt_stride = dt_raw_row_stride; cv.dt_bias = dt_bias;
+    cv.doc = doc_ids;
+    cv.out = xbc; cv.out_stride = C;
+    cv.dt_out = dtw;
+    TRY(hip_status(fn, ssd::launch_conv(cv, s)));
+
+    const unsigned char* xb = static_cast<const unsigned char*>(xbc);
+    ssd::BwdArgs a{};
+    a.B = B; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.dtype = dtype;
+    a.x = xb; a.x_stride = C;
+    a.Bm = xb + HP * es; a.B_stride = C;
+    a.Cm = xb + (HP + GN) * es; a.C_stride = C;
+    a.dt = dtw; a.dt_stride = H;
+    a.dt_softplus = 0; a.chain_from_dt = 1; a.dt_bias = nullptr;   // dt = softplus(dt_raw + dt_bias)
+    a.A = A; a.D = D;
+    a.z = z; a.z_stride = z_row_stride;
+    a.doc = doc_ids;
+    a.gy = grad_y; a.gy_stride = grad_y_row_stride;
+    a.dx = dxbc; a.dx_stride = C;
+    a.dB = dxbc + HP; a.dB_stride = C;
+    a.dC = dxbc + HP + GN; a.dC_stride = C;
+    a.ddt = ddt_raw; a.ddt_stride = ddt_raw_row_stride;
+    a.dz = dz; a.dz_stride = dz_row_stride;
+    a.ddt_bias = ddt_bias; a.dA = dA; a.dD = D ? dD : nullptr;
+    if (!D) TRY(hip_status(fn, ssd::launch_zero_f32(dD, (size_t)H, s)));
+    TRY(run_scan_bwd(fn, a, scan_ws, s));
+    return run_conv_bwd(fn, B, L, (int)C, dtype, xbc_raw, xbc_raw_row_stride, conv_w, conv_b, doc_ids, act, dxbc, C,
+                        dxbc_raw, dxbc_raw_row_stride, dconv_w, dconv_b, conv_ws, s);
+}
+
 size_t ssd_s6_workspace_size(int B, int L, int D, int N, int dtype) {
     (void)dtype;
     if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;

@@ -1,0 +1,699 @@
+// bwd.hip -- backward (vector-Jacobian product) of the chunked scan and of the
+// conv for a zero-state prefill, on gfx950.
+//
+// The backward of a prefill from a zero state, given dLoss/dy, recomputing the
+// forward (mojolearn.Mamba3Block docs, backward(): no gradient for a carried
+// state, no final-state cotangent).  Per chunk of 64 tokens and head, with cs
+// the cumulative sum of dt*A restarted at each document start, seg(t) the last
+// document start in the chunk at or before t (none: -1), Hin the state
+// entering the chunk and Gout the adjoint of the state leaving it:
+//
+//   Lm[t,s]  = exp(cs_t - cs_s) for s <= t in the same segment, else 0
+//   M        = (C B^T) o Lm o dt_s            (the chunk's token mixing)
+//   in_t     = exp(cs_t) if seg(t) = -1 else 0  (the share of Hin in h_t)
+//   el_s     = exp(cs_end - cs_s) if s is in the chunk's last segment, else 0
+//   y_t      = (M X + in o (C Hin) + D X)_t * silu(z_t)
+//   H_leave  = [seg(end) = -1] exp(cs_end) Hin + sum_s el_s dt_s B_s x_s^T
+//
+// The backward of these expressions, with dyr = dy o silu(z):
+//   dX  = M^T dyr + D dyr + (el o dt) o (B Gout)
+//   dB  = dG^T C + (el o dt) o (X Gout^T),  dG = (dyr X^T) o Lm o dt_s
+//   dC  = dG B + in o (dyr Hin^T)
+//   ddt = colsum((dyr X^T) o G o Lm) + el o u + A * revcumsum_seg(dcs),
+//         u_s = B_s^T Gout x_s, dcs from the exponents of Lm, in and el
+// Hin and Gout come from two passes over the chunks: the chunk-local states
+// S_c = sum_s el_s dt_s B_s x_s^T and the adjoint inputs dS_c = sum_t in_t
+// C_t dyr_t^T are computed for every chunk in parallel, then scanned in order
+// (Hin) and in reverse order (Gout) per state element.  dB and dC are summed
+// over a group's heads inside one workgroup, and the per-head parameter
+// gradients (dA, dD, dt_bias) go through per-chunk partial sums reduced in a
+// fixed order, so every result is deterministic.
+//
+// All arithmetic is fp32 on the VALU: 64x64 products from LDS tiles, each
+// thread owning a 4x4 block of the output.
+#include <algorithm>
+
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kQ = 64;       // chunk
+constexpr int kBT = 256;     // threads per workgroup
+constexpr int kLD = 68;      // padded row of a 64-wide fp32 tile (16-byte aligned, banks shifted)
+
+__device__ __forceinline__ float ldT(const float* p) { return *p; }
+__device__ __forceinline__ float ldT(const uint16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ float sigmoid_acc(float v) { return 1.0f / (1.0f + expf(-v)); }
+__device__ __forceinline__ float silu_acc(float v) { return v * sigmoid_acc(v); }
+// d silu / dv = s (1 + v (1 - s)), s = sigmoid(v)
+__device__ __forceinline__ float dsilu_acc(float v) {
+    const float s = sigmoid_acc(v);
+    return s * (1.0f + v * (1.0f - s));
+}
+
+// acc[i][j] += sum_{k < K} A(r0 + i, k) * B(k, c0 + j), K a multiple of 4, with
+//   A(i, k) = AT ? A[k * lda + i] : A[i * lda + k]
+//   B(k, j) = BT ? Bm[j * ldb + k] : Bm[k * ldb + j]
+// (all offsets multiples of 4 floats, so every read is one 16-byte LDS read).
+template <bool AT, bool BT>
+__device__ __forceinline__ void mm44(float (&acc)[4][4], const float* A, int lda, int r0, const float* Bm, int ldb,
+                                     int c0, int K) {
+#pragma unroll 2
+    for (int k = 0; k < K; k += 4) {
+        float av[4][4], bv[4][4];   // av[i][kk], bv[kk][j]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (AT) {
+                const float4 v = *reinterpret_cast<const float4*>(A + (k + q) * lda + r0);
+                av[0][q] = v.x; av[1][q] = v.y; av[2][q] = v.z; av[3][q] = v.w;
+            } else {
+                const float4 v = *reinterpret_cast<const float4*>(A + (r0 + q) * lda + k);
+                av[q][0] = v.x; av[q][1] = v.y; av[q][2] = v.z; av[q][3] = v.w;
+            }
+            if (BT) {
+                const float4 v = *reinterpret_cast<const float4*>(Bm + (c0 + q) * ldb + k);
+                bv[0][q] = v.x; bv[1][q] = v.y; bv[2][q] = v.z; bv[3][q] = v.w;
+            } else {
+                const float4 v = *reinterpret_cast<const float4*>(Bm + (k + q) * ldb + c0);
+                bv[q][0] = v.x; bv[q][1] = v.y; bv[q][2] = v.z; bv[q][3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i][q], bv[q][j], acc[i][j]);
+    }
+}
+
+// sum over the 16 lanes that share lane / 16
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+__device__ __forceinline__ float sum64(float v) {
+    v = sum16(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Per-row scalars of one (batch row, head, chunk), computed by one wave: the
+// activated dt, the chain factor d dt / d(dt input), the segmented cumulative
+// sum of dt*A and the last document start at or before each row.
+__device__ __forceinline__ void chunk_rows(const BwdArgs& a, int b, int h, int t0, int Qv, int lane, float& dtv,
+                                           float& chain, float& cs, int& seg) {
+    const bool valid = lane < Qv;
+    const int tg = t0 + lane;
+    dtv = 0.0f;
+    chain = 1.0f;
+    if (valid) {
+        const float r = a.dt[((size_t)b * a.L + tg) * a.dt_stride + h];
+        if (a.dt_softplus) {
+            const float v = r + (a.dt_bias ? a.dt_bias[h] : 0.0f);
+            dtv = softplus_f(v);
+            chain = sigmoid_acc(v);
+        } else {
+            dtv = r;
+            chain = a.chain_from_dt ? -expm1f(-r) : 1.0f;
+        }
+    }
+    const int f = (valid && tg > 0 && a.doc && a.doc[(size_t)b * a.L + tg] != a.doc[(size_t)b * a.L + tg - 1]) ? 1 : 0;
+    cs = dtv * a.A[h];
+    seg = f ? lane : -1;
+    wave_segscan(cs, f, seg);
+}
+
+// ---- pass 1: chunk-local states (y = 0) and adjoint inputs (y = 1)
+template <typename T, int N>
+__global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
+    constexpr int P = 64, LDN = N + 4;
+    __shared__ __attribute__((aligned(16))) float sW[kQ * LDN];
+    __shared__ __attribute__((aligned(16))) float sV[kQ * kLD];
+    __shared__ float s_dt[kQ], s_cs[kQ];
+    __shared__ int s_seg[kQ];
+    const int tid = threadIdx.x, nc = a.nc;
+    const int c = blockIdx.x % nc;
+    const int bh = blockIdx.x / nc;
+    const int h = bh % a.H, b = bh / a.H;
+    const int g = h / (a.H / a.G);
+    const int mode = blockIdx.y;
+    const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
+    const size_t row0 = (size_t)b * a.L + t0;
+    if (tid < 64) {
+        float dtv, chain, cs;
+        int seg;
+        chunk_rows(a, b, h, t0, Qv, tid, dtv, chain, cs, seg);
+        s_dt[tid] = dtv;
+        s_cs[tid] = cs;
+        s_seg[tid] = seg;
+    }
+    __syncthreads();
+    const int end = Qv - 1;
+    const float cs_end = s_cs[end];
+    const int seg_end = s_seg[end];
+    const T* W = static_cast<const T*>(mode == 0 ? a.Bm : a.Cm);
+    const int64_t Ws = mode == 0 ? a.B_stride : a.C_stride;
+    for (int i = tid; i < kQ * N; i += kBT) {
+        const int r = i / N, n = i % N;
+        float v = 0.0f;
+        if (r < Qv) {
+            const float coef = mode == 0 ? (s_seg[r] == seg_end ? expf(cs_end - s_cs[r]) * s_dt[r] : 0.0f)
+                                         : (s_seg[r] < 0 ? expf(s_cs[r]) : 0.0f);
+            v = coef * ldT(W + (row0 + r) * Ws + (size_t)g * N + n);
+        }
+        sW[r * LDN + n] = v;
+    }
+    for (int i = tid; i < kQ * P; i += kBT) {
+        const int r = i / P, p = i % P;
+        float v = 0.0f;
+        if (r < Qv) {
+            if (mode == 0) {
+                v = ldT(static_cast<const T*>(a.x) + (row0 + r) * a.x_stride + (size_t)h * P + p);
+            } else {
+                v = a.gy[(row0 + r) * a.gy_stride + (size_t)h * P + p];
+                if (a.z) v *= silu_acc(ldT(static_cast<const T*>(a.z) + (row0 + r) * a.z_stride + (size_t)h * P + p));
+            }
+        }
+        sV[r * kLD + p] = v;
+    }
+    __syncthreads();
+    const int rb = tid >> 4, cb = tid & 15;
+    if (4 * rb < N) {
+        float acc[4][4] = {};
+        mm44<true, false>(acc, sW, LDN, 4 * rb, sV, kLD, 4 * cb, kQ);
+        float* out = (mode == 0 ? a.S : a.dS) + (((size_t)b * a.H + h) * nc + c) * N * P;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(out + (size_t)(4 * rb + i) * P + 4 * cb) =
+                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+    if (mode == 0 && tid == 0) a.dec[((size_t)b * a.H + h) * nc + c] = seg_end < 0 ? expf(cs_end) : 0.0f;
+}
+
+// ---- pass 2: states entering each chunk (y = 0, in order) and adjoints of
+// the states leaving each chunk (y = 1, in reverse order), per state element
+template <int N>
+__global__ __launch_bounds__(kBT) void ssd_bwd_pass_kernel(BwdArgs a) {
+    constexpr int NP = N * 64;
+    constexpr int per = NP / kBT;
+    const int nc = a.nc;
+    const int bh = blockIdx.x / per;
+    const int e = (blockIdx.x % per) * kBT + threadIdx.x;
+    const float* dec = a.dec + (size_t)bh * nc;
+    if (blockIdx.y == 0) {
+        float* S = a.S + (size_t)bh * nc * NP + e;
+        float hs = 0.0f;
+        for (int c = 0; c < nc; ++c) {
+            const float v = S[(size_t)c * NP];
+            S[(size_t)c * NP] = hs;
+            hs = fmaf(dec[c], hs, v);
+        }
+    } else {
+        float* dS = a.dS + (size_t)bh * nc * NP + e;
+        float gs = 0.0f;
+        for (int c = nc - 1; c >= 0; --c) {
+            const float v = dS[(size_t)c * NP];
+            dS[(size_t)c * NP] = gs;
+            gs = fmaf(dec[c], gs, v);
+        }
+    }
+}
+
+// ---- pass 3: every gradient of one (batch row, group, chunk)
+template <typename T, int N>
+__global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
+    constexpr int P = 64, LDN = N + 4;
+    __shared__ __attribute__((aligned(16))) float sB[kQ * LDN];
+    __shared__ __attribute__((aligned(16))) float sC[kQ * LDN];
+    __shared__ __attribute__((aligned(16))) float sG[kQ * kLD];
+    __shared__ __attribute__((aligned(16))) float sX[kQ * kLD];
+    __shared__ __attribute__((aligned(16))) float sDy[kQ * kLD];
+    __shared__ __attribute__((aligned(16))) float sM[kQ * kLD];
+    __shared__ __attribute__((aligned(16))) float sDG[kQ * kLD];
+    __shared__ __attribute__((aligned(16))) float sHin[N * kLD];
+    __shared__ __attribute__((aligned(16))) float sGo[N * kLD];
+    __shared__ float s_dt[kQ], s_cs[kQ], s_chain[kQ], s_dcs[kQ], s_ddt[kQ], s_u[kQ];
+    __shared__ int s_seg[kQ];
+    __shared__ float s_red[2][4][kQ];
+    __shared__ float s_scal[2][4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rb = tid >> 4, cb = tid & 15;
+    const int nc = a.nc;
+    const int c = blockIdx.x % nc;
+    const int bg = blockIdx.x / nc;
+    const int g = bg % a.G, b = bg / a.G;
+    const int hpg = a.H / a.G;
+    const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
+    const size_t row0 = (size_t)b * a.L + t0;
+    const bool nact = 4 * cb < N;                  // owns a 4x4 block of a [64][N] output
+
+    // the group's B and C rows (fp32, zero past the valid rows) and G = C B^T
+    for (int i = tid; i < kQ * N; i += kBT) {
+        const int r = i / N, n = i % N;
+        float bv = 0.0f, cv = 0.0f;
+        if (r < Qv) {
+            bv = ldT(static_cast<const T*>(a.Bm) + (row0 + r) * a.B_stride + (size_t)g * N + n);
+            cv = ldT(static_cast<const T*>(a.Cm) + (row0 + r) * a.C_stride + (size_t)g * N + n);
+        }
+        sB[r * LDN + n] = bv;
+        sC[r * LDN + n] = cv;
+    }
+    __syncthreads();
+    {
+        float acc[4][4] = {};
+        mm44<false, true>(acc, sC, LDN, 4 * rb, sB, LDN, 4 * cb, N);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(sG + (4 * rb + i) * kLD + 4 * cb) =
+                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+    float aB[4][4] = {}, aC[4][4] = {};            // dB, dC of the group, summed over its heads
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const float Ah = a.A[h], Dh = a.D ? a.D[h] : 0.0f;
+        const size_t bhc = ((size_t)b * a.H + h) * nc + c;
+        if (wave == 0) {
+            float dtv, chain, cs;
+            int seg;
+            chunk_rows(a, b, h, t0, Qv, lane, dtv, chain, cs, seg);
+            s_dt[lane] = dtv;
+            s_cs[lane] = cs;
+            s_seg[lane] = seg;
+            s_chain[lane] = chain;
+            s_dcs[lane] = 0.0f;
+            s_ddt[lane] = 0.0f;
+            s_u[lane] = 0.0f;
+        }
+        for (int i = tid; i < kQ * P; i += kBT) {
+            const int r = i / P, p = i % P;
+            float xv = 0.0f, dy = 0.0f;
+            if (r < Qv) {
+                xv = ldT(static_cast<const T*>(a.x) + (row0 + r) * a.x_stride + (size_t)h * P + p);
+                dy = a.gy[(row0 + r) * a.gy_stride + (size_t)h * P + p];
+                if (a.z) dy *= silu_acc(ldT(static_cast<const T*>(a.z) + (row0 + r) * a.z_stride + (size_t)h * P + p));
+            }
+            sX[r * kLD + p] = xv;
+            sDy[r * kLD + p] = dy;
+        }
+        float hg = 0.0f;                           // <Gout, Hin> partial
+        for (int i = tid; i < N * P; i += kBT) {
+            const int n = i / P, p = i % P;
+            const float hv = a.S[bhc * N * P + i], gv = a.dS[bhc * N * P + i];
+            sHin[n * kLD + p] = hv;
+            sGo[n * kLD + p] = gv;
+            hg = fmaf(hv, gv, hg);
+        }
+        __syncthreads();
+
+        const int end = Qv - 1;
+        const float cs_end = s_cs[end];
+        const int seg_end = s_seg[end];
+        float in_r[4], el_r[4], dt_r[4];
+        int seg_r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * rb + i;
+            seg_r[i] = s_seg[t];
+            dt_r[i] = s_dt[t];
+            in_r[i] = (t < Qv && seg_r[i] < 0) ? expf(s_cs[t]) : 0.0f;
+            el_r[i] = (t < Qv && seg_r[i] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
+        }
+        // M = G o Lm o dt_s
+        auto lmask = [&](int i, int j) {
+            const int t = 4 * rb + i, s = 4 * cb + j;
+            return (s <= t && s_seg[s] == seg_r[i]) ? expf(s_cs[t] - s_cs[s]) : 0.0f;
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * rb + i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s = 4 * cb + j;
+                sM[t * kLD + s] = sG[t * kLD + s] * lmask(i, j) * s_dt[s];
+            }
+        }
+        __syncthreads();
+
+        // y (before the gate) = M X + in o (C Hin) + D X; dz; the in_t share of dcs; dD
+        {
+            float y1[4][4] = {}, y2[4][4] = {};
+            mm44<false, false>(y1, sM, kLD, 4 * rb, sX, kLD, 4 * cb, kQ);
+            mm44<false, false>(y2, sC, LDN, 4 * rb, sHin, kLD, 4 * cb, N);
+            float rin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pD = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * rb + i;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = 4 * cb + j;
+                    const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
+                    rin[i] = fmaf(y2[i][j], dy, rin[i]);
+                    pD = fmaf(dy, xv, pD);
+                    if (a.dz && t < Qv) {
+                        const size_t o = (row0 + t) * a.z_stride + (size_t)h * P + p;
+                        const float zv = ldT(static_cast<const T*>(a.z) + o);
+                        const float yr = y1[i][j] + in_r[i] * y2[i][j] + Dh * xv;
+                        a.dz[(row0 + t) * a.dz_stride + (size_t)h * P + p] =
+                            a.gy[(row0 + t) * a.gy_stride + (size_t)h * P + p] * yr * dsilu_acc(zv);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = sum16(rin[i]);
+                if (cb == 0) s_dcs[4 * rb + i] += in_r[i] * v;
+            }
+            pD = sum64(pD);
+            hg = sum64(hg);
+            if (lane == 0) {
+                s_scal[0][wave] = pD;
+                s_scal[1][wave] = hg;
+            }
+        }
+
+        // dM = dyr X^T -> dG, the Lm share of dcs, the direct share of ddt
+        {
+            float dm[4][4] = {};
+            mm44<false, true>(dm, sDy, kLD, 4 * rb, sX, kLD, 4 * cb, P);
+            float rowT[4] = {0.0f, 0.0f, 0.0f, 0.0f}, colT[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float colD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * rb + i;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 4 * cb + j;
+                    const float tt = dm[i][j] * sM[t * kLD + s];
+                    const float lm = lmask(i, j);
+                    rowT[i] += tt;
+                    colT[j] += tt;
+                    colD[j] = fmaf(dm[i][j], sG[t * kLD + s] * lm, colD[j]);
+                    sDG[t * kLD + s] = dm[i][j] * lm * s_dt[s];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = sum16(rowT[i]);
+                if (cb == 0) s_dcs[4 * rb + i] += v;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = colT[j], w = colD[j];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                w += __shfl_xor(w, 16);
+                w += __shfl_xor(w, 32);
+                if (lane < 16) {
+                    s_red[0][wave][4 * cb + j] = v;
+                    s_red[1][wave][4 * cb + j] = w;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            s_dcs[tid] -= (s_red[0][0][tid] + s_red[0][1][tid]) + (s_red[0][2][tid] + s_red[0][3][tid]);
+            s_ddt[tid] += (s_red[1][0][tid] + s_red[1][1][tid]) + (s_red[1][2][tid] + s_red[1][3][tid]);
+        }
+
+        // dX = M^T dyr + D dyr + (el o dt) o (B Gout); u_s = (B Gout)_s . x_s
+        {
+            float d1[4][4] = {}, bgo[4][4] = {};
+            mm44<true, false>(d1, sM, kLD, 4 * rb, sDy, kLD, 4 * cb, kQ);
+            mm44<false, false>(bgo, sB, LDN, 4 * rb, sGo, kLD, 4 * cb, N);
+            float ru[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * rb + i;
+                const float we = el_r[i] * dt_r[i];
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = 4 * cb + j;
+                    ru[i] = fmaf(bgo[i][j], sX[s * kLD + p], ru[i]);
+                    o[j] = d1[i][j] + Dh * sDy[s * kLD + p] + we * bgo[i][j];
+                }
+                if (s < Qv)
+                    *reinterpret_cast<float4*>(a.dx + (row0 + s) * a.dx_stride + (size_t)h * P + 4 * cb) =
+                        make_float4(o[0], o[1], o[2], o[3]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = sum16(ru[i]);
+                if (cb == 0) s_u[4 * rb + i] = v;
+            }
+        }
+        // dB += dG^T C + (el o dt) o (X Gout^T);  dC += dG B + in o (dyr Hin^T)
+        if (nact) {
+            mm44<true, false>(aB, sDG, kLD, 4 * rb, sC, LDN, 4 * cb, kQ);
+            mm44<false, false>(aC, sDG, kLD, 4 * rb, sB, LDN, 4 * cb, kQ);
+            float xg[4][4] = {}, dh[4][4] = {};
+            mm44<false, true>(xg, sX, kLD, 4 * rb, sGo, kLD, 4 * cb, P);
+            mm44<false, true>(dh, sDy, kLD, 4 * rb, sHin, kLD, 4 * cb, P);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float we = el_r[i] * dt_r[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    aB[i][j] = fmaf(we, xg[i][j], aB[i][j]);
+                    aC[i][j] = fmaf(in_r[i], dh[i][j], aC[i][j]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // per row: the el share of dcs and ddt, the reverse segmented cumsum of
+        // dcs into ddt and dA, the chain to the dt input, the partial sums
+        if (wave == 0) {
+            const int t = lane;
+            const bool valid = t < Qv;
+            const float el = (valid && s_seg[t] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
+            const float dtv = s_dt[t], u = s_u[t];
+            const float wu = el * dtv * u;
+            float dcs = s_dcs[t] - wu;
+            const float sum_wu = sum64(wu);
+            const float hgt = (s_scal[1][0] + s_scal[1][1]) + (s_scal[1][2] + s_scal[1][3]);
+            if (t == end) dcs += sum_wu + (seg_end < 0 ? expf(cs_end) : 0.0f) * hgt;
+            float ddt = s_ddt[t] + el * u;
+            // segments in reverse order start where the original row ends one
+            const int fend = (t == kQ - 1 || s_seg[t + 1 < kQ ? t + 1 : t] == t + 1) ? 1 : 0;
+            float vr = __shfl(dcs, 63 - lane);
+            const int fr = __shfl(fend, 63 - lane);
+            int sr = fr ? lane : -1;
+            wave_segscan(vr, fr, sr);
+            const float rc = __shfl(vr, 63 - lane);
+            ddt = fmaf(Ah, rc, ddt);
+            const float pA = sum64(valid ? dtv * rc : 0.0f);
+            const float dout = ddt * s_chain[t];
+            const float pBias = sum64(valid ? dout : 0.0f);
+            if (valid) a.ddt[(row0 + t) * a.ddt_stride + h] = dout;
+            if (lane == 0) {
+                const size_t bc = (size_t)b * nc + c;
+                const size_t nbc = (size_t)a.B * nc;
+                a.part[(0 * nbc + bc) * a.H + h] = pA;
+                a.part[(1 * nbc + bc) * a.H + h] = (s_scal[0][0] + s_scal[0][1]) + (s_scal[0][2] + s_scal[0][3]);
+                a.part[(2 * nbc + bc) * a.H + h] = pBias;
+            }
+        }
+        __syncthreads();
+    }
+    if (nact) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rb + i;
+            if (r < Qv) {
+                *reinterpret_cast<float4*>(a.dB + (row0 + r) * a.dB_stride + (size_t)g * N + 4 * cb) =
+                    make_float4(aB[i][0], aB[i][1], aB[i][2], aB[i][3]);
+                *reinterpret_cast<float4*>(a.dC + (row0 + r) * a.dC_stride + (size_t)g * N + 4 * cb) =
+                    make_float4(aC[i][0], aC[i][1], aC[i][2], aC[i][3]);
+            }
+        }
+    }
+}
+
+// Fixed-order sums of the per-chunk partials part[q][i][k] (q < 3, i < rows,
+// k < per) into o_q[k].
+__global__ __launch_bounds__(kBT) void ssd_bwd_reduce_kernel(const float* part, int rows, int per, float* o0,
+                                                             float* o1, float* o2) {
+    const int j = blockIdx.x * kBT + threadIdx.x;
+    if (j >= 3 * per) return;
+    const int q = j / per, k = j % per;
+    float s = 0.0f;
+    for (int i = 0; i < rows; ++i) s += part[((size_t)q * rows + i) * per + k];
+    float* o = q == 0 ? o0 : (q == 1 ? o1 : o2);
+    if (o) o[k] = s;
+}
+
+__global__ __launch_bounds__(kBT) void ssd_zero_kernel(float* p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * kBT + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ---- conv backward: one channel per thread, 64 tokens per workgroup
+template <typename T>
+__global__ __launch_bounds__(kBT) void ssd_conv_bwd_kernel(ConvBwdArgs a) {
+    constexpr int K = 4, TC = 64, TE = TC + K - 1;
+    __shared__ float s_dp[TE][kBT];                // d(pre-activation) of rows t0 .. t0 + TE - 1
+    __shared__ int s_start[TE + K];                // document starts at rows t0 - 3 .. t0 + TE - 1
+    const int C = a.C, L = a.L, tid = threadIdx.x;
+    const int nblk = (C + kBT - 1) / kBT;
+    const int blk = blockIdx.x % nblk;
+    const int tc = (blockIdx.x / nblk) % a.ntc;
+    const int b = blockIdx.x / (nblk * a.ntc);
+    const int c = blk * kBT + tid;
+    const bool on = c < C;
+    const int cc = min(c, C - 1);
+    const int t0 = tc * TC, t1 = min(t0 + TC, L), tE = min(t0 + TE, L);
+    const int32_t* docb = a.doc ? a.doc + (size_t)b * L : nullptr;
+    for (int i = tid; i < TE + K - 1; i += kBT) {
+        const int t = t0 - (K - 1) + i;
+        s_start[i] = (docb && t > 0 && t < L && docb[t] != docb[t - 1]) ? 1 : 0;
+    }
+    __syncthreads();
+    auto start_at = [&](int t) { return s_start[t - t0 + K - 1]; };
+    float w[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = a.w[(size_t)cc * K + k];
+    const float bias = a.bias ? a.bias[cc] : 0.0f;
+    const T* rawb = static_cast<const T*>(a.raw) + (size_t)b * L * a.raw_stride + cc;
+    const float* doutb = a.dout + (size_t)b * L * a.dout_stride + cc;
+    // window of raw rows t-3 .. t (0 outside [0, L))
+    float win[K];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+        const int t = t0 - (K - 1) + k;
+        win[k + 1] = (t >= 0) ? ldT(rawb + (size_t)t * a.raw_stride) : 0.0f;
+    }
+    float gw[K] = {0.0f, 0.0f, 0.0f, 0.0f}, gb = 0.0f;
+    for (int t = t0; t < tE; ++t) {
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
+        win[K - 1] = ldT(rawb + (size_t)t * a.raw_stride);
+        // tap k reads row t - 3 + k: valid if no document starts in (t - 3 + k, t]
+        float pre = bias;
+        bool ok[K];
+        bool cut = false;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {
+            const int tau = t - (K - 1) + k;
+            ok[k] = !cut && tau >= 0;
+            if (k > 0 && tau >= 0 && start_at(tau)) cut = true;   // a start at tau cuts taps before it
+            if (ok[k]) pre = fmaf(w[k], win[k], pre);
+        }
+        const float go = doutb[(size_t)t * a.dout_stride];
+        const float gp = a.act == 0 ? go * dsilu_acc(pre) : go;
+        s_dp[t - t0][tid] = gp;
+        if (t < t1) {
+            gb += gp;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (ok[k]) gw[k] = fmaf(gp, win[k], gw[k]);
+        }
+    }
+    // draw[s] = sum_k w[k] dpre[s + 3 - k] over the taps that read row s
+    for (int s = t0; s < t1; ++s) {
+        float acc = 0.0f;
+        bool cut = false;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {
+            const int tp = s + (K - 1) - k;                  // the token whose tap k reads row s
+            if (tp > s && tp < L && start_at(tp)) cut = true;
+            if (!cut && tp < L) acc = fmaf(w[k], s_dp[tp - t0][tid], acc);
+        }
+        if (on) a.draw[((size_t)b * L + s) * a.draw_stride + c] = acc;
+    }
+    if (on) {
+        float* pp = a.part + (((size_t)b * a.ntc + tc) * C + c) * (K + 1);
+#pragma unroll
+        for (int k = 0; k < K; ++k) pp[k] = gw[k];
+        pp[K] = gb;
+    }
+}
+
+// dw[c][k] and dbias[c] from the per-chunk partials [rows][C][5]
+__global__ __launch_bounds__(kBT) void ssd_conv_bwd_reduce_kernel(const float* part, int rows, int C, float* dw,
+                                                                  float* dbias) {
+    const int j = blockIdx.x * kBT + threadIdx.x;
+    if (j >= C * 5) return;
+    float s = 0.0f;
+    for (int i = 0; i < rows; ++i) s += part[(size_t)i * C * 5 + j];
+    const int c = j / 5, k = j % 5;
+    if (k < 4) dw[(size_t)c * 4 + k] = s;
+    else if (dbias) dbias[c] = s;
+}
+
+template <typename T, int N>
+hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t stream) {
+    const int bhc = a.B * a.H * a.nc;
+    hipLaunchKernelGGL((ssd_bwd_sums_kernel<T, N>), dim3(bhc, 2), dim3(kBT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ssd_bwd_pass_kernel<N>), dim3(a.B * a.H * (N * 64 / kBT), 2), dim3(kBT), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3(a.B * a.G * a.nc), dim3(kBT), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((3 * a.H + kBT - 1) / kBT), dim3(kBT), 0, stream, a.part,
+                       a.B * a.nc, a.H, a.dA, a.dD, a.ddt_bias);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+    switch (a.N) {
+        case 16: return launch_bwd_n<T, 16>(a, stream);
+        case 32: return launch_bwd_n<T, 32>(a, stream);
+        case 64: return launch_bwd_n<T, 64>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_bytes(int B, int L, int H, int P, int N) {
+    const size_t nc = (size_t)(L + kQ - 1) / kQ;
+    const size_t st = (size_t)B * H * nc * N * P * sizeof(float);
+    auto r256 = [](size_t n) { return (n + 255) / 256 * 256; };
+    return 2 * r256(st) + r256((size_t)B * H * nc * sizeof(float)) + r256(3 * (size_t)B * nc * H * sizeof(float));
+}
+
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.L == 0) return hipSuccess;
+    return a.dtype == 0 ? launch_bwd_t<float>(a, stream) : launch_bwd_t<uint16_t>(a, stream);
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream) {
+    if (!p || n == 0) return hipSuccess;
+    hipLaunchKernelGGL(ssd_zero_kernel, dim3((unsigned)((n + kBT - 1) / kBT)), dim3(kBT), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+size_t conv_bwd_workspace_bytes(int B, int L, int C) {
+    const size_t ntc = (size_t)(L + 63) / 64;
+    return (size_t)B * ntc * C * 5 * sizeof(float);
+}
+
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.L == 0) return hipSuccess;
+    const int nblk = (a.C + kBT - 1) / kBT;
+    if (a.dtype == 0)
+        hipLaunchKernelGGL((ssd_conv_bwd_kernel<float>), dim3(a.B * a.ntc * nblk), dim3(kBT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ssd_conv_bwd_kernel<uint16_t>), dim3(a.B * a.ntc * nblk), dim3(kBT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ssd_conv_bwd_reduce_kernel, dim3((a.C * 5 + kBT - 1) / kBT), dim3(kBT), 0, stream, a.part,
+                       a.B * a.ntc, a.C, a.dw, a.dbias);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -83,6 +83,51 @@ struct S6Args {
     float* hloc; float* sdt; float* h0;
 };
 
+// Backward (VJP) of the chunked scan for a zero initial state.  Inputs as in
+// ScanArgs (dt fp32: activated, or raw with dt_softplus); gy = dLoss/dy.
+// Outputs fp32; dB / dC are summed over a group's heads.
+struct BwdArgs {
+    int B, L, H, P, N, G, dtype;
+    const void* x; int64_t x_stride;
+    const void* Bm; int64_t B_stride;
+    const void* Cm; int64_t C_stride;
+    const float* dt; int64_t dt_stride;
+    // dt_softplus = 1: dt is raw and dt := softplus(dt + dt_bias); ddt is then
+    // with respect to the raw value.  chain_from_dt = 1 (dt_softplus = 0): dt
+    // is softplus(v) of some v and ddt is with respect to v, using
+    // softplus'(v) = 1 - exp(-dt).
+    int dt_softplus, chain_from_dt; const float* dt_bias;
+    const float* A; const float* D;
+    const void* z; int64_t z_stride;
+    const int32_t* doc;
+    const float* gy; int64_t gy_stride;
+    float* dx; int64_t dx_stride;
+    float* dB; int64_t dB_stride;
+    float* dC; int64_t dC_stride;
+    float* ddt; int64_t ddt_stride;
+    float* dz; int64_t dz_stride;
+    float* ddt_bias; float* dA; float* dD;   // [H] or null
+    // workspace: nc chunks of 64 tokens
+    int nc;
+    float* S;      // [B][H][nc][N][P]  chunk-local states, then the state entering each chunk
+    float* dS;     // [B][H][nc][N][P]  chunk adjoint inputs, then the adjoint of the state leaving each chunk
+    float* dec;    // [B][H][nc]        decay across each chunk (0 where a document starts in it)
+    float* part;   // [3][B * nc][H]    per-chunk partial sums of dA, dD and ddt_bias
+};
+
+// Backward of the conv (zero conv state): dout = dLoss/d(conv output) fp32.
+struct ConvBwdArgs {
+    int B, L, C, dtype, act;
+    const void* raw; int64_t raw_stride;
+    const float* w; const float* bias;
+    const int32_t* doc;
+    const float* dout; int64_t dout_stride;
+    float* draw; int64_t draw_stride;
+    float* dw; float* dbias;               // [C][4], [C] (dbias may be null)
+    int ntc;                               // token chunks of 64
+    float* part;                           // [B * ntc][C][5] per-chunk partial sums of dw and dbias
+};
+
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // Sequence split chosen for these sizes (1 = none) and its superchunk length.
@@ -101,6 +146,13 @@ hipError_t launch_copy_rows(const void* src, int64_t src_row_stride, int64_t src
 size_t step_lds_bytes(int H, int P, int N, int G);
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream);
+
+size_t scan_bwd_workspace_bytes(int B, int L, int H, int P, int N);
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
+size_t conv_bwd_workspace_bytes(int B, int L, int C);
+// Zero fill of n floats by a kernel (no memset node).
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t stream);
 void s6_split(int B, int L, int D, int& K, int& S);
 size_t s6_workspace_bytes(int B, int L, int D, int N);
 

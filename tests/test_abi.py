@@ -275,3 +275,60 @@ def test_s6_workspace_size(lib):
     assert n > 0 and n % 4 == 0
     # hloc + sdt grow with N only through hloc; the initial-state copy is B*D*N floats
     assert f(5, 8192, 2048, 32, 1) > n
+
+
+def bwd_args(**over):
+    a = dict(B=2, L=128, H=8, P=64, N=64, G=2, chunk=64, dtype=1, x=FAKE, xs=512, Bm=FAKE, bs=128, Cm=FAKE, cs=128,
+             dt=FAKE, dts=8, sp=1, db=None, A=FAKE, D=None, z=None, zs=0, doc=None, gy=FAKE, gys=512, dx=FAKE,
+             dxs=512, dB=FAKE, dBs=128, dC=FAKE, dCs=128, ddt=FAKE, ddts=8, ddb=None, dA=FAKE, dD=None, dz=None, dzs=0,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return a
+
+
+def call_bwd(lib, a):
+    f = lib.ssd_chunk_scan_bwd
+    I, P, I64, SZ = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    f.restype = I
+    f.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P, I64, P, P, I64, P, I64, P,
+                  I64, P, I64, P, I64, P, P, P, P, I64, P, SZ, P]
+    return f(a["B"], a["L"], a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"], a["x"], a["xs"], a["Bm"], a["bs"],
+             a["Cm"], a["cs"], a["dt"], a["dts"], a["sp"], a["db"], a["A"], a["D"], a["z"], a["zs"], a["doc"], a["gy"],
+             a["gys"], a["dx"], a["dxs"], a["dB"], a["dBs"], a["dC"], a["dCs"], a["ddt"], a["ddts"], a["ddb"], a["dA"],
+             a["dD"], a["dz"], a["dzs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(N=128), 3, "N=128 is not supported by the backward"),
+    (dict(chunk=32), 3, "chunk=32"),
+    (dict(dtype=5), 3, "dtype=5"),
+    (dict(gy=None), 1, "grad_y is NULL"),
+    (dict(dx=None), 1, "dx is NULL"),
+    (dict(ddt=None), 1, "ddt is NULL"),
+    (dict(dA=None), 1, "dA is NULL"),
+    (dict(dxs=514), 4, "dx row stride 514"),
+    (dict(dBs=100), 2, "dB row stride 100"),
+    (dict(dz=FAKE, dzs=512), 1, "dz is given but z is NULL"),
+    (dict(ws=None, wsb=0), 5, "workspace_bytes=0"),
+    (dict(ws=MIS), 4, "workspace=.*not 16-byte aligned"),
+    (dict(sp=3), 3, "dt_softplus=3"),
+])
+def test_scan_bwd_refusals(lib, over, status, needle):
+    st = call_bwd(lib, bwd_args(**over))
+    assert st == status, (st, lib.ssd_last_error())
+    assert re.search(needle, lib.ssd_last_error().decode()), lib.ssd_last_error()
+
+
+def test_bwd_workspace_sizes(lib):
+    I, SZ = ctypes.c_int, ctypes.c_size_t
+    for nm in ("ssd_chunk_scan_bwd_workspace_size", "ssd_conv_bwd_workspace_size", "ssd_mixer_bwd_workspace_size"):
+        getattr(lib, nm).restype = SZ
+        getattr(lib, nm).argtypes = [I] * 7
+    s = lib.ssd_chunk_scan_bwd_workspace_size(5, 8192, 32, 64, 64, 8, 1)
+    # two [B][H][L/64][N][P] fp32 state arrays dominate
+    assert s >= 2 * 5 * 32 * 128 * 64 * 64 * 4
+    c = lib.ssd_conv_bwd_workspace_size(5, 8192, 32, 64, 64, 8, 1)
+    assert c == 5 * 128 * 3072 * 5 * 4
+    m = lib.ssd_mixer_bwd_workspace_size(5, 8192, 32, 64, 64, 8, 1)
+    assert m >= s + c + 5 * 8192 * 3072 * (2 + 4)
+    assert lib.ssd_chunk_scan_bwd_workspace_size(0, 8192, 32, 64, 64, 8, 1) == 0
