@@ -15,8 +15,9 @@ step; "roofline" = the scan call's algorithmic bytes / its average duration
 "extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
 two kernels behind one call; fused: the conv computed inside the scan
 kernels), the other workloads (packed documents, the large layer, the decode
-step), the chunk-resume decode (ssd_resume_fwd) on the decode workload, and
-the Mamba-1 selective scan (ssd_s6_scan_fwd) priced against the VALU rate.
+step), the chunk-resume decode (ssd_resume_fwd) on the decode workload, the
+Mamba-1 selective scan (ssd_s6_scan_fwd) priced against the VALU rate, and
+the backward of the mixer (ssd_mixer_bwd) on the Mini-K3 batch.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -362,6 +363,48 @@ def s6_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
             "algorithmic_bytes": nb, "workspace_bytes": ws_bytes}
 
 
+def bwd_flops(wl):
+    """Algorithmic fp32 flops of one ssd_mixer_bwd's scan passes: per (batch row, head, 64-token chunk) the chunk
+    kernel's products (M X, C Hin, dyr X^T, M^T dyr, B Gout: 64x64x64 or 64xNx64 each, and the four 64x64xN
+    products of dB and dC) and the first pass's two 64xNx64 products, plus C B^T once per group."""
+    nc = (wl.L + 63) // 64
+    Q, P, N = 64, wl.P, wl.N
+    per_bhc = 3 * Q * Q * P + 2 * Q * N * P + 4 * Q * Q * N + 2 * Q * N * P
+    per_bgc = Q * Q * N
+    return 2.0 * (wl.B * wl.H * nc * per_bhc + wl.B * wl.G * nc * per_bgc)
+
+
+def bwd_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
+    """ssd_mixer_bwd (conv recompute, the scan's backward passes, the conv's backward) on one batch."""
+    dev = "cuda"
+    prm = synth.params(wl, seed, device=dev)
+    raw = synth.raw_inputs(wl, seed, device=dev)
+    g = torch.Generator(device=dev).manual_seed(seed + 7)
+    gy = torch.randn(wl.B, wl.L, wl.H * wl.P, generator=g, device=dev)
+    code = ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32
+    ws = torch.empty(ssd.ssd_mixer_bwd_workspace_size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, code), dtype=torch.uint8,
+                     device=dev)
+    t = Timer(torch)
+
+    def one(timed):
+        f = lambda: ssd.ssd_mixer_bwd(raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], gy, H=wl.H, P=wl.P,
+                                      N=wl.N, G=wl.G, dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], workspace=ws)
+        t.around(f) if timed else f()
+
+    for _ in range(warmup):
+        one(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        one(True)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    fl = bwd_flops(wl)
+    return {"workload": wl.name + " (ssd_mixer_bwd: conv recompute + scan backward + conv backward)",
+            "ms_per_step": ms, "value": wl.B * wl.L * wl.H / (ms * 1e-3), "unit": "head-tokens/s",
+            "scan_bwd_TFLOPs_over_call": fl / (ms * 1e-3) / 1e12, "algorithmic_flops": fl,
+            "workspace_bytes": ws.numel()}
+
+
 def cpu_baseline(synth, wl, rows):
     """The fp64 oracle (conv + scan, as it stands) on `rows` batch rows of the workload."""
     import oracle
@@ -445,6 +488,7 @@ def main():
                        "unit": "head-tokens/s (B*H per step)"})
         extras.append(resume_bench(ssd, synth, torch, dw, args.warmup))
         extras.append(s6_bench(ssd, synth, torch, synth.WORKLOADS["s6_bf16"], args.steps, args.warmup))
+        extras.append(bwd_bench(ssd, synth, torch, wl, max(5, args.steps // 5), args.warmup))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -132,58 +132,75 @@ __device__ __forceinline__ void chunk_rows(const BwdArgs& a, int b, int h, int t
     wave_segscan(cs, f, seg);
 }
 
-// ---- pass 1: chunk-local states (y = 0) and adjoint inputs (y = 1)
-template <typename T, int N>
+// A z pointer that is always safe to read: without a gate, gy's rows stand in
+// (same row positions in bytes, the values are discarded).
+template <typename T>
+__device__ __forceinline__ const T* z_or_gy(const BwdArgs& a, int64_t& stride) {
+    if (a.z) {
+        stride = a.z_stride;
+        return static_cast<const T*>(a.z);
+    }
+    stride = a.gy_stride * (int64_t)(sizeof(float) / sizeof(T));
+    return reinterpret_cast<const T*>(a.gy);
+}
+
+// ---- pass 1: chunk-local states (MODE 0) and adjoint inputs (MODE 1)
+template <typename T, int N, int MODE>
 __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
     constexpr int P = 64, LDN = N + 4;
     __shared__ __attribute__((aligned(16))) float sW[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sV[kQ * kLD];
-    __shared__ float s_dt[kQ], s_cs[kQ];
-    __shared__ int s_seg[kQ];
+    __shared__ float s_coef[kQ];
     const int tid = threadIdx.x, nc = a.nc;
     const int c = blockIdx.x % nc;
     const int bh = blockIdx.x / nc;
     const int h = bh % a.H, b = bh / a.H;
     const int g = h / (a.H / a.G);
-    const int mode = blockIdx.y;
+    constexpr int mode = MODE;
     const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
     const size_t row0 = (size_t)b * a.L + t0;
+    // per row: mode 0, the weight el_s dt_s of token s in the chunk's end state;
+    // mode 1, the share in_t of the entering state in h_t
     if (tid < 64) {
         float dtv, chain, cs;
         int seg;
         chunk_rows(a, b, h, t0, Qv, tid, dtv, chain, cs, seg);
-        s_dt[tid] = dtv;
-        s_cs[tid] = cs;
-        s_seg[tid] = seg;
+        const int end = Qv - 1;
+        const float cs_end = __shfl(cs, end);
+        const int seg_end = __shfl(seg, end);
+        float coef = 0.0f;
+        if (tid < Qv) coef = mode == 0 ? (seg == seg_end ? expf(cs_end - cs) * dtv : 0.0f) : (seg < 0 ? expf(cs) : 0.0f);
+        s_coef[tid] = coef;
+        if (mode == 0 && tid == 0) a.dec[((size_t)b * a.H + h) * nc + c] = seg_end < 0 ? expf(cs_end) : 0.0f;
     }
-    __syncthreads();
-    const int end = Qv - 1;
-    const float cs_end = s_cs[end];
-    const int seg_end = s_seg[end];
     const T* W = static_cast<const T*>(mode == 0 ? a.Bm : a.Cm);
     const int64_t Ws = mode == 0 ? a.B_stride : a.C_stride;
-    for (int i = tid; i < kQ * N; i += kBT) {
-        const int r = i / N, n = i % N;
-        float v = 0.0f;
-        if (r < Qv) {
-            const float coef = mode == 0 ? (s_seg[r] == seg_end ? expf(cs_end - s_cs[r]) * s_dt[r] : 0.0f)
-                                         : (s_seg[r] < 0 ? expf(s_cs[r]) : 0.0f);
-            v = coef * ldT(W + (row0 + r) * Ws + (size_t)g * N + n);
-        }
-        sW[r * LDN + n] = v;
+    float wv[kQ * N / kBT], vv[kQ * P / kBT], zq[kQ * P / kBT];
+    int64_t zs;
+    const T* zp = z_or_gy<T>(a, zs);
+#pragma unroll
+    for (int q = 0; q < kQ * N / kBT; ++q) {
+        const int i = tid + q * kBT, r = i / N, n = i % N;
+        wv[q] = ldT(W + (row0 + min(r, Qv - 1)) * Ws + (size_t)g * N + n);   // coef is 0 past Qv
     }
-    for (int i = tid; i < kQ * P; i += kBT) {
-        const int r = i / P, p = i % P;
-        float v = 0.0f;
-        if (r < Qv) {
-            if (mode == 0) {
-                v = ldT(static_cast<const T*>(a.x) + (row0 + r) * a.x_stride + (size_t)h * P + p);
-            } else {
-                v = a.gy[(row0 + r) * a.gy_stride + (size_t)h * P + p];
-                if (a.z) v *= silu_acc(ldT(static_cast<const T*>(a.z) + (row0 + r) * a.z_stride + (size_t)h * P + p));
-            }
-        }
-        sV[r * kLD + p] = v;
+#pragma unroll
+    for (int q = 0; q < kQ * P / kBT; ++q) {
+        const int i = tid + q * kBT, p = i % P;
+        const size_t rr = row0 + min(i / P, Qv - 1);   // a valid row; rows past Qv carry a zero coef
+        vv[q] = mode == 0 ? ldT(static_cast<const T*>(a.x) + rr * a.x_stride + (size_t)h * P + p)
+                          : a.gy[rr * a.gy_stride + (size_t)h * P + p];
+        zq[q] = mode == 1 ? ldT(zp + rr * zs + (size_t)h * P + p) : 0.0f;
+    }
+    __syncthreads();                               // s_coef
+#pragma unroll
+    for (int q = 0; q < kQ * N / kBT; ++q) {
+        const int i = tid + q * kBT, r = i / N, n = i % N;
+        sW[r * LDN + n] = s_coef[r] * wv[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kQ * P / kBT; ++q) {
+        const int i = tid + q * kBT;
+        sV[(i / P) * kLD + i % P] = (mode == 1 && a.z) ? vv[q] * silu_acc(zq[q]) : vv[q];
     }
     __syncthreads();
     const int rb = tid >> 4, cb = tid & 15;
@@ -196,7 +213,6 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
             *reinterpret_cast<float4*>(out + (size_t)(4 * rb + i) * P + 4 * cb) =
                 make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
-    if (mode == 0 && tid == 0) a.dec[((size_t)b * a.H + h) * nc + c] = seg_end < 0 ? expf(cs_end) : 0.0f;
 }
 
 // ---- pass 2: states entering each chunk (y = 0, in order) and adjoints of
@@ -258,15 +274,14 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     const bool nact = 4 * cb < N;                  // owns a 4x4 block of a [64][N] output
 
     // the group's B and C rows (fp32, zero past the valid rows) and G = C B^T
-    for (int i = tid; i < kQ * N; i += kBT) {
-        const int r = i / N, n = i % N;
-        float bv = 0.0f, cv = 0.0f;
-        if (r < Qv) {
-            bv = ldT(static_cast<const T*>(a.Bm) + (row0 + r) * a.B_stride + (size_t)g * N + n);
-            cv = ldT(static_cast<const T*>(a.Cm) + (row0 + r) * a.C_stride + (size_t)g * N + n);
-        }
-        sB[r * LDN + n] = bv;
-        sC[r * LDN + n] = cv;
+#pragma unroll
+    for (int q = 0; q < kQ * N / kBT; ++q) {
+        const int i = tid + q * kBT, r = i / N, n = i % N;
+        const size_t rr = row0 + min(r, Qv - 1);
+        const float bv = ldT(static_cast<const T*>(a.Bm) + rr * a.B_stride + (size_t)g * N + n);
+        const float cv = ldT(static_cast<const T*>(a.Cm) + rr * a.C_stride + (size_t)g * N + n);
+        sB[r * LDN + n] = r < Qv ? bv : 0.0f;
+        sC[r * LDN + n] = r < Qv ? cv : 0.0f;
     }
     __syncthreads();
     {
@@ -295,27 +310,62 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             s_ddt[lane] = 0.0f;
             s_u[lane] = 0.0f;
         }
-        for (int i = tid; i < kQ * P; i += kBT) {
-            const int r = i / P, p = i % P;
-            float xv = 0.0f, dy = 0.0f;
-            if (r < Qv) {
-                xv = ldT(static_cast<const T*>(a.x) + (row0 + r) * a.x_stride + (size_t)h * P + p);
-                dy = a.gy[(row0 + r) * a.gy_stride + (size_t)h * P + p];
-                if (a.z) dy *= silu_acc(ldT(static_cast<const T*>(a.z) + (row0 + r) * a.z_stride + (size_t)h * P + p));
+        // x, dyr = dy silu(z) and qd = dy silu'(z) for this thread's 4x4 block
+        // (rows 4rb.., columns 4cb..), so dz = qd o y needs no reload; the
+        // states entering and leaving the chunk
+        float qd[4][4];
+        {
+            constexpr int NS = N * P / (4 * kBT);
+            float4 hv[NS], ov[NS];
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const int i = 4 * (tid + q * kBT);
+                hv[q] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + i);
+                ov[q] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + i);
             }
-            sX[r * kLD + p] = xv;
-            sDy[r * kLD + p] = dy;
-        }
-        float hg = 0.0f;                           // <Gout, Hin> partial
-        for (int i = tid; i < N * P; i += kBT) {
-            const int n = i / P, p = i % P;
-            const float hv = a.S[bhc * N * P + i], gv = a.dS[bhc * N * P + i];
-            sHin[n * kLD + p] = hv;
-            sGo[n * kLD + p] = gv;
-            hg = fmaf(hv, gv, hg);
+            int64_t zs;
+            const T* zp = z_or_gy<T>(a, zs);
+            float xv[4][4], gv[4][4], zv[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t rr = row0 + min(4 * rb + i, Qv - 1);   // a valid row; zeroed below past Qv
+                const size_t col = (size_t)h * P + 4 * cb;
+                const float4 g4 = *reinterpret_cast<const float4*>(a.gy + rr * a.gy_stride + col);
+                gv[i][0] = g4.x; gv[i][1] = g4.y; gv[i][2] = g4.z; gv[i][3] = g4.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xv[i][j] = ldT(static_cast<const T*>(a.x) + rr * a.x_stride + col + j);
+                    zv[i][j] = ldT(zp + rr * zs + col + j);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rb + i;
+                const bool ok = r < Qv;
+                float4 xo, dyo;
+                float* xa = &xo.x;
+                float* da = &dyo.x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float zz = zv[i][j], gg = ok ? gv[i][j] : 0.0f;
+                    xa[j] = ok ? xv[i][j] : 0.0f;
+                    da[j] = a.z ? gg * silu_acc(zz) : gg;
+                    qd[i][j] = a.z ? gg * dsilu_acc(zz) : 0.0f;
+                }
+                *reinterpret_cast<float4*>(sX + r * kLD + 4 * cb) = xo;
+                *reinterpret_cast<float4*>(sDy + r * kLD + 4 * cb) = dyo;
+            }
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const int i = 4 * (tid + q * kBT), n = i / P, p = i % P;
+                *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[q];
+                *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[q];
+            }
         }
         __syncthreads();
 
+        float hg = 0.0f;                           // <Gout, Hin> partial
+        for (int i = tid; i < N * P; i += kBT) hg = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], hg);
         const int end = Qv - 1;
         const float cs_end = s_cs[end];
         const int seg_end = s_seg[end];
@@ -360,14 +410,11 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                     const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
                     rin[i] = fmaf(y2[i][j], dy, rin[i]);
                     pD = fmaf(dy, xv, pD);
-                    if (a.dz && t < Qv) {
-                        const size_t o = (row0 + t) * a.z_stride + (size_t)h * P + p;
-                        const float zv = ldT(static_cast<const T*>(a.z) + o);
-                        const float yr = y1[i][j] + in_r[i] * y2[i][j] + Dh * xv;
-                        a.dz[(row0 + t) * a.dz_stride + (size_t)h * P + p] =
-                            a.gy[(row0 + t) * a.gy_stride + (size_t)h * P + p] * yr * dsilu_acc(zv);
-                    }
+                    y1[i][j] = qd[i][j] * (y1[i][j] + in_r[i] * y2[i][j] + Dh * xv);   // dz
                 }
+                if (a.dz && t < Qv)
+                    *reinterpret_cast<float4*>(a.dz + (row0 + t) * a.dz_stride + (size_t)h * P + 4 * cb) =
+                        make_float4(y1[i][0], y1[i][1], y1[i][2], y1[i][3]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -522,16 +569,26 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 }
 
 // Fixed-order sums of the per-chunk partials part[q][i][k] (q < 3, i < rows,
-// k < per) into o_q[k].
+// k < per) into o_q[k]: 16 columns per workgroup, each summed by 16 threads
+// over interleaved rows, then the 16 partials added in order.
 __global__ __launch_bounds__(kBT) void ssd_bwd_reduce_kernel(const float* part, int rows, int per, float* o0,
                                                              float* o1, float* o2) {
-    const int j = blockIdx.x * kBT + threadIdx.x;
-    if (j >= 3 * per) return;
-    const int q = j / per, k = j % per;
+    __shared__ float s_p[16][16];
+    const int col = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int j = blockIdx.x * 16 + col;
+    const bool on = j < 3 * per;
+    const int q = on ? j / per : 0, k = on ? j % per : 0;
     float s = 0.0f;
-    for (int i = 0; i < rows; ++i) s += part[((size_t)q * rows + i) * per + k];
-    float* o = q == 0 ? o0 : (q == 1 ? o1 : o2);
-    if (o) o[k] = s;
+    if (on)
+        for (int i = sl; i < rows; i += 16) s += part[((size_t)q * rows + i) * per + k];
+    s_p[sl][col] = s;
+    __syncthreads();
+    if (sl == 0 && on) {
+        float t = 0.0f;
+        for (int u = 0; u < 16; ++u) t += s_p[u][col];
+        float* o = q == 0 ? o0 : (q == 1 ? o1 : o2);
+        if (o) o[k] = t;
+    }
 }
 
 __global__ __launch_bounds__(kBT) void ssd_zero_kernel(float* p, size_t n) {
@@ -575,29 +632,42 @@ __global__ __launch_bounds__(kBT) void ssd_conv_bwd_kernel(ConvBwdArgs a) {
         win[k + 1] = (t >= 0) ? ldT(rawb + (size_t)t * a.raw_stride) : 0.0f;
     }
     float gw[K] = {0.0f, 0.0f, 0.0f, 0.0f}, gb = 0.0f;
-    for (int t = t0; t < tE; ++t) {
+    constexpr int U = 8;                           // tokens whose loads are issued together
+    for (int tb = t0; tb < tE; tb += U) {
+        float rv[U], gv[U];
 #pragma unroll
-        for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
-        win[K - 1] = ldT(rawb + (size_t)t * a.raw_stride);
-        // tap k reads row t - 3 + k: valid if no document starts in (t - 3 + k, t]
-        float pre = bias;
-        bool ok[K];
-        bool cut = false;
-#pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-            const int tau = t - (K - 1) + k;
-            ok[k] = !cut && tau >= 0;
-            if (k > 0 && tau >= 0 && start_at(tau)) cut = true;   // a start at tau cuts taps before it
-            if (ok[k]) pre = fmaf(w[k], win[k], pre);
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u;
+            const int tl = min(t, L - 1);          // rows past the end load a valid row, unused
+            rv[u] = ldT(rawb + (size_t)tl * a.raw_stride);
+            gv[u] = doutb[(size_t)tl * a.dout_stride];
         }
-        const float go = doutb[(size_t)t * a.dout_stride];
-        const float gp = a.act == 0 ? go * dsilu_acc(pre) : go;
-        s_dp[t - t0][tid] = gp;
-        if (t < t1) {
-            gb += gp;
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                if (ok[k]) gw[k] = fmaf(gp, win[k], gw[k]);
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u;
+            if (t >= tE) break;
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
+            win[K - 1] = rv[u];
+            // tap k reads row t - 3 + k: valid if no document starts in (t - 3 + k, t]
+            float pre = bias;
+            bool ok[K];
+            bool cut = false;
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                const int tau = t - (K - 1) + k;
+                ok[k] = !cut && tau >= 0;
+                if (k > 0 && tau >= 0 && start_at(tau)) cut = true;   // a start at tau cuts taps before it
+                if (ok[k]) pre = fmaf(w[k], win[k], pre);
+            }
+            const float gp = a.act == 0 ? gv[u] * dsilu_acc(pre) : gv[u];
+            s_dp[t - t0][tid] = gp;
+            if (t < t1) {
+                gb += gp;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (ok[k]) gw[k] = fmaf(gp, win[k], gw[k]);
+            }
         }
     }
     // draw[s] = sum_k w[k] dpre[s + 3 - k] over the taps that read row s
@@ -620,29 +690,41 @@ __global__ __launch_bounds__(kBT) void ssd_conv_bwd_kernel(ConvBwdArgs a) {
     }
 }
 
-// dw[c][k] and dbias[c] from the per-chunk partials [rows][C][5]
+// dw[c][k] and dbias[c] from the per-chunk partials [rows][C][5], reduced as
+// in ssd_bwd_reduce_kernel
 __global__ __launch_bounds__(kBT) void ssd_conv_bwd_reduce_kernel(const float* part, int rows, int C, float* dw,
                                                                   float* dbias) {
-    const int j = blockIdx.x * kBT + threadIdx.x;
-    if (j >= C * 5) return;
+    __shared__ float s_p[16][16];
+    const int col = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int j = blockIdx.x * 16 + col;
+    const bool on = j < C * 5;
     float s = 0.0f;
-    for (int i = 0; i < rows; ++i) s += part[(size_t)i * C * 5 + j];
-    const int c = j / 5, k = j % 5;
-    if (k < 4) dw[(size_t)c * 4 + k] = s;
-    else if (dbias) dbias[c] = s;
+    if (on)
+        for (int i = sl; i < rows; i += 16) s += part[(size_t)i * C * 5 + j];
+    s_p[sl][col] = s;
+    __syncthreads();
+    if (sl == 0 && on) {
+        float t = 0.0f;
+        for (int u = 0; u < 16; ++u) t += s_p[u][col];
+        const int c = j / 5, k = j % 5;
+        if (k < 4) dw[(size_t)c * 4 + k] = t;
+        else if (dbias) dbias[c] = t;
+    }
 }
 
 template <typename T, int N>
 hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t stream) {
     const int bhc = a.B * a.H * a.nc;
-    hipLaunchKernelGGL((ssd_bwd_sums_kernel<T, N>), dim3(bhc, 2), dim3(kBT), 0, stream, a);
+    hipLaunchKernelGGL((ssd_bwd_sums_kernel<T, N, 0>), dim3(bhc), dim3(kBT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ssd_bwd_sums_kernel<T, N, 1>), dim3(bhc), dim3(kBT), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((ssd_bwd_pass_kernel<N>), dim3(a.B * a.H * (N * 64 / kBT), 2), dim3(kBT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3(a.B * a.G * a.nc), dim3(kBT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((3 * a.H + kBT - 1) / kBT), dim3(kBT), 0, stream, a.part,
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((3 * a.H + 15) / 16), dim3(kBT), 0, stream, a.part,
                        a.B * a.nc, a.H, a.dA, a.dD, a.ddt_bias);
     return hipGetLastError();
 }
@@ -691,7 +773,7 @@ hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((ssd_conv_bwd_kernel<uint16_t>), dim3(a.B * a.ntc * nblk), dim3(kBT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ssd_conv_bwd_reduce_kernel, dim3((a.C * 5 + kBT - 1) / kBT), dim3(kBT), 0, stream, a.part,
+    hipLaunchKernelGGL(ssd_conv_bwd_reduce_kernel, dim3((a.C * 5 + 15) / 16), dim3(kBT), 0, stream, a.part,
                        a.B * a.ntc, a.C, a.dw, a.dbias);
     return hipGetLastError();
 }
