@@ -29,8 +29,8 @@
 // gradients (dA, dD, dt_bias) go through per-chunk partial sums reduced in a
 // fixed order, so every result is deterministic.
 //
-// All arithmetic is fp32 on the VALU: 64x64 products from LDS tiles, each
-// thread owning a 4x4 block of the output.
+// All arithmetic is fp32: the chunk kernel's 64x64 products run on the fp32
+// MFMA from LDS tiles, the first pass's on the VALU (each thread a 4x4 block).
 #include <algorithm>
 
 #include "ssd_device.hpp"
@@ -244,10 +244,47 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_pass_kernel(BwdArgs a) {
     }
 }
 
-// ---- pass 3: every gradient of one (batch row, group, chunk)
+// Product of a 16-row strip on the fp32 MFMA (16x16x4): acc[c] += A(r0 + ., k)
+// B(k, 16c + .) over k < K (a multiple of 16), c < NC, with the layouts of
+// mm44.  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
+// and B(4q..4q+3, 16c + i) of each 16-wide K block, and element e of acc[c]
+// is the output at row r0 + 4q + e, column 16c + i.
+template <bool AT, bool BT, int NC>
+__device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
+                                           int ldb, int K, int q, int li) {
+    for (int kb = 0; kb < K; kb += 16) {
+        const int k0 = kb + 4 * q;
+        float4 af;
+        if (AT) {
+            af.x = A[(k0 + 0) * lda + r0 + li];
+            af.y = A[(k0 + 1) * lda + r0 + li];
+            af.z = A[(k0 + 2) * lda + r0 + li];
+            af.w = A[(k0 + 3) * lda + r0 + li];
+        } else {
+            af = *reinterpret_cast<const float4*>(A + (r0 + li) * lda + k0);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float4 bf;
+            if (BT) {
+                bf = *reinterpret_cast<const float4*>(Bm + (16 * c + li) * ldb + k0);
+            } else {
+                bf.x = Bm[(k0 + 0) * ldb + 16 * c + li];
+                bf.y = Bm[(k0 + 1) * ldb + 16 * c + li];
+                bf.z = Bm[(k0 + 2) * ldb + 16 * c + li];
+                bf.w = Bm[(k0 + 3) * ldb + 16 * c + li];
+            }
+            acc[c] = mma_f32(acc[c], af, bf);
+        }
+    }
+}
+
+// ---- pass 3: every gradient of one (batch row, group, chunk).  Each wave
+// owns rows 16w .. 16w + 15 of every [64][.] product; a lane holds rows
+// R(e) = 16w + 4q + e (e < 4) at columns 16c + li.
 template <typename T, int N>
 __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
-    constexpr int P = 64, LDN = N + 4;
+    constexpr int P = 64, LDN = N + 4, NCN = N / 16;
     __shared__ __attribute__((aligned(16))) float sB[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sC[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sG[kQ * kLD];
@@ -263,7 +300,8 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     __shared__ float s_scal[2][4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rb = tid >> 4, cb = tid & 15;
+    const int q = lane >> 4, li = lane & 15;
+    const int r0 = 16 * wave;                      // this wave's strip
     const int nc = a.nc;
     const int c = blockIdx.x % nc;
     const int bg = blockIdx.x / nc;
@@ -271,12 +309,12 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     const int hpg = a.H / a.G;
     const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
     const size_t row0 = (size_t)b * a.L + t0;
-    const bool nact = 4 * cb < N;                  // owns a 4x4 block of a [64][N] output
+    auto R = [&](int e) { return r0 + 4 * q + e; };
 
     // the group's B and C rows (fp32, zero past the valid rows) and G = C B^T
 #pragma unroll
-    for (int q = 0; q < kQ * N / kBT; ++q) {
-        const int i = tid + q * kBT, r = i / N, n = i % N;
+    for (int u = 0; u < kQ * N / kBT; ++u) {
+        const int i = tid + u * kBT, r = i / N, n = i % N;
         const size_t rr = row0 + min(r, Qv - 1);
         const float bv = ldT(static_cast<const T*>(a.Bm) + rr * a.B_stride + (size_t)g * N + n);
         const float cv = ldT(static_cast<const T*>(a.Cm) + rr * a.C_stride + (size_t)g * N + n);
@@ -285,14 +323,14 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     {
-        float acc[4][4] = {};
-        mm44<false, true>(acc, sC, LDN, 4 * rb, sB, LDN, 4 * cb, N);
+        f32x4 acc[4] = {};
+        mfma_strip<false, true, 4>(acc, sC, LDN, r0, sB, LDN, N, q, li);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4*>(sG + (4 * rb + i) * kLD + 4 * cb) =
-                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[R(e) * kLD + 16 * cc + li] = acc[cc][e];
     }
-    float aB[4][4] = {}, aC[4][4] = {};            // dB, dC of the group, summed over its heads
+    f32x4 aB[NCN] = {}, aC[NCN] = {};             // dB, dC of the group, summed over its heads
 
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
@@ -310,56 +348,48 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             s_ddt[lane] = 0.0f;
             s_u[lane] = 0.0f;
         }
-        // x, dyr = dy silu(z) and qd = dy silu'(z) for this thread's 4x4 block
-        // (rows 4rb.., columns 4cb..), so dz = qd o y needs no reload; the
-        // states entering and leaving the chunk
+        // x, dyr = dy silu(z) and qd = dy silu'(z) at this lane's elements, so
+        // dz = qd o y needs no reload; the states entering and leaving the chunk
         float qd[4][4];
         {
             constexpr int NS = N * P / (4 * kBT);
             float4 hv[NS], ov[NS];
 #pragma unroll
-            for (int q = 0; q < NS; ++q) {
-                const int i = 4 * (tid + q * kBT);
-                hv[q] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + i);
-                ov[q] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + i);
+            for (int u = 0; u < NS; ++u) {
+                const int i = 4 * (tid + u * kBT);
+                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + i);
+                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + i);
             }
             int64_t zs;
             const T* zp = z_or_gy<T>(a, zs);
             float xv[4][4], gv[4][4], zv[4][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t rr = row0 + min(4 * rb + i, Qv - 1);   // a valid row; zeroed below past Qv
-                const size_t col = (size_t)h * P + 4 * cb;
-                const float4 g4 = *reinterpret_cast<const float4*>(a.gy + rr * a.gy_stride + col);
-                gv[i][0] = g4.x; gv[i][1] = g4.y; gv[i][2] = g4.z; gv[i][3] = g4.w;
+            for (int e = 0; e < 4; ++e) {
+                const size_t rr = row0 + min(R(e), Qv - 1);   // a valid row; zeroed below past Qv
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    xv[i][j] = ldT(static_cast<const T*>(a.x) + rr * a.x_stride + col + j);
-                    zv[i][j] = ldT(zp + rr * zs + col + j);
+                for (int cc = 0; cc < 4; ++cc) {
+                    const size_t col = (size_t)h * P + 16 * cc + li;
+                    xv[cc][e] = ldT(static_cast<const T*>(a.x) + rr * a.x_stride + col);
+                    gv[cc][e] = a.gy[rr * a.gy_stride + col];
+                    zv[cc][e] = ldT(zp + rr * zs + col);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * rb + i;
-                const bool ok = r < Qv;
-                float4 xo, dyo;
-                float* xa = &xo.x;
-                float* da = &dyo.x;
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = R(e) < Qv;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float zz = zv[i][j], gg = ok ? gv[i][j] : 0.0f;
-                    xa[j] = ok ? xv[i][j] : 0.0f;
-                    da[j] = a.z ? gg * silu_acc(zz) : gg;
-                    qd[i][j] = a.z ? gg * dsilu_acc(zz) : 0.0f;
+                for (int cc = 0; cc < 4; ++cc) {
+                    const float zz = zv[cc][e], gg = ok ? gv[cc][e] : 0.0f;
+                    sX[R(e) * kLD + 16 * cc + li] = ok ? xv[cc][e] : 0.0f;
+                    sDy[R(e) * kLD + 16 * cc + li] = a.z ? gg * silu_acc(zz) : gg;
+                    qd[cc][e] = a.z ? gg * dsilu_acc(zz) : 0.0f;
                 }
-                *reinterpret_cast<float4*>(sX + r * kLD + 4 * cb) = xo;
-                *reinterpret_cast<float4*>(sDy + r * kLD + 4 * cb) = dyo;
             }
 #pragma unroll
-            for (int q = 0; q < NS; ++q) {
-                const int i = 4 * (tid + q * kBT), n = i / P, p = i % P;
-                *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[q];
-                *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[q];
+            for (int u = 0; u < NS; ++u) {
+                const int i = 4 * (tid + u * kBT), n = i / P, p = i % P;
+                *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
+                *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
             }
         }
         __syncthreads();
@@ -372,54 +402,51 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         float in_r[4], el_r[4], dt_r[4];
         int seg_r[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * rb + i;
-            seg_r[i] = s_seg[t];
-            dt_r[i] = s_dt[t];
-            in_r[i] = (t < Qv && seg_r[i] < 0) ? expf(s_cs[t]) : 0.0f;
-            el_r[i] = (t < Qv && seg_r[i] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
+        for (int e = 0; e < 4; ++e) {
+            const int t = R(e);
+            seg_r[e] = s_seg[t];
+            dt_r[e] = s_dt[t];
+            in_r[e] = (t < Qv && seg_r[e] < 0) ? expf(s_cs[t]) : 0.0f;
+            el_r[e] = (t < Qv && seg_r[e] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
         }
-        // M = G o Lm o dt_s
-        auto lmask = [&](int i, int j) {
-            const int t = 4 * rb + i, s = 4 * cb + j;
-            return (s <= t && s_seg[s] == seg_r[i]) ? expf(s_cs[t] - s_cs[s]) : 0.0f;
+        auto lmask = [&](int e, int s) {
+            const int t = R(e);
+            return (s <= t && s_seg[s] == seg_r[e]) ? expf(s_cs[t] - s_cs[s]) : 0.0f;
         };
+        // M = G o Lm o dt_s
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * rb + i;
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = 4 * cb + j;
-                sM[t * kLD + s] = sG[t * kLD + s] * lmask(i, j) * s_dt[s];
+            for (int cc = 0; cc < 4; ++cc) {
+                const int t = R(e), s = 16 * cc + li;
+                sM[t * kLD + s] = sG[t * kLD + s] * lmask(e, s) * s_dt[s];
             }
-        }
         __syncthreads();
 
         // y (before the gate) = M X + in o (C Hin) + D X; dz; the in_t share of dcs; dD
         {
-            float y1[4][4] = {}, y2[4][4] = {};
-            mm44<false, false>(y1, sM, kLD, 4 * rb, sX, kLD, 4 * cb, kQ);
-            mm44<false, false>(y2, sC, LDN, 4 * rb, sHin, kLD, 4 * cb, N);
+            f32x4 y1[4] = {}, y2[4] = {};
+            mfma_strip<false, false, 4>(y1, sM, kLD, r0, sX, kLD, kQ, q, li);
+            mfma_strip<false, false, 4>(y2, sC, LDN, r0, sHin, kLD, N, q, li);
             float rin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pD = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * rb + i;
+            for (int e = 0; e < 4; ++e) {
+                const int t = R(e);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = 4 * cb + j;
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int p = 16 * cc + li;
                     const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
-                    rin[i] = fmaf(y2[i][j], dy, rin[i]);
+                    rin[e] = fmaf(y2[cc][e], dy, rin[e]);
                     pD = fmaf(dy, xv, pD);
-                    y1[i][j] = qd[i][j] * (y1[i][j] + in_r[i] * y2[i][j] + Dh * xv);   // dz
+                    if (a.dz && t < Qv)
+                        a.dz[(row0 + t) * a.dz_stride + (size_t)h * P + p] =
+                            qd[cc][e] * (y1[cc][e] + in_r[e] * y2[cc][e] + Dh * xv);
                 }
-                if (a.dz && t < Qv)
-                    *reinterpret_cast<float4*>(a.dz + (row0 + t) * a.dz_stride + (size_t)h * P + 4 * cb) =
-                        make_float4(y1[i][0], y1[i][1], y1[i][2], y1[i][3]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = sum16(rin[i]);
-                if (cb == 0) s_dcs[4 * rb + i] += in_r[i] * v;
+            for (int e = 0; e < 4; ++e) {
+                const float v = sum16(rin[e]);
+                if (li == 0) s_dcs[R(e)] += in_r[e] * v;
             }
             pD = sum64(pD);
             hg = sum64(hg);
@@ -431,39 +458,40 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 
         // dM = dyr X^T -> dG, the Lm share of dcs, the direct share of ddt
         {
-            float dm[4][4] = {};
-            mm44<false, true>(dm, sDy, kLD, 4 * rb, sX, kLD, 4 * cb, P);
+            f32x4 dm[4] = {};
+            mfma_strip<false, true, 4>(dm, sDy, kLD, r0, sX, kLD, P, q, li);
             float rowT[4] = {0.0f, 0.0f, 0.0f, 0.0f}, colT[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             float colD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * rb + i;
+            for (int e = 0; e < 4; ++e) {
+                const int t = R(e);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 4 * cb + j;
-                    const float tt = dm[i][j] * sM[t * kLD + s];
-                    const float lm = lmask(i, j);
-                    rowT[i] += tt;
-                    colT[j] += tt;
-                    colD[j] = fmaf(dm[i][j], sG[t * kLD + s] * lm, colD[j]);
-                    sDG[t * kLD + s] = dm[i][j] * lm * s_dt[s];
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int s = 16 * cc + li;
+                    const float d = dm[cc][e];
+                    const float tt = d * sM[t * kLD + s];
+                    const float lm = lmask(e, s);
+                    rowT[e] += tt;
+                    colT[cc] += tt;
+                    colD[cc] = fmaf(d, sG[t * kLD + s] * lm, colD[cc]);
+                    sDG[t * kLD + s] = d * lm * s_dt[s];
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = sum16(rowT[i]);
-                if (cb == 0) s_dcs[4 * rb + i] += v;
+            for (int e = 0; e < 4; ++e) {
+                const float v = sum16(rowT[e]);
+                if (li == 0) s_dcs[R(e)] += v;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float v = colT[j], w = colD[j];
+            for (int cc = 0; cc < 4; ++cc) {
+                float v = colT[cc], w = colD[cc];
                 v += __shfl_xor(v, 16);
                 v += __shfl_xor(v, 32);
                 w += __shfl_xor(w, 16);
                 w += __shfl_xor(w, 32);
-                if (lane < 16) {
-                    s_red[0][wave][4 * cb + j] = v;
-                    s_red[1][wave][4 * cb + j] = w;
+                if (q == 0) {
+                    s_red[0][wave][16 * cc + li] = v;
+                    s_red[1][wave][16 * cc + li] = w;
                 }
             }
         }
@@ -475,47 +503,43 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 
         // dX = M^T dyr + D dyr + (el o dt) o (B Gout); u_s = (B Gout)_s . x_s
         {
-            float d1[4][4] = {}, bgo[4][4] = {};
-            mm44<true, false>(d1, sM, kLD, 4 * rb, sDy, kLD, 4 * cb, kQ);
-            mm44<false, false>(bgo, sB, LDN, 4 * rb, sGo, kLD, 4 * cb, N);
+            f32x4 d1[4] = {}, bgo[4] = {};
+            mfma_strip<true, false, 4>(d1, sM, kLD, r0, sDy, kLD, kQ, q, li);
+            mfma_strip<false, false, 4>(bgo, sB, LDN, r0, sGo, kLD, N, q, li);
             float ru[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 4 * rb + i;
-                const float we = el_r[i] * dt_r[i];
-                float o[4];
+            for (int e = 0; e < 4; ++e) {
+                const int s = R(e);
+                const float we = el_r[e] * dt_r[e];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = 4 * cb + j;
-                    ru[i] = fmaf(bgo[i][j], sX[s * kLD + p], ru[i]);
-                    o[j] = d1[i][j] + Dh * sDy[s * kLD + p] + we * bgo[i][j];
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int p = 16 * cc + li;
+                    ru[e] = fmaf(bgo[cc][e], sX[s * kLD + p], ru[e]);
+                    if (s < Qv)
+                        a.dx[(row0 + s) * a.dx_stride + (size_t)h * P + p] =
+                            d1[cc][e] + Dh * sDy[s * kLD + p] + we * bgo[cc][e];
                 }
-                if (s < Qv)
-                    *reinterpret_cast<float4*>(a.dx + (row0 + s) * a.dx_stride + (size_t)h * P + 4 * cb) =
-                        make_float4(o[0], o[1], o[2], o[3]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = sum16(ru[i]);
-                if (cb == 0) s_u[4 * rb + i] = v;
+            for (int e = 0; e < 4; ++e) {
+                const float v = sum16(ru[e]);
+                if (li == 0) s_u[R(e)] = v;
             }
         }
         // dB += dG^T C + (el o dt) o (X Gout^T);  dC += dG B + in o (dyr Hin^T)
-        if (nact) {
-            mm44<true, false>(aB, sDG, kLD, 4 * rb, sC, LDN, 4 * cb, kQ);
-            mm44<false, false>(aC, sDG, kLD, 4 * rb, sB, LDN, 4 * cb, kQ);
-            float xg[4][4] = {}, dh[4][4] = {};
-            mm44<false, true>(xg, sX, kLD, 4 * rb, sGo, kLD, 4 * cb, P);
-            mm44<false, true>(dh, sDy, kLD, 4 * rb, sHin, kLD, 4 * cb, P);
+        {
+            mfma_strip<true, false, NCN>(aB, sDG, kLD, r0, sC, LDN, kQ, q, li);
+            mfma_strip<false, false, NCN>(aC, sDG, kLD, r0, sB, LDN, kQ, q, li);
+            f32x4 xg[NCN] = {}, dh[NCN] = {};
+            mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, P, q, li);
+            mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, P, q, li);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float we = el_r[i] * dt_r[i];
+            for (int cc = 0; cc < NCN; ++cc)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    aB[i][j] = fmaf(we, xg[i][j], aB[i][j]);
-                    aC[i][j] = fmaf(in_r[i], dh[i][j], aC[i][j]);
+                for (int e = 0; e < 4; ++e) {
+                    aB[cc][e] = fmaf(el_r[e] * dt_r[e], xg[cc][e], aB[cc][e]);
+                    aC[cc][e] = fmaf(in_r[e], dh[cc][e], aC[cc][e]);
                 }
-            }
         }
         __syncthreads();
 
@@ -554,15 +578,14 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         }
         __syncthreads();
     }
-    if (nact) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * rb + i;
-            if (r < Qv) {
-                *reinterpret_cast<float4*>(a.dB + (row0 + r) * a.dB_stride + (size_t)g * N + 4 * cb) =
-                    make_float4(aB[i][0], aB[i][1], aB[i][2], aB[i][3]);
-                *reinterpret_cast<float4*>(a.dC + (row0 + r) * a.dC_stride + (size_t)g * N + 4 * cb) =
-                    make_float4(aC[i][0], aC[i][1], aC[i][2], aC[i][3]);
+    for (int e = 0; e < 4; ++e) {
+        const int r = R(e);
+        if (r < Qv) {
+#pragma unroll
+            for (int cc = 0; cc < NCN; ++cc) {
+                a.dB[(row0 + r) * a.dB_stride + (size_t)g * N + 16 * cc + li] = aB[cc][e];
+                a.dC[(row0 + r) * a.dC_stride + (size_t)g * N + 16 * cc + li] = aC[cc][e];
             }
         }
     }
