@@ -245,13 +245,13 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_pass_kernel(BwdArgs a) {
 }
 
 // Product of a 16-row strip on the fp32 MFMA (16x16x4): acc[c] += A(r0 + ., k)
-// B(k, 16c + .) over k < K (a multiple of 16), c < NC, with the layouts of
-// mm44.  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
-// and B(4q..4q+3, 16c + i) of each 16-wide K block, and element e of acc[c]
-// is the output at row r0 + 4q + e, column 16c + i.
+// B(k, c0 + 16c + .) over k < K (a multiple of 16), c < NC, with the layouts
+// of mm44.  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
+// and B(4q..4q+3, c0 + 16c + i) of each 16-wide K block, and element e of
+// acc[c] is the output at row r0 + 4q + e, column c0 + 16c + i.
 template <bool AT, bool BT, int NC>
 __device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
-                                           int ldb, int K, int q, int li) {
+                                           int ldb, int c0, int K, int q, int li) {
     for (int kb = 0; kb < K; kb += 16) {
         const int k0 = kb + 4 * q;
         float4 af;
@@ -265,26 +265,32 @@ __device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
+            const int col = c0 + 16 * c + li;
             float4 bf;
             if (BT) {
-                bf = *reinterpret_cast<const float4*>(Bm + (16 * c + li) * ldb + k0);
+                bf = *reinterpret_cast<const float4*>(Bm + col * ldb + k0);
             } else {
-                bf.x = Bm[(k0 + 0) * ldb + 16 * c + li];
-                bf.y = Bm[(k0 + 1) * ldb + 16 * c + li];
-                bf.z = Bm[(k0 + 2) * ldb + 16 * c + li];
-                bf.w = Bm[(k0 + 3) * ldb + 16 * c + li];
+                bf.x = Bm[(k0 + 0) * ldb + col];
+                bf.y = Bm[(k0 + 1) * ldb + col];
+                bf.z = Bm[(k0 + 2) * ldb + col];
+                bf.w = Bm[(k0 + 3) * ldb + col];
             }
             acc[c] = mma_f32(acc[c], af, bf);
         }
     }
 }
 
-// ---- pass 3: every gradient of one (batch row, group, chunk).  Each wave
-// owns rows 16w .. 16w + 15 of every [64][.] product; a lane holds rows
-// R(e) = 16w + 4q + e (e < 4) at columns 16c + li.
+constexpr int kCT = 512;     // chunk kernel: eight waves
+
+// ---- pass 3: every gradient of one (batch row, group, chunk).  Wave w owns
+// rows 16 (w % 4) .. +15 and the column half w / 4 of every [64][.] product:
+// a lane holds rows R(e) = 16 (w % 4) + 4q + e (e < 4) at columns
+// 32 (w / 4) + 16c + li (c < 2).  Row sums of the two halves meet in LDS and
+// are added in a fixed order.
 template <typename T, int N>
-__global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
-    constexpr int P = 64, LDN = N + 4, NCN = N / 16;
+__global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
+    constexpr int P = 64, LDN = N + 4;
+    constexpr int NCN = N / 32 > 0 ? N / 32 : 1;   // dB / dC tiles per half (N = 16: half 0 only)
     __shared__ __attribute__((aligned(16))) float sB[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sC[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sG[kQ * kLD];
@@ -294,14 +300,16 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sDG[kQ * kLD];
     __shared__ __attribute__((aligned(16))) float sHin[N * kLD];
     __shared__ __attribute__((aligned(16))) float sGo[N * kLD];
-    __shared__ float s_dt[kQ], s_cs[kQ], s_chain[kQ], s_dcs[kQ], s_ddt[kQ], s_u[kQ];
+    __shared__ float s_dt[kQ], s_cs[kQ], s_chain[kQ], s_ddt[kQ];
+    __shared__ float s_dcs2[2][kQ], s_u2[2][kQ];   // row sums per column half
     __shared__ int s_seg[kQ];
     __shared__ float s_red[2][4][kQ];
-    __shared__ float s_scal[2][4];
+    __shared__ float s_scal[2][8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, li = lane & 15;
-    const int r0 = 16 * wave;                      // this wave's strip
+    const int r0 = 16 * (wave & 3);                // this wave's rows
+    const int half = wave >> 2, c0 = 32 * half;    // and column half
     const int nc = a.nc;
     const int c = blockIdx.x % nc;
     const int bg = blockIdx.x / nc;
@@ -309,12 +317,16 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     const int hpg = a.H / a.G;
     const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
     const size_t row0 = (size_t)b * a.L + t0;
+    // the [64][N] products (dB, dC) split their N columns the same way: N/2
+    // per half (N = 16: one tile, half 0 only)
+    const bool nact = N >= 32 || half == 0;
+    const int c0N = N >= 32 ? half * (N / 2) : 0;
     auto R = [&](int e) { return r0 + 4 * q + e; };
 
     // the group's B and C rows (fp32, zero past the valid rows) and G = C B^T
 #pragma unroll
-    for (int u = 0; u < kQ * N / kBT; ++u) {
-        const int i = tid + u * kBT, r = i / N, n = i % N;
+    for (int u = 0; u < kQ * N / kCT; ++u) {
+        const int i = tid + u * kCT, r = i / N, n = i % N;
         const size_t rr = row0 + min(r, Qv - 1);
         const float bv = ldT(static_cast<const T*>(a.Bm) + rr * a.B_stride + (size_t)g * N + n);
         const float cv = ldT(static_cast<const T*>(a.Cm) + rr * a.C_stride + (size_t)g * N + n);
@@ -323,12 +335,12 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     {
-        f32x4 acc[4] = {};
-        mfma_strip<false, true, 4>(acc, sC, LDN, r0, sB, LDN, N, q, li);
+        f32x4 acc[2] = {};
+        mfma_strip<false, true, 2>(acc, sC, LDN, r0, sB, LDN, c0, N, q, li);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sG[R(e) * kLD + 16 * cc + li] = acc[cc][e];
+            for (int e = 0; e < 4; ++e) sG[R(e) * kLD + c0 + 16 * cc + li] = acc[cc][e];
     }
     f32x4 aB[NCN] = {}, aC[NCN] = {};             // dB, dC of the group, summed over its heads
 
@@ -344,31 +356,29 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             s_cs[lane] = cs;
             s_seg[lane] = seg;
             s_chain[lane] = chain;
-            s_dcs[lane] = 0.0f;
             s_ddt[lane] = 0.0f;
-            s_u[lane] = 0.0f;
         }
         // x, dyr = dy silu(z) and qd = dy silu'(z) at this lane's elements, so
         // dz = qd o y needs no reload; the states entering and leaving the chunk
-        float qd[4][4];
+        float qd[2][4];
         {
-            constexpr int NS = N * P / (4 * kBT);
+            constexpr int NS = (N * P / 4 + kCT - 1) / kCT;
             float4 hv[NS], ov[NS];
 #pragma unroll
             for (int u = 0; u < NS; ++u) {
-                const int i = 4 * (tid + u * kBT);
-                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + i);
-                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + i);
+                const int i4 = min(tid + u * kCT, N * P / 4 - 1);
+                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + 4 * i4);
+                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + 4 * i4);
             }
             int64_t zs;
             const T* zp = z_or_gy<T>(a, zs);
-            float xv[4][4], gv[4][4], zv[4][4];
+            float xv[2][4], gv[2][4], zv[2][4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const size_t rr = row0 + min(R(e), Qv - 1);   // a valid row; zeroed below past Qv
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const size_t col = (size_t)h * P + 16 * cc + li;
+                for (int cc = 0; cc < 2; ++cc) {
+                    const size_t col = (size_t)h * P + c0 + 16 * cc + li;
                     xv[cc][e] = ldT(static_cast<const T*>(a.x) + rr * a.x_stride + col);
                     gv[cc][e] = a.gy[rr * a.gy_stride + col];
                     zv[cc][e] = ldT(zp + rr * zs + col);
@@ -378,75 +388,72 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const bool ok = R(e) < Qv;
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
+                for (int cc = 0; cc < 2; ++cc) {
                     const float zz = zv[cc][e], gg = ok ? gv[cc][e] : 0.0f;
-                    sX[R(e) * kLD + 16 * cc + li] = ok ? xv[cc][e] : 0.0f;
-                    sDy[R(e) * kLD + 16 * cc + li] = a.z ? gg * silu_acc(zz) : gg;
+                    const int o = R(e) * kLD + c0 + 16 * cc + li;
+                    sX[o] = ok ? xv[cc][e] : 0.0f;
+                    sDy[o] = a.z ? gg * silu_acc(zz) : gg;
                     qd[cc][e] = a.z ? gg * dsilu_acc(zz) : 0.0f;
                 }
             }
 #pragma unroll
             for (int u = 0; u < NS; ++u) {
-                const int i = 4 * (tid + u * kBT), n = i / P, p = i % P;
-                *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
-                *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
+                const int i4 = tid + u * kCT;
+                if (i4 < N * P / 4) {
+                    const int n = 4 * i4 / P, p = 4 * i4 % P;
+                    *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
+                    *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
+                }
             }
         }
         __syncthreads();
 
         float hg = 0.0f;                           // <Gout, Hin> partial
-        for (int i = tid; i < N * P; i += kBT) hg = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], hg);
+        for (int i = tid; i < N * P; i += kCT) hg = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], hg);
         const int end = Qv - 1;
         const float cs_end = s_cs[end];
         const int seg_end = s_seg[end];
-        float in_r[4], el_r[4], dt_r[4];
-        int seg_r[4];
+        float in_r[4], we_r[4];                    // in_t, and el_s dt_s, of this lane's rows
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = R(e);
-            seg_r[e] = s_seg[t];
-            dt_r[e] = s_dt[t];
-            in_r[e] = (t < Qv && seg_r[e] < 0) ? expf(s_cs[t]) : 0.0f;
-            el_r[e] = (t < Qv && seg_r[e] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
+            const int t = R(e), sg = s_seg[t];
+            in_r[e] = (t < Qv && sg < 0) ? expf(s_cs[t]) : 0.0f;
+            we_r[e] = (t < Qv && sg == seg_end) ? expf(cs_end - s_cs[t]) * s_dt[t] : 0.0f;
         }
         auto lmask = [&](int e, int s) {
             const int t = R(e);
-            return (s <= t && s_seg[s] == seg_r[e]) ? expf(s_cs[t] - s_cs[s]) : 0.0f;
+            return (s <= t && s_seg[s] == s_seg[t]) ? expf(s_cs[t] - s_cs[s]) : 0.0f;
         };
         // M = G o Lm o dt_s
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int t = R(e), s = 16 * cc + li;
+            for (int cc = 0; cc < 2; ++cc) {
+                const int t = R(e), s = c0 + 16 * cc + li;
                 sM[t * kLD + s] = sG[t * kLD + s] * lmask(e, s) * s_dt[s];
             }
         __syncthreads();
 
+        float rowD[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this half's share of dcs per row
         // y (before the gate) = M X + in o (C Hin) + D X; dz; the in_t share of dcs; dD
         {
-            f32x4 y1[4] = {}, y2[4] = {};
-            mfma_strip<false, false, 4>(y1, sM, kLD, r0, sX, kLD, kQ, q, li);
-            mfma_strip<false, false, 4>(y2, sC, LDN, r0, sHin, kLD, N, q, li);
-            float rin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pD = 0.0f;
+            f32x4 y1[2] = {}, y2[2] = {};
+            mfma_strip<false, false, 2>(y1, sM, kLD, r0, sX, kLD, c0, kQ, q, li);
+            mfma_strip<false, false, 2>(y2, sC, LDN, r0, sHin, kLD, c0, N, q, li);
+            float pD = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = R(e);
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const int p = 16 * cc + li;
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int p = c0 + 16 * cc + li;
                     const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
-                    rin[e] = fmaf(y2[cc][e], dy, rin[e]);
+                    rowD[e] = fmaf(in_r[e] * y2[cc][e], dy, rowD[e]);
                     pD = fmaf(dy, xv, pD);
                     if (a.dz && t < Qv)
                         a.dz[(row0 + t) * a.dz_stride + (size_t)h * P + p] =
                             qd[cc][e] * (y1[cc][e] + in_r[e] * y2[cc][e] + Dh * xv);
                 }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = sum16(rin[e]);
-                if (li == 0) s_dcs[R(e)] += in_r[e] * v;
             }
             pD = sum64(pD);
             hg = sum64(hg);
@@ -458,20 +465,19 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 
         // dM = dyr X^T -> dG, the Lm share of dcs, the direct share of ddt
         {
-            f32x4 dm[4] = {};
-            mfma_strip<false, true, 4>(dm, sDy, kLD, r0, sX, kLD, P, q, li);
-            float rowT[4] = {0.0f, 0.0f, 0.0f, 0.0f}, colT[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            float colD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 dm[2] = {};
+            mfma_strip<false, true, 2>(dm, sDy, kLD, r0, sX, kLD, c0, P, q, li);
+            float colT[2] = {0.0f, 0.0f}, colD[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = R(e);
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const int s = 16 * cc + li;
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int s = c0 + 16 * cc + li;
                     const float d = dm[cc][e];
                     const float tt = d * sM[t * kLD + s];
                     const float lm = lmask(e, s);
-                    rowT[e] += tt;
+                    rowD[e] += tt;
                     colT[cc] += tt;
                     colD[cc] = fmaf(d, sG[t * kLD + s] * lm, colD[cc]);
                     sDG[t * kLD + s] = d * lm * s_dt[s];
@@ -479,41 +485,37 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = sum16(rowT[e]);
-                if (li == 0) s_dcs[R(e)] += v;
+                const float v = sum16(rowD[e]);
+                if (li == 0) s_dcs2[half][R(e)] = v;
             }
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
+            for (int cc = 0; cc < 2; ++cc) {
                 float v = colT[cc], w = colD[cc];
                 v += __shfl_xor(v, 16);
                 v += __shfl_xor(v, 32);
                 w += __shfl_xor(w, 16);
                 w += __shfl_xor(w, 32);
                 if (q == 0) {
-                    s_red[0][wave][16 * cc + li] = v;
-                    s_red[1][wave][16 * cc + li] = w;
+                    s_red[0][wave & 3][c0 + 16 * cc + li] = v;
+                    s_red[1][wave & 3][c0 + 16 * cc + li] = w;
                 }
             }
         }
         __syncthreads();
-        if (tid < 64) {
-            s_dcs[tid] -= (s_red[0][0][tid] + s_red[0][1][tid]) + (s_red[0][2][tid] + s_red[0][3][tid]);
-            s_ddt[tid] += (s_red[1][0][tid] + s_red[1][1][tid]) + (s_red[1][2][tid] + s_red[1][3][tid]);
-        }
 
         // dX = M^T dyr + D dyr + (el o dt) o (B Gout); u_s = (B Gout)_s . x_s
         {
-            f32x4 d1[4] = {}, bgo[4] = {};
-            mfma_strip<true, false, 4>(d1, sM, kLD, r0, sDy, kLD, kQ, q, li);
-            mfma_strip<false, false, 4>(bgo, sB, LDN, r0, sGo, kLD, N, q, li);
+            f32x4 d1[2] = {}, bgo[2] = {};
+            mfma_strip<true, false, 2>(d1, sM, kLD, r0, sDy, kLD, c0, kQ, q, li);
+            mfma_strip<false, false, 2>(bgo, sB, LDN, r0, sGo, kLD, c0, N, q, li);
             float ru[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = R(e);
-                const float we = el_r[e] * dt_r[e];
+                const float we = we_r[e];
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const int p = 16 * cc + li;
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int p = c0 + 16 * cc + li;
                     ru[e] = fmaf(bgo[cc][e], sX[s * kLD + p], ru[e]);
                     if (s < Qv)
                         a.dx[(row0 + s) * a.dx_stride + (size_t)h * P + p] =
@@ -523,21 +525,21 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float v = sum16(ru[e]);
-                if (li == 0) s_u[R(e)] = v;
+                if (li == 0) s_u2[half][R(e)] = v;
             }
         }
         // dB += dG^T C + (el o dt) o (X Gout^T);  dC += dG B + in o (dyr Hin^T)
-        {
-            mfma_strip<true, false, NCN>(aB, sDG, kLD, r0, sC, LDN, kQ, q, li);
-            mfma_strip<false, false, NCN>(aC, sDG, kLD, r0, sB, LDN, kQ, q, li);
+        if (nact) {
+            mfma_strip<true, false, NCN>(aB, sDG, kLD, r0, sC, LDN, c0N, kQ, q, li);
+            mfma_strip<false, false, NCN>(aC, sDG, kLD, r0, sB, LDN, c0N, kQ, q, li);
             f32x4 xg[NCN] = {}, dh[NCN] = {};
-            mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, P, q, li);
-            mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, P, q, li);
+            mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, c0N, P, q, li);
+            mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, c0N, P, q, li);
 #pragma unroll
             for (int cc = 0; cc < NCN; ++cc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    aB[cc][e] = fmaf(el_r[e] * dt_r[e], xg[cc][e], aB[cc][e]);
+                    aB[cc][e] = fmaf(we_r[e], xg[cc][e], aB[cc][e]);
                     aC[cc][e] = fmaf(in_r[e], dh[cc][e], aC[cc][e]);
                 }
         }
@@ -549,13 +551,15 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             const int t = lane;
             const bool valid = t < Qv;
             const float el = (valid && s_seg[t] == seg_end) ? expf(cs_end - s_cs[t]) : 0.0f;
-            const float dtv = s_dt[t], u = s_u[t];
+            const float dtv = s_dt[t], u = s_u2[0][t] + s_u2[1][t];
             const float wu = el * dtv * u;
-            float dcs = s_dcs[t] - wu;
+            const float colsumT = (s_red[0][0][t] + s_red[0][1][t]) + (s_red[0][2][t] + s_red[0][3][t]);
+            float dcs = (s_dcs2[0][t] + s_dcs2[1][t]) - colsumT - wu;
             const float sum_wu = sum64(wu);
-            const float hgt = (s_scal[1][0] + s_scal[1][1]) + (s_scal[1][2] + s_scal[1][3]);
+            const float hgt = ((s_scal[1][0] + s_scal[1][1]) + (s_scal[1][2] + s_scal[1][3])) +
+                              ((s_scal[1][4] + s_scal[1][5]) + (s_scal[1][6] + s_scal[1][7]));
             if (t == end) dcs += sum_wu + (seg_end < 0 ? expf(cs_end) : 0.0f) * hgt;
-            float ddt = s_ddt[t] + el * u;
+            float ddt = (s_red[1][0][t] + s_red[1][1][t]) + (s_red[1][2][t] + s_red[1][3][t]) + el * u;
             // segments in reverse order start where the original row ends one
             const int fend = (t == kQ - 1 || s_seg[t + 1 < kQ ? t + 1 : t] == t + 1) ? 1 : 0;
             float vr = __shfl(dcs, 63 - lane);
@@ -572,20 +576,24 @@ __global__ __launch_bounds__(kBT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 const size_t bc = (size_t)b * nc + c;
                 const size_t nbc = (size_t)a.B * nc;
                 a.part[(0 * nbc + bc) * a.H + h] = pA;
-                a.part[(1 * nbc + bc) * a.H + h] = (s_scal[0][0] + s_scal[0][1]) + (s_scal[0][2] + s_scal[0][3]);
+                a.part[(1 * nbc + bc) * a.H + h] = ((s_scal[0][0] + s_scal[0][1]) + (s_scal[0][2] + s_scal[0][3])) +
+                                                    ((s_scal[0][4] + s_scal[0][5]) + (s_scal[0][6] + s_scal[0][7]));
                 a.part[(2 * nbc + bc) * a.H + h] = pBias;
             }
         }
         __syncthreads();
     }
+    if (nact) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int r = R(e);
-        if (r < Qv) {
+        for (int e = 0; e < 4; ++e) {
+            const int r = R(e);
+            if (r < Qv) {
 #pragma unroll
-            for (int cc = 0; cc < NCN; ++cc) {
-                a.dB[(row0 + r) * a.dB_stride + (size_t)g * N + 16 * cc + li] = aB[cc][e];
-                a.dC[(row0 + r) * a.dC_stride + (size_t)g * N + 16 * cc + li] = aC[cc][e];
+                for (int cc = 0; cc < NCN; ++cc) {
+                    const size_t col = (size_t)g * N + c0N + 16 * cc + li;
+                    a.dB[(row0 + r) * a.dB_stride + col] = aB[cc][e];
+                    a.dC[(row0 + r) * a.dC_stride + col] = aC[cc][e];
+                }
             }
         }
     }
@@ -745,7 +753,7 @@ hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((ssd_bwd_pass_kernel<N>), dim3(a.B * a.H * (N * 64 / kBT), 2), dim3(kBT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3(a.B * a.G * a.nc), dim3(kBT), 0, stream, a);
+    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3(a.B * a.G * a.nc), dim3(kCT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((3 * a.H + 15) / 16), dim3(kBT), 0, stream, a.part,
                        a.B * a.nc, a.H, a.dA, a.dD, a.ddt_bias);
