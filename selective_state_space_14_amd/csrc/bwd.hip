@@ -628,90 +628,131 @@ __global__ __launch_bounds__(kBT) void ssd_zero_kernel(float* p, size_t n) {
 }
 
 // ---- conv backward: one channel per thread, 64 tokens per workgroup
+constexpr int kCB = 256;     // channels per workgroup
+
+// d silu / dv with the hardware exp2 and reciprocal (a few ulp)
+__device__ __forceinline__ float dsilu_fast(float v) {
+    const float s = fast_rcp(1.0f + fast_exp2(-v * kLog2e));
+    return s * (1.0f + v * (1.0f - s));
+}
+
 template <typename T>
-__global__ __launch_bounds__(kBT) void ssd_conv_bwd_kernel(ConvBwdArgs a) {
-    constexpr int K = 4, TC = 64, TE = TC + K - 1;
-    __shared__ float s_dp[TE][kBT];                // d(pre-activation) of rows t0 .. t0 + TE - 1
-    __shared__ int s_start[TE + K];                // document starts at rows t0 - 3 .. t0 + TE - 1
+__global__ __launch_bounds__(kCB) void ssd_conv_bwd_kernel(ConvBwdArgs a) {
+    constexpr int K = 4, TC = 64, U = 8;
+    __shared__ unsigned long long s_mask[2];       // document starts at rows t0 - 3 + i, i < 128
     const int C = a.C, L = a.L, tid = threadIdx.x;
-    const int nblk = (C + kBT - 1) / kBT;
+    const int nblk = (C + kCB - 1) / kCB;
     const int blk = blockIdx.x % nblk;
     const int tc = (blockIdx.x / nblk) % a.ntc;
     const int b = blockIdx.x / (nblk * a.ntc);
-    const int c = blk * kBT + tid;
+    const int c = blk * kCB + tid;
     const bool on = c < C;
     const int cc = min(c, C - 1);
-    const int t0 = tc * TC, t1 = min(t0 + TC, L), tE = min(t0 + TE, L);
+    const int t0 = tc * TC, t1 = min(t0 + TC, L);
     const int32_t* docb = a.doc ? a.doc + (size_t)b * L : nullptr;
-    for (int i = tid; i < TE + K - 1; i += kBT) {
-        const int t = t0 - (K - 1) + i;
-        s_start[i] = (docb && t > 0 && t < L && docb[t] != docb[t - 1]) ? 1 : 0;
+    if (tid < 64) {
+        auto start = [&](int t) { return docb && t > 0 && t < L && docb[t] != docb[t - 1]; };
+        const unsigned long long lo = __ballot(start(t0 - (K - 1) + tid));
+        const unsigned long long hi = __ballot(start(t0 - (K - 1) + 64 + tid));
+        if (tid == 0) {
+            s_mask[0] = lo;
+            s_mask[1] = hi;
+        }
     }
     __syncthreads();
-    auto start_at = [&](int t) { return s_start[t - t0 + K - 1]; };
+    // (readfirstlane returns a signed int: widen through uint32_t)
+    auto uniform64 = [](unsigned long long v) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return ((uint64_t)hi << 32) | lo;
+    };
+    const uint64_t mlo = uniform64(s_mask[0]);
+    const uint64_t mhi = uniform64(s_mask[1]);
+    auto start_at = [&](int t) {                   // uniform: a document starts at row t
+        const int i = t - t0 + K - 1;
+        return ((i < 64 ? mlo >> i : mhi >> (i - 64)) & 1u) != 0;
+    };
     float w[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) w[k] = a.w[(size_t)cc * K + k];
     const float bias = a.bias ? a.bias[cc] : 0.0f;
     const T* rawb = static_cast<const T*>(a.raw) + (size_t)b * L * a.raw_stride + cc;
     const float* doutb = a.dout + (size_t)b * L * a.dout_stride + cc;
-    // window of raw rows t-3 .. t (0 outside [0, L))
-    float win[K];
+    float* drawb = a.draw + (size_t)b * L * a.draw_stride + c;
+    // raw rows t-3 .. t (0 before row 0) and d(pre-activation) of rows t-3 .. t
+    float win[K], dp[K] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < K - 1; ++k) {
         const int t = t0 - (K - 1) + k;
-        win[k + 1] = (t >= 0) ? ldT(rawb + (size_t)t * a.raw_stride) : 0.0f;
+        const float v = ldT(rawb + (size_t)max(t, 0) * a.raw_stride);
+        win[k + 1] = t < 0 ? 0.0f : v;
     }
     float gw[K] = {0.0f, 0.0f, 0.0f, 0.0f}, gb = 0.0f;
-    constexpr int U = 8;                           // tokens whose loads are issued together
-    for (int tb = t0; tb < tE; tb += U) {
-        float rv[U], gv[U];
+    // Rows t0 .. t1 + 2: dpre[t] for t < L (the three rows past the tile feed
+    // the tile's last draw rows), and draw[t - 3] as soon as dpre[t] is known.
+    // Two register sets of loads are used in turn, one block ahead.
+    const int tEnd = t1 + K - 1;
+    float ra[U], ga[U], rb[U], gb2[U];
+    auto load_block = [&](int tb, float* r, float* gg) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = tb + u;
-            const int tl = min(t, L - 1);          // rows past the end load a valid row, unused
-            rv[u] = ldT(rawb + (size_t)tl * a.raw_stride);
-            gv[u] = doutb[(size_t)tl * a.dout_stride];
+            const int tl = min(tb + u, L - 1);     // rows past the end load a valid row, unused
+            r[u] = ldT(rawb + (size_t)tl * a.raw_stride);
+            gg[u] = doutb[(size_t)tl * a.dout_stride];
         }
+    };
+    auto compute_block = [&](int tb, const float* rv, const float* gv) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = tb + u;
-            if (t >= tE) break;
+            if (t >= tEnd) break;
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
-            win[K - 1] = rv[u];
-            // tap k reads row t - 3 + k: valid if no document starts in (t - 3 + k, t]
-            float pre = bias;
-            bool ok[K];
-            bool cut = false;
-#pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                const int tau = t - (K - 1) + k;
-                ok[k] = !cut && tau >= 0;
-                if (k > 0 && tau >= 0 && start_at(tau)) cut = true;   // a start at tau cuts taps before it
-                if (ok[k]) pre = fmaf(w[k], win[k], pre);
+            for (int k = 0; k < K - 1; ++k) {
+                win[k] = win[k + 1];
+                dp[k] = dp[k + 1];
             }
-            const float gp = a.act == 0 ? gv[u] * dsilu_acc(pre) : gv[u];
-            s_dp[t - t0][tid] = gp;
+            win[K - 1] = rv[u];
+            // tap k reads row t - 3 + k: valid if it is a row (>= 0) and no
+            // document starts in (t - 3 + k, t]
+            bool ok[K];
+            ok[K - 1] = true;
+            bool run = true;
+#pragma unroll
+            for (int k = K - 2; k >= 0; --k) {
+                run = run && !start_at(t - (K - 1) + k + 1);
+                ok[k] = run && t - (K - 1) + k >= 0;
+            }
+            float pre = bias;
+#pragma unroll
+            for (int k = 0; k < K; ++k) pre = fmaf(w[k], ok[k] ? win[k] : 0.0f, pre);
+            const float gp = t < L ? (a.act == 0 ? gv[u] * dsilu_fast(pre) : gv[u]) : 0.0f;
+            dp[K - 1] = gp;
             if (t < t1) {
                 gb += gp;
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    if (ok[k]) gw[k] = fmaf(gp, win[k], gw[k]);
+                for (int k = 0; k < K; ++k) gw[k] = fmaf(gp, ok[k] ? win[k] : 0.0f, gw[k]);
+            }
+            // draw[s], s = t - 3: sum over the taps k that read row s, of the
+            // tokens s + 3 - k (dp[3 - k]) with no document start in (s, s + 3 - k]
+            const int s = t - (K - 1);
+            if (s >= t0) {
+                float acc = w[K - 1] * dp[0];
+                bool r2 = true;
+#pragma unroll
+                for (int k = K - 2; k >= 0; --k) {
+                    r2 = r2 && !start_at(s + (K - 1) - k);
+                    acc = fmaf(w[k], r2 ? dp[K - 1 - k] : 0.0f, acc);
+                }
+                if (on) drawb[(size_t)s * a.draw_stride] = acc;
             }
         }
-    }
-    // draw[s] = sum_k w[k] dpre[s + 3 - k] over the taps that read row s
-    for (int s = t0; s < t1; ++s) {
-        float acc = 0.0f;
-        bool cut = false;
-#pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-            const int tp = s + (K - 1) - k;                  // the token whose tap k reads row s
-            if (tp > s && tp < L && start_at(tp)) cut = true;
-            if (!cut && tp < L) acc = fmaf(w[k], s_dp[tp - t0][tid], acc);
-        }
-        if (on) a.draw[((size_t)b * L + s) * a.draw_stride + c] = acc;
+    };
+    load_block(t0, ra, ga);
+    for (int tb = t0; tb < tEnd; tb += 2 * U) {
+        load_block(tb + U, rb, gb2);
+        compute_block(tb, ra, ga);
+        load_block(tb + 2 * U, ra, ga);
+        compute_block(tb + U, rb, gb2);
     }
     if (on) {
         float* pp = a.part + (((size_t)b * a.ntc + tc) * C + c) * (K + 1);
@@ -797,11 +838,11 @@ size_t conv_bwd_workspace_bytes(int B, int L, int C) {
 
 hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t stream) {
     if (a.B == 0 || a.L == 0) return hipSuccess;
-    const int nblk = (a.C + kBT - 1) / kBT;
+    const int nblk = (a.C + kCB - 1) / kCB;
     if (a.dtype == 0)
-        hipLaunchKernelGGL((ssd_conv_bwd_kernel<float>), dim3(a.B * a.ntc * nblk), dim3(kBT), 0, stream, a);
+        hipLaunchKernelGGL((ssd_conv_bwd_kernel<float>), dim3(a.B * a.ntc * nblk), dim3(kCB), 0, stream, a);
     else
-        hipLaunchKernelGGL((ssd_conv_bwd_kernel<uint16_t>), dim3(a.B * a.ntc * nblk), dim3(kBT), 0, stream, a);
+        hipLaunchKernelGGL((ssd_conv_bwd_kernel<uint16_t>), dim3(a.B * a.ntc * nblk), dim3(kCB), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ssd_conv_bwd_reduce_kernel, dim3((a.C * 5 + 15) / 16), dim3(kBT), 0, stream, a.part,

@@ -99,6 +99,25 @@ def test_conv_bwd_vs_oracle(gpu_lib, dtype, act, docs):
         _check(got[k], ref[k], f"d{k}")
 
 
+def test_conv_bwd_document_starts_at_mask_edges(gpu_lib):
+    """Document starts at the rows whose flags sit at bits 31, 32, 63 and 64 of the conv backward's per-tile
+    start mask (local rows 28, 29, 60, 61), and at a tile's first row."""
+    wl = synth.Workload("cbwd_edges", 1, 320, 4, 64, 32, 2, "f32")
+    prm = synth.params(wl, 12, conv_bias=True)
+    raw = synth.raw_inputs(wl, 12)["xbc_raw"]
+    ids = torch.zeros(1, 320, dtype=torch.int32)
+    for t in (28, 64 + 29, 128 + 60, 192 + 61, 256):
+        ids[0, t:] += 1
+    gx = torch.randn(1, 320, wl.conv_dim, generator=torch.Generator().manual_seed(13))
+    g = lambda t: t.to(DEV)
+    got = gpu_lib.ssd_conv_bwd(g(raw), g(prm["conv_w"]), g(gx), H=wl.H, P=64, N=wl.N, G=wl.G, conv_b=g(prm["conv_b"]),
+                               doc_ids=g(ids))
+    torch.cuda.synchronize()
+    ref = oracle.conv_bwd(_np(raw), _np(prm["conv_w"]), _np(gx), _np(prm["conv_b"]), doc_ids=ids.numpy())
+    for k in ("raw", "w", "bias"):
+        _check(got[k], ref[k], f"d{k}")
+
+
 def _mixer_inputs(wl, seed, docs, mean_len=1024.0, L=None):
     prm = synth.params(wl, seed, conv_bias=True)
     raw = synth.raw_inputs(wl, seed, L=L)
