@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
 
@@ -172,6 +172,13 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
  *   D       f32 [H] or NULL (no skip)
  *   z       T   [B][L][H*P] row stride z_row_stride, or NULL (no gate)
  *   doc_ids i32 [B][L] or NULL
+ *   lengths i32 [B] or NULL: a ragged batch (mojolearn.Mamba3Block docs,
+ *               forward(): row b is real at positions t < lengths[b]).  Every
+ *               output at t >= lengths[b] is exactly +0.0; real positions are
+ *               causal and equal the row run alone at its own length
+ *               (bitwise without a workspace).  Values are read on the
+ *               device and clamped to [0, L]; padding inputs must be finite.
+ *               Not allowed with init_state / final_state (SSD_ERR_BAD_SHAPE).
  *   init_state  f32 [B][H][P][N] or NULL (zero)
  *   final_state f32 [B][H][P][N] or NULL; may equal init_state (in place)
  *   y       f32 [B][L][H*P]  row stride y_row_stride; must not overlap inputs
@@ -190,7 +197,7 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
                        int dt_softplus, const float *dt_bias,
                        const float *A, const float *D,
                        const void *z, int64_t z_row_stride,
-                       const int32_t *doc_ids,
+                       const int32_t *doc_ids, const int32_t *lengths,
                        const float *init_state, float *final_state,
                        float *y, int64_t y_row_stride,
                        void *workspace, size_t workspace_bytes, void *stream);
@@ -226,9 +233,10 @@ size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, i
  *                ssd_conv_fwd
  *   dt_raw       T  [B][L][H], row stride dt_raw_row_stride (even for bf16:
  *                read in 4-byte words; base 4-byte aligned)
- *   dt_bias      f32 [H] or NULL; A, D, z, doc_ids, init_state, final_state
- *                and y as in ssd_chunk_scan_fwd (final_state may equal
- *                init_state)
+ *   dt_bias      f32 [H] or NULL; A, D, z, doc_ids, lengths, init_state,
+ *                final_state and y as in ssd_chunk_scan_fwd (final_state may
+ *                equal init_state; lengths excludes every carried state,
+ *                the conv states included)
  *   conv_state_in, conv_state_out  T [B][K-1][conv_dim] or NULL, as in
  *                ssd_conv_fwd, except that they must not overlap
  *                (SSD_ERR_BAD_SHAPE): several workgroups read the incoming
@@ -246,7 +254,7 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
                   const void *dt_raw, int64_t dt_raw_row_stride, const float *dt_bias,
                   const float *A, const float *D,
                   const void *z, int64_t z_row_stride,
-                  const int32_t *doc_ids,
+                  const int32_t *doc_ids, const int32_t *lengths,
                   const void *conv_state_in, void *conv_state_out,
                   const float *init_state, float *final_state,
                   int act, float *y, int64_t y_row_stride,

@@ -65,12 +65,13 @@ def load() -> ctypes.CDLL:
     lib.ssd_conv_fwd.restype = I
     lib.ssd_conv_fwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I, P, I64, P, P]
     lib.ssd_chunk_scan_fwd.restype = I
+    # ... z, z_row_stride, doc_ids, lengths, init_state, final_state, y, y_row_stride, workspace, bytes, stream
     lib.ssd_chunk_scan_fwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P,
-                                       I64, P, P, P, P, I64, P, SZ, P]
+                                       I64, P, P, P, P, P, I64, P, SZ, P]
     lib.ssd_chunk_scan_workspace_size.restype = SZ
     lib.ssd_chunk_scan_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.ssd_mixer_fwd.restype = I
-    lib.ssd_mixer_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I64, P, P, P, P, P,
+    lib.ssd_mixer_fwd.argtypes = [I, I, I, I, I, I, I, I, I, P, I64, P, P, P, I64, P, P, P, P, I64, P, P, P, P, P, P,
                                   I, P, I64, P, SZ, P]
     lib.ssd_mixer_workspace_size.restype = SZ
     lib.ssd_mixer_workspace_size.argtypes = [I, I, I, I, I, I, I]
@@ -194,7 +195,7 @@ def ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
     return int(load().ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype))
 
 
-def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=None, init_state=None,
+def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=None, lengths=None, init_state=None,
                        final_state=None, y=None, dt_softplus=False, dt_bias=None, chunk=64, workspace=None,
                        stream=None):
     """SSD scan.  x [B,L,H*P], Bm/Cm [B,L,G*N] (same dtype), dt [B,L,H] fp32, A [H] fp32.
@@ -215,6 +216,7 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=
     _contig(D, "D", (H,))
     _contig(dt_bias, "dt_bias", (H,))
     _contig(doc_ids, "doc_ids", (B, L))
+    _contig(lengths, "lengths", (B,))
     _contig(init_state, "init_state", (B, H, P, N))
     _contig(final_state, "final_state", (B, H, P, N))
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -223,7 +225,7 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=
         _ptr(x, "x"), rs_x, _ptr(Bm, "Bm", x.dtype), rs_b, _ptr(Cm, "Cm", x.dtype), rs_c,
         _ptr(dt, "dt", torch.float32), rs_dt, int(bool(dt_softplus)), _ptr(dt_bias, "dt_bias", torch.float32),
         _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
-        _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32), _ptr(lengths, "lengths", torch.int32),
         _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
         _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
     _check(st)
@@ -235,7 +237,7 @@ def ssd_mixer_workspace_size(B, L, H, P, N, G, dtype=SSD_BF16) -> int:
 
 
 def ssd_mixer_fwd(xbc_raw, dt_raw, conv_w, A, *, H, P, N, G, K=4, conv_b=None, dt_bias=None, D=None, z=None,
-                  doc_ids=None, conv_state_in=None, conv_state_out=None, init_state=None, final_state=None,
+                  doc_ids=None, lengths=None, conv_state_in=None, conv_state_out=None, init_state=None, final_state=None,
                   act=SSD_ACT_SILU, y=None, chunk=64, workspace=None, stream=None):
     """Conv prologue + scan in one pass.  xbc_raw [B, L, conv_dim], dt_raw [B, L, H] (same dtype),
     conv_w [conv_dim, K] fp32, A [H] fp32; the rest as in ssd_conv_fwd / ssd_chunk_scan_fwd.
@@ -257,6 +259,7 @@ def ssd_mixer_fwd(xbc_raw, dt_raw, conv_w, A, *, H, P, N, G, K=4, conv_b=None, d
     _contig(A, "A", (H,))
     _contig(D, "D", (H,))
     _contig(doc_ids, "doc_ids", (B, L))
+    _contig(lengths, "lengths", (B,))
     _contig(conv_state_in, "conv_state_in", (B, K - 1, C))
     _contig(conv_state_out, "conv_state_out", (B, K - 1, C))
     _contig(init_state, "init_state", (B, H, P, N))
@@ -268,7 +271,7 @@ def ssd_mixer_fwd(xbc_raw, dt_raw, conv_w, A, *, H, P, N, G, K=4, conv_b=None, d
         _ptr(conv_w, "conv_w", torch.float32), _ptr(conv_b, "conv_b", torch.float32),
         _ptr(dt_raw, "dt_raw", xbc_raw.dtype), rs_dt, _ptr(dt_bias, "dt_bias", torch.float32),
         _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
-        _ptr(z, "z", xbc_raw.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32),
+        _ptr(z, "z", xbc_raw.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32), _ptr(lengths, "lengths", torch.int32),
         _ptr(conv_state_in, "conv_state_in", xbc_raw.dtype), _ptr(conv_state_out, "conv_state_out", xbc_raw.dtype),
         _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
         int(act), _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))

@@ -178,11 +178,14 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
                        int dt_softplus, const float* dt_bias,
                        const float* A, const float* D,
                        const void* z, int64_t z_row_stride,
-                       const int32_t* doc_ids,
+                       const int32_t* doc_ids, const int32_t* lengths,
                        const float* init_state, float* final_state,
                        float* y, int64_t y_row_stride,
                        void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "ssd_chunk_scan_fwd";
+    if (lengths && (init_state || final_state))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: lengths cannot be combined with init_state / final_state", fn);
+    TRY(check_ptr(fn, "lengths", lengths, false, false));
     TRY(check_dims(fn, B, L, H, P, N, G, 4, dtype));
     if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
     if (dt_softplus != 0 && dt_softplus != 1)
@@ -248,7 +251,9 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
         a.dec = a.hloc + u * (size_t)P * N;
         if (init_state) a.h0 = a.dec + ((u * sizeof(float) + 255) / 256) * 256 / sizeof(float);
     }
-    return hip_status(fn, ssd::launch_scan(a, s));
+    TRY(hip_status(fn, ssd::launch_scan(a, s)));
+    if (lengths) return hip_status(fn, ssd::launch_zero_rows(y, y_row_stride, B, L, H * P, lengths, s));
+    return ok();
 }
 
 size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {
@@ -265,12 +270,15 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
                   const void* dt_raw, int64_t dt_raw_row_stride, const float* dt_bias,
                   const float* A, const float* D,
                   const void* z, int64_t z_row_stride,
-                  const int32_t* doc_ids,
+                  const int32_t* doc_ids, const int32_t* lengths,
                   const void* conv_state_in, void* conv_state_out,
                   const float* init_state, float* final_state,
                   int act, float* y, int64_t y_row_stride,
                   void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "ssd_mixer_fwd";
+    if (lengths && (init_state || final_state || conv_state_in || conv_state_out))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: lengths cannot be combined with carried states", fn);
+    TRY(check_ptr(fn, "lengths", lengths, false, false));
     TRY(check_dims(fn, B, L, H, P, N, G, K, dtype));
     if (chunk != 64) return fail(SSD_ERR_UNSUPPORTED, "%s: chunk=%d is not supported (must be 64)", fn, chunk);
     if (act != SSD_ACT_SILU && act != SSD_ACT_NONE)
@@ -389,7 +397,9 @@ int ssd_mixer_fwd(int B, int L, int H, int P, int N, int G, int K, int chunk, in
         a.dec = a.hloc + u * (size_t)P * N;
         if (init_state) a.h0 = a.dec + ((u * sizeof(float) + 255) / 256) * 256 / sizeof(float);
     }
-    return hip_status(fn, ssd::launch_scan(a, s));
+    TRY(hip_status(fn, ssd::launch_scan(a, s)));
+    if (lengths) return hip_status(fn, ssd::launch_zero_rows(y, y_row_stride, B, L, H * P, lengths, s));
+    return ok();
 }
 
 int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos, int n,

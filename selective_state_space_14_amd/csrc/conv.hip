@@ -250,6 +250,27 @@ __global__ void copy_rows_kernel(const char* src, int64_t srs, int64_t sbs, char
     }
 }
 
+// Rows t >= lengths[b] of y (fp32 [B][L][width], rows `stride` floats apart)
+// set to +0.0; one workgroup per (64-row tile, batch row).  lengths are read
+// on the device and clamped to [0, L].
+__global__ void zero_rows_kernel(float* y, int64_t stride, int L, int width4, const int32_t* lengths) {
+    const int b = blockIdx.y, t0 = blockIdx.x * 64;
+    const int len = min(max(lengths[b], 0), L);
+    const int r0 = max(t0, len), r1 = min(t0 + 64, L);
+    for (int64_t i = threadIdx.x; i < (int64_t)(r1 - r0) * width4; i += blockDim.x) {
+        const int r = r0 + (int)(i / width4), w = (int)(i % width4);
+        *reinterpret_cast<float4*>(y + ((int64_t)b * L + r) * stride + 4 * w) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+}
+
+hipError_t launch_zero_rows(float* y, int64_t stride, int B, int L, int width, const int32_t* lengths,
+                            hipStream_t stream) {
+    if (B == 0 || L == 0 || width == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((L + 63) / 64, B), dim3(256), 0, stream, y, stride, L, width / 4,
+                       lengths);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy16(const void* src, void* dst, size_t n, hipStream_t stream) {
     if (n == 0 || src == dst) return hipSuccess;
     const unsigned blocks = (unsigned)((n + 255) / 256);

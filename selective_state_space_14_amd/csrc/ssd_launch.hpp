@@ -144,6 +144,10 @@ hipError_t launch_copy_rows(const void* src, int64_t src_row_stride, int64_t src
                             hipStream_t stream);
 
 size_t step_lds_bytes(int H, int P, int N, int G);
+// Ragged batches: rows t >= lengths[b] of y (fp32, width a multiple of 4,
+// rows 16-byte aligned) set to +0.0.
+hipError_t launch_zero_rows(float* y, int64_t stride, int B, int L, int width, const int32_t* lengths,
+                            hipStream_t stream);
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream);
 

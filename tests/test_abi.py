@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_version() == 1
+    assert lib.ssd_version() == 2
     assert lib.ssd_status_string(0) == b"SSD_OK"
     assert lib.ssd_status_string(2) == b"SSD_ERR_BAD_SHAPE"
     assert lib.ssd_status_string(99) == b"SSD_ERR_UNKNOWN"
@@ -53,7 +53,7 @@ MIS = 0x10008           # 8-byte aligned only
 def scan_args(**over):
     a = dict(B=2, L=128, H=32, P=64, N=64, G=8, chunk=64, dtype=1,
              x=FAKE, xs=3072, Bm=FAKE, bs=3072, Cm=FAKE, cs=3072, dt=FAKE, dts=32, dt_softplus=0, dt_bias=None,
-             A=FAKE, D=None, z=None, zs=0, doc=None, h0=None, hf=None, y=FAKE, ys=2048, ws=None, wsb=0,
+             A=FAKE, D=None, z=None, zs=0, doc=None, len=None, h0=None, hf=None, y=FAKE, ys=2048, ws=None, wsb=0,
              stream=None)
     a.update(over)
     return a
@@ -63,11 +63,13 @@ def call_scan(lib, a):
     return lib.ssd_chunk_scan_fwd(a["B"], a["L"], a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"],
                                   a["x"], a["xs"], a["Bm"], a["bs"], a["Cm"], a["cs"], a["dt"], a["dts"],
                                   a["dt_softplus"], a["dt_bias"], a["A"], a["D"], a["z"], a["zs"], a["doc"],
-                                  a["h0"], a["hf"], a["y"], a["ys"], a["ws"], a["wsb"], a["stream"])
+                                  a["len"], a["h0"], a["hf"], a["y"], a["ys"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status,needle", [
     (dict(H=30, G=8), 2, "H=30 is not divisible by G=8"),
+    (dict(len=FAKE, h0=FAKE), 2, "lengths cannot be combined"),
+    (dict(len=FAKE, hf=FAKE), 2, "lengths cannot be combined"),
     (dict(P=32), 3, "P=32"),
     (dict(N=48), 3, "N=48"),
     (dict(chunk=128), 3, "chunk=128"),
@@ -120,17 +122,18 @@ def test_conv_refusals(lib, over, status, needle):
 
 def call_mixer(lib, **over):
     a = dict(B=2, L=100, H=32, P=64, N=64, G=8, K=4, chunk=64, dtype=1, raw=FAKE, rs=3072, w=FAKE, b=None,
-             dtr=FAKE, dtrs=32, dtb=None, A=FAKE, D=None, z=None, zs=0, doc=None, si=None, so=None, h0=None,
+             dtr=FAKE, dtrs=32, dtb=None, A=FAKE, D=None, z=None, zs=0, doc=None, len=None, si=None, so=None, h0=None,
              hf=None, act=0, y=FAKE + 0x100000, ys=2048, ws=None, wsb=0, stream=None)
     a.update(over)
     return lib.ssd_mixer_fwd(a["B"], a["L"], a["H"], a["P"], a["N"], a["G"], a["K"], a["chunk"], a["dtype"],
                              a["raw"], a["rs"], a["w"], a["b"], a["dtr"], a["dtrs"], a["dtb"], a["A"], a["D"],
-                             a["z"], a["zs"], a["doc"], a["si"], a["so"], a["h0"], a["hf"], a["act"], a["y"],
+                             a["z"], a["zs"], a["doc"], a["len"], a["si"], a["so"], a["h0"], a["hf"], a["act"], a["y"],
                              a["ys"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status,needle", [
     (dict(K=2), 3, "K=2"),
+    (dict(len=FAKE, so=FAKE), 2, "lengths cannot be combined with carried states"),
     (dict(chunk=32), 3, "chunk=32"),
     (dict(act=3), 3, "act=3"),
     (dict(raw=None), 1, "xbc_raw is NULL"),
