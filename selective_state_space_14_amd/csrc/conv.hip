@@ -8,7 +8,9 @@
 // coalesced row segments.  A ring of kBatch rows is kept loading ahead of
 // the row being convolved.  SiLU uses the hardware exp2 and reciprocal (a
 // few fp32 ulp, far inside one bf16 ulp).  An extra column of blocks
-// (blockIdx.x == number of channel blocks) computes dt for the same tokens.
+// (blockIdx.x == number of channel blocks) computes dt for the same tokens,
+// in 16-byte pieces when the heads and rows line up (else element by
+// element), with several loads per lane in flight.
 //
 // Document isolation (Mini-K3-1H card, "Checkpoint and training": the conv
 // history resets at every document boundary): when token t starts a new
@@ -30,8 +32,10 @@ namespace ssd {
 namespace {
 
 constexpr int kConvThreads = 64;
-constexpr int kTile = 64;     // tokens per block
+constexpr int kTile = 64;     // tokens per block (a multiple of 64)
+constexpr int kStartWords = kTile / 64;
 constexpr int kBatch = 8;     // rows loaded before use
+constexpr int kDtBatch = 8;   // dt elements loaded per lane before use
 
 template <typename T> struct CV;
 template <> struct CV<float> {
@@ -76,21 +80,80 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
         // ---- dt = softplus(dt_raw + dt_bias) for the tile's tokens
         if (a.dt_raw == nullptr) return;
         const int H = a.H;
-        for (int i = threadIdx.x; i < (t1 - t0) * H; i += kConvThreads) {
-            const int t = t0 + i / H, h = i % H;
-            const float r = CV<T>::scalar(a.dt_raw, ((size_t)b * a.Lb_in + t) * a.dt_stride + h);
-            a.dt_out[((size_t)b * a.Lb_out + t) * H + h] = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
+        // 16-byte pieces: a lane takes DV consecutive heads of one token when
+        // the heads, the row stride and the three arrays line up
+        constexpr int DV = 16 / sizeof(T);
+        const bool vec = H % DV == 0 && a.dt_stride % DV == 0 && (reinterpret_cast<uintptr_t>(a.dt_raw) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.dt_out) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.dt_bias) & 15) == 0;
+        if (vec) {
+            const int hv = H / DV;               // pieces per token
+            const int n = (t1 - t0) * hv;
+            for (int i0 = threadIdx.x; i0 < n; i0 += kDtBatch * kConvThreads) {
+                uint4 r[kDtBatch];
+#pragma unroll
+                for (int u = 0; u < kDtBatch; ++u) {
+                    const int i = min(i0 + u * kConvThreads, n - 1);
+                    r[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.dt_raw) +
+                                                           ((size_t)b * a.Lb_in + t0 + i / hv) * a.dt_stride +
+                                                           (i % hv) * DV);
+                }
+#pragma unroll
+                for (int u = 0; u < kDtBatch; ++u) {
+                    const int i = i0 + u * kConvThreads;
+                    if (i < n) {
+                        const int h = (i % hv) * DV;
+                        float v[DV];
+                        CV<T>::unpack(r[u], v);
+                        float* o = a.dt_out + ((size_t)b * a.Lb_out + t0 + i / hv) * H + h;
+#pragma unroll
+                        for (int e = 0; e < DV; e += 4) {
+                            float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
+                            if (a.dt_bias) bb = *reinterpret_cast<const float4*>(a.dt_bias + h + e);
+                            *reinterpret_cast<float4*>(o + e) =
+                                make_float4(softplus_f(v[e] + bb.x), softplus_f(v[e + 1] + bb.y),
+                                            softplus_f(v[e + 2] + bb.z), softplus_f(v[e + 3] + bb.w));
+                        }
+                    }
+                }
+            }
+            return;
+        }
+        const int n = (t1 - t0) * H;
+        // kDtBatch independent loads per lane are in flight before any is used
+        // (indices clamp to the last element, whose store alone is kept)
+        for (int i0 = threadIdx.x; i0 < n; i0 += kDtBatch * kConvThreads) {
+            float r[kDtBatch];
+#pragma unroll
+            for (int u = 0; u < kDtBatch; ++u) {
+                const int i = min(i0 + u * kConvThreads, n - 1);
+                r[u] = CV<T>::scalar(a.dt_raw, ((size_t)b * a.Lb_in + t0 + i / H) * a.dt_stride + i % H);
+            }
+#pragma unroll
+            for (int u = 0; u < kDtBatch; ++u) {
+                const int i = i0 + u * kConvThreads;
+                if (i < n) {
+                    const int h = i % H;
+                    a.dt_out[((size_t)b * a.Lb_out + t0 + i / H) * H + h] =
+                        softplus_f(r[u] + (a.dt_bias ? a.dt_bias[h] : 0.0f));
+                }
+            }
         }
         return;
     }
 
-    // document starts inside the tile as a bit mask (bit i: token t0 + i starts
-    // a document), one doc-id pair per lane; built before any lane leaves
-    uint64_t starts = 0;
+    // document starts inside the tile as a bit mask (bit i of word j: token
+    // t0 + 64 j + i starts a document), one doc-id pair per lane and word;
+    // built before any lane leaves
+    uint64_t starts[kStartWords] = {};
     if (doc) {
-        const int tt = min(t0 + (int)threadIdx.x, t1 - 1);
-        const bool s_here = t0 + (int)threadIdx.x < t1 && tt > 0 && doc[tt] != doc[tt - 1];
-        starts = __ballot(s_here);
+#pragma unroll
+        for (int j = 0; j < kStartWords; ++j) {
+            const int tj = t0 + 64 * j + (int)threadIdx.x;
+            const int tt = min(tj, t1 - 1);
+            const bool s_here = tj < t1 && tt > 0 && doc[tt] != doc[tt - 1];
+            starts[j] = __ballot(s_here);
+        }
     }
 
     const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * VEC;
@@ -143,7 +206,7 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv_kernel(ConvArgs a) {
     auto conv_row = [&](const uint4& rv, int t) {
         float cur[VEC], o[VEC];
         CV<T>::unpack(rv, cur);
-        if ((starts >> (t - t0)) & 1) {
+        if ((starts[(t - t0) >> 6] >> ((t - t0) & 63)) & 1) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) h3[e] = h2[e] = h1[e] = 0.0f;
         }

@@ -65,6 +65,31 @@ def test_conv_parity_small(gpu_lib, dtype, docs, state, act, bias):
     np.testing.assert_array_equal(hp.np64(st_out), sref)
 
 
+@pytest.mark.parametrize("dtype,H", [("bf16", 8), ("bf16", 16), ("f32", 4), ("f32", 12)])
+def test_conv_dt_piece_and_element_paths(gpu_lib, dtype, H):
+    """dt = softplus(dt_raw + dt_bias) read in 16-byte pieces (aligned rows, H a multiple of the piece) and element
+    by element (the same values in a view 4 bytes off 16-byte alignment, row stride H + 4 bytes): bit-identical,
+    and within the fp32 bar of the oracle."""
+    wl = small_wl(dtype, H=H, L=203, B=2)
+    _say(f"conv dt paths {dtype} H={H}")
+    prm = synth.params(wl, 4)
+    raw = synth.raw_inputs(wl, 4)
+    off = 2 if dtype == "bf16" else 1                 # elements in 4 bytes (the call's alignment floor)
+    wide = torch.zeros(wl.B, wl.L, H + off, dtype=wl.torch_dtype)
+    wide[:, :, off:] = raw["dt_raw"]
+    g = lambda t: None if t is None else t.to(DEV)
+    outs = []
+    for dt_in in (g(raw["dt_raw"]), g(wide)[:, :, off:]):
+        _, dt = gpu_lib.ssd_conv_fwd(g(raw["xbc_raw"]), g(prm["conv_w"]), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                     dt_raw=dt_in, dt_bias=g(prm["dt_bias"]))
+        outs.append(dt)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "piece and element paths differ"
+    _, dref, _ = oracle.conv(raw["xbc_raw"], prm["conv_w"], prm["conv_b"], raw["dt_raw"], prm["dt_bias"], None, None,
+                             act=0, want_state=True)
+    hp.assert_fp32(outs[0], dref, "dt_out")
+
+
 @pytest.mark.parametrize("L", [1, 2, 3, 4, 31, 32, 33])
 def test_conv_short_and_in_place_state(gpu_lib, L):
     wl = small_wl("bf16", L=L, docs=True, B=3)
