@@ -416,9 +416,15 @@ def cpu_baseline(synth, wl, rows):
     oracle.forward(raw["xbc_raw"], prm["conv_w"], None, raw["dt_raw"], prm["dt_bias"], prm["A"], prm["D"], raw["z"],
                    H=wl.H, P=wl.P, N=wl.N, G=wl.G, round_bf16=True)
     sec = time.perf_counter() - t0
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": rows * wl.L * wl.H / sec, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {wl.B} batch rows of the {wl.name} workload (L={wl.L}, all {wl.H} heads), "
-                      f"conv + scan in fp64, {sec:.2f} s"}
+                      f"conv + scan in fp64, {sec:.2f} s on {threads} threads of {model}"}
 
 
 def main():
