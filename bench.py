@@ -10,7 +10,8 @@ so no step runs out of the 256 MB last-level cache.
 
 Prints ONE JSON line: value = head-tokens (B*L*H) per second over the whole
 step; "roofline" = the scan call's algorithmic bytes / its average duration
-(HIP events around each call on the launch stream) against 8 TB/s;
+against 8 TB/s, the duration measured over back-to-back launches of that call
+alone, bracketed by one pair of HIP events on the launch stream;
 "cpu_baseline" = the fp64 oracle (conv + scan) timed on this host.  Under
 "extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
 two kernels behind one call; fused: the conv computed inside the scan
@@ -117,24 +118,18 @@ def step_bytes(wl):
     return b
 
 
-class Timer:
-    """Sums HIP-event intervals recorded on the current (launch) stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def around(self, fn):
-        t = self.torch
-        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        s.record()
-        out = fn()
-        e.record()
-        self.pairs.append((s, e))
-        return out
-
-    def mean_ms(self):
-        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+def loop_ms(torch, calls, n):
+    """Mean duration in ms of one call when `n` calls run back to back on the launch stream (cycling through
+    `calls`, e.g. one per input set), bracketed by ONE pair of HIP events: no event or host work sits between
+    the kernels, so the figure is the calls' own device time plus the launch gaps between them."""
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(n):
+        calls[i % len(calls)]()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
 
 
 def mixer_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0, plan="staged"):
@@ -155,30 +150,19 @@ def mixer_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed
     y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
     fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
     cs = torch.empty(wl.B, 3, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
-    t_mix = Timer(torch)
-
-    def one(i, timed):
-        raw, ids = sets[i % 2]
-        f = lambda: ssd.ssd_mixer_fwd(raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], H=wl.H, P=wl.P,
-                                      N=wl.N, G=wl.G, dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], doc_ids=ids,
-                                      conv_state_out=cs, init_state=raw["h0"] if h0 else None, final_state=fs,
-                                      y=y, workspace=ws)
-        t_mix.around(f) if timed else f()
-
+    calls = []
+    for k in range(2):
+        raw, ids = sets[k]
+        calls.append(lambda raw=raw, ids=ids: ssd.ssd_mixer_fwd(
+            raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+            dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], doc_ids=ids, conv_state_out=cs,
+            init_state=raw["h0"] if h0 else None, final_state=fs, y=y, workspace=ws))
     for i in range(warmup):
-        one(i, False)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        one(i, True)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+        calls[i % 2]()
+    ms = loop_ms(torch, calls, steps)
     mb = mixer_bytes(wl, docs, h0)
-    mix_ms = t_mix.mean_ms()
-    return {"ms_per_step": ms, "value": wl.B * wl.L * wl.H / (ms * 1e-3), "mixer_us": mix_ms * 1e3,
-            "mixer_bytes": mb, "mixer_GBs": mb / (mix_ms * 1e-3) / 1e9, "mixer_workspace_bytes": ws_bytes}
+    return {"ms_per_step": ms, "value": wl.B * wl.L * wl.H / (ms * 1e-3), "mixer_us": ms * 1e3,
+            "mixer_bytes": mb, "mixer_GBs": mb / (ms * 1e-3) / 1e9, "mixer_workspace_bytes": ws_bytes}
 
 
 def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0):
@@ -194,40 +178,28 @@ def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, se
     ws_bytes = ssd.ssd_chunk_scan_workspace_size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G,
                                                  ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    xbc = torch.empty(wl.B, wl.L, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
-    dt = torch.empty(wl.B, wl.L, wl.H, dtype=torch.float32, device=dev)
     y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
     fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
-    t_conv, t_scan = Timer(torch), Timer(torch)
-
-    def one(i, timed):
-        raw, ids = sets[i % 2]
-        conv = lambda: ssd.ssd_conv_fwd(raw["xbc_raw"], prm["conv_w"], H=wl.H, P=wl.P, N=wl.N, G=wl.G,
-                                        dt_raw=raw["dt_raw"], dt_bias=prm["dt_bias"], doc_ids=ids,
-                                        xbc_out=xbc, dt_out=dt)
-        scan = lambda: ssd.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, prm["A"],
-                                              H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=prm["D"], z=raw["z"],
-                                              doc_ids=ids, init_state=raw["h0"] if h0 else None,
-                                              final_state=fs, y=y, workspace=ws)
-        if timed:
-            t_conv.around(conv)
-            t_scan.around(scan)
-        else:
-            conv()
-            scan()
-
+    convs, scans = [], []
+    for k in range(2):   # each input set has its own conv output, so the scan-only loop reads real data
+        raw, ids = sets[k]
+        xbc = torch.empty(wl.B, wl.L, wl.conv_dim, dtype=wl.torch_dtype, device=dev)
+        dt = torch.empty(wl.B, wl.L, wl.H, dtype=torch.float32, device=dev)
+        convs.append(lambda raw=raw, ids=ids, xbc=xbc, dt=dt: ssd.ssd_conv_fwd(
+            raw["xbc_raw"], prm["conv_w"], H=wl.H, P=wl.P, N=wl.N, G=wl.G, dt_raw=raw["dt_raw"],
+            dt_bias=prm["dt_bias"], doc_ids=ids, xbc_out=xbc, dt_out=dt))
+        scans.append(lambda raw=raw, ids=ids, xbc=xbc, dt=dt: ssd.ssd_chunk_scan_fwd(
+            xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, prm["A"], H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+            D=prm["D"], z=raw["z"], doc_ids=ids, init_state=raw["h0"] if h0 else None, final_state=fs, y=y,
+            workspace=ws))
+    steps_fn = [lambda k=k: (convs[k](), scans[k]()) for k in range(2)]
     for i in range(warmup):
-        one(i, False)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        one(i, True)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+        steps_fn[i % 2]()
+    # the step (conv then scan, back to back), then each call alone over as many launches
+    ms = loop_ms(torch, steps_fn, steps)
+    conv_ms = loop_ms(torch, convs, steps)
+    scan_ms = loop_ms(torch, scans, steps)
     sb, cb = scan_bytes(wl, docs, h0), conv_bytes(wl, docs)
-    scan_ms, conv_ms = t_scan.mean_ms(), t_conv.mean_ms()
     return {
         "ms_per_step": ms,
         "value": wl.B * wl.L * wl.H / (ms * 1e-3),
@@ -247,28 +219,15 @@ def decode_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
     conv = torch.randn(wl.B, 3, wl.conv_dim, generator=g, device=dev).to(wl.torch_dtype)
     ins = [synth.step_inputs(wl, s, seed, device=dev) for s in range(2)]
     y = torch.empty(wl.B, wl.H * wl.P, dtype=torch.float32, device=dev)
-    t_step = Timer(torch)
-
-    def one(i, timed):
-        st = ins[i % 2]
-        f = lambda: ssd.ssd_step(st["xbc_raw"], st["dt_raw"], prm["conv_w"], prm["A"], conv, ssm, H=wl.H, P=wl.P,
-                                 N=wl.N, G=wl.G, z=st["z"], dt_bias=prm["dt_bias"], D=prm["D"], y=y)
-        t_step.around(f) if timed else f()
-
+    calls = [lambda st=st: ssd.ssd_step(st["xbc_raw"], st["dt_raw"], prm["conv_w"], prm["A"], conv, ssm, H=wl.H,
+                                        P=wl.P, N=wl.N, G=wl.G, z=st["z"], dt_bias=prm["dt_bias"], D=prm["D"], y=y)
+             for st in ins]
     for i in range(warmup):
-        one(i, False)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        one(i, True)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+        calls[i % 2]()
+    ms = loop_ms(torch, calls, steps)
     kb = step_bytes(wl)
-    k_ms = t_step.mean_ms()
-    return {"ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "step_us": k_ms * 1e3, "step_bytes": kb,
-            "step_GBs": kb / (k_ms * 1e-3) / 1e9}
+    return {"ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "step_us": ms * 1e3, "step_bytes": kb,
+            "step_GBs": kb / (ms * 1e-3) / 1e9}
 
 
 def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
@@ -336,22 +295,13 @@ def s6_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     y = torch.empty(wl.B, wl.L, Dn, dtype=torch.float32, device=dev)
     fs = torch.empty(wl.B, Dn, wl.N, dtype=torch.float32, device=dev)
-    t = Timer(torch)
-
-    def one(i, timed):
-        a = sets[i % 2]
-        f = lambda: ssd.ssd_s6_scan_fwd(a["x"], a["dt_raw"], prm["A"], a["Bm"], a["Cm"], D_skip=prm["D_skip"],
-                                        z=a["z"], final_state=fs, y=y, dt_softplus=True, dt_bias=prm["dt_bias"],
-                                        workspace=ws)
-        t.around(f) if timed else f()
-
+    calls = [lambda a=a: ssd.ssd_s6_scan_fwd(a["x"], a["dt_raw"], prm["A"], a["Bm"], a["Cm"], D_skip=prm["D_skip"],
+                                             z=a["z"], final_state=fs, y=y, dt_softplus=True,
+                                             dt_bias=prm["dt_bias"], workspace=ws)
+             for a in sets]
     for i in range(warmup):
-        one(i, False)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        one(i, True)
-    torch.cuda.synchronize()
-    ms = t.mean_ms()
+        calls[i % 2]()
+    ms = loop_ms(torch, calls, steps)
     upd = wl.B * wl.L * Dn * wl.N
     peak = VALU_LANE_OPS / S6_SLOTS_PER_UPDATE
     nb = s6_bytes(wl)
@@ -384,20 +334,11 @@ def bwd_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
     code = ssd.SSD_BF16 if wl.dtype == "bf16" else ssd.SSD_F32
     ws = torch.empty(ssd.ssd_mixer_bwd_workspace_size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, code), dtype=torch.uint8,
                      device=dev)
-    t = Timer(torch)
-
-    def one(timed):
-        f = lambda: ssd.ssd_mixer_bwd(raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], gy, H=wl.H, P=wl.P,
-                                      N=wl.N, G=wl.G, dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], workspace=ws)
-        t.around(f) if timed else f()
-
+    call = lambda: ssd.ssd_mixer_bwd(raw["xbc_raw"], raw["dt_raw"], prm["conv_w"], prm["A"], gy, H=wl.H, P=wl.P,
+                                     N=wl.N, G=wl.G, dt_bias=prm["dt_bias"], D=prm["D"], z=raw["z"], workspace=ws)
     for _ in range(warmup):
-        one(False)
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        one(True)
-    torch.cuda.synchronize()
-    ms = t.mean_ms()
+        call()
+    ms = loop_ms(torch, [call], steps)
     fl = bwd_flops(wl)
     return {"workload": wl.name + " (ssd_mixer_bwd: conv recompute + scan backward + conv backward)",
             "ms_per_step": ms, "value": wl.B * wl.L * wl.H / (ms * 1e-3), "unit": "head-tokens/s",
