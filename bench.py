@@ -6,7 +6,9 @@ ssd_conv_fwd (causal conv + SiLU + dt softplus) then ssd_chunk_scan_fwd
 (chunked scan, groups, D skip, z gate, final state), at the Mini-K3 mixer
 shape B=5, L=8192, H=32, P=64, N=64, G=8, bf16 inputs, fp32 state and y.
 Inputs are resident in HBM before the timed region; two input sets alternate
-so no step runs out of the 256 MB last-level cache.
+so no step runs out of the 256 MB last-level cache.  The default warm-up of 50
+steps (~15 ms) runs past the GPU's ramp from idle: from a cold start the first
+~40 steps run up to 10% slower than the steady state.
 
 Prints ONE JSON line: value = head-tokens (B*L*H) per second over the whole
 step; "roofline" = the scan call's algorithmic bytes / its average duration
@@ -372,7 +374,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=5)
