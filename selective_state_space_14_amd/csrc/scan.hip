@@ -23,7 +23,9 @@
 //
 // Kernels:
 //   ssd_scan_kernel<float, N, MODE>  fp32 inputs: one (b, h) per workgroup,
-//       register-prefetch staging, fp32 MFMA; MODE kStateOnly is its pre-pass.
+//       register-prefetch staging, operands split into bf16 high and low
+//       halves in LDS and multiplied on the bf16 MFMA (three products per
+//       tile); MODE kStateOnly is its pre-pass.
 //   ssd_scan_bf16_kernel<N, SP, HPW> bf16 inputs: HPW heads of one B/C group
 //       per workgroup, every per-chunk input staged by LDS DMA, bf16 MFMA.
 //   ssd_scan_state_kernel<...>       bf16 state-only pre-pass of the split.
@@ -55,52 +57,12 @@ constexpr int kXS = Q + kPad;    // row stride of the s-contiguous matrices
 constexpr int kNumMTiles = 10;   // 16x16 tiles (si <= ti) of the 64x64 lower triangle
 
 template <typename T> struct Tr;
-template <> struct Tr<uint16_t> {          // bf16 storage
-    using E = uint16_t;
-    using Frag = FragBF;
-    using Raw4 = uint2;                    // 4 consecutive elements
-    static constexpr int VE = 8;           // elements per 16 bytes
-    __device__ static Frag ld(const E* p) { const uint2 v = *reinterpret_cast<const uint2*>(p); return {v.x, v.y}; }
-    __device__ static Frag zero() { return {0u, 0u}; }
-    __device__ static Frag from_acc(f32x4 v) { return frag_from_f32(v); }
-    __device__ static f32x4 mma2(f32x4 acc, Frag a0, Frag a1, Frag b0, Frag b1) { return mma_bf16(acc, a0, a1, b0, b1); }
-    __device__ static float el(Raw4 v, int r) {
-        const uint32_t w = r < 2 ? v.x : v.y;
-        return (r & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-    __device__ static E from_f(float v) { return (E)f32_to_bf16_bits(v); }
-    __device__ static E raw_el(Raw4 v, int r) {
-        const uint32_t w = r < 2 ? v.x : v.y;
-        return (E)((r & 1) ? (w >> 16) : (w & 0xffffu));
-    }
-    __device__ static Raw4 zero4() { return make_uint2(0u, 0u); }
-    // two elements of consecutive rows, packed for one LDS store
-    __device__ static uint32_t pair(uint4 lo_row, uint4 hi_row, int e) {
-        const uint32_t a = (&lo_row.x)[e >> 1], b = (&hi_row.x)[e >> 1];
-        return (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    using Pair = uint32_t;
-};
-template <> struct Tr<float> {             // fp32 storage
+template <> struct Tr<float> {             // fp32 storage (register side of the generic kernel)
     using E = float;
-    using Frag = float4;
     using Raw4 = float4;
     static constexpr int VE = 4;
-    __device__ static Frag ld(const E* p) { return *reinterpret_cast<const float4*>(p); }
-    __device__ static Frag zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ static Frag from_acc(f32x4 v) { return make_float4(v[0], v[1], v[2], v[3]); }
-    __device__ static f32x4 mma2(f32x4 acc, Frag a0, Frag a1, Frag b0, Frag b1) {
-        acc = mma_f32(acc, a0, b0);
-        return mma_f32(acc, a1, b1);
-    }
     __device__ static float el(Raw4 v, int r) { return (&v.x)[r]; }
-    __device__ static E from_f(float v) { return v; }
-    __device__ static E raw_el(Raw4 v, int r) { return (&v.x)[r]; }
     __device__ static Raw4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ static float2 pair(uint4 lo_row, uint4 hi_row, int e) {
-        return make_float2(__uint_as_float((&lo_row.x)[e]), __uint_as_float((&hi_row.x)[e]));
-    }
-    using Pair = float2;
 };
 
 // Tiles of the lower triangle, dealt round-robin to the waves: tile k -> (si, ti).
@@ -131,6 +93,58 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // decay (negative if a document starts inside it, i.e. the carried state is
 // dropped there) into the workspace.
 enum { kFull = 0, kStateOnly = 1 };
+
+// fp32 operands of the generic kernel's contractions are held in LDS as two
+// bf16 planes, v = hi + lo + e with hi = bf16(v), lo = bf16(v - hi) (both
+// rounded to nearest even; v - hi is exact), so |e| <= 2^-18 |v|.  A matrix
+// region of `cnt` fp32 slots keeps its byte size: the hi plane is its first
+// cnt 16-bit elements, the lo plane the next cnt.  A product of two split
+// operands is formed on the bf16 MFMA as lo*hi + hi*lo + hi*hi with fp32
+// accumulation (the lo*lo term, ~2^-16 of the product, is dropped): three
+// 16x16x32 MFMAs replace the eight 16x16x4 fp32 ones for the same 32-wide K
+// range, at ~2^-16 relative error per product.
+struct Split4 { FragBF hi, lo; };      // 4 consecutive K elements of a fragment
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
+}
+__device__ __forceinline__ Split4 split4(float a, float b, float c, float d) {
+    Split4 r;
+    split_pair(a, b, r.hi.a, r.lo.a);
+    split_pair(c, d, r.hi.b, r.lo.b);
+    return r;
+}
+__device__ __forceinline__ Split4 split_zero() { return {{0u, 0u}, {0u, 0u}}; }
+// the 4 elements at index i (a multiple of 4) of a split region of cnt slots
+__device__ __forceinline__ Split4 pld(const uint16_t* p, int cnt, int i) {
+    const uint2 h = *reinterpret_cast<const uint2*>(p + i);
+    const uint2 l = *reinterpret_cast<const uint2*>(p + cnt + i);
+    return {{h.x, h.y}, {l.x, l.y}};
+}
+__device__ __forceinline__ void pst4(uint16_t* p, int cnt, int i, float a, float b, float c, float d) {
+    const Split4 v = split4(a, b, c, d);
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(v.hi.a, v.hi.b);
+    *reinterpret_cast<uint2*>(p + cnt + i) = make_uint2(v.lo.a, v.lo.b);
+}
+// two consecutive elements at index i (even)
+__device__ __forceinline__ void pst2(uint16_t* p, int cnt, int i, float a, float b) {
+    uint32_t hi, lo;
+    split_pair(a, b, hi, lo);
+    *reinterpret_cast<uint32_t*>(p + i) = hi;
+    *reinterpret_cast<uint32_t*>(p + cnt + i) = lo;
+}
+__device__ __forceinline__ void pst1(uint16_t* p, int cnt, int i, float v) {
+    const uint32_t hi = f32_to_bf16_bits(v);
+    p[i] = (uint16_t)hi;
+    p[cnt + i] = (uint16_t)f32_to_bf16_bits(v - __uint_as_float(hi << 16));
+}
+// acc += A B over two 16-wide K blocks (a0/b0: block 0, a1/b1: block 1)
+__device__ __forceinline__ f32x4 mma_split(f32x4 acc, const Split4& a0, const Split4& a1, const Split4& b0,
+                                           const Split4& b1) {
+    acc = mma_bf16(acc, a0.lo, a1.lo, b0.hi, b1.hi);
+    acc = mma_bf16(acc, a0.hi, a1.hi, b0.lo, b1.lo);
+    return mma_bf16(acc, a0.hi, a1.hi, b0.hi, b1.hi);
+}
 
 // LDS plan (element offsets).  kFull: region R0 holds B row-major while the
 // M^T tiles are built, then this wave's (w o X)^T for the chunk state; C,
@@ -170,7 +184,6 @@ template <typename T, int N, int MODE>
 __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
     using R = Tr<T>;
     using E = typename R::E;
-    using Frag = typename R::Frag;
     using Raw4 = typename R::Raw4;
     using LD = Lds<T, N, MODE>;
     using CR = ChunkRegs<T, N>;
@@ -180,13 +193,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
     constexpr bool BF16 = !std::is_same<T, float>::value;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    E* sm = reinterpret_cast<E*>(smem_raw);
-    E* sB = sm + LD::oB;
-    E* sXwt = sm + LD::oXwt;
-    E* sC = sm + LD::oC;
-    E* sBt = sm + LD::oBt;
-    E* sXt = sm + LD::oXt;
-    E* sM = sm + LD::oM;
+    static_assert(!BF16, "the generic kernel takes fp32 inputs");
+    // split regions (see Split4): base of the hi plane and the region's slot count
+    auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(smem_raw + off * sizeof(E)); };
+    uint16_t* sB = plane(LD::oB);                 // B [Q][NS], later (w o X)^T [64][kXS]
+    uint16_t* sXwt = plane(LD::oXwt);
+    uint16_t* sC = plane(LD::oC);
+    uint16_t* sBt = plane(LD::oBt);
+    uint16_t* sXt = plane(LD::oXt);
+    uint16_t* sM = plane(LD::oM);
+    constexpr int cR0 = (int)LD::r0, cC = Q * NS, cBt = N * kXS, cXt = 64 * kXS, cM = kNumMTiles * 256;
+    constexpr int cXw = FULL ? cR0 : cXt;
     float* sScal = reinterpret_cast<float*>(smem_raw + ((LD::nE * sizeof(E) + 15) / 16) * 16);
     float* sCs = sScal;
     float* sDt = sScal + Q;
@@ -361,15 +378,18 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                     if (t0 + s >= tend) { b0 = zz; c0 = zz; }
                     if (t0 + s + 1 >= tend) { b1 = zz; c1 = zz; }
                 }
+                const float* fb0 = reinterpret_cast<const float*>(&b0);
+                const float* fb1 = reinterpret_cast<const float*>(&b1);
                 if (FULL) {
-                    *reinterpret_cast<uint4*>(sB + s * NS + n0) = b0;
-                    *reinterpret_cast<uint4*>(sB + (s + 1) * NS + n0) = b1;
-                    *reinterpret_cast<uint4*>(sC + s * NS + n0) = c0;
-                    *reinterpret_cast<uint4*>(sC + (s + 1) * NS + n0) = c1;
+                    const float* fc0 = reinterpret_cast<const float*>(&c0);
+                    const float* fc1 = reinterpret_cast<const float*>(&c1);
+                    pst4(sB, cR0, s * NS + n0, fb0[0], fb0[1], fb0[2], fb0[3]);
+                    pst4(sB, cR0, (s + 1) * NS + n0, fb1[0], fb1[1], fb1[2], fb1[3]);
+                    pst4(sC, cC, s * NS + n0, fc0[0], fc0[1], fc0[2], fc0[3]);
+                    pst4(sC, cC, (s + 1) * NS + n0, fc1[0], fc1[1], fc1[2], fc1[3]);
                 }
 #pragma unroll
-                for (int e = 0; e < R::VE; ++e)
-                    *reinterpret_cast<typename R::Pair*>(sBt + (n0 + e) * kXS + s) = R::pair(b0, b1, e);
+                for (int e = 0; e < R::VE; ++e) pst2(sBt, cBt, (n0 + e) * kXS + s, fb0[e], fb1[e]);
             }
         }
         // ---- (w o X)^T (kStateOnly) or X^T (kFull) of this wave's channels
@@ -378,11 +398,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
             const int t = 16 * ti + j16;
             if (FULL) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sXt[(p0 + 4 * q4 + r) * kXS + t] = R::raw_el(xv[ti], r);
+                for (int r = 0; r < 4; ++r) pst1(sXt, cXt, (p0 + 4 * q4 + r) * kXS + t, R::el(xv[ti], r));
             } else {
                 const float w = sWw[t];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sXwt[(p0 + 4 * q4 + r) * kXS + t] = R::from_f(w * R::el(xv[ti], r));
+                for (int r = 0; r < 4; ++r) pst1(sXwt, cXt, (p0 + 4 * q4 + r) * kXS + t, w * R::el(xv[ti], r));
             }
         }
         // ---- per-token scalars of the chunk
@@ -404,11 +424,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += 2) {
-                    const Frag a0 = R::ld(sB + (16 * si + j16) * NS + 16 * nb + 4 * q4);
-                    const Frag b0 = R::ld(sC + (16 * ti + j16) * NS + 16 * nb + 4 * q4);
-                    const Frag a1 = nb + 1 < NT ? R::ld(sB + (16 * si + j16) * NS + 16 * (nb + 1) + 4 * q4) : R::zero();
-                    const Frag b1 = nb + 1 < NT ? R::ld(sC + (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4) : R::zero();
-                    acc = R::mma2(acc, a0, a1, b0, b1);
+                    const Split4 a0 = pld(sB, cR0, (16 * si + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 b0 = pld(sC, cC, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 a1 = nb + 1 < NT ? pld(sB, cR0, (16 * si + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                                                  : split_zero();
+                    const Split4 b1 = nb + 1 < NT ? pld(sC, cC, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                                                  : split_zero();
+                    acc = mma_split(acc, a0, a1, b0, b1);
                 }
                 // acc[r] = G^T[s = 16si + 4q4 + r][t = 16ti + j16]
                 const int t = 16 * ti + j16;
@@ -423,12 +445,12 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                     const bool ok = (si < ti || s <= t) && (!has_bnd || s >= segt);
                     m[r] = ok ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
                 }
-                *reinterpret_cast<Frag*>(sM + kt * 256 + lane * 4) = R::from_acc(m);
+                pst4(sM, cM, kt * 256 + lane * 4, m[0], m[1], m[2], m[3]);
             }
-            // bf16 (or fp32) copy of the carried state for the C.H contraction
-            Frag hf[NT];
+            // split copy of the carried state for the C.H contraction
+            Split4 hf[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hf[nt] = R::from_acc(Hs[nt]);
+            for (int nt = 0; nt < NT; ++nt) hf[nt] = split4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
             __syncthreads();   // all M^T tiles are in LDS; B row-major is no longer read
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, then the output
@@ -437,20 +459,21 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
-                    const Frag a0 = R::ld(sXt + (p0 + j16) * kXS + 16 * sb + 4 * q4);
-                    const Frag b0 = R::ld(sM + mtile_index(sb, ti) * 256 + lane * 4);
+                    const Split4 a0 = pld(sXt, cXt, (p0 + j16) * kXS + 16 * sb + 4 * q4);
+                    const Split4 b0 = pld(sM, cM, mtile_index(sb, ti) * 256 + lane * 4);
                     const bool two = sb + 1 <= ti;
-                    const Frag a1 = two ? R::ld(sXt + (p0 + j16) * kXS + 16 * (sb + 1) + 4 * q4) : R::zero();
-                    const Frag b1 = two ? R::ld(sM + mtile_index(sb + 1, ti) * 256 + lane * 4) : R::zero();
-                    yd = R::mma2(yd, a0, a1, b0, b1);
+                    const Split4 a1 = two ? pld(sXt, cXt, (p0 + j16) * kXS + 16 * (sb + 1) + 4 * q4) : split_zero();
+                    const Split4 b1 = two ? pld(sM, cM, mtile_index(sb + 1, ti) * 256 + lane * 4) : split_zero();
+                    yd = mma_split(yd, a0, a1, b0, b1);
                 }
                 f32x4 yo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += 2) {
-                    const Frag c0 = R::ld(sC + (16 * ti + j16) * NS + 16 * nb + 4 * q4);
-                    const Frag c1 = nb + 1 < NT ? R::ld(sC + (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4) : R::zero();
-                    const Frag h1 = nb + 1 < NT ? hf[nb + 1] : R::zero();
-                    yo = R::mma2(yo, hf[nb], h1, c0, c1);
+                    const Split4 c0 = pld(sC, cC, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 c1 = nb + 1 < NT ? pld(sC, cC, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                                                  : split_zero();
+                    const Split4 h1 = nb + 1 < NT ? hf[nb + 1] : split_zero();
+                    yo = mma_split(yo, hf[nb], h1, c0, c1);
                 }
                 // lane holds y[t = 16ti + j16][p = p0 + 4q4 + r]
                 const int t = 16 * ti + j16;
@@ -472,24 +495,26 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 const int t = 16 * ti + j16;
                 const float w = sWw[t];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sB[(p0 + 4 * q4 + r) * kXS + t] = R::from_f(w * R::el(xv[ti], r));
+                for (int r = 0; r < 4; ++r) pst1(sB, cR0, (p0 + 4 * q4 + r) * kXS + t, w * R::el(xv[ti], r));
             }
         }
 
         // ---- chunk state S = B^T (w o X): lane holds S[n = 16nt + 4q4 + r][p0 + j16],
         // then the state passing, strictly in chunk order
-        const E* xw = FULL ? sB : sXwt;
+        const uint16_t* xw = FULL ? sB : sXwt;
         const float dec = fast_exp2(cs_end);
+        // this wave's (w o X)^T fragments are the same for every n tile
+        Split4 xwf[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) xwf[sb] = pld(xw, cXw, (p0 + j16) * kXS + 16 * sb + 4 * q4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sb = 0; sb < 4; sb += 2) {
-                const Frag a0 = R::ld(sBt + (16 * nt + j16) * kXS + 16 * sb + 4 * q4);
-                const Frag a1 = R::ld(sBt + (16 * nt + j16) * kXS + 16 * (sb + 1) + 4 * q4);
-                const Frag b0 = R::ld(xw + (p0 + j16) * kXS + 16 * sb + 4 * q4);
-                const Frag b1 = R::ld(xw + (p0 + j16) * kXS + 16 * (sb + 1) + 4 * q4);
-                acc = R::mma2(acc, a0, a1, b0, b1);
+                const Split4 a0 = pld(sBt, cBt, (16 * nt + j16) * kXS + 16 * sb + 4 * q4);
+                const Split4 a1 = pld(sBt, cBt, (16 * nt + j16) * kXS + 16 * (sb + 1) + 4 * q4);
+                acc = mma_split(acc, a0, a1, xwf[sb], xwf[sb + 1]);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) Hs[nt][r] = has_bnd ? acc[r] : fmaf(dec, Hs[nt][r], acc[r]);
