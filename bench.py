@@ -18,7 +18,8 @@ alone, bracketed by one pair of HIP events on the launch stream;
 "extra": ssd_mixer_fwd on the same workload in both plans (staged: the same
 two kernels behind one call; fused: the conv computed inside the scan
 kernels), the other workloads (packed documents, the large layer, the decode
-step), the chunk-resume decode (ssd_resume_fwd) on the decode workload, the
+step), the chunk-resume decode (ssd_resume_fwd) and the fp32 4096-token
+prefill (conv + scan) on the decode workload, the
 Mamba-1 selective scan (ssd_s6_scan_fwd) priced against the VALU rate, and
 the backward of the mixer (ssd_mixer_bwd) on the Mini-K3 batch.
 
@@ -232,6 +233,37 @@ def decode_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
             "step_GBs": kb / (ms * 1e-3) / 1e9}
 
 
+def f32_prefill_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
+    """The fp32 prefill of the decode workload (conv then scan with its split workspace, one input set: 36 GB of
+    inputs, far beyond any cache), each call timed alone over back-to-back launches."""
+    dev = "cuda"
+    HP, GN = wl.H * wl.P, wl.G * wl.N
+    prm = synth.params(wl, seed, device=dev)
+    raw = synth.raw_inputs(wl, seed, device=dev)
+    ws_bytes = ssd.ssd_chunk_scan_workspace_size(wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, ssd.SSD_F32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    xbc = torch.empty(wl.B, wl.L, wl.conv_dim, dtype=torch.float32, device=dev)
+    dt = torch.empty(wl.B, wl.L, wl.H, dtype=torch.float32, device=dev)
+    y = torch.empty(wl.B, wl.L, HP, dtype=torch.float32, device=dev)
+    fs = torch.empty(wl.B, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
+    conv = lambda: ssd.ssd_conv_fwd(raw["xbc_raw"], prm["conv_w"], H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                                    dt_raw=raw["dt_raw"], dt_bias=prm["dt_bias"], xbc_out=xbc, dt_out=dt)
+    scan = lambda: ssd.ssd_chunk_scan_fwd(xbc[..., :HP], xbc[..., HP:HP + GN], xbc[..., HP + GN:], dt, prm["A"],
+                                          H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=prm["D"], z=raw["z"], final_state=fs,
+                                          y=y, workspace=ws)
+    for _ in range(warmup):
+        conv()
+        scan()
+    conv_ms, scan_ms = loop_ms(torch, [conv], steps), loop_ms(torch, [scan], steps)
+    sb = scan_bytes(wl)
+    del raw, xbc, y
+    return {"workload": wl.name + " prefill (fp32 ssd_conv_fwd + ssd_chunk_scan_fwd, B=%d L=%d H=%d N=%d)"
+            % (wl.B, wl.L, wl.H, wl.N), "ms_per_step": conv_ms + scan_ms, "conv_ms": conv_ms, "scan_ms": scan_ms,
+            "scan_bytes": sb, "scan_GBs": sb / (scan_ms * 1e-3) / 1e9,
+            "scan_frac": sb / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "value": wl.B * wl.L * wl.H / (scan_ms * 1e-3), "unit": "head-tokens/s (scan)"}
+
+
 def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
     """ssd_resume_fwd one token at a time over one full working chunk (64 steps, pos 0..63): the decode that
     continues the forward bit for bit.  Returns the mean per step."""
@@ -436,6 +468,8 @@ def main():
         extras.append({"workload": dw.name + " (ssd_step)", **r, "step_frac": r["step_GBs"] / HBM_PEAK_GBS,
                        "unit": "head-tokens/s (B*H per step)"})
         extras.append(resume_bench(ssd, synth, torch, dw, args.warmup))
+        extras.append(f32_prefill_bench(ssd, synth, torch, dw, 3, 2))
+        torch.cuda.empty_cache()
         extras.append(s6_bench(ssd, synth, torch, synth.WORKLOADS["s6_bf16"], args.steps, args.warmup))
         extras.append(bwd_bench(ssd, synth, torch, wl, max(5, args.steps // 5), args.warmup))
 
