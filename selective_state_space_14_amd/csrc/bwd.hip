@@ -29,8 +29,8 @@
 // gradients (dA, dD, dt_bias) go through per-chunk partial sums reduced in a
 // fixed order, so every result is deterministic.
 //
-// All arithmetic is fp32: the chunk kernel's 64x64 products run on the fp32
-// MFMA from LDS tiles, the first pass's on the VALU (each thread a 4x4 block).
+// All arithmetic is fp32: the 64x64 products of the chunk kernel and of the
+// first pass run on the fp32 MFMA from LDS tiles.
 #include <algorithm>
 
 #include "ssd_device.hpp"
@@ -53,42 +53,6 @@ __device__ __forceinline__ float silu_acc(float v) { return v * sigmoid_acc(v); 
 __device__ __forceinline__ float dsilu_acc(float v) {
     const float s = sigmoid_acc(v);
     return s * (1.0f + v * (1.0f - s));
-}
-
-// acc[i][j] += sum_{k < K} A(r0 + i, k) * B(k, c0 + j), K a multiple of 4, with
-//   A(i, k) = AT ? A[k * lda + i] : A[i * lda + k]
-//   B(k, j) = BT ? Bm[j * ldb + k] : Bm[k * ldb + j]
-// (all offsets multiples of 4 floats, so every read is one 16-byte LDS read).
-template <bool AT, bool BT>
-__device__ __forceinline__ void mm44(float (&acc)[4][4], const float* A, int lda, int r0, const float* Bm, int ldb,
-                                     int c0, int K) {
-#pragma unroll 2
-    for (int k = 0; k < K; k += 4) {
-        float av[4][4], bv[4][4];   // av[i][kk], bv[kk][j]
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (AT) {
-                const float4 v = *reinterpret_cast<const float4*>(A + (k + q) * lda + r0);
-                av[0][q] = v.x; av[1][q] = v.y; av[2][q] = v.z; av[3][q] = v.w;
-            } else {
-                const float4 v = *reinterpret_cast<const float4*>(A + (r0 + q) * lda + k);
-                av[q][0] = v.x; av[q][1] = v.y; av[q][2] = v.z; av[q][3] = v.w;
-            }
-            if (BT) {
-                const float4 v = *reinterpret_cast<const float4*>(Bm + (c0 + q) * ldb + k);
-                bv[0][q] = v.x; bv[1][q] = v.y; bv[2][q] = v.z; bv[3][q] = v.w;
-            } else {
-                const float4 v = *reinterpret_cast<const float4*>(Bm + (k + q) * ldb + c0);
-                bv[q][0] = v.x; bv[q][1] = v.y; bv[q][2] = v.z; bv[q][3] = v.w;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i][q], bv[q][j], acc[i][j]);
-    }
 }
 
 // sum over the 16 lanes that share lane / 16
@@ -142,6 +106,44 @@ __device__ __forceinline__ const T* z_or_gy(const BwdArgs& a, int64_t& stride) {
     }
     stride = a.gy_stride * (int64_t)(sizeof(float) / sizeof(T));
     return reinterpret_cast<const T*>(a.gy);
+}
+
+// Product of a 16-row strip on the fp32 MFMA (16x16x4): acc[c] += A(r0 + ., k)
+// B(k, c0 + 16c + .) over k < K (a multiple of 16), c < NC, with the layouts
+//   A(i, k) = AT ? A[k * lda + i] : A[i * lda + k]
+//   B(k, j) = BT ? Bm[j * ldb + k] : Bm[k * ldb + j]
+// (offsets multiples of 4 floats).  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
+// and B(4q..4q+3, c0 + 16c + i) of each 16-wide K block, and element e of
+// acc[c] is the output at row r0 + 4q + e, column c0 + 16c + i.
+template <bool AT, bool BT, int NC>
+__device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
+                                           int ldb, int c0, int K, int q, int li) {
+    for (int kb = 0; kb < K; kb += 16) {
+        const int k0 = kb + 4 * q;
+        float4 af;
+        if (AT) {
+            af.x = A[(k0 + 0) * lda + r0 + li];
+            af.y = A[(k0 + 1) * lda + r0 + li];
+            af.z = A[(k0 + 2) * lda + r0 + li];
+            af.w = A[(k0 + 3) * lda + r0 + li];
+        } else {
+            af = *reinterpret_cast<const float4*>(A + (r0 + li) * lda + k0);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c0 + 16 * c + li;
+            float4 bf;
+            if (BT) {
+                bf = *reinterpret_cast<const float4*>(Bm + col * ldb + k0);
+            } else {
+                bf.x = Bm[(k0 + 0) * ldb + col];
+                bf.y = Bm[(k0 + 1) * ldb + col];
+                bf.z = Bm[(k0 + 2) * ldb + col];
+                bf.w = Bm[(k0 + 3) * ldb + col];
+            }
+            acc[c] = mma_f32(acc[c], af, bf);
+        }
+    }
 }
 
 // ---- pass 1: chunk-local states (MODE 0) and adjoint inputs (MODE 1)
@@ -203,20 +205,30 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
         sV[(i / P) * kLD + i % P] = (mode == 1 && a.z) ? vv[q] * silu_acc(zq[q]) : vv[q];
     }
     __syncthreads();
-    const int rb = tid >> 4, cb = tid & 15;
-    if (4 * rb < N) {
-        float acc[4][4] = {};
-        mm44<true, false>(acc, sW, LDN, 4 * rb, sV, kLD, 4 * cb, kQ);
+    // [N][64] = W^T V on the fp32 MFMA: the N/16 x 4 output tiles are dealt
+    // to the four waves, NC 16-column tiles of one 16-row strip each
+    {
+        constexpr int NC = N / 16;
+        const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, li = lane & 15;
+        const int r0 = 16 * ((wave * NC) / 4);            // this wave's rows (state index n)
+        const int c0 = 16 * NC * (wave % (4 / NC));       // its first column (head channel p)
+        f32x4 acc[NC] = {};
+        mfma_strip<true, false, NC>(acc, sW, LDN, r0, sV, kLD, c0, kQ, q, li);
         float* out = (mode == 0 ? a.S : a.dS) + (((size_t)b * a.H + h) * nc + c) * N * P;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4*>(out + (size_t)(4 * rb + i) * P + 4 * cb) =
-                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(size_t)(r0 + 4 * q + e) * P + c0 + 16 * cc + li] = acc[cc][e];
     }
 }
 
 // ---- pass 2: states entering each chunk (y = 0, in order) and adjoints of
-// the states leaving each chunk (y = 1, in reverse order), per state element
+// the states leaving each chunk (y = 1, in reverse order), per state element.
+// The recurrence is serial in the chunks, so the loads run a block of kPD
+// chunks ahead of it: the next block's values are in flight while the
+// current block's results are stored (one load per chunk in flight would
+// leave this pass waiting on memory latency at every chunk).
+constexpr int kPD = 8;
 template <int N>
 __global__ __launch_bounds__(kBT) void ssd_bwd_pass_kernel(BwdArgs a) {
     constexpr int NP = N * 64;
@@ -225,58 +237,49 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_pass_kernel(BwdArgs a) {
     const int bh = blockIdx.x / per;
     const int e = (blockIdx.x % per) * kBT + threadIdx.x;
     const float* dec = a.dec + (size_t)bh * nc;
-    if (blockIdx.y == 0) {
-        float* S = a.S + (size_t)bh * nc * NP + e;
-        float hs = 0.0f;
-        for (int c = 0; c < nc; ++c) {
-            const float v = S[(size_t)c * NP];
-            S[(size_t)c * NP] = hs;
-            hs = fmaf(dec[c], hs, v);
-        }
-    } else {
-        float* dS = a.dS + (size_t)bh * nc * NP + e;
-        float gs = 0.0f;
-        for (int c = nc - 1; c >= 0; --c) {
-            const float v = dS[(size_t)c * NP];
-            dS[(size_t)c * NP] = gs;
-            gs = fmaf(dec[c], gs, v);
+    const bool fwd = blockIdx.y == 0;
+    float* X = (fwd ? a.S : a.dS) + (size_t)bh * nc * NP + e;
+    // chunk of step i (0 .. nc-1) in this direction
+    auto chunk = [&](int i) { return fwd ? i : nc - 1 - i; };
+    float acc = 0.0f;
+    const int nb = nc / kPD;                      // whole blocks; the rest one chunk at a time
+    float v[kPD], d[kPD];
+    if (nb > 0) {
+#pragma unroll
+        for (int j = 0; j < kPD; ++j) {
+            v[j] = X[(size_t)chunk(j) * NP];
+            d[j] = dec[chunk(j)];
         }
     }
-}
-
-// Product of a 16-row strip on the fp32 MFMA (16x16x4): acc[c] += A(r0 + ., k)
-// B(k, c0 + 16c + .) over k < K (a multiple of 16), c < NC, with the layouts
-// of mm44.  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
-// and B(4q..4q+3, c0 + 16c + i) of each 16-wide K block, and element e of
-// acc[c] is the output at row r0 + 4q + e, column c0 + 16c + i.
-template <bool AT, bool BT, int NC>
-__device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
-                                           int ldb, int c0, int K, int q, int li) {
-    for (int kb = 0; kb < K; kb += 16) {
-        const int k0 = kb + 4 * q;
-        float4 af;
-        if (AT) {
-            af.x = A[(k0 + 0) * lda + r0 + li];
-            af.y = A[(k0 + 1) * lda + r0 + li];
-            af.z = A[(k0 + 2) * lda + r0 + li];
-            af.w = A[(k0 + 3) * lda + r0 + li];
-        } else {
-            af = *reinterpret_cast<const float4*>(A + (r0 + li) * lda + k0);
+    for (int blk = 0; blk < nb; ++blk) {
+        const int i0 = blk * kPD;
+        float vn[kPD], dn[kPD];
+        const bool more = blk + 1 < nb;           // uniform
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < kPD; ++j) {
+                vn[j] = X[(size_t)chunk(i0 + kPD + j) * NP];
+                dn[j] = dec[chunk(i0 + kPD + j)];
+            }
         }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c0 + 16 * c + li;
-            float4 bf;
-            if (BT) {
-                bf = *reinterpret_cast<const float4*>(Bm + col * ldb + k0);
-            } else {
-                bf.x = Bm[(k0 + 0) * ldb + col];
-                bf.y = Bm[(k0 + 1) * ldb + col];
-                bf.z = Bm[(k0 + 2) * ldb + col];
-                bf.w = Bm[(k0 + 3) * ldb + col];
-            }
-            acc[c] = mma_f32(acc[c], af, bf);
+        for (int j = 0; j < kPD; ++j) {
+            X[(size_t)chunk(i0 + j) * NP] = acc;
+            acc = fmaf(d[j], acc, v[j]);
         }
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < kPD; ++j) {
+                v[j] = vn[j];
+                d[j] = dn[j];
+            }
+        }
+    }
+    for (int i = nb * kPD; i < nc; ++i) {
+        const int c = chunk(i);
+        const float vv = X[(size_t)c * NP];
+        X[(size_t)c * NP] = acc;
+        acc = fmaf(dec[c], acc, vv);
     }
 }
 
