@@ -1,24 +1,22 @@
 // step.hip -- ssd_step: one decode token per sequence on gfx950.
 //
 // Per sequence b (one workgroup of 1024 threads):
-//   1. the B and C columns: conv window [conv_state rows 0..K-2, new raw
-//      row] -> act -> rounded to the storage dtype (as a prefill would store
-//      it) -> fp32 in LDS, the conv buffer shifting by one row in place (the
-//      thread that reads a channel's rows writes them); dt = softplus(dt_raw +
-//      dt_bias) and a = exp(dt * A) per head in LDS.
+//   1. every conv channel: window [conv_state rows 0..K-2, new raw row] ->
+//      act -> rounded to the storage dtype (as a prefill would store it) ->
+//      fp32 in LDS, the conv buffer shifting by one row in place (the thread
+//      that reads a channel's rows writes them); silu(z), dt = softplus(dt_raw
+//      + dt_bias) and a = exp(dt * A) per head, in LDS too.
 //   2. a streaming read-modify-write of the fp32 state [H][P][N], a round of
-//      rows at a time: eight lanes share a row (four float4 each for N = 128);
-//      row h*P + p also convolves x channel h*P + p (its inputs loaded one
-//      round ahead) and shifts that channel's buffer rows, then
+//      64 KiB at a time, thread t holding float4 t + 1024 j of the round, so
+//      each instruction of the workgroup covers 16 KiB of contiguous state;
 //          h[p, n] = a * h[p, n] + (dt * x_p) * B_n
-//      and the row's lanes reduce C . h with a fixed DPP butterfly, so the
+//      and the N/4 lanes of a row reduce C . h with a fixed butterfly, so the
 //      result is deterministic and independent of the batch size;
 //   y[p] = (C . h[p] + D x_p) * silu(z_p).
 // The state is 96% of the bytes (B*H*P*N*4 read + written per token): its
 // loads and stores are nontemporal (it is touched once per token), loads run
-// one round ahead of the round being computed (deeper prefetch measured no
-// faster: 64 KB per round and CU already covers the latency), and the first
-// round's loads are issued even before the B/C conv phase.
+// one round ahead of the round being computed, and the first round's loads
+// are issued before the conv phase.
 // The recurrence is the Mamba-2 SSD layer of the Codestral-Mamba port header
 // (codestral_mamba.ts); step == forward at length 1 with the state carried
 // follows mojolearn.Mamba3Block's step() description.
@@ -49,25 +47,29 @@ __device__ __forceinline__ float round_to(float v, float*) { return v; }
 __device__ __forceinline__ float round_to(float v, uint16_t*) { return __uint_as_float(f32_to_bf16_bits(v) << 16); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Sum over aligned groups of W lanes (W = 4 or 8), every lane of a group
-// receiving the group's sum: quad-permute xor 1, xor 2, then (W = 8) the
-// half-row mirror, which pairs each lane with one of the other quad.
+// Sum over aligned groups of W consecutive lanes (W = 4, 8, 16 or 32) in a
+// fixed butterfly: quad permutes xor 1 and xor 2, then the half-row mirror
+// (lane i with 7 - i) and the row mirror (i with 15 - i), after each of which
+// the partners hold equal partial sums; for W = 32 the row broadcast then adds
+// lane 15 of each even 16-lane row into the odd row after it.  The group's
+// last lane always holds the group's sum, and the order of every addition is
+// fixed, so the result does not depend on the batch.
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 template <int W>
-__device__ __forceinline__ float row_sum(float v) {
-    static_assert(W == 4 || W == 8, "group width");
-    v = dpp_add<0xB1>(v);            // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);            // quad_perm [2,3,0,1]
-    if (W == 8) v = dpp_add<0x141>(v);   // row_half_mirror
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "group width");
+    v = dpp_add<0xB1>(v);                 // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);                 // quad_perm [2,3,0,1]
+    if (W >= 8) v = dpp_add<0x141>(v);    // row_half_mirror
+    if (W >= 16) v = dpp_add<0x140>(v);   // row_mirror
+    if (W >= 32) v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));   // row_bcast:15
     return v;
 }
 
@@ -82,179 +84,190 @@ __global__ __launch_bounds__(kStepThreads) void ssd_step_kernel(StepArgs a) {
     const int hpg = H / G;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    float* xbc_s = smem;              // [C]
-    float* dt_s = smem + C;           // [H]
-    float* a_s = dt_s + H;            // [H]
-    int* gofs_s = reinterpret_cast<int*>(a_s + H);   // [H]: offset of the head's group in B and C
-    float* d_s = a_s + 2 * H;                         // [H]: D (0 when absent)
+    float* xz_s = smem;               // [H*P][2]: per x channel, the convolved x and its gate silu(z) (1 without z)
+    float* bc_s = smem + 2 * HP;      // [2*G*N]: the convolved B columns, then the C columns
+    float4* hd_s = reinterpret_cast<float4*>(bc_s + 2 * GN);   // [H]: per head {exp(dt A), dt, D (0 when absent), 0}
 
-    // ---- state rows: row = h * P + p holds NQ float4 (n fastest).  LPR lanes
-    // share a row, lane q of a row holds float4 q + LPR j (j < FPL), so every
-    // load instruction reads whole 128-byte row segments; a wave covers RPW
-    // consecutive rows (one head) per round, the workgroup RPR rows.
+    // ---- the state [H*P rows][N] as a flat array of float4: round r covers
+    // float4 r*4096 .. +4095, and thread t holds float4 t + 1024 j of it (j <
+    // F).  Each load or store instruction of the workgroup therefore covers
+    // 16 KiB of contiguous state (measured here at ~6.2 TB/s for this
+    // read-modify-write, against ~5.5 TB/s when each wave instead streams its
+    // own 4 KiB).  A row's NQ float4 sit in NQ consecutive lanes; the lane's
+    // n-quad q = t mod NQ is the same in every round.
     constexpr int NQ = N / 4;
-    constexpr int LPR = NQ < 8 ? NQ : 8;
-    constexpr int FPL = NQ / LPR;
-    constexpr int RPW = 64 / LPR;
-    constexpr int RPR = RPW * (kStepThreads / 64);
-    const int nrows = H * P;                         // a multiple of 64, so rounds cover whole waves
-    const int wave = tid >> 6, lane = tid & 63;
-    const int q = lane % LPR;
-    // The state goes through range-checked buffer loads and stores with the
-    // nontemporal bit: rows past the end read 0 and their stores are dropped,
-    // so the loop has no branches around memory operations and the compiler
-    // counts the loads in flight exactly.
+    constexpr int F = 4;
+    constexpr int PER_ROUND = kStepThreads * F;
+    const int nrows = HP;
+    const int total = nrows * NQ;
+    const int nrounds = (total + PER_ROUND - 1) / PER_ROUND;
+    const int q = tid % NQ;
+    // range-checked nontemporal buffer operations: float4 past the end read 0
+    // and their stores are dropped, so no memory operation sits under a branch
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-        a.ssm_state + (size_t)b * H * P * N, 0, nrows * NQ * 16, 0x00020000);
+        a.ssm_state + (size_t)b * H * P * N, 0, total * 16, 0x00020000);
     constexpr int kNT = 2;                           // cache policy: nontemporal
-    f4v s_cur[FPL], s_nxt[FPL];       // rounds r, r+1
-    auto row_of = [&](int r) { return r * RPR + wave * RPW + lane / LPR; };
-    auto off_of = [&](int row, int j) { return (uint32_t)((row * NQ + q + j * LPR) * 16); };
+    auto idx = [&](int r, int j) { return r * PER_ROUND + j * kStepThreads + tid; };
+    f4v s_cur[F], s_nxt[F];           // rounds r, r+1
     auto load_round = [&](int r, f4v* dst) {
-        const int row = row_of(r);
 #pragma unroll
-        for (int j = 0; j < FPL; ++j)
-            dst[j] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(sr, off_of(row, j), 0, kNT));
+        for (int j = 0; j < F; ++j)
+            dst[j] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)idx(r, j) * 16u, 0, kNT));
     };
     load_round(0, s_cur);             // independent of the conv phase: start it now
 
-    // ---- 1. the B and C columns: conv window, activation, buffer shift, to
-    // LDS (every state row reads them); dt, the decay, D per head.  The x
-    // columns are convolved inside the state loop by the rows they feed.
+    // ---- 1. every conv channel up front: window [conv_state rows 0..K-2, new
+    // raw row] -> act -> rounded to the storage dtype (as a prefill would store
+    // it) -> fp32 in LDS, the buffer shifting by one row in place (the thread
+    // that reads a channel's rows writes them); silu(z) of the x channels;
+    // dt = softplus(dt_raw + dt_bias) and a = exp(dt * A) per head.
     const T* raw = static_cast<const T*>(a.xbc_raw) + (size_t)b * C;
     T* cst = static_cast<T*>(a.conv_state) + (size_t)b * (K - 1) * C;
-    for (int c0 = HP + tid * VEC; c0 < C; c0 += kStepThreads * VEC) {
-        // the three carried rows and the new row, as raw 16-byte words
-        const uint4 q0 = *reinterpret_cast<const uint4*>(cst + c0);
-        const uint4 q1 = *reinterpret_cast<const uint4*>(cst + C + c0);
-        const uint4 q2 = *reinterpret_cast<const uint4*>(cst + 2 * C + c0);
-        const uint4 qr = *reinterpret_cast<const uint4*>(raw + c0);
-        // shift: row0 <- row1, row1 <- row2, row2 <- new row (bits copied as they are)
-        *reinterpret_cast<uint4*>(cst + c0) = q1;
-        *reinterpret_cast<uint4*>(cst + C + c0) = q2;
-        *reinterpret_cast<uint4*>(cst + 2 * C + c0) = qr;
+    const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
+    // the gate inputs first: the conv loop below stores, and these loads must not wait behind it
+    constexpr int ZI = 4096 / (kStepThreads * VEC) > 0 ? 4096 / (kStepThreads * VEC) : 1;
+    uint4 zq[ZI];
+#pragma unroll
+    for (int i = 0; i < ZI; ++i) {
+        const int c0 = (tid + i * kStepThreads) * VEC;
+        zq[i] = zb && c0 < HP ? *reinterpret_cast<const uint4*>(zb + c0) : make_uint4(0, 0, 0, 0);
+    }
+    // per-head inputs, one head per thread (the LDS budget keeps H*P, so H, far below 1024)
+    float dt_in = 0.0f, A_h = 0.0f, D_h = 0.0f;
+    if (tid < H) {
+        dt_in = load1(static_cast<const T*>(a.dt_raw) + (size_t)b * H + tid) + (a.dt_bias ? a.dt_bias[tid] : 0.0f);
+        A_h = a.A[tid];
+        D_h = a.D ? a.D[tid] : 0.0f;
+    }
+    // one conv group: VEC channels from c0, their three carried rows and new
+    // row as raw 16-byte words; the rows shift by one (row0 <- row1, row1 <-
+    // row2, row2 <- new row, bits copied as they are) and the convolved,
+    // activated, storage-rounded values go to LDS
+    auto conv_group = [&](int c0, const uint4 (&w)[4]) {
+        *reinterpret_cast<uint4*>(cst + c0) = w[1];
+        *reinterpret_cast<uint4*>(cst + C + c0) = w[2];
+        *reinterpret_cast<uint4*>(cst + 2 * C + c0) = w[3];
         float r0[VEC], r1[VEC], r2[VEC], cur[VEC];
-        unpack16(q0, r0, (T*)nullptr);
-        unpack16(q1, r1, (T*)nullptr);
-        unpack16(q2, r2, (T*)nullptr);
-        unpack16(qr, cur, (T*)nullptr);
+        unpack16(w[0], r0, (T*)nullptr);
+        unpack16(w[1], r1, (T*)nullptr);
+        unpack16(w[2], r2, (T*)nullptr);
+        unpack16(w[3], cur, (T*)nullptr);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const int c = c0 + e;
-            const float4 w = *reinterpret_cast<const float4*>(a.conv_w + (size_t)c * K);
+            const float4 cw = *reinterpret_cast<const float4*>(a.conv_w + (size_t)c * K);
             float v = a.conv_b ? a.conv_b[c] : 0.0f;
-            v = fmaf(w.x, r0[e], v);
-            v = fmaf(w.y, r1[e], v);
-            v = fmaf(w.z, r2[e], v);
-            v = fmaf(w.w, cur[e], v);
+            v = fmaf(cw.x, r0[e], v);
+            v = fmaf(cw.y, r1[e], v);
+            v = fmaf(cw.z, r2[e], v);
+            v = fmaf(cw.w, cur[e], v);
             if (a.act == 0) v = silu_f(v);
-            xbc_s[c] = round_to(v, (T*)nullptr);
+            v = round_to(v, (T*)nullptr);
+            if (c < HP) xz_s[2 * c] = v;
+            else bc_s[c - HP] = v;
+        }
+    };
+    auto conv_load = [&](int c0, uint4 (&w)[4]) {
+        w[0] = *reinterpret_cast<const uint4*>(cst + c0);
+        w[1] = *reinterpret_cast<const uint4*>(cst + C + c0);
+        w[2] = *reinterpret_cast<const uint4*>(cst + 2 * C + c0);
+        w[3] = *reinterpret_cast<const uint4*>(raw + c0);
+    };
+    // the first two groups of every thread load before either stores, so a
+    // thread with two groups waits for one memory latency, not two
+    constexpr int CI = 2;
+    uint4 cw_in[CI][4];
+#pragma unroll
+    for (int i = 0; i < CI; ++i) {
+        const int c0 = (tid + i * kStepThreads) * VEC;
+        if (c0 < C) conv_load(c0, cw_in[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CI; ++i) {
+        const int c0 = (tid + i * kStepThreads) * VEC;
+        if (c0 < C) conv_group(c0, cw_in[i]);
+    }
+    for (int c0 = (tid + CI * kStepThreads) * VEC; c0 < C; c0 += kStepThreads * VEC) {
+        uint4 w[4];
+        conv_load(c0, w);
+        conv_group(c0, w);
+    }
+    if (tid < H) {
+        const float dt = softplus_f(dt_in);
+        hd_s[tid] = make_float4(expf(dt * A_h), dt, D_h, 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < ZI; ++i) {
+        const int c0 = (tid + i * kStepThreads) * VEC;
+        if (c0 < HP) {
+            float zz[VEC];
+            unpack16(zq[i], zz, (T*)nullptr);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) xz_s[2 * (c0 + e) + 1] = zb ? silu_f(zz[e]) : 1.0f;
         }
     }
-    for (int h = tid; h < H; h += kStepThreads) {
-        float r = load1(static_cast<const T*>(a.dt_raw) + (size_t)b * H + h);
-        float dt = softplus_f(r + (a.dt_bias ? a.dt_bias[h] : 0.0f));
-        dt_s[h] = dt;
-        a_s[h] = expf(dt * a.A[h]);
-        gofs_s[h] = (h / hpg) * N;
-        d_s[h] = a.D ? a.D[h] : 0.0f;
+    for (int c0 = (tid + ZI * kStepThreads) * VEC; c0 < HP; c0 += kStepThreads * VEC) {
+        float zz[VEC];
+        if (zb) unpack16(*reinterpret_cast<const uint4*>(zb + c0), zz, (T*)nullptr);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xz_s[2 * (c0 + e) + 1] = zb ? silu_f(zz[e]) : 1.0f;
     }
-
-    // ---- per-row x inputs, loaded one round ahead of their use: row h*P + p
-    // is x channel h*P + p, so a row's lanes convolve their own channel (all
-    // of them, from the same addresses) and its first lane shifts the buffer.
-    const T* zb = a.z ? static_cast<const T*>(a.z) + (size_t)b * HP : nullptr;
-    struct XIn {
-        T q0, q1, q2, qr;     // carried rows and the new raw value (bits as stored)
-        float4 w;
-        float bias, z;
-    };
-    auto load_x = [&](int r, XIn& o) {
-        const int ch = min(row_of(r), nrows - 1);    // the row's x channel, clamped past the end
-        o.q0 = cst[ch];
-        o.q1 = cst[C + ch];
-        o.q2 = cst[2 * C + ch];
-        o.qr = raw[ch];
-        o.w = *reinterpret_cast<const float4*>(a.conv_w + (size_t)ch * K);
-        o.bias = a.conv_b ? a.conv_b[ch] : 0.0f;
-        o.z = zb ? load1(zb + ch) : 0.0f;
-    };
-    XIn x_cur, x_nxt;
-    load_x(0, x_cur);
     __syncthreads();
 
-    // ---- 2. state read-modify-write, one round of RPR rows at a time; the
-    // next round's loads are issued before the current round is computed
-    // y through a range-checked buffer store: lanes other than a row's first
+    // ---- 2. state read-modify-write, one round at a time, the next round's
+    // loads issued before the current round is computed:
+    //     h[p, n] = a * h[p, n] + (dt * x_p) * B_n,   y[p] = (C . h[p] + D x_p) * silu(z_p)
+    // y through a range-checked buffer store: lanes other than a row's last
     // aim past the range and are dropped, so the store is never skipped
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)b * HP, 0, HP * 4, 0x00020000);
-    const int nrounds = (nrows + RPR - 1) / RPR;
-    // B and C of this lane's n-quads for the current group, reloaded only when
-    // the group changes (never, for one group)
-    float4 Bq[FPL], Cq[FPL];
-    int cur_gofs = -1;
+    // h / hpg as a multiply and shift: with m = floor((2^32 - 1) / hpg) + 1
+    // (2^32 for hpg = 1), h * m / 2^32 exceeds h / hpg by less than h / 2^32,
+    // which stays below the gap 1 / hpg to the next integer while h * hpg < 2^32
+    // (here h < H <= 2^16)
+    const uint64_t inv_hpg = 0xffffffffull / (uint64_t)hpg + 1ull;
     for (int r = 0; r < nrounds; ++r) {
         load_round(r + 1, s_nxt);                    // past the last round: out of range, reads 0
-        load_x(r + 1, x_nxt);
-        const int row = row_of(r);
-        // a wave's rows lie in one head; a wave past the end computes on clamped
-        // rows and its stores fall outside the ranges or are skipped
-        const int hrow = min(row, nrows - 1);
-        const int h = __builtin_amdgcn_readfirstlane(hrow / P);
-        const int p = hrow % P;
-        const int gofs = gofs_s[h];
-        if (gofs != cur_gofs) {                     // uniform: gofs is per head
-            cur_gofs = gofs;
+        // every LDS operand of the round first, so their latencies overlap
+        int f[F], row[F];
+        float2 xz[F];                 // x_p, silu(z_p)
+        float4 hd[F], Bv[F], Cv[F];   // {a, dt, D, 0} of the head; B and C of its group
 #pragma unroll
-            for (int j = 0; j < FPL; ++j) {
-                Bq[j] = *reinterpret_cast<const float4*>(xbc_s + HP + gofs + 4 * (q + j * LPR));
-                Cq[j] = *reinterpret_cast<const float4*>(xbc_s + HP + GN + gofs + 4 * (q + j * LPR));
-            }
+        for (int j = 0; j < F; ++j) {
+            f[j] = idx(r, j);
+            row[j] = f[j] < total ? f[j] / NQ : nrows - 1;   // past the end: the last row, nothing kept
+            // a wave's 64 float4 are 64-aligned and a head's P*N/4 (>= 256)
+            // float4 start at a multiple of 64: the head is the wave's
+            const int h = __builtin_amdgcn_readfirstlane(row[j] / P);
+            const int gofs = (int)(((uint64_t)(uint32_t)h * inv_hpg) >> 32) * N;
+            xz[j] = *reinterpret_cast<const float2*>(xz_s + 2 * row[j]);
+            hd[j] = hd_s[h];
+            Bv[j] = *reinterpret_cast<const float4*>(bc_s + gofs + 4 * q);
+            Cv[j] = *reinterpret_cast<const float4*>(bc_s + GN + gofs + 4 * q);
         }
-        // the row's x channel: conv window, activation, rounded to T as a prefill stores it
-        float xp;
-        {
-            float v = x_cur.bias;
-            v = fmaf(x_cur.w.x, to_f32(x_cur.q0), v);
-            v = fmaf(x_cur.w.y, to_f32(x_cur.q1), v);
-            v = fmaf(x_cur.w.z, to_f32(x_cur.q2), v);
-            v = fmaf(x_cur.w.w, to_f32(x_cur.qr), v);
-            if (a.act == 0) v = silu_f(v);
-            xp = round_to(v, (T*)nullptr);
-        }
-        if (q == 0 && row < nrows) {                 // shift the channel's buffer rows
-            cst[row] = x_cur.q1;
-            cst[C + row] = x_cur.q2;
-            cst[2 * C + row] = x_cur.qr;
-        }
-        const float dec = a_s[h];
-        const float dx = dt_s[h] * xp;
-        float part = 0.0f;
+        float part[F];
 #pragma unroll
-        for (int j = 0; j < FPL; ++j) {
-            const float4 Bv = Bq[j], Cv = Cq[j];
+        for (int j = 0; j < F; ++j) {
+            const float dxj = hd[j].y * xz[j].x;
+            const float dec = hd[j].x;
             f4v v = s_cur[j];
-            v.x = fmaf(dec, v.x, dx * Bv.x);
-            v.y = fmaf(dec, v.y, dx * Bv.y);
-            v.z = fmaf(dec, v.z, dx * Bv.z);
-            v.w = fmaf(dec, v.w, dx * Bv.w);
-            part = fmaf(Cv.x, v.x, part);
-            part = fmaf(Cv.y, v.y, part);
-            part = fmaf(Cv.z, v.z, part);
-            part = fmaf(Cv.w, v.w, part);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr, off_of(row, j), 0, kNT);
+            v.x = fmaf(dec, v.x, dxj * Bv[j].x);
+            v.y = fmaf(dec, v.y, dxj * Bv[j].y);
+            v.z = fmaf(dec, v.z, dxj * Bv[j].z);
+            v.w = fmaf(dec, v.w, dxj * Bv[j].w);
+            float s = Cv[j].x * v.x;
+            s = fmaf(Cv[j].y, v.y, s);
+            s = fmaf(Cv[j].z, v.z, s);
+            part[j] = fmaf(Cv[j].w, v.w, s);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr, (uint32_t)f[j] * 16u, 0, kNT);
         }
-        // sum over the LPR lanes of the row (a fixed order: deterministic)
-        part = row_sum<LPR>(part);
-        float yv = fmaf(d_s[h], xp, part);
-        if (zb) yv *= silu_f(x_cur.z);
-        const bool first = q == 0 && row < nrows;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yr, first ? (uint32_t)(h * P + p) * 4 : 0x7fffffffu, 0, 0);
 #pragma unroll
-        for (int j = 0; j < FPL; ++j) {
-            s_cur[j] = s_nxt[j];
+        for (int j = 0; j < F; ++j) {
+            const float yv = fmaf(hd[j].z, xz[j].x, group_sum<NQ>(part[j])) * xz[j].y;
+            const bool first = q == NQ - 1 && f[j] < total;   // the group's last lane holds its sum
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), yr, first ? (uint32_t)row[j] * 4 : 0x7fffffffu, 0, 0);
         }
-        x_cur = x_nxt;
+#pragma unroll
+        for (int j = 0; j < F; ++j) s_cur[j] = s_nxt[j];
     }
 }
 
