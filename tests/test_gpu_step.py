@@ -52,6 +52,9 @@ def oracle_single_pass(wl, prm, raw, steps, seed, rows, device):
     ("f32", 64, 1, 3, 100, 8),
     ("bf16", 128, 1, 1, 70, 6),
     ("f32", 16, 1, 1, 65, 5),
+    # N = 32 (8 lanes per state row); one head per group (H/G = 1); three heads per group
+    ("bf16", 32, 3, 3, 90, 7),
+    ("f32", 32, 2, 6, 75, 6),
 ])
 def test_prefill_then_steps_small(gpu_lib, dtype, N, G, H, L, steps):
     wl = synth.Workload("dec_" + dtype, 3, L, H, 64, N, G, dtype, steps=steps)
