@@ -35,7 +35,7 @@ namespace {
 constexpr int kConvThreads = 128;   // two waves: 2 KiB of each bf16 row per block
 constexpr int kTile = 64;     // tokens per block (a multiple of 64)
 constexpr int kStartWords = kTile / 64;
-constexpr int kBatch = 8;     // rows loaded before use
+constexpr int kBatch = 16;    // rows loaded before use
 constexpr int kDtBatch = 8;   // dt elements loaded per lane before use
 
 template <typename T> struct CV;
