@@ -324,6 +324,10 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
  *   conv_state T   [B][K-1][conv_dim], read and updated in place
  *   ssm_state  f32 [B][H][P][N],     read and updated in place
  *   y          f32 [B][H*P]
+ * Rows are contiguous.  xbc_raw, z, conv_w, conv_state and ssm_state must be
+ * 16-byte aligned (they are read in 16-byte pieces); dt_raw, the parameter
+ * vectors and y 4-byte aligned.  A misaligned pointer is refused with
+ * SSD_ERR_ALIGNMENT before any launch.
  * One workgroup serves one sequence, so B should be >= the CU count (256)
  * for full-device bandwidth.  Deterministic and batch-invariant: a row's
  * result does not depend on B or on the other rows.  The conv row, the gate

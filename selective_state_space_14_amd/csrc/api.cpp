@@ -891,7 +891,7 @@ int ssd_step(int B, int H, int P, int N, int G, int K, int dtype,
     const int64_t C = (int64_t)H * P + 2LL * G * N;
     TRY(check_ptr(fn, "xbc_raw", xbc_raw, work, true));
     TRY(check_ptr(fn, "dt_raw", dt_raw, work, false));
-    TRY(check_ptr(fn, "z", z, false, false));
+    TRY(check_ptr(fn, "z", z, false, true));      // read in 16-byte pieces
     TRY(check_ptr(fn, "conv_w", conv_w, work, true));
     TRY(check_ptr(fn, "conv_b", conv_b, false, false));
     TRY(check_ptr(fn, "dt_bias", dt_bias, false, false));

@@ -646,12 +646,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
-// The same for a wave-uniform n in [0, 31] (larger n waits for 31): a chain of
+// The same for a wave-uniform n in [0, 63] (larger n waits for 63): a chain of
 // scalar compares picks the immediate.
 template <int LO = 0>
 __device__ __forceinline__ void wait_vmcnt_n(int n) {
-    if constexpr (LO == 31) {
-        wait_vmcnt<31>();
+    if constexpr (LO == 63) {
+        wait_vmcnt<63>();
     } else {
         if (n <= LO) wait_vmcnt<LO>();
         else wait_vmcnt_n<LO + 1>(n);
@@ -761,25 +761,29 @@ __device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw
     }
 }
 
-// LDS plan of the full pass: two stages of B, C and the heads' X tiles, the
-// heads' M^T fragments, each wave's z tile, the heads' dt / doc ids (one
-// buffer), and two buffers of per-token scalars.
-template <int N, int HPW>
+// LDS plan of the full pass: NS stages of a chunk's inputs -- B, C and the
+// heads' X tiles, every wave's z tile, the heads' dt / doc ids -- then the
+// heads' M^T fragments and two buffers of per-token scalars.  A chunk's
+// inputs are copied NS - 1 chunks ahead of its compute.
+template <int N, int HPW, int NS_ = 2>
 struct LdsBf {
+    static constexpr int NS = NS_;
     static constexpr int NW = 4 * HPW;                // waves
     static constexpr int RB = N * 2;                  // bytes per B / C row
     static constexpr int XB = 128;                    // bytes per X row of one head (64 channels)
     static constexpr int TB = Q * RB;                 // B or C tile
     static constexpr int TX = Q * XB;                 // X tile of one head
-    static constexpr int oB = 0, oC = TB, oX = 2 * TB;   // then the HPW X tiles
-    static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q] each
-    static constexpr int STAGE = oX + HPW * TX;
-    static constexpr int MB = kNumMTiles * 512;       // one head's M^T tiles, bf16 fragments
-    static constexpr int oM = 2 * STAGE;
     static constexpr int ZW = Q * 32;                 // one wave's z tile [Q][16] bf16
-    static constexpr int oZ = oM + HPW * MB;
-    static constexpr int oD = oZ + NW * ZW;           // dt / doc ids
-    static constexpr int oS = oD + DB;
+    static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q] each
+    static constexpr int oB = 0, oC = TB, oX = 2 * TB;   // then the HPW X tiles
+    static constexpr int oZs = oX + HPW * TX;         // the waves' z tiles
+    static constexpr int oDs = oZs + NW * ZW;         // the heads' dt / doc ids
+    static constexpr int STAGE = oDs + DB;
+    // one head's M^T tiles as bf16 fragments: the high halves of the 10 tiles,
+    // then the low halves (M = hi + lo to ~2^-17 relative)
+    static constexpr int MB = 2 * kNumMTiles * 512;
+    static constexpr int oM = NS * STAGE;
+    static constexpr int oS = oM + HPW * MB;
     // per-token scalars of one chunk, floats: per head cs, dt, eo, w [Q] each;
     // then the segment start per token [Q] (int); cs_end per head; last_seg
     static constexpr int SC_SEG = 4 * HPW * Q;
@@ -800,9 +804,9 @@ struct LdsBf {
     static constexpr int NI_MIN = NI / NW;            // fewest
 };
 
-template <int N, bool SP, int HPW, bool CV>
+template <int N, bool SP, int HPW, bool CV, int NS>
 __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
-    using LD = LdsBf<N, HPW>;
+    using LD = LdsBf<N, HPW, NS>;
     static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
     static_assert(SP || !CV, "the fused conv takes raw dt through the softplus");
     constexpr int NT = N / 16;
@@ -856,8 +860,9 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
     const int Ys = (int)a.y_stride;
 
-    unsigned char* zbuf = smem + LD::oZ + wave * LD::ZW;              // this wave's z tile
-    unsigned char* dbuf = smem + LD::oD + hh * 3 * Q * 4;             // this head's dt, doc, doc-1
+    // in stage st: this wave's z tile, and this head's dt, doc, doc-1
+    auto zbuf = [&](int st) { return smem + st * LD::STAGE + LD::oZs + wave * LD::ZW; };
+    auto dbuf = [&](int st) { return smem + st * LD::STAGE + LD::oDs + hh * 3 * Q * 4; };
 
     // Copy slots of this wave: slot j is copy instruction wave + NW j of the
     // chunk (B tile, then C tile, then the X tiles).  Per slot: the uniform
@@ -910,23 +915,32 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         }
     };
     // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
-    auto issue_scalars = [&](int t0) {
+    auto issue_scalars = [&](int t0, int st) {
         const int rowl = min(lane, tl - t0);
-        dma4(static_cast<const char*>(dtbase) + (size_t)t0 * Ds4, (uint32_t)(rowl * Ds4), dbuf);
+        unsigned char* d = dbuf(st);
+        dma4(static_cast<const char*>(dtbase) + (size_t)t0 * Ds4, (uint32_t)(rowl * Ds4), d);
         if (docs) {
-            dma4(docbase, (uint32_t)(t0 + rowl) * 4, dbuf + Q * 4);
-            dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, dbuf + 2 * Q * 4);
+            dma4(docbase, (uint32_t)(t0 + rowl) * 4, d + Q * 4);
+            dma4(docbase, (uint32_t)max(t0 + rowl - 1, 0) * 4, d + 2 * Q * 4);
         }
     };
     // z of this wave's 16 channels: row r of the chunk -> zbuf + 32 r
-    auto issue_z = [&](int t0) {
+    auto issue_z = [&](int t0, int st) {
         const int lim = tl - t0;
         const char* Zc = reinterpret_cast<const char*>(zbase + (size_t)t0 * (Zs2 / 2));
+        unsigned char* zb = zbuf(st);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int row = min(32 * i + (lane >> 1), lim);
-            dma16(Zc, (uint32_t)(row * Zs2) + (lane & 1) * 16, zbuf + i * 1024);
+            dma16(Zc, (uint32_t)(row * Zs2) + (lane & 1) * 16, zb + i * 1024);
         }
+    };
+    // every input of the chunk at t0 into stage st: n_grp operations of this wave
+    const int n_grp = n_scal + n_tiles + 2;
+    auto issue_chunk = [&](int t0, int st) {
+        if (lead) issue_scalars(t0, st);
+        issue_tiles(t0, st);
+        issue_z(t0, st);
     };
 
     // ---- initial state: the given one, then the superchunks before k folded in
@@ -1070,15 +1084,13 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     }
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
-    if (nchunks > 0) {
-        if (lead) issue_scalars(tbeg);
-        issue_tiles(tbeg, 0);
-        issue_z(tbeg);
-    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+        if (j < nchunks) issue_chunk(tbeg + j * Q, j);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
-        const int st = c & 1;
+        const int st = c % NS;
         const bool more = c + 1 < nchunks;
         const unsigned char* sB = smem + st * LD::STAGE + LD::oB;
         const unsigned char* sC = smem + st * LD::STAGE + LD::oC;
@@ -1086,18 +1098,23 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         float* sc = scal + (c & 1) * LD::SCW;      // this chunk's scalars
         float* sch = sc + hh * 4 * Q;              // ... of this wave's head: cs, dt, eo, w
 
-        // chunk c's B/C/X (and, in lead waves, dt / doc ids) have landed: only
-        // the y stores of chunk c-1 and the z copies of chunk c may be newer
-        if (c == 0) wait_vmcnt<2>();
-        else wait_vmcnt<6>();
+        // every input of chunk c has landed.  Newer operations of this wave: the
+        // 4 y stores of each of the last min(c, NS-1) chunks, and the copies of
+        // the chunks after c already issued (at most NS-2 of them).
+        if constexpr (NS == 2) {
+            if (c == 0) wait_vmcnt<0>();
+            else wait_vmcnt<4>();
+        } else {
+            wait_vmcnt_n(4 * min(c, NS - 1) + n_grp * max(0, min(NS - 2, nchunks - 1 - c)));
+        }
         // ---- lead waves: segmented cumulative sum of dt*A (log2 domain), lane = token
         if (lead) {
             const bool tok_ok = t0 + lane < tend;
-            float dtl = reinterpret_cast<const float*>(dbuf)[lane];
-            const int d0 = reinterpret_cast<const int*>(dbuf)[Q + lane];
-            const int d1 = reinterpret_cast<const int*>(dbuf)[2 * Q + lane];
+            const unsigned char* db = dbuf(st);
+            float dtl = reinterpret_cast<const float*>(db)[lane];
+            const int d0 = reinterpret_cast<const int*>(db)[Q + lane];
+            const int d1 = reinterpret_cast<const int*>(db)[2 * Q + lane];
             lds_wait();
-            if (more) issue_scalars(t0 + Q);
             if (CV) {
                 const uint32_t wd = __float_as_uint(dtl);
                 dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
@@ -1132,7 +1149,8 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             }
         }
         lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
-        if (more) issue_tiles(t0 + Q, st ^ 1);
+        // refill the stage chunk c-1 used with chunk c + NS - 1
+        if (c + NS - 1 < nchunks) issue_chunk(t0 + (NS - 1) * Q, (c + NS - 1) % NS);
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
@@ -1202,17 +1220,18 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         m[r] = ok[r] ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
-                    *reinterpret_cast<FragBF*>(sM + e * LD::MB + kt * 512 + lane * 8) = frag_from_f32(m);
+                    const FragBF mh = frag_from_f32(m);
+                    const f32x4 ml = {m[0] - bf16_lo(mh.a), m[1] - bf16_hi(mh.a), m[2] - bf16_lo(mh.b),
+                                      m[3] - bf16_hi(mh.b)};
+                    *reinterpret_cast<FragBF*>(sM + e * LD::MB + kt * 512 + lane * 8) = mh;
+                    *reinterpret_cast<FragBF*>(sM + e * LD::MB + (kNumMTiles + kt) * 512 + lane * 8) =
+                        frag_from_f32(ml);
                 }
             }
             FragBF hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = frag_from_f32(Hs[nt]);
             lds_barrier();   // B: all M^T tiles are in LDS
-            // z of chunk c has landed: only this wave's copies of chunk c+1 (and,
-            // in lead waves, its dt / doc ids) may be newer
-            if (more) wait_vmcnt_n(n_tiles + n_scal);
-            else wait_vmcnt<0>();
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, output
             const unsigned char* sMh = sM + hh * LD::MB;
@@ -1222,19 +1241,25 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             const uint32_t xtr = SX::off(4 * q4 + j16 / 4, p0 + 4 * (j16 % 4));
             uint2 zr[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) zr[ti] = *reinterpret_cast<const uint2*>(zbuf + (16 * ti + j16) * 32 + q4 * 8);
+            for (int ti = 0; ti < 4; ++ti) zr[ti] = *reinterpret_cast<const uint2*>(zbuf(st) + (16 * ti + j16) * 32 + q4 * 8);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
+                    // X is exact in bf16; M^T enters as its high and low halves
                     const FragBF a0 = tr_read(sX, xtr + 16 * sb * XB);
-                    const FragBF b0 = plain_read(sMh + mtile_index(sb, ti) * 512 + lane * 8);
-                    FragBF a1 = {0u, 0u}, b1 = {0u, 0u};
+                    const int m0 = mtile_index(sb, ti) * 512 + lane * 8;
+                    const FragBF b0 = plain_read(sMh + m0);
+                    const FragBF l0 = plain_read(sMh + kNumMTiles * 512 + m0);
+                    FragBF a1 = {0u, 0u}, b1 = {0u, 0u}, l1 = {0u, 0u};
                     if (sb + 1 <= ti) {
                         a1 = tr_read(sX, xtr + 16 * (sb + 1) * XB);
-                        b1 = plain_read(sMh + mtile_index(sb + 1, ti) * 512 + lane * 8);
+                        const int m1 = mtile_index(sb + 1, ti) * 512 + lane * 8;
+                        b1 = plain_read(sMh + m1);
+                        l1 = plain_read(sMh + kNumMTiles * 512 + m1);
                     }
+                    yd = mma_bf16(yd, a0, a1, l0, l1);
                     yd = mma_bf16(yd, a0, a1, b0, b1);
                 }
                 f32x4 yo = {0.f, 0.f, 0.f, 0.f};
@@ -1263,11 +1288,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                 // rows past the unit's end fall outside the buffer range and are dropped
                 __builtin_amdgcn_raw_buffer_store_b128(o, yr, (uint32_t)(t * Ys + p0 + 4 * q4) * 4, 0, 0);
             }
-            // every wave's output stores are issued before any wave refills its z
-            // buffer: the four 64-byte pieces of a y row (one per wave of the head)
-            // then reach the L2 close together, which shortens the pass by ~8%
+            // every wave's output stores are issued before any wave goes on: the
+            // four 64-byte pieces of a y row (one per wave of the head) then reach
+            // the L2 close together, which shortens the pass by ~8%
             lds_barrier();
-            if (more) issue_z(t0 + Q);
         }
 
         // ---- chunk state S = B^T (w o X) from the row-major tiles via transpose reads
@@ -1673,10 +1697,15 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     }
 }
 
-template <int N, bool SP, int HPW, bool CV>
+// Stages of the full pass: the deepest of 4, 3, 2 whose plan fits a CU's LDS.
+template <int N, int HPW>
+constexpr int bf16_stages() {
+    return LdsBf<N, HPW, 4>::bytes <= 163840 ? 4 : LdsBf<N, HPW, 3>::bytes <= 163840 ? 3 : 2;
+}
+template <int N, bool SP, int HPW, bool CV, int NS>
 hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV>);
-    const size_t lds = LdsBf<N, HPW>::bytes;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV, NS>);
+    const size_t lds = LdsBf<N, HPW, NS>::bytes;
     static bool checked = false;
     if (!checked) {
         // The kernel's explicit vector-memory waits count only its own copies,
@@ -1689,14 +1718,15 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
         if (e != hipSuccess) return e;
         checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV>), dim3(units), dim3(256 * HPW), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV, NS>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
 }
 template <int N, int HPW>
 hipError_t launch_scan_bf16_full(const ScanArgs& a, int units, hipStream_t stream) {
-    if (a.conv) return launch_scan_bf16_k<N, true, HPW, true>(a, units, stream);
-    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW, false>(a, units, stream)
-                         : launch_scan_bf16_k<N, false, HPW, false>(a, units, stream);
+    constexpr int NS = bf16_stages<N, HPW>();
+    if (a.conv) return launch_scan_bf16_k<N, true, HPW, true, NS>(a, units, stream);
+    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW, false, NS>(a, units, stream)
+                         : launch_scan_bf16_k<N, false, HPW, false, NS>(a, units, stream);
 }
 // the state-only pre-pass: PRE_HPW heads per workgroup, kPrePB channel blocks
 // per wave (one with the fused conv, whose in-LDS pass wants every wave of a
@@ -1763,9 +1793,8 @@ template <int N>
 size_t bf16_lds_n(int hpw, bool full) {
     if (full) {
         switch (hpw) {
-            case 1: return LdsBf<N, 1>::bytes;
-            case 2: return LdsBf<N, 2>::bytes;
-            case 4: return N <= 64 ? LdsBf<N, (N <= 64 ? 4 : 1)>::bytes : kLdsPerCU + 1;
+            case 1: return LdsBf<N, 1, bf16_stages<N, 1>()>::bytes;
+            case 2: return LdsBf<N, 2, bf16_stages<N, 2>()>::bytes;
         }
     } else {
         switch (hpw) {
@@ -1792,12 +1821,12 @@ int bf16_wgs_per_cu(int N, int hpw, bool full) {
     const int waves = full ? 4 * hpw : 4 * hpw / kPrePB;
     return (int)std::min<size_t>(kLdsPerCU / bytes, (size_t)(kMaxWavesPerCU / waves));
 }
-// Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a
-// group and gives the most waves per CU.
+// Heads per workgroup: 2 or 1, whichever divides the heads of a group and
+// gives the most waves per CU.
 int bf16_hpw(int N, int H, int G) {
     const int hg = H / G;
     int best = 1, best_waves = 0;
-    for (int hpw : {4, 2, 1}) {
+    for (int hpw : {2, 1}) {
         if (hg % hpw) continue;
         const int waves = bf16_wgs_per_cu(N, hpw, true) * 4 * hpw;
         if (waves > best_waves) { best_waves = waves; best = hpw; }
@@ -1818,7 +1847,6 @@ hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
     if constexpr (!std::is_same<T, float>::value) {
         const int pre = bf16_pre_hpw(N, a.H, a.G);
         switch (bf16_hpw(N, a.H, a.G)) {
-            case 4: return launch_scan_bf16<N, (N <= 64 ? 4 : 2)>(a, pre, stream);
             case 2: return launch_scan_bf16<N, 2>(a, pre, stream);
             default: return launch_scan_bf16<N, 1>(a, pre, stream);
         }

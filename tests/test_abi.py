@@ -182,6 +182,8 @@ def call_step(lib, **over):
     (dict(N=256), 3, "N=256"),
     (dict(sst=None), 1, "ssm_state is NULL"),
     (dict(cst=MIS), 4, "conv_state"),
+    (dict(z=FAKE + 4), 4, "z="),
+    (dict(z=MIS), 4, "z="),
     (dict(H=256, G=1), 3, "64 KiB LDS"),
 ])
 def test_step_refusals(lib, over, status, needle):

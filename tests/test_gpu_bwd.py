@@ -3,12 +3,13 @@
 Bars, per gradient tensor:
   * inputs the two sides read identically (fp32 inputs, or bf16 inputs fed to the scan or the conv directly):
     max |gpu - oracle| <= 1e-3 * RMS(oracle) -- fp32 arithmetic throughout on the GPU.
-  * ssd_mixer_bwd with bf16 inputs: relative L2 error <= 1e-3 per tensor.  The conv output is stored as bf16
-    in both pipelines, and the GPU's fp32 pre-activation and the oracle's fp64 one can round to adjacent bf16
-    values; such a one-ulp (2^-8 relative) change of a scan input moves that token's gradients by up to the
-    same relative amount.  These flips are sparse (about 1 in 10^4 conv outputs), so they break an
-    element-wise bar but not an L2 one; element-wise parity at full size is shown with fp32 inputs and with
-    bf16 inputs fed to the scan backward directly.
+  * ssd_mixer_bwd with bf16 inputs, element-wise at the same bar against the oracle's backward fed the GPU's
+    own conv output (the bf16 [x | B | C] rows and fp32 dt of ssd_conv_fwd, which ssd_mixer_bwd recomputes bit
+    for bit): oracle.scan_bwd on those rows, then oracle.conv_bwd on its gradient.  Against the oracle's own
+    end-to-end backward (oracle.mixer_bwd, which rounds its fp64 conv output to bf16) the relative L2 error
+    is also held under 1e-3 per tensor: the two conv outputs can round to adjacent bf16 values (about 1 in
+    10^4), and each such one-ulp (2^-8 relative) change of a scan input moves that token's gradients by up
+    to the same relative amount -- sparse, so an L2 bar and not an element-wise one.
 Document isolation is bitwise: a loss on a later document gives exactly 0.0 gradient on every earlier-document
 input.  Two calls on the same inputs give identical bits.
 """
@@ -144,6 +145,30 @@ def _mixer_oracle(wl, prm, raw, ids, gy, rows=None):
                             doc_ids=None if ids is None else sl(ids).numpy(), round_bf16=wl.dtype == "bf16")
 
 
+def _mixer_oracle_on_gpu_conv(lib, wl, prm, raw, ids, gy, rows=None):
+    """The oracle's mixer backward with its conv step replaced by the GPU's ssd_conv_fwd output: oracle.scan_bwd
+    on the GPU's [x | B | C] rows and dt, then oracle.conv_bwd on the resulting conv-output gradient."""
+    g = lambda t: None if t is None else t.to(DEV)
+    xbc, dt = lib.ssd_conv_fwd(g(raw["xbc_raw"]), g(prm["conv_w"]), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                               conv_b=g(prm.get("conv_b")), dt_raw=g(raw["dt_raw"]), dt_bias=g(prm["dt_bias"]),
+                               doc_ids=g(ids))
+    torch.cuda.synchronize()
+    sl = (lambda t: t) if rows is None else (lambda t: t[rows])
+    HP, GN = wl.H * wl.P, wl.G * wl.N
+    xg, dg = _np(sl(xbc.cpu())), _np(sl(dt.cpu()))
+    idn = None if ids is None else sl(ids).numpy()
+    gs = oracle.scan_bwd(xg[..., :HP], xg[..., HP:HP + GN], xg[..., HP + GN:], dg, _np(prm["A"]), _np(sl(gy)),
+                         _np(prm["D"]), _np(sl(raw["z"])), idn, H=wl.H, P=wl.P, N=wl.N, G=wl.G)
+    dxbc = np.concatenate([gs["x"], gs["Bm"], gs["Cm"]], axis=2)
+    gc = oracle.conv_bwd(_np(sl(raw["xbc_raw"])), _np(prm["conv_w"]), dxbc, _np(prm.get("conv_b")),
+                         _np(sl(raw["dt_raw"])), _np(prm["dt_bias"]), gs["dt"], idn)
+    out = {"raw": gc["raw"], "w": gc["w"], "dt_raw": gc["dt_raw"], "A": gs["A"]}
+    for k, src in (("bias", gc), ("dt_bias", gc), ("D", gs), ("z", gs)):
+        if k in src:
+            out[k] = src[k]
+    return out
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mixer_bwd_vs_oracle(gpu_lib, dtype):
     wl = synth.Workload(f"mbwd_{dtype}", 2, 333, 8, 64, 64, 2, dtype)
@@ -156,6 +181,11 @@ def test_mixer_bwd_vs_oracle(gpu_lib, dtype):
             _check(got[k], ref[k], f"d{k}")
         else:
             hp.assert_rel_l2(got[k], ref[k], f"d{k}")
+    if dtype == "bf16":
+        same = _mixer_oracle_on_gpu_conv(gpu_lib, wl, prm, raw, ids, gy)
+        assert set(same) == set(ref)
+        for k in same:
+            _check(got[k], same[k], f"d{k} (oracle fed the GPU conv output)")
 
 
 def test_bwd_document_isolation_and_determinism(gpu_lib):
@@ -227,8 +257,9 @@ def test_bwd_empty_and_refusals(gpu_lib):
 @pytest.mark.parametrize("name", ["mini_k3_packed", "mini_k3_bf16"])
 def test_mixer_bwd_full_workload(gpu_lib, name, dtype):
     """The Mini-K3 mixer shape (B=5, L=8192, H=32, N=64, G=8) end to end against the oracle's backward on all
-    five rows, every gradient (parameter gradients included): element-wise with fp32 inputs, relative L2 with
-    bf16 inputs (see the module doc)."""
+    five rows, every gradient (parameter gradients included): element-wise with fp32 inputs; with bf16 inputs
+    element-wise against the oracle fed the GPU's conv output, and relative L2 against the oracle's own
+    end-to-end backward (see the module doc)."""
     wl = synth.WORKLOADS[name].with_(dtype=dtype)
     _say(f"mixer bwd full workload {name} {dtype}")
     prm, raw, ids, gy = _mixer_inputs(wl, 0, wl.docs)
@@ -239,6 +270,11 @@ def test_mixer_bwd_full_workload(gpu_lib, name, dtype):
             _check(got[k], ref[k], f"d{k}")
         else:
             hp.assert_rel_l2(got[k], ref[k], f"d{k}")
+    if dtype == "bf16":
+        del ref
+        same = _mixer_oracle_on_gpu_conv(gpu_lib, wl, prm, raw, ids, gy)
+        for k in same:
+            _check(got[k], same[k], f"d{k} (oracle fed the GPU conv output)")
 
 
 def test_scan_bwd_full_workload_bf16(gpu_lib):

@@ -4,8 +4,10 @@ Two bars on seeded synthetic inputs:
   * bit identity with the two-call path ssd_conv_fwd -> ssd_chunk_scan_fwd (dt_softplus = 0 on the conv's
     dt) with the same workspace choice: the fused kernels convolve each chunk in LDS with the conv
     kernel's fp32 arithmetic, so y, the final state and the conv state must agree exactly;
-  * the fp64 oracle's conv -> scan pipeline (oracle.forward) within the bars of tests/helpers.py, and the
-    outgoing conv state (raw rows) exactly.
+  * the fp64 oracle, call by call on identical inputs: the conv (run alone on the GPU; the mixer equals the
+    two-call path bit for bit) within one bf16 ulp of the oracle conv, and the scan within the flat 0.03125
+    (bf16) or 1e-3 * RMS (fp32) of the oracle scan fed that conv's exact output; the outgoing conv state (raw
+    rows) exactly.
 """
 import numpy as np
 import pytest
@@ -74,22 +76,43 @@ def run_two_call(lib, wl, raw, prm, ids=None, cs_in=None, h0=None, act=0, split=
     return y, fs, cs_out
 
 
-def check_oracle(wl, raw, prm, ids, cs_in, h0, act, y, fs, cs_out, rows=None):
+def gpu_conv(lib, wl, raw, prm, ids=None, cs_in=None, act=0):
+    """ssd_conv_fwd alone: the [x | B | C] rows and dt that the mixer's scan reads (the mixer equals the
+    two-call path bit for bit)."""
+    xbc, dt = lib.ssd_conv_fwd(_g(raw["xbc_raw"]), _g(prm["conv_w"]), H=wl.H, P=wl.P, N=wl.N, G=wl.G,
+                               conv_b=_g(prm.get("conv_b")), dt_raw=_g(raw["dt_raw"]), dt_bias=_g(prm["dt_bias"]),
+                               doc_ids=_g(ids), conv_state_in=_g(cs_in), act=act)
+    torch.cuda.synchronize()
+    return xbc, dt
+
+
+def check_oracle(lib, wl, raw, prm, ids, cs_in, h0, act, y, fs, cs_out, rows=None):
+    """Call by call against the oracle on identical inputs (module doc), on whole batch rows."""
     rows = range(raw["xbc_raw"].shape[0]) if rows is None else rows
     bf = wl.dtype == "bf16"
+    HP, GN = wl.H * wl.P, wl.G * wl.N
+    xbc, dt = gpu_conv(lib, wl, raw, prm, ids, cs_in, act)
     for b in rows:
         sl = slice(b, b + 1)
         cpu = lambda t: None if t is None else t[sl].cpu()
-        yr, fr, cr, xr, _ = oracle.forward(cpu(raw["xbc_raw"]), prm["conv_w"], prm.get("conv_b"), cpu(raw["dt_raw"]),
-                                           prm["dt_bias"], prm["A"], prm["D"], cpu(raw["z"]), H=wl.H, P=wl.P, N=wl.N,
-                                           G=wl.G, doc_ids=None if ids is None else ids[sl],
-                                           conv_state_in=cpu(cs_in), init_state=cpu(h0), act=act, round_bf16=bf)
+        ids_b = None if ids is None else ids[sl].cpu()
+        ref, dref, cr = oracle.conv(cpu(raw["xbc_raw"]), prm["conv_w"], prm.get("conv_b"), cpu(raw["dt_raw"]),
+                                    prm["dt_bias"], ids_b, cpu(cs_in), act=act, want_state=True)
+        xg, dg = xbc[sl].cpu(), dt[sl].cpu()
         if bf:
-            hp.assert_pipeline(y[sl], yr, xr[..., :wl.H * wl.P], cpu(raw["z"]), prm["D"], wl.H, wl.P, f"y row {b}")
-            hp.assert_bf16(fs[sl], fr, f"final_state row {b}")
+            ab = lambda t: None if t is None else hp.np64(t).__abs__()
+            mag, _, _ = oracle.conv(ab(cpu(raw["xbc_raw"])), ab(prm["conv_w"]), ab(prm.get("conv_b")), doc_ids=ids_b,
+                                    state_in=ab(cpu(cs_in)), act=1)
+            hp.assert_within_ulp(xg, ref, f"conv row {b}", mag)
         else:
-            hp.assert_fp32(y[sl], yr, f"y row {b}")
-            hp.assert_fp32(fs[sl], fr, f"final_state row {b}")
+            hp.assert_fp32(xg, ref, f"conv row {b}")
+        hp.assert_fp32(dg, dref, f"dt row {b}")
+        yr, fr = oracle.scan(xg[..., :HP], xg[..., HP:HP + GN], xg[..., HP + GN:], dg, prm["A"], prm["D"],
+                             cpu(raw["z"]), ids_b, cpu(h0), H=wl.H, P=wl.P, N=wl.N, G=wl.G, dt_softplus=False,
+                             want_state=True)
+        check = hp.assert_bf16 if bf else hp.assert_fp32
+        check(y[sl], yr, f"y row {b}")
+        check(fs[sl], fr, f"final_state row {b}")
         np.testing.assert_array_equal(hp.np64(cs_out[sl]), cr, err_msg=f"conv_state_out row {b}")
 
 
@@ -137,7 +160,7 @@ def test_mixer_small(gpu_lib, dtype, N, G, H, L, docs, cs, h0, gate, act, bias, 
     assert torch.equal(y, y2), hp.report("mixer vs two-call y", y, y2)
     assert torch.equal(fs, fs2), hp.report("mixer vs two-call final_state", fs, fs2)
     assert torch.equal(co, co2), "mixer vs two-call conv_state_out"
-    check_oracle(wl, raw, prm, ids, cs_in, raw["h0"], act, y, fs, co)
+    check_oracle(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, y, fs, co)
 
 
 SPLIT_CASES = [
@@ -165,7 +188,7 @@ def test_mixer_split(gpu_lib, dtype, N, G, H, L, docs, cs, h0):
     assert torch.equal(y, y2), hp.report("mixer vs two-call y", y, y2)
     assert torch.equal(fs, fs2), hp.report("mixer vs two-call final_state", fs, fs2)
     assert torch.equal(co, co2), "mixer vs two-call conv_state_out"
-    check_oracle(wl, raw, prm, ids, cs_in, raw["h0"], 0, y, fs, co)
+    check_oracle(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], 0, y, fs, co)
 
 
 def test_mixer_strided_views(gpu_lib):
@@ -206,8 +229,8 @@ def test_mixer_empty_sequence_passes_states_through(gpu_lib):
 @pytest.mark.parametrize("plan", ["fused", "staged"])
 @pytest.mark.parametrize("name", ["mini_k3_packed", "large_layer_bf16"])
 def test_mixer_full_workload(gpu_lib, name, plan):
-    """The full-size workloads with the split: bit-identical to the two-call path on every output, and
-    within the pipeline bound of the oracle on the first and last batch rows."""
+    """The full-size workloads with the split: bit-identical to the two-call path on every output, and call by
+    call within the flat bars of the oracle on the first and last batch rows."""
     wl = synth.WORKLOADS[name]
     _say(f"mixer full {name} {plan}")
     prm = synth.params(wl, 0)
@@ -218,7 +241,7 @@ def test_mixer_full_workload(gpu_lib, name, plan):
     assert torch.equal(y, y2), hp.report("mixer vs two-call y", y, y2)
     assert torch.equal(fs, fs2) and torch.equal(co, co2)
     del y2, fs2
-    check_oracle(wl, raw, prm, ids, None, raw["h0"], 0, y, fs, co, rows=(0, wl.B - 1))
+    check_oracle(gpu_lib, wl, raw, prm, ids, None, raw["h0"], 0, y, fs, co, rows=(0, wl.B - 1))
 
 
 @pytest.mark.parametrize("cut", [64, 1024, 1984])

@@ -144,6 +144,36 @@ def test_resume_decode_workload_shape(gpu_lib):
     assert rs.pos == 0 and torch.equal(rs.state, f_ref)
 
 
+def test_resume_decode_workload_full(gpu_lib):
+    """The decode workload in full: B = 256 sequences, H = 64, P = 64, N = 128, one group, fp32, a 4096-token
+    prefill and then all 1024 decode steps through ssd_resume_fwd, one token per call.  Every decode output of
+    every sequence equals the one-call 5120-token forward bit for bit, and so does the resumed state at the
+    first, a middle and the last chunk end (the forward's final state at those lengths)."""
+    wl = synth.WORKLOADS["decode_fp32"]
+    steps = wl.steps
+    _say(f"resume decode workload full: B={wl.B} prefill={wl.L} steps={steps}")
+    prm, raw, _ = setup(wl, 35, wl.L + steps)
+    y_ref, _, _ = forward(gpu_lib, wl, raw, prm, wl.L + steps)
+    _, fs, cs = forward(gpu_lib, wl, raw, prm, wl.L)
+    rs = Resumer(gpu_lib, wl, prm, wl.B, fs, cs)
+    del fs, cs
+    checked = {64, 512, steps}
+    ys = []
+    for s in range(steps):
+        ys.append(rs.append(raw, wl.L + s, 1))
+        if s + 1 in checked:
+            assert rs.pos == 0
+            _, f_at, _ = forward(gpu_lib, wl, raw, prm, wl.L + s + 1)
+            assert torch.equal(rs.state, f_at), f"state after chunk end at token {wl.L + s + 1}"
+            del f_at
+            _say(f"  state equal after {s + 1} steps")
+    torch.cuda.synchronize()
+    y = torch.cat(ys, 1)
+    assert torch.equal(y, y_ref[:, wl.L:]), hp.report("resumed decode y vs one forward", y, y_ref[:, wl.L:])
+    del raw, y_ref, y, ys, rs
+    torch.cuda.empty_cache()
+
+
 def test_resume_refusals(gpu_lib):
     wl = synth.Workload("resume_ref", 1, 64, 4, 64, 32, 1, "bf16")
     prm, raw, _ = setup(wl, 34, 70)

@@ -20,7 +20,7 @@ def _say(msg):
 def decode_run(gpu_lib, wl, prm, raw, steps, seed, gen_device):
     """GPU prefill over raw, then `steps` ssd_step calls (step inputs drawn on gen_device, the same device the
     oracle side draws them on); returns (y_prefill, [y_step], ssm, conv)."""
-    y, fs, cs, _ = gpu_forward(gpu_lib, wl, raw, prm)
+    y, fs, cs, _, _ = gpu_forward(gpu_lib, wl, raw, prm)
     ys = []
     g = lambda t: None if t is None else t.to(DEV)
     for s in range(steps):
