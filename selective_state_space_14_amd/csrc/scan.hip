@@ -762,12 +762,16 @@ __device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw
 }
 
 // LDS plan of the full pass: NS stages of a chunk's inputs -- B, C and the
-// heads' X tiles, every wave's z tile, the heads' dt / doc ids -- then the
-// heads' M^T fragments and two buffers of per-token scalars.  A chunk's
-// inputs are copied NS - 1 chunks ahead of its compute.
-template <int N, int HPW, int NS_ = 2>
+// heads' X tiles, the heads' dt / doc ids and (ZR) every wave's z tile --
+// then the heads' M^T fragments, (!ZR) one z tile per wave, and two buffers
+// of per-token scalars.  A chunk's tiles are copied NS - 1 chunks ahead of
+// its compute; z in the ring likewise, z outside it (NS = 2 only) right after
+// the previous chunk's outputs.  MS: M^T is held as bf16 high and low halves,
+// else as one bf16 rounding.
+template <int N, int HPW, int NS_ = 2, bool ZR_ = true, bool MS_ = true>
 struct LdsBf {
     static constexpr int NS = NS_;
+    static constexpr bool ZR = ZR_, MS = MS_;
     static constexpr int NW = 4 * HPW;                // waves
     static constexpr int RB = N * 2;                  // bytes per B / C row
     static constexpr int XB = 128;                    // bytes per X row of one head (64 channels)
@@ -776,14 +780,16 @@ struct LdsBf {
     static constexpr int ZW = Q * 32;                 // one wave's z tile [Q][16] bf16
     static constexpr int DB = HPW * 3 * Q * 4;        // per head: dt, doc, doc of the previous token [Q] each
     static constexpr int oB = 0, oC = TB, oX = 2 * TB;   // then the HPW X tiles
-    static constexpr int oZs = oX + HPW * TX;         // the waves' z tiles
-    static constexpr int oDs = oZs + NW * ZW;         // the heads' dt / doc ids
-    static constexpr int STAGE = oDs + DB;
+    static constexpr int oZs = oX + HPW * TX;         // the waves' z tiles (ZR)
+    static constexpr int oDs = oZs + (ZR ? NW * ZW : 0);   // the heads' dt / doc ids (ZR)
+    static constexpr int STAGE = oDs + (ZR ? DB : 0);
     // one head's M^T tiles as bf16 fragments: the high halves of the 10 tiles,
-    // then the low halves (M = hi + lo to ~2^-17 relative)
-    static constexpr int MB = 2 * kNumMTiles * 512;
+    // then (MS) the low halves (M = hi + lo to ~2^-17 relative)
+    static constexpr int MB = (MS ? 2 : 1) * kNumMTiles * 512;
     static constexpr int oM = NS * STAGE;
-    static constexpr int oS = oM + HPW * MB;
+    static constexpr int oZ1 = oM + HPW * MB;         // the waves' z tiles (!ZR)
+    static constexpr int oD1 = oZ1 + (ZR ? 0 : NW * ZW);   // the heads' dt / doc ids (!ZR)
+    static constexpr int oS = oD1 + (ZR ? 0 : DB);
     // per-token scalars of one chunk, floats: per head cs, dt, eo, w [Q] each;
     // then the segment start per token [Q] (int); cs_end per head; last_seg
     static constexpr int SC_SEG = 4 * HPW * Q;
@@ -804,10 +810,11 @@ struct LdsBf {
     static constexpr int NI_MIN = NI / NW;            // fewest
 };
 
-template <int N, bool SP, int HPW, bool CV, int NS>
+template <int N, bool SP, int HPW, bool CV, int NS, bool ZR, bool MS>
 __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
-    using LD = LdsBf<N, HPW, NS>;
+    using LD = LdsBf<N, HPW, NS, ZR, MS>;
     static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
+    static_assert(ZR || NS == 2, "z outside the ring is single-buffered");
     static_assert(SP || !CV, "the fused conv takes raw dt through the softplus");
     constexpr int NT = N / 16;
     constexpr int NW = LD::NW;
@@ -861,8 +868,12 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int Ys = (int)a.y_stride;
 
     // in stage st: this wave's z tile, and this head's dt, doc, doc-1
-    auto zbuf = [&](int st) { return smem + st * LD::STAGE + LD::oZs + wave * LD::ZW; };
-    auto dbuf = [&](int st) { return smem + st * LD::STAGE + LD::oDs + hh * 3 * Q * 4; };
+    auto zbuf = [&](int st) {
+        return ZR ? smem + st * LD::STAGE + LD::oZs + wave * LD::ZW : smem + LD::oZ1 + wave * LD::ZW;
+    };
+    auto dbuf = [&](int st) {
+        return (ZR ? smem + st * LD::STAGE + LD::oDs : smem + LD::oD1) + hh * 3 * Q * 4;
+    };
 
     // Copy slots of this wave: slot j is copy instruction wave + NW j of the
     // chunk (B tile, then C tile, then the X tiles).  Per slot: the uniform
@@ -873,7 +884,9 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     uint32_t s_lds[LD::NI_W];
     int s_row[LD::NI_W];
     uint32_t s_col[LD::NI_W];
+    uint32_t s_off[LD::NI_W];      // the lane's byte offset in the chunk when no row is clamped
     bool s_on[LD::NI_W];
+    constexpr bool kAllOn = LD::NI % NW == 0;   // every wave issues NI_W copies
 #pragma unroll
     for (int j = 0; j < LD::NI_W; ++j) {
         const int i = wave + NW * j;
@@ -897,6 +910,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             s_row[j] = r;
             s_col[j] = (uint32_t)(((lane % (XB / 16)) ^ SX::f(r)) * 16);
         }
+        s_off[j] = (uint32_t)(s_row[j] * s_stride[j]) + s_col[j];
     }
     // vector-memory operations this wave issues per chunk for the tiles, and
     // (lead waves) for dt / doc ids: the exact counts its waits are built from
@@ -906,12 +920,16 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     auto issue_tiles = [&](int t0, int st) {
         const int lim = tl - t0;
         unsigned char* base = smem + st * LD::STAGE;
+        if (lim >= Q - 1) {          // every row inside the unit: the precomputed offsets
 #pragma unroll
-        for (int j = 0; j < LD::NI_W; ++j) {
-            if (s_on[j]) {
-                const char* src = s_base[j] + (size_t)t0 * s_stride[j];
-                dma16(src, (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j], base + s_lds[j]);
-            }
+            for (int j = 0; j < LD::NI_W; ++j)
+                if (kAllOn || s_on[j]) dma16(s_base[j] + (size_t)t0 * s_stride[j], s_off[j], base + s_lds[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < LD::NI_W; ++j)
+                if (kAllOn || s_on[j])
+                    dma16(s_base[j] + (size_t)t0 * s_stride[j], (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j],
+                          base + s_lds[j]);
         }
     };
     // lead waves: dt and the doc ids of tokens t0 + lane and t0 + lane - 1
@@ -935,12 +953,17 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             dma16(Zc, (uint32_t)(row * Zs2) + (lane & 1) * 16, zb + i * 1024);
         }
     };
-    // every input of the chunk at t0 into stage st: n_grp operations of this wave
+    // the chunk at t0 into stage st: n_grp operations of this wave (ZR: dt / doc
+    // ids and z too; otherwise those follow their own schedule)
     const int n_grp = n_scal + n_tiles + 2;
     auto issue_chunk = [&](int t0, int st) {
-        if (lead) issue_scalars(t0, st);
-        issue_tiles(t0, st);
-        issue_z(t0, st);
+        if constexpr (ZR) {
+            if (lead) issue_scalars(t0, st);
+            issue_tiles(t0, st);
+            issue_z(t0, st);
+        } else {
+            issue_tiles(t0, st);
+        }
     };
 
     // ---- initial state: the given one, then the superchunks before k folded in
@@ -1084,9 +1107,11 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     }
 
     const int nchunks = (tend - tbeg + Q - 1) / Q;
+    if (!ZR && lead && nchunks > 0) issue_scalars(tbeg, 0);
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
         if (j < nchunks) issue_chunk(tbeg + j * Q, j);
+    if (!ZR && nchunks > 0) issue_z(tbeg, 0);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
@@ -1098,10 +1123,14 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         float* sc = scal + (c & 1) * LD::SCW;      // this chunk's scalars
         float* sch = sc + hh * 4 * Q;              // ... of this wave's head: cs, dt, eo, w
 
-        // every input of chunk c has landed.  Newer operations of this wave: the
-        // 4 y stores of each of the last min(c, NS-1) chunks, and the copies of
-        // the chunks after c already issued (at most NS-2 of them).
-        if constexpr (NS == 2) {
+        // every input of chunk c has landed (z outside the ring: every other
+        // input).  Newer operations of this wave: the 4 y stores of each of the
+        // last min(c, NS-1) chunks, the copies of the chunks after c already
+        // issued (at most NS-2 of them), and (!ZR) the z copies of chunk c.
+        if constexpr (!ZR) {
+            if (c == 0) wait_vmcnt<2>();
+            else wait_vmcnt<6>();
+        } else if constexpr (NS == 2) {
             if (c == 0) wait_vmcnt<0>();
             else wait_vmcnt<4>();
         } else {
@@ -1115,6 +1144,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             const int d0 = reinterpret_cast<const int*>(db)[Q + lane];
             const int d1 = reinterpret_cast<const int*>(db)[2 * Q + lane];
             lds_wait();
+            if (!ZR && more) issue_scalars(t0 + Q, 0);     // refilled right after it is read
             if (CV) {
                 const uint32_t wd = __float_as_uint(dtl);
                 dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
@@ -1221,17 +1251,25 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                     for (int r = 0; r < 4; ++r)
                         m[r] = ok[r] ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
                     const FragBF mh = frag_from_f32(m);
-                    const f32x4 ml = {m[0] - bf16_lo(mh.a), m[1] - bf16_hi(mh.a), m[2] - bf16_lo(mh.b),
-                                      m[3] - bf16_hi(mh.b)};
                     *reinterpret_cast<FragBF*>(sM + e * LD::MB + kt * 512 + lane * 8) = mh;
-                    *reinterpret_cast<FragBF*>(sM + e * LD::MB + (kNumMTiles + kt) * 512 + lane * 8) =
-                        frag_from_f32(ml);
+                    if constexpr (MS) {
+                        const f32x4 ml = {m[0] - bf16_lo(mh.a), m[1] - bf16_hi(mh.a), m[2] - bf16_lo(mh.b),
+                                          m[3] - bf16_hi(mh.b)};
+                        *reinterpret_cast<FragBF*>(sM + e * LD::MB + (kNumMTiles + kt) * 512 + lane * 8) =
+                            frag_from_f32(ml);
+                    }
                 }
             }
             FragBF hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = frag_from_f32(Hs[nt]);
             lds_barrier();   // B: all M^T tiles are in LDS
+            if constexpr (!ZR) {
+                // z of chunk c has landed: only this wave's copies of chunk c+1
+                // (and, in lead waves, its dt / doc ids) may be newer
+                if (more) wait_vmcnt_n(n_tiles + n_scal);
+                else wait_vmcnt<0>();
+            }
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, output
             const unsigned char* sMh = sM + hh * LD::MB;
@@ -1241,25 +1279,29 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             const uint32_t xtr = SX::off(4 * q4 + j16 / 4, p0 + 4 * (j16 % 4));
             uint2 zr[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) zr[ti] = *reinterpret_cast<const uint2*>(zbuf(st) + (16 * ti + j16) * 32 + q4 * 8);
+            for (int ti = 0; ti < 4; ++ti)
+                zr[ti] = *reinterpret_cast<const uint2*>(zbuf(st) + (16 * ti + j16) * 32 + q4 * 8);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
-                    // X is exact in bf16; M^T enters as its high and low halves
+                    // X is exact in bf16; M^T enters as its high and (MS) low halves
                     const FragBF a0 = tr_read(sX, xtr + 16 * sb * XB);
                     const int m0 = mtile_index(sb, ti) * 512 + lane * 8;
                     const FragBF b0 = plain_read(sMh + m0);
-                    const FragBF l0 = plain_read(sMh + kNumMTiles * 512 + m0);
-                    FragBF a1 = {0u, 0u}, b1 = {0u, 0u}, l1 = {0u, 0u};
+                    FragBF a1 = {0u, 0u}, b1 = {0u, 0u};
                     if (sb + 1 <= ti) {
                         a1 = tr_read(sX, xtr + 16 * (sb + 1) * XB);
-                        const int m1 = mtile_index(sb + 1, ti) * 512 + lane * 8;
-                        b1 = plain_read(sMh + m1);
-                        l1 = plain_read(sMh + kNumMTiles * 512 + m1);
+                        b1 = plain_read(sMh + mtile_index(sb + 1, ti) * 512 + lane * 8);
                     }
-                    yd = mma_bf16(yd, a0, a1, l0, l1);
+                    if constexpr (MS) {
+                        const FragBF l0 = plain_read(sMh + kNumMTiles * 512 + m0);
+                        const FragBF l1 = sb + 1 <= ti
+                                              ? plain_read(sMh + (kNumMTiles + mtile_index(sb + 1, ti)) * 512 + lane * 8)
+                                              : FragBF{0u, 0u};
+                        yd = mma_bf16(yd, a0, a1, l0, l1);
+                    }
                     yd = mma_bf16(yd, a0, a1, b0, b1);
                 }
                 f32x4 yo = {0.f, 0.f, 0.f, 0.f};
@@ -1277,21 +1319,32 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                 const float eo = sch[2 * Q + t];
                 const uint2 xr = *reinterpret_cast<const uint2*>(sX + SX::off(t, p0 + 4 * q4));
                 const float xs[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
-                const float zsv[4] = {bf16_lo(zr[ti].x), bf16_hi(zr[ti].x), bf16_lo(zr[ti].y), bf16_hi(zr[ti].y)};
+                // the gate factors silu(z) of the lane's 4 outputs (1 without a gate)
+                float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (gate) {
+                    gz[0] = silu_f(bf16_lo(zr[ti].x));
+                    gz[1] = silu_f(bf16_hi(zr[ti].x));
+                    gz[2] = silu_f(bf16_lo(zr[ti].y));
+                    gz[3] = silu_f(bf16_hi(zr[ti].y));
+                }
                 u32x4_t o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float v = fmaf(eo, yo[r], yd[r]);
                     v = fmaf(Dh, xs[r], v);
-                    o[r] = __float_as_uint(gate ? v * silu_f(zsv[r]) : v);
+                    o[r] = __float_as_uint(v * gz[r]);
                 }
                 // rows past the unit's end fall outside the buffer range and are dropped
                 __builtin_amdgcn_raw_buffer_store_b128(o, yr, (uint32_t)(t * Ys + p0 + 4 * q4) * 4, 0, 0);
             }
-            // every wave's output stores are issued before any wave goes on: the
-            // four 64-byte pieces of a y row (one per wave of the head) then reach
-            // the L2 close together, which shortens the pass by ~8%
+            // every wave's output stores are issued before any wave goes on (and,
+            // z outside the ring, refills its z tile): the four 64-byte pieces of
+            // a y row (one per wave of the head) then reach the L2 close together,
+            // which shortens the pass by ~8%
             lds_barrier();
+            if constexpr (!ZR) {
+                if (more) issue_z(t0 + Q, 0);
+            }
         }
 
         // ---- chunk state S = B^T (w o X) from the row-major tiles via transpose reads
@@ -1697,15 +1750,25 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     }
 }
 
-// Stages of the full pass: the deepest of 4, 3, 2 whose plan fits a CU's LDS.
+// LDS layout of the full pass for N and HPW.  Two stages: copies one chunk
+// ahead already cover the HBM latency (three- and four-stage rings measured
+// no faster on the Mini-K3 and large-layer workloads) and leave the most LDS
+// for resident workgroups.  z goes in the ring and M^T is split into halves
+// where the layout fits a CU; otherwise z is single-buffered, then M^T is
+// one bf16 rounding.  ok: some layout fits.
 template <int N, int HPW>
-constexpr int bf16_stages() {
-    return LdsBf<N, HPW, 4>::bytes <= 163840 ? 4 : LdsBf<N, HPW, 3>::bytes <= 163840 ? 3 : 2;
-}
-template <int N, bool SP, int HPW, bool CV, int NS>
+struct BfPlan {
+    static constexpr int NS = 2;
+    static constexpr bool ZR = LdsBf<N, HPW, NS, true, true>::bytes <= 163840;
+    static constexpr bool MS = ZR || LdsBf<N, HPW, NS, false, true>::bytes <= 163840;
+    using LD = LdsBf<N, HPW, NS, ZR, MS>;
+    static constexpr bool ok = LD::bytes <= 163840;
+};
+template <int N, bool SP, int HPW, bool CV>
 hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) {
-    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV, NS>);
-    const size_t lds = LdsBf<N, HPW, NS>::bytes;
+    using PL = BfPlan<N, HPW>;
+    const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV, PL::NS, PL::ZR, PL::MS>);
+    const size_t lds = PL::LD::bytes;
     static bool checked = false;
     if (!checked) {
         // The kernel's explicit vector-memory waits count only its own copies,
@@ -1718,15 +1781,15 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
         if (e != hipSuccess) return e;
         checked = true;
     }
-    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV, NS>), dim3(units), dim3(256 * HPW), lds, stream, a);
+    hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV, PL::NS, PL::ZR, PL::MS>), dim3(units), dim3(256 * HPW),
+                       lds, stream, a);
     return hipGetLastError();
 }
 template <int N, int HPW>
 hipError_t launch_scan_bf16_full(const ScanArgs& a, int units, hipStream_t stream) {
-    constexpr int NS = bf16_stages<N, HPW>();
-    if (a.conv) return launch_scan_bf16_k<N, true, HPW, true, NS>(a, units, stream);
-    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW, false, NS>(a, units, stream)
-                         : launch_scan_bf16_k<N, false, HPW, false, NS>(a, units, stream);
+    if (a.conv) return launch_scan_bf16_k<N, true, HPW, true>(a, units, stream);
+    return a.dt_softplus ? launch_scan_bf16_k<N, true, HPW, false>(a, units, stream)
+                         : launch_scan_bf16_k<N, false, HPW, false>(a, units, stream);
 }
 // the state-only pre-pass: PRE_HPW heads per workgroup, kPrePB channel blocks
 // per wave (one with the fused conv, whose in-LDS pass wants every wave of a
@@ -1793,8 +1856,9 @@ template <int N>
 size_t bf16_lds_n(int hpw, bool full) {
     if (full) {
         switch (hpw) {
-            case 1: return LdsBf<N, 1, bf16_stages<N, 1>()>::bytes;
-            case 2: return LdsBf<N, 2, bf16_stages<N, 2>()>::bytes;
+            case 1: return BfPlan<N, 1>::LD::bytes;
+            case 2: return BfPlan<N, 2>::LD::bytes;
+            case 4: return BfPlan<N, 4>::LD::bytes;
         }
     } else {
         switch (hpw) {
@@ -1821,12 +1885,12 @@ int bf16_wgs_per_cu(int N, int hpw, bool full) {
     const int waves = full ? 4 * hpw : 4 * hpw / kPrePB;
     return (int)std::min<size_t>(kLdsPerCU / bytes, (size_t)(kMaxWavesPerCU / waves));
 }
-// Heads per workgroup: 2 or 1, whichever divides the heads of a group and
-// gives the most waves per CU.
+// Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a
+// group and gives the most waves per CU.
 int bf16_hpw(int N, int H, int G) {
     const int hg = H / G;
     int best = 1, best_waves = 0;
-    for (int hpw : {2, 1}) {
+    for (int hpw : {4, 2, 1}) {
         if (hg % hpw) continue;
         const int waves = bf16_wgs_per_cu(N, hpw, true) * 4 * hpw;
         if (waves > best_waves) { best_waves = waves; best = hpw; }
@@ -1847,6 +1911,9 @@ hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
     if constexpr (!std::is_same<T, float>::value) {
         const int pre = bf16_pre_hpw(N, a.H, a.G);
         switch (bf16_hpw(N, a.H, a.G)) {
+            case 4:
+                if constexpr (BfPlan<N, 4>::ok) return launch_scan_bf16<N, 4>(a, pre, stream);
+                return hipErrorInvalidConfiguration;   // not chosen: bf16_hpw sees no room for 4 heads
             case 2: return launch_scan_bf16<N, 2>(a, pre, stream);
             default: return launch_scan_bf16<N, 1>(a, pre, stream);
         }
