@@ -155,9 +155,10 @@ int ssd_conv_fwd(int B, int L, int H, int P, int N, int G, int K, int dtype,
  * multiple of 64 tokens with the state carried is bitwise identical to one
  * call.  With a workspace of ssd_chunk_scan_workspace_size() bytes the
  * sequence may additionally be cut into superchunks scanned in parallel:
- * a first pass stores each superchunk's local end state and total decay in
- * the workspace and the main pass folds them in (the state passing of the
- * SSD paper's chunked algorithm, one level up).  Results then agree with the
+ * a first pass stores each superchunk's local end state (scanned from a zero
+ * state) and total decay in the workspace, and the main pass folds the
+ * preceding superchunks' states into its starting state, in order, exactly
+ * as chunk states are passed between chunks.  Results then agree with the
  * sequential pass to fp32 rounding, not bitwise.  The first pass also copies
  * init_state into the workspace and the main pass reads only that copy, so
  * final_state may alias init_state on either path.
