@@ -207,6 +207,40 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
  * these sizes; 0 when no split pays (then the workspace is ignored). */
 size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, int dtype);
 
+/* Size of the library's static scratch buffer (per GPU) used by
+ * ssd_chunk_scan_fwd_static. */
+#define SSD_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * ssd_chunk_scan_fwd_static -- ssd_chunk_scan_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Arguments and results are those of ssd_chunk_scan_fwd called with a
+ * workspace of ssd_chunk_scan_workspace_size() bytes (bit for bit the same
+ * outputs), except that the workspace is a file-scope device array of the
+ * library, SSD_STATIC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends.  The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.  Sizes whose workspace exceeds the static
+ * buffer are refused with SSD_ERR_WORKSPACE before any launch (the call
+ * without a workspace, ssd_chunk_scan_fwd(..., NULL, 0, stream), needs
+ * none).  Every call on one GPU shares that GPU's buffer and leaves its
+ * contents behind (nothing in it needs to start at zero): calls that may
+ * overlap in time on one GPU -- on different streams, or from different
+ * threads -- race and must be ordered by the caller.
+ */
+int ssd_chunk_scan_fwd_static(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                              const void *x, int64_t x_row_stride,
+                              const void *Bm, int64_t B_row_stride,
+                              const void *Cm, int64_t C_row_stride,
+                              const float *dt, int64_t dt_row_stride,
+                              int dt_softplus, const float *dt_bias,
+                              const float *A, const float *D,
+                              const void *z, int64_t z_row_stride,
+                              const int32_t *doc_ids, const int32_t *lengths,
+                              const float *init_state, float *final_state,
+                              float *y, int64_t y_row_stride, void *stream);
+
 /*
  * ssd_mixer_fwd -- the conv prologue and the scan in one pass.
  *

@@ -4,6 +4,8 @@ The entry points mirror the C ABI in include/ssd.h one to one:
 
     ssd_conv_fwd        causal depthwise conv (k=4) + SiLU, dt = softplus(dt + dt_bias)
     ssd_chunk_scan_fwd  chunked (64) SSD scan with groups, documents, states, D skip, z gate
+    ssd_chunk_scan_fwd_static  the same scan with its split workspace in the library's static
+                        scratch: for callers that cannot allocate device memory
     ssd_mixer_fwd       both in one call (staged, or the scan convolving the raw columns on chip)
     ssd_resume_fwd      decode tokens rescanned with the working chunk: bit-identical to the forward
     ssd_step            one decode token per sequence
@@ -24,7 +26,7 @@ import os
 
 import torch
 
-__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_resume_fwd", "ssd_step",
+__all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_static", "SSD_STATIC_SCRATCH_BYTES", "ssd_mixer_fwd", "ssd_resume_fwd", "ssd_step",
            "ssd_s6_scan_fwd", "ssd_chunk_scan_workspace_size", "ssd_mixer_workspace_size", "ssd_s6_workspace_size",
            "ssd_chunk_scan_bwd", "ssd_conv_bwd", "ssd_mixer_bwd", "ssd_chunk_scan_bwd_workspace_size",
            "ssd_conv_bwd_workspace_size", "ssd_mixer_bwd_workspace_size",
@@ -33,6 +35,7 @@ __all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_mixer_fwd", "ssd_r
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
+SSD_STATIC_SCRATCH_BYTES = 32 << 20     # include/ssd.h
 SSD_ACT_SILU, SSD_ACT_NONE = 0, 1
 
 _lib = None
@@ -68,6 +71,9 @@ def load() -> ctypes.CDLL:
     # ... z, z_row_stride, doc_ids, lengths, init_state, final_state, y, y_row_stride, workspace, bytes, stream
     lib.ssd_chunk_scan_fwd.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P,
                                        I64, P, P, P, P, P, I64, P, SZ, P]
+    lib.ssd_chunk_scan_fwd_static.restype = I
+    lib.ssd_chunk_scan_fwd_static.argtypes = [I, I, I, I, I, I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, P, P, P,
+                                              I64, P, P, P, P, P, I64, P]
     lib.ssd_chunk_scan_workspace_size.restype = SZ
     lib.ssd_chunk_scan_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.ssd_mixer_fwd.restype = I
@@ -228,6 +234,41 @@ def ssd_chunk_scan_fwd(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=
         _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32), _ptr(lengths, "lengths", torch.int32),
         _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
         _ptr(y, "y", torch.float32), rs_y, _ptr(workspace, "workspace"), ws, _stream(stream))
+    _check(st)
+    return y
+
+
+def ssd_chunk_scan_fwd_static(x, Bm, Cm, dt, A, *, H, P, N, G, D=None, z=None, doc_ids=None, lengths=None,
+                              init_state=None, final_state=None, y=None, dt_softplus=False, dt_bias=None, chunk=64,
+                              stream=None):
+    """ssd_chunk_scan_fwd with the split workspace taken from the library's static scratch (allocates no
+    device memory itself when y is given).  Same arguments and results as ssd_chunk_scan_fwd with a workspace."""
+    lib = load()
+    B, L = x.shape[0], x.shape[1]
+    dtype = _dtype_code(x, "x")
+    rs_x = _rows(x, "x", B, L, H * P)
+    rs_b = _rows(Bm, "Bm", B, L, G * N)
+    rs_c = _rows(Cm, "Cm", B, L, G * N)
+    rs_dt = _rows(dt, "dt", B, L, H)
+    rs_z = _rows(z, "z", B, L, H * P)
+    if y is None:
+        y = torch.empty((B, L, H * P), dtype=torch.float32, device=x.device)
+    rs_y = _rows(y, "y", B, L, H * P)
+    _contig(A, "A", (H,))
+    _contig(D, "D", (H,))
+    _contig(dt_bias, "dt_bias", (H,))
+    _contig(doc_ids, "doc_ids", (B, L))
+    _contig(lengths, "lengths", (B,))
+    _contig(init_state, "init_state", (B, H, P, N))
+    _contig(final_state, "final_state", (B, H, P, N))
+    st = lib.ssd_chunk_scan_fwd_static(
+        B, L, H, P, N, G, chunk, dtype,
+        _ptr(x, "x"), rs_x, _ptr(Bm, "Bm", x.dtype), rs_b, _ptr(Cm, "Cm", x.dtype), rs_c,
+        _ptr(dt, "dt", torch.float32), rs_dt, int(bool(dt_softplus)), _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(D, "D", torch.float32),
+        _ptr(z, "z", x.dtype), rs_z, _ptr(doc_ids, "doc_ids", torch.int32), _ptr(lengths, "lengths", torch.int32),
+        _ptr(init_state, "init_state", torch.float32), _ptr(final_state, "final_state", torch.float32),
+        _ptr(y, "y", torch.float32), rs_y, _stream(stream))
     _check(st)
     return y
 

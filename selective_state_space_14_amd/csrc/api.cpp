@@ -170,19 +170,15 @@ size_t ssd_chunk_scan_workspace_size(int B, int L, int H, int P, int N, int G, i
     return ssd::scan_workspace_bytes(B, L, H, P, N, G, dtype);
 }
 
-int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
-                       const void* x, int64_t x_row_stride,
-                       const void* Bm, int64_t B_row_stride,
-                       const void* Cm, int64_t C_row_stride,
-                       const float* dt, int64_t dt_row_stride,
-                       int dt_softplus, const float* dt_bias,
-                       const float* A, const float* D,
-                       const void* z, int64_t z_row_stride,
-                       const int32_t* doc_ids, const int32_t* lengths,
-                       const float* init_state, float* final_state,
-                       float* y, int64_t y_row_stride,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "ssd_chunk_scan_fwd";
+// The scan behind ssd_chunk_scan_fwd and ssd_chunk_scan_fwd_static.
+// static_ws: take the split workspace from the library's static scratch.
+static int chunk_scan_fwd(const char* fn, bool static_ws, int B, int L, int H, int P, int N, int G, int chunk,
+                          int dtype, const void* x, int64_t x_row_stride, const void* Bm, int64_t B_row_stride,
+                          const void* Cm, int64_t C_row_stride, const float* dt, int64_t dt_row_stride,
+                          int dt_softplus, const float* dt_bias, const float* A, const float* D, const void* z,
+                          int64_t z_row_stride, const int32_t* doc_ids, const int32_t* lengths,
+                          const float* init_state, float* final_state, float* y, int64_t y_row_stride,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     if (lengths && (init_state || final_state))
         return fail(SSD_ERR_BAD_SHAPE, "%s: lengths cannot be combined with init_state / final_state", fn);
     TRY(check_ptr(fn, "lengths", lengths, false, false));
@@ -212,6 +208,14 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     // A workspace enables the sequence split (when these sizes call for one);
     // without one the scan is a single sequential pass over every (b, h).
     const size_t need = ssd_chunk_scan_workspace_size(B, L, H, P, N, G, dtype);
+    if (static_ws && need > 0) {
+        if (need > SSD_STATIC_SCRATCH_BYTES)
+            return fail(SSD_ERR_WORKSPACE,
+                        "%s: these sizes need %zu bytes of workspace, more than the %zu-byte static scratch "
+                        "(use ssd_chunk_scan_fwd with a caller workspace, or none)",
+                        fn, need, (size_t)SSD_STATIC_SCRATCH_BYTES);
+        TRY(hip_status(fn, ssd::scan_static_scratch(&workspace, &workspace_bytes)));
+    }
     const bool split = workspace != nullptr && need > 0;
     if (split && workspace_bytes < need)
         return fail(SSD_ERR_WORKSPACE, "%s: workspace_bytes=%zu is smaller than the required %zu", fn,
@@ -254,6 +258,41 @@ int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int 
     TRY(hip_status(fn, ssd::launch_scan(a, s)));
     if (lengths) return hip_status(fn, ssd::launch_zero_rows(y, y_row_stride, B, L, H * P, lengths, s));
     return ok();
+}
+
+int ssd_chunk_scan_fwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                       const void* x, int64_t x_row_stride,
+                       const void* Bm, int64_t B_row_stride,
+                       const void* Cm, int64_t C_row_stride,
+                       const float* dt, int64_t dt_row_stride,
+                       int dt_softplus, const float* dt_bias,
+                       const float* A, const float* D,
+                       const void* z, int64_t z_row_stride,
+                       const int32_t* doc_ids, const int32_t* lengths,
+                       const float* init_state, float* final_state,
+                       float* y, int64_t y_row_stride,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_scan_fwd("ssd_chunk_scan_fwd", false, B, L, H, P, N, G, chunk, dtype, x, x_row_stride, Bm,
+                          B_row_stride, Cm, C_row_stride, dt, dt_row_stride, dt_softplus, dt_bias, A, D, z,
+                          z_row_stride, doc_ids, lengths, init_state, final_state, y, y_row_stride, workspace,
+                          workspace_bytes, stream);
+}
+
+int ssd_chunk_scan_fwd_static(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
+                              const void* x, int64_t x_row_stride,
+                              const void* Bm, int64_t B_row_stride,
+                              const void* Cm, int64_t C_row_stride,
+                              const float* dt, int64_t dt_row_stride,
+                              int dt_softplus, const float* dt_bias,
+                              const float* A, const float* D,
+                              const void* z, int64_t z_row_stride,
+                              const int32_t* doc_ids, const int32_t* lengths,
+                              const float* init_state, float* final_state,
+                              float* y, int64_t y_row_stride, void* stream) {
+    return chunk_scan_fwd("ssd_chunk_scan_fwd_static", true, B, L, H, P, N, G, chunk, dtype, x, x_row_stride, Bm,
+                          B_row_stride, Cm, C_row_stride, dt, dt_row_stride, dt_softplus, dt_bias, A, D, z,
+                          z_row_stride, doc_ids, lengths, init_state, final_state, y, y_row_stride, nullptr, 0,
+                          stream);
 }
 
 size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dtype) {

@@ -40,8 +40,10 @@
 // the next contraction's operand layout (see ssd_device.hpp), so G^T feeds
 // the Y contraction and H feeds the C.H contraction without any shuffle.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
+#include "../../include/ssd.h"
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -1974,6 +1976,34 @@ void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S) {
     const int per = (nch + k - 1) / k;           // chunks per superchunk
     K = (nch + per - 1) / per;
     S = per * Q;
+}
+
+// Static scratch of the no-allocation scan entry point: the split workspace
+// (local end states, decays, the copy of init_state) of one call at a time
+// per GPU.  In host code the array's name is only a stand-in for the symbol;
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = SSD_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t scan_static_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kStaticScratchBytes;
+    return hipSuccess;
 }
 
 size_t scan_workspace_bytes(int B, int L, int H, int P, int N, int G, int dtype) {

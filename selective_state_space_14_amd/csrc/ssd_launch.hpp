@@ -133,6 +133,10 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // Sequence split chosen for these sizes (1 = none) and its superchunk length.
 void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S);
 size_t scan_workspace_bytes(int B, int L, int H, int P, int N, int G, int dtype);
+// The scan's file-scope static scratch on the current device: its address,
+// looked up once per device (hipGetSymbolAddress) and cached; *bytes = its
+// size.  Allocates nothing.
+hipError_t scan_static_scratch(void** ptr, size_t* bytes);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 // Copies n 16-byte words src -> dst (src == nullptr: zero fill); used for the
 // L = 0 state pass-through without a memset node.

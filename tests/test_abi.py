@@ -192,6 +192,30 @@ def test_step_refusals(lib, over, status, needle):
     assert needle in lib.ssd_last_error().decode()
 
 
+def test_static_scan_refuses_workspace_beyond_static_scratch(lib):
+    """ssd_chunk_scan_fwd_static: sizes whose split workspace exceeds SSD_STATIC_SCRATCH_BYTES are refused on
+    the host, before any HIP call (the pointers here are never dereferenced)."""
+    import selective_state_space_14_amd as ssd
+    src = open(HEADER).read()
+    assert "#define SSD_STATIC_SCRATCH_BYTES ((size_t)32 << 20)" in src
+    assert ssd.SSD_STATIC_SCRATCH_BYTES == 32 << 20
+    a = scan_args(B=5, L=8192, H=64, N=128, G=8, xs=4096, bs=1024, cs=1024, dts=64, ys=4096)
+    need = lib.ssd_chunk_scan_workspace_size(5, 8192, 64, 64, 128, 8, 1)
+    assert need > ssd.SSD_STATIC_SCRATCH_BYTES
+    st = lib.ssd_chunk_scan_fwd_static(a["B"], a["L"], a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"],
+                                       a["x"], a["xs"], a["Bm"], a["bs"], a["Cm"], a["cs"], a["dt"], a["dts"],
+                                       a["dt_softplus"], a["dt_bias"], a["A"], a["D"], a["z"], a["zs"], a["doc"],
+                                       a["len"], a["h0"], a["hf"], a["y"], a["ys"], a["stream"])
+    assert st == 5, (st, lib.ssd_last_error())
+    assert b"static scratch" in lib.ssd_last_error()
+    # the same validation as ssd_chunk_scan_fwd runs first
+    st = lib.ssd_chunk_scan_fwd_static(a["B"], a["L"], 30, a["P"], a["N"], a["G"], a["chunk"], a["dtype"],
+                                       a["x"], a["xs"], a["Bm"], a["bs"], a["Cm"], a["cs"], a["dt"], a["dts"],
+                                       a["dt_softplus"], a["dt_bias"], a["A"], a["D"], a["z"], a["zs"], a["doc"],
+                                       a["len"], a["h0"], a["hf"], a["y"], a["ys"], a["stream"])
+    assert st == 2 and b"H=30" in lib.ssd_last_error()
+
+
 def test_error_message_cleared_on_success_path_is_thread_local(lib):
     call_scan(lib, scan_args(P=32))
     assert b"P=32" in lib.ssd_last_error()
