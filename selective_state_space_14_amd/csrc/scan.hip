@@ -148,84 +148,107 @@ __device__ __forceinline__ f32x4 mma_split(f32x4 acc, const Split4& a0, const Sp
     return mma_bf16(acc, a0.hi, a1.hi, b0.hi, b1.hi);
 }
 
-// LDS plan (element offsets).  kFull: region R0 holds B row-major while the
-// M^T tiles are built, then this wave's (w o X)^T for the chunk state; C,
-// B^T, X^T, the M^T tiles, then fp32 per-token scalars.  kStateOnly: B^T,
-// (w o X)^T, scalars.
-template <typename T, int N, int MODE>
+// Transposed reads of 16-bit tiles (ds_read_b64_tr_b16): in each 16-lane
+// group, result lane j element e is element (j mod 4) of source lane 4e + j/4,
+// so a lane (q, m) that addresses row 4q + m/4, column 4(m mod 4) of a tile
+// receives column m, rows 4q..4q+3 -- the operand fragment of the transposed
+// tile.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#define SSD_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ FragBF tr_read(const unsigned char* lds_base, uint32_t byte_off) {
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS v4i16_t*)(lds_base + byte_off));
+    FragBF f;
+    f.a = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    f.b = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+    return f;
+}
+__device__ __forceinline__ FragBF plain_read(const unsigned char* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return {v.x, v.y};
+}
+
+// LDS plan of the fp32 kernel, in fp32 slots; every matrix region is split
+// (Split4: the hi plane, then the lo plane, in the region's byte size).
+// B and C row-major [Q][NS] for the group of the workgroup's HPW heads; per
+// head a block of X row-major [Q][kXS] -- each wave's 16 columns are later
+// overwritten by its w o X -- and (kFull) the head's M^T tiles.  B^T, X^T
+// and (w o X) operands come from the row-major planes through transposed
+// reads.  Then fp32 scalars: per head (kFull)
+// cs, dt, segment start and the Yoff scale [Q] each, then per wave its
+// chunk-state weights [Q].  kStateOnly: B and the (w o X)^T blocks only.
+template <int N, int MODE, int HPW>
 struct Lds {
-    using E = typename Tr<T>::E;
+    static constexpr bool FULL = MODE == kFull;
     static constexpr int NS = N + kPad;                          // row stride of B and C
-    static constexpr size_t r0 = (size_t)Q * NS > (size_t)64 * kXS ? (size_t)Q * NS : (size_t)64 * kXS;
-    static constexpr size_t oB = 0;                              // B [Q][NS]      (kFull)
-    static constexpr size_t oXwt = MODE == kFull ? 0 : (size_t)N * kXS;   // (wX)^T [64 p][kXS]
-    static constexpr size_t oC = r0;                             // C [Q][NS]      (kFull)
-    static constexpr size_t oBt = MODE == kFull ? oC + (size_t)Q * NS : 0;  // B^T [N][kXS]
-    static constexpr size_t oXt = oBt + (size_t)N * kXS;         // X^T [64 p][kXS] (kFull)
-    static constexpr size_t oM = oXt + (size_t)64 * kXS;         // M^T tiles [10][64 lanes][4] (kFull)
-    static constexpr size_t nE = MODE == kFull ? oM + (size_t)kNumMTiles * 256 : oXwt + (size_t)64 * kXS;
-    // per-token scalars (kFull: cs, dt, segment start, Yoff scale), then the
-    // chunk-state weights, one private row per wave
-    static constexpr int nScal = (MODE == kFull ? 4 : 0) + kWaves;
-    static constexpr size_t bytes = ((nE * sizeof(E) + 15) / 16) * 16 + (size_t)nScal * Q * sizeof(float);
+    static constexpr int cB = Q * NS, cX = 64 * kXS, cM = kNumMTiles * 256;
+    static constexpr size_t oB = 0;
+    static constexpr size_t oC = cB;                             // (kFull)
+    static constexpr size_t oH = (FULL ? 2 : 1) * (size_t)cB;   // first head block
+    static constexpr size_t HB = cX + (FULL ? cM : 0);          // slots per head block
+    static constexpr size_t nE = oH + HPW * HB;
+    static constexpr int NW = 4 * HPW;
+    static constexpr int nScal = (FULL ? 4 * HPW : 0) + NW;
+    static constexpr size_t bytes = ((nE * 4 + 15) / 16) * 16 + (size_t)nScal * Q * sizeof(float);
 };
 
-template <typename T, int N>
+template <int N, int HPW>
 struct ChunkRegs {
-    using R = Tr<T>;
-    static constexpr int CPR = N * (int)sizeof(typename R::E) / 16;   // 16-byte chunks per B/C row
-    static constexpr int NITEMS = 32 * CPR;                            // (row pair, chunk) items
-    static constexpr int NIT = (NITEMS + kThreads - 1) / kThreads;
+    static constexpr int CPR = N * 4 / 16;                       // 16-byte pieces per B/C row
+    static constexpr int NITEMS = 32 * CPR;                      // (row pair, piece) items
+    static constexpr int NIT = (NITEMS + 256 * HPW - 1) / (256 * HPW);
     uint4 b[NIT][2], c[NIT][2];
-    typename R::Raw4 x[4], z[4];
+    float4 x[4], z[4];
     float dt;
     int d0, d1;       // document id of the token and of the one before it
 };
 
-template <typename T, int N, int MODE>
-__global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
-    using R = Tr<T>;
-    using E = typename R::E;
-    using Raw4 = typename R::Raw4;
-    using LD = Lds<T, N, MODE>;
-    using CR = ChunkRegs<T, N>;
+// fp32 scan: HPW heads of one B/C group per workgroup (4 waves per head,
+// wave w -> head w / 4, channels 16 (w mod 4) .. +16), one superchunk of one
+// batch row; the next chunk's inputs are prefetched into registers while the
+// current one is computed.  B and C are staged (split into bf16 halves) once
+// for the HPW heads and each G^T tile is built once and turned into every
+// head's M^T tile.  MODE kFull: the scan itself.  MODE kStateOnly: the
+// pre-pass of the sequence split -- for superchunk k < K-1 it runs the
+// chunk-state recurrence from a zero state and stores the local end state and
+// the superchunk's total decay (negative if a document starts inside it, i.e.
+// the carried state is dropped there) into the workspace.
+template <typename T, int N, int MODE, int HPW>
+__global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
+    using LD = Lds<N, MODE, HPW>;
+    using CR = ChunkRegs<N, HPW>;
     constexpr int NT = N / 16;            // n tiles
     constexpr int NS = LD::NS;
+    constexpr int NW = LD::NW;
+    constexpr int NTH = 256 * HPW;
     constexpr bool FULL = MODE == kFull;
-    constexpr bool BF16 = !std::is_same<T, float>::value;
+    static_assert(std::is_same<T, float>::value, "the generic kernel takes fp32 inputs");
+    static_assert(LD::bytes <= 163840, "LDS plan exceeds a CU");
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    static_assert(!BF16, "the generic kernel takes fp32 inputs");
     // split regions (see Split4): base of the hi plane and the region's slot count
-    auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(smem_raw + off * sizeof(E)); };
-    uint16_t* sB = plane(LD::oB);                 // B [Q][NS], later (w o X)^T [64][kXS]
-    uint16_t* sXwt = plane(LD::oXwt);
+    auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(smem_raw + off * 4); };
+    constexpr int cB = LD::cB, cX = LD::cX, cM = LD::cM;
+    uint16_t* sB = plane(LD::oB);
     uint16_t* sC = plane(LD::oC);
-    uint16_t* sBt = plane(LD::oBt);
-    uint16_t* sXt = plane(LD::oXt);
-    uint16_t* sM = plane(LD::oM);
-    constexpr int cR0 = (int)LD::r0, cC = Q * NS, cBt = N * kXS, cXt = 64 * kXS, cM = kNumMTiles * 256;
-    constexpr int cXw = FULL ? cR0 : cXt;
-    float* sScal = reinterpret_cast<float*>(smem_raw + ((LD::nE * sizeof(E) + 15) / 16) * 16);
-    float* sCs = sScal;
-    float* sDt = sScal + Q;
-    int* sSeg = reinterpret_cast<int*>(sScal + 2 * Q);
-    float* sEo = sScal + 3 * Q;
-    float* sW = sScal + (FULL ? 4 : 0) * Q;   // [kWaves][Q]
 
     const int L = a.L, H = a.H, G = a.G;
-    const int KU = FULL ? a.K : a.K - 1;  // superchunks handled by this launch per (b, h)
-    const int id = xcd_remap(blockIdx.x, a.B * H * KU);
-    const int h = id % H;
-    const int k = (id / H) % KU;
-    const int b = id / (H * KU);
-    const int g = h / (H / G);
+    const int HQ = H / HPW;
+    const int KU = FULL ? a.K : a.K - 1;  // superchunks handled by this launch per (b, head group)
+    const int id = xcd_remap(blockIdx.x, a.B * HQ * KU);
+    const int hq = id % HQ;
+    const int k = (id / HQ) % KU;
+    const int b = id / (HQ * KU);
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
+    const int hh = wave >> 2;             // head of this wave within the workgroup
+    const int h = hq * HPW + hh;
+    const int g = (hq * HPW) / (H / G);
     const int q4 = lane >> 4;             // lane group (K sub-block / row group)
     const int j16 = lane & 15;            // row/column index inside a tile
-    const int p0 = wave * 16;             // this wave's head channels
+    const int p0 = (wave & 3) * 16;       // this wave's head channels
     const float A2 = a.A[h] * kLog2e;
     const float Dh = a.D ? a.D[h] : 0.0f;
     const float dtb = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h] : 0.0f;
@@ -234,13 +257,23 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
     const int tl = tend - 1;              // last token of this unit (loads clamp to it)
     const bool gate = a.z != nullptr;
 
+    uint16_t* sX = plane(LD::oH + hh * LD::HB);            // this head's X / (w o X) rows
+    uint16_t* sM = plane(LD::oH + hh * LD::HB + cX);       // this head's M^T tiles (kFull)
+    float* sScal = reinterpret_cast<float*>(smem_raw + ((LD::nE * 4 + 15) / 16) * 16);
+    float* sHd = sScal + (FULL ? 4 * Q * hh : 0);          // this head's scalars (kFull)
+    float* sCs = sHd;
+    float* sDt = sHd + Q;
+    int* sSeg = reinterpret_cast<int*>(sHd + 2 * Q);
+    float* sEo = sHd + 3 * Q;
+    float* sWw = sScal + (FULL ? 4 * HPW : 0) * Q + wave * Q;   // this wave's chunk-state weights
+
     // Row bases (uniform) and per-lane element offsets; a chunk's loads are
     // base + t0 * stride (scalar) + lane offset, rows clamped only in the tail.
-    const E* xbase = static_cast<const E*>(a.x) + (size_t)b * a.Lb * a.x_stride;
-    const E* zbase = gate ? static_cast<const E*>(a.z) + (size_t)b * a.Lb * a.z_stride : xbase;
+    const float* xbase = static_cast<const float*>(a.x) + (size_t)b * a.Lb * a.x_stride;
+    const float* zbase = gate ? static_cast<const float*>(a.z) + (size_t)b * a.Lb * a.z_stride : xbase;
     const int64_t zs = gate ? a.z_stride : a.x_stride;
-    const E* Bbase = static_cast<const E*>(a.Bm) + (size_t)b * a.Lb * a.B_stride;
-    const E* Cbase = static_cast<const E*>(a.Cm) + (size_t)b * a.Lb * a.C_stride;
+    const float* Bbase = static_cast<const float*>(a.Bm) + (size_t)b * a.Lb * a.B_stride;
+    const float* Cbase = static_cast<const float*>(a.Cm) + (size_t)b * a.Lb * a.C_stride;
     const float* dtbase = a.dt + (size_t)b * a.Lb * a.dt_stride;
     const int32_t* docg = a.doc ? a.doc + (size_t)b * a.Lb : nullptr;
     // absent doc ids: load (unused) in-bounds words of dt instead, keeping loads unconditional
@@ -248,47 +281,28 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
     const int xcol = h * 64 + p0 + 4 * q4;
     float* yg = a.y + (size_t)b * a.Lb * a.y_stride + xcol;
 
-    // Loads: a uniform chunk base (t0 * stride, scalar) plus a 32-bit per-lane
-    // byte offset fixed for the whole unit; only a chunk that runs past the
-    // unit's end recomputes offsets with rows clamped to its last token.
-    constexpr int ES = (int)sizeof(E);
-    int bo[CR::NIT];                       // B/C: (row pair, 16-byte column) item of this thread
-#pragma unroll
-    for (int it = 0; it < CR::NIT; ++it) {
-        const int item = min(tid + it * kThreads, CR::NITEMS - 1);
-        const int rp = item / CR::CPR, col = item % CR::CPR;
-        bo[it] = rp;
-        (void)col;
-    }
-    auto bc_col = [&](int it) { return (min(tid + it * kThreads, CR::NITEMS - 1) % CR::CPR) * R::VE; };
-    auto load_chunk = [&](int t0, CR& r) {
+    auto bc_item = [&](int it) { return min(tid + it * NTH, CR::NITEMS - 1); };
+    // B, C, dt and the doc ids of the chunk at t0 (x and z: load_xz)
+    auto load_bc = [&](int t0, CR& r) {
         const int lim = tl - t0;                     // last valid row inside the chunk
         const bool clamp = lim < Q - 1;              // uniform
         const char* Bb = reinterpret_cast<const char*>(Bbase + (size_t)t0 * a.B_stride + g * N);
         const char* Cb = reinterpret_cast<const char*>(Cbase + (size_t)t0 * a.C_stride + g * N);
 #pragma unroll
         for (int it = 0; it < CR::NIT; ++it) {
-            const int col = bc_col(it);
+            const int item = bc_item(it);
+            const int rp = item / CR::CPR, col = (item % CR::CPR) * 4;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                int row = 2 * bo[it] + kk;
+                int row = 2 * rp + kk;
                 if (clamp) row = min(row, lim);
-                const uint32_t ob = (uint32_t)(row * (int)a.B_stride + col) * ES;
+                const uint32_t ob = (uint32_t)(row * (int)a.B_stride + col) * 4;
                 r.b[it][kk] = *reinterpret_cast<const uint4*>(Bb + ob);
                 if (FULL) {
-                    const uint32_t oc = (uint32_t)(row * (int)a.C_stride + col) * ES;
+                    const uint32_t oc = (uint32_t)(row * (int)a.C_stride + col) * 4;
                     r.c[it][kk] = *reinterpret_cast<const uint4*>(Cb + oc);
                 }
             }
-        }
-        const char* xb = reinterpret_cast<const char*>(xbase + (size_t)t0 * a.x_stride + xcol);
-        const char* zb = reinterpret_cast<const char*>(zbase + (size_t)t0 * zs + xcol);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            int row = 16 * ti + j16;
-            if (clamp) row = min(row, lim);
-            r.x[ti] = *reinterpret_cast<const Raw4*>(xb + (uint32_t)(row * (int)a.x_stride) * ES);
-            if (FULL) r.z[ti] = *reinterpret_cast<const Raw4*>(zb + (uint32_t)(row * (int)zs) * ES);
         }
         int row = lane;
         if (clamp) row = min(row, lim);
@@ -296,6 +310,20 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
         r.dt = *reinterpret_cast<const float*>(db + (uint32_t)(row * (int)a.dt_stride) * 4);
         r.d0 = docsrc[t0 + row];
         r.d1 = docsrc[max(t0 + row - 1, 0)];
+    };
+    // this wave's x (and z) rows of the chunk at t0
+    auto load_xz = [&](int t0, CR& r) {
+        const int lim = tl - t0;
+        const bool clamp = lim < Q - 1;
+        const char* xb = reinterpret_cast<const char*>(xbase + (size_t)t0 * a.x_stride + xcol);
+        const char* zb = reinterpret_cast<const char*>(zbase + (size_t)t0 * zs + xcol);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            int row = 16 * ti + j16;
+            if (clamp) row = min(row, lim);
+            r.x[ti] = *reinterpret_cast<const float4*>(xb + (uint32_t)(row * (int)a.x_stride) * 4);
+            if (FULL) r.z[ti] = *reinterpret_cast<const float4*>(zb + (uint32_t)(row * (int)zs) * 4);
+        }
     };
 
     // ---- state at the unit's first token: lane (q4, j16) of n-tile nt holds
@@ -332,15 +360,32 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
     float log2dec = 0.0f;                 // kStateOnly: sum of the chunks' cs_end
     bool reset = false;                   // kStateOnly: a document starts in the unit
 
+    // byte offsets of this lane's transposed reads in the hi planes (the lo
+    // plane is the region's slot count * 2 bytes on): B^T of n tile nt, token
+    // block sb at btr + (16 sb NS + 16 nt) * 2; the wave's X^T / (w o X)
+    // fragments of token block sb at xtr + 16 sb kXS * 2
+    const uint32_t btr = (uint32_t)(((4 * q4 + j16 / 4) * NS + 4 * (j16 % 4)) * 2);
+    const uint32_t xtr = (uint32_t)(((4 * q4 + j16 / 4) * kXS + p0 + 4 * (j16 % 4)) * 2);
+    const unsigned char* sBb = reinterpret_cast<const unsigned char*>(sB);
+    const unsigned char* sXb = reinterpret_cast<const unsigned char*>(sX);
+    auto xfrag = [&](int sb) {
+        const uint32_t o = xtr + (uint32_t)(16 * sb * kXS * 2);
+        return Split4{tr_read(sXb, o), tr_read(sXb, o + cX * 2)};
+    };
+
     const int nchunks = (tend - tbeg + Q - 1) / Q;
     CR regs;
-    if (nchunks > 0) load_chunk(tbeg, regs);
+    if (nchunks > 0) {
+        load_bc(tbeg, regs);
+        load_xz(tbeg, regs);
+    }
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
         const bool tail = t0 + Q > tend;              // chunk-uniform
         const bool tok_ok = t0 + lane < tend;
-        // ---- segmented cumulative sum of dt*A (log2 domain), lane = token
+        // ---- segmented cumulative sum of dt*A (log2 domain), lane = token; every
+        // wave of a head computes it (no wave waits for another)
         float dtl = a.dt_softplus ? softplus_f(regs.dt + dtb) : regs.dt;
         if (tail && !tok_ok) dtl = 0.0f;
         const int bnd = (docg && tok_ok && t0 + lane > 0 && regs.d0 != regs.d1) ? 1 : 0;
@@ -352,27 +397,26 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
         const bool has_bnd = last_seg >= 0;
         const int wseg = has_bnd ? last_seg : 0;   // first token of the chunk's last segment
 
-        // registers of this chunk, kept across the prefetch of the next one
-        Raw4 xv[4], zv[4];
+        // this chunk's x and z stay in registers until the last use; the next
+        // chunk's are loaded after it (load_xz), its B, C, dt earlier (load_bc)
+        float4* xv = regs.x;
+        const float4* zv = regs.z;
+        if (tail) {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            xv[ti] = regs.x[ti];
-            zv[ti] = regs.z[ti];
-            if (tail && t0 + 16 * ti + j16 >= tend) xv[ti] = R::zero4();
+            for (int ti = 0; ti < 4; ++ti)
+                if (t0 + 16 * ti + j16 >= tend) xv[ti] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        __syncthreads();   // the previous chunk's LDS readers are done
+
         // chunk-state weight of token `lane`: decay to the chunk end, last segment only
-        float* sWw = sW + wave * Q;
         sWw[lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
-
-        __syncthreads();   // previous chunk's LDS readers are done
-
-        // ---- stage B (row-major + transposed) and C; rows past the end are zero
+        // ---- stage B (and C) row-major; rows past the end are zero
 #pragma unroll
         for (int it = 0; it < CR::NIT; ++it) {
-            const int item = tid + it * kThreads;
+            const int item = tid + it * NTH;
             if (item < CR::NITEMS) {
                 const int rp = item / CR::CPR, col = item % CR::CPR;
-                const int s = 2 * rp, n0 = col * R::VE;
+                const int s = 2 * rp, n0 = col * 4;
                 uint4 b0 = regs.b[it][0], b1 = regs.b[it][1];
                 uint4 c0 = regs.c[it][0], c1 = regs.c[it][1];
                 if (tail) {
@@ -382,33 +426,25 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 }
                 const float* fb0 = reinterpret_cast<const float*>(&b0);
                 const float* fb1 = reinterpret_cast<const float*>(&b1);
+                pst4(sB, cB, s * NS + n0, fb0[0], fb0[1], fb0[2], fb0[3]);
+                pst4(sB, cB, (s + 1) * NS + n0, fb1[0], fb1[1], fb1[2], fb1[3]);
                 if (FULL) {
                     const float* fc0 = reinterpret_cast<const float*>(&c0);
                     const float* fc1 = reinterpret_cast<const float*>(&c1);
-                    pst4(sB, cR0, s * NS + n0, fb0[0], fb0[1], fb0[2], fb0[3]);
-                    pst4(sB, cR0, (s + 1) * NS + n0, fb1[0], fb1[1], fb1[2], fb1[3]);
-                    pst4(sC, cC, s * NS + n0, fc0[0], fc0[1], fc0[2], fc0[3]);
-                    pst4(sC, cC, (s + 1) * NS + n0, fc1[0], fc1[1], fc1[2], fc1[3]);
+                    pst4(sC, cB, s * NS + n0, fc0[0], fc0[1], fc0[2], fc0[3]);
+                    pst4(sC, cB, (s + 1) * NS + n0, fc1[0], fc1[1], fc1[2], fc1[3]);
                 }
-#pragma unroll
-                for (int e = 0; e < R::VE; ++e) pst2(sBt, cBt, (n0 + e) * kXS + s, fb0[e], fb1[e]);
             }
         }
-        // ---- (w o X)^T (kStateOnly) or X^T (kFull) of this wave's channels
+        // ---- this wave's columns of X (kFull) or of w o X (kStateOnly), row-major
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             const int t = 16 * ti + j16;
-            if (FULL) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pst1(sXt, cXt, (p0 + 4 * q4 + r) * kXS + t, R::el(xv[ti], r));
-            } else {
-                const float w = sWw[t];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pst1(sXwt, cXt, (p0 + 4 * q4 + r) * kXS + t, w * R::el(xv[ti], r));
-            }
+            const float w = FULL ? 1.0f : sWw[t];
+            pst4(sX, cX, t * kXS + p0 + 4 * q4, w * xv[ti].x, w * xv[ti].y, w * xv[ti].z, w * xv[ti].w);
         }
-        // ---- per-token scalars of the chunk
-        if (FULL && wave == 0) {
+        // ---- per-token scalars of the chunk, once per head
+        if (FULL && (wave & 3) == 0) {
             sCs[lane] = cs;
             sDt[lane] = dtl;
             sSeg[lane] = seg < 0 ? 0 : seg;
@@ -416,44 +452,52 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
             sEo[lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
         }
         __syncthreads();
-        if (c + 1 < nchunks) load_chunk(t0 + Q, regs);
+        if (c + 1 < nchunks) {
+            load_bc(t0 + Q, regs);
+            if (!FULL) load_xz(t0 + Q, regs);
+        }
 
         if (FULL) {
-            // ---- M^T tiles (this wave's share of the lower triangle)
-            for (int kt = wave; kt < kNumMTiles; kt += kWaves) {
+            // ---- G^T tiles (this wave's share of the lower triangle), each turned
+            // into every head's M^T tile
+            for (int kt = wave; kt < kNumMTiles; kt += NW) {
                 int si, ti;
                 mtile(kt, si, ti);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += 2) {
-                    const Split4 a0 = pld(sB, cR0, (16 * si + j16) * NS + 16 * nb + 4 * q4);
-                    const Split4 b0 = pld(sC, cC, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
-                    const Split4 a1 = nb + 1 < NT ? pld(sB, cR0, (16 * si + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                    const Split4 a0 = pld(sB, cB, (16 * si + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 b0 = pld(sC, cB, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 a1 = nb + 1 < NT ? pld(sB, cB, (16 * si + j16) * NS + 16 * (nb + 1) + 4 * q4)
                                                   : split_zero();
-                    const Split4 b1 = nb + 1 < NT ? pld(sC, cC, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                    const Split4 b1 = nb + 1 < NT ? pld(sC, cB, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
                                                   : split_zero();
                     acc = mma_split(acc, a0, a1, b0, b1);
                 }
                 // acc[r] = G^T[s = 16si + 4q4 + r][t = 16ti + j16]
                 const int t = 16 * ti + j16;
-                const float cst = sCs[t];
-                const int segt = sSeg[t];
-                const float4 css = *reinterpret_cast<const float4*>(sCs + 16 * si + 4 * q4);
-                const float4 dts = *reinterpret_cast<const float4*>(sDt + 16 * si + 4 * q4);
-                f32x4 m;
+                bool ok[4];
+                for (int e = 0; e < HPW; ++e) {
+                    const float* sce = sScal + 4 * Q * e;
+                    const float cst = sce[t];
+                    const int segt = reinterpret_cast<const int*>(sce + 2 * Q)[t];
+                    const float4 css = *reinterpret_cast<const float4*>(sce + 16 * si + 4 * q4);
+                    const float4 dts = *reinterpret_cast<const float4*>(sce + Q + 16 * si + 4 * q4);
+                    f32x4 m;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * si + 4 * q4 + r;
-                    const bool ok = (si < ti || s <= t) && (!has_bnd || s >= segt);
-                    m[r] = ok ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = 16 * si + 4 * q4 + r;
+                        ok[r] = (si < ti || s <= t) && (!has_bnd || s >= segt);
+                        m[r] = ok[r] ? acc[r] * fast_exp2(cst - (&css.x)[r]) * (&dts.x)[r] : 0.0f;
+                    }
+                    pst4(plane(LD::oH + e * LD::HB + cX), cM, kt * 256 + lane * 4, m[0], m[1], m[2], m[3]);
                 }
-                pst4(sM, cM, kt * 256 + lane * 4, m[0], m[1], m[2], m[3]);
             }
             // split copy of the carried state for the C.H contraction
             Split4 hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = split4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-            __syncthreads();   // all M^T tiles are in LDS; B row-major is no longer read
+            __syncthreads();   // all M^T tiles are in LDS
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, then the output
 #pragma unroll
@@ -461,18 +505,18 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
-                    const Split4 a0 = pld(sXt, cXt, (p0 + j16) * kXS + 16 * sb + 4 * q4);
+                    const Split4 a0 = xfrag(sb);
                     const Split4 b0 = pld(sM, cM, mtile_index(sb, ti) * 256 + lane * 4);
                     const bool two = sb + 1 <= ti;
-                    const Split4 a1 = two ? pld(sXt, cXt, (p0 + j16) * kXS + 16 * (sb + 1) + 4 * q4) : split_zero();
+                    const Split4 a1 = two ? xfrag(sb + 1) : split_zero();
                     const Split4 b1 = two ? pld(sM, cM, mtile_index(sb + 1, ti) * 256 + lane * 4) : split_zero();
                     yd = mma_split(yd, a0, a1, b0, b1);
                 }
                 f32x4 yo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += 2) {
-                    const Split4 c0 = pld(sC, cC, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
-                    const Split4 c1 = nb + 1 < NT ? pld(sC, cC, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
+                    const Split4 c0 = pld(sC, cB, (16 * ti + j16) * NS + 16 * nb + 4 * q4);
+                    const Split4 c1 = nb + 1 < NT ? pld(sC, cB, (16 * ti + j16) * NS + 16 * (nb + 1) + 4 * q4)
                                                   : split_zero();
                     const Split4 h1 = nb + 1 < NT ? hf[nb + 1] : split_zero();
                     yo = mma_split(yo, hf[nb], h1, c0, c1);
@@ -480,42 +524,49 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
                 // lane holds y[t = 16ti + j16][p = p0 + 4q4 + r]
                 const int t = 16 * ti + j16;
                 const float eo = sEo[t];
+                float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (gate) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gz[r] = silu_f((&zv[ti].x)[r]);
+                }
                 float o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float v = fmaf(eo, yo[r], yd[r]);
-                    v = fmaf(Dh, R::el(xv[ti], r), v);
-                    if (gate) v *= silu_f(R::el(zv[ti], r));
-                    o[r] = v;
+                    v = fmaf(Dh, (&xv[ti].x)[r], v);
+                    o[r] = v * gz[r];
                 }
                 if (!tail || t0 + t < tend)
                     *reinterpret_cast<float4*>(yg + (size_t)(t0 + t) * a.y_stride) = make_float4(o[0], o[1], o[2], o[3]);
             }
-            // ---- (w o X)^T of this wave's channels, into the B row-major area
+            // ---- w o X over this wave's own X columns (only this wave reads them,
+            // and its LDS operations are performed in order)
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 const int t = 16 * ti + j16;
                 const float w = sWw[t];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pst1(sB, cR0, (p0 + 4 * q4 + r) * kXS + t, w * R::el(xv[ti], r));
+                pst4(sX, cX, t * kXS + p0 + 4 * q4, w * xv[ti].x, w * xv[ti].y, w * xv[ti].z, w * xv[ti].w);
             }
+            if (c + 1 < nchunks) load_xz(t0 + Q, regs);
         }
 
         // ---- chunk state S = B^T (w o X): lane holds S[n = 16nt + 4q4 + r][p0 + j16],
-        // then the state passing, strictly in chunk order
-        const uint16_t* xw = FULL ? sB : sXwt;
+        // then the state passing, strictly in chunk order.  B^T comes from the
+        // row-major B planes through transposed reads.
         const float dec = fast_exp2(cs_end);
         // this wave's (w o X)^T fragments are the same for every n tile
         Split4 xwf[4];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) xwf[sb] = pld(xw, cXw, (p0 + j16) * kXS + 16 * sb + 4 * q4);
+        for (int sb = 0; sb < 4; ++sb) xwf[sb] = xfrag(sb);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sb = 0; sb < 4; sb += 2) {
-                const Split4 a0 = pld(sBt, cBt, (16 * nt + j16) * kXS + 16 * sb + 4 * q4);
-                const Split4 a1 = pld(sBt, cBt, (16 * nt + j16) * kXS + 16 * (sb + 1) + 4 * q4);
+                const uint32_t o0 = btr + (uint32_t)((16 * sb * NS + 16 * nt) * 2);
+                const uint32_t o1 = btr + (uint32_t)((16 * (sb + 1) * NS + 16 * nt) * 2);
+                const Split4 a0 = {tr_read(sBb, o0), tr_read(sBb, o0 + cB * 2)};
+                const Split4 a1 = {tr_read(sBb, o1), tr_read(sBb, o1 + cB * 2)};
                 acc = mma_split(acc, a0, a1, xwf[sb], xwf[sb + 1]);
             }
 #pragma unroll
@@ -540,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             *reinterpret_cast<float4*>(hl + 16 * nt) = make_float4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-        if (tid == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+        if (lane == 0 && (wave & 3) == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
         if (k == 0 && a.h0) {
             // the main pass reads this copy instead of init_state
 #pragma unroll
@@ -583,21 +634,6 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(ScanArgs a) {
 // exactly 4.  Barriers wait only for LDS traffic (lgkmcnt), never for the
 // copies in flight.
 // ============================================================================
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-#define SSD_LDS __attribute__((address_space(3)))
-
-__device__ __forceinline__ FragBF tr_read(const unsigned char* lds_base, uint32_t byte_off) {
-    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS v4i16_t*)(lds_base + byte_off));
-    FragBF f;
-    f.a = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
-    f.b = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
-    return f;
-}
-__device__ __forceinline__ FragBF plain_read(const unsigned char* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    return {v.x, v.y};
-}
 // LDS DMA: lane l's 16 (or 4) bytes at base + voff land at lds + 16 l (4 l).
 // base and lds are wave-uniform.  Written as inline assembly so the compiler
 // does not model the copy: it would otherwise wait for every copy in flight
@@ -1835,18 +1871,27 @@ hipError_t launch_scan_bf16(const ScanArgs& a, int pre_hpw, hipStream_t stream) 
     return launch_scan_bf16_full<N, HPW>(a, a.B * (a.H / HPW) * a.K, stream);
 }
 
-template <typename T, int N, int MODE>
-hipError_t launch_scan_mode(const ScanArgs& a, int units, hipStream_t stream) {
-    const size_t lds = Lds<T, N, MODE>::bytes;
+template <typename T, int N, int MODE, int HPW>
+hipError_t launch_scan_mode(const ScanArgs& a, hipStream_t stream) {
+    const size_t lds = Lds<N, MODE, HPW>::bytes;
     static bool attr_set = false;   // raise the dynamic-LDS cap once per process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_scan_kernel<T, N, MODE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_scan_kernel<T, N, MODE, HPW>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((ssd_scan_kernel<T, N, MODE>), dim3(units), dim3(kThreads), lds, stream, a);
+    const int units = a.B * (a.H / HPW) * (MODE == kFull ? a.K : a.K - 1);
+    hipLaunchKernelGGL((ssd_scan_kernel<T, N, MODE, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
+}
+template <typename T, int N, int HPW>
+hipError_t launch_scan_f32(const ScanArgs& a, hipStream_t stream) {
+    if (a.K > 1) {
+        hipError_t e = launch_scan_mode<T, N, kStateOnly, HPW>(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_scan_mode<T, N, kFull, HPW>(a, stream);
 }
 
 // ---- bf16 plan: heads per workgroup, then the sequence split.
@@ -1908,6 +1953,10 @@ int bf16_pre_hpw(int N, int H, int G) {
     return 1;
 }
 
+// fp32 heads per workgroup: two where the heads of a group pair up (the plan
+// fits a CU at every supported N), else one.
+int f32_hpw(int H, int G) { return (H / G) % 2 == 0 ? 2 : 1; }
+
 template <typename T, int N>
 hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
     if constexpr (!std::is_same<T, float>::value) {
@@ -1920,12 +1969,7 @@ hipError_t launch_scan_n(const ScanArgs& a, hipStream_t stream) {
             default: return launch_scan_bf16<N, 1>(a, pre, stream);
         }
     } else {
-        const int bh = a.B * a.H;
-        if (a.K > 1) {
-            hipError_t e = launch_scan_mode<T, N, kStateOnly>(a, bh * (a.K - 1), stream);
-            if (e != hipSuccess) return e;
-        }
-        return launch_scan_mode<T, N, kFull>(a, bh * a.K, stream);
+        return f32_hpw(a.H, a.G) == 2 ? launch_scan_f32<T, N, 2>(a, stream) : launch_scan_f32<T, N, 1>(a, stream);
     }
 }
 
@@ -1954,8 +1998,8 @@ void scan_split(int B, int L, int H, int N, int G, int dtype, int& K, int& S) {
     if (dtype == 0) {   // fp32
         constexpr long kTargetUnits = 1024;   // 4 workgroups per CU on 256 CUs
         constexpr int kMinChunks = 8;
-        const long bh = (long)B * H;
-        while (bh * k < kTargetUnits && nch / (2 * k) >= kMinChunks) k *= 2;
+        const long wgs = (long)B * (H / f32_hpw(H, G));
+        while (wgs * k < kTargetUnits && nch / (2 * k) >= kMinChunks) k *= 2;
     } else {
         const int hpw = bf16_hpw(N, H, G);
         const long units = (long)B * (H / hpw);
