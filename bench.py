@@ -301,10 +301,12 @@ def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
             "ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "unit": "head-tokens/s (B*H per step)"}
 
 
-# fp32 VALU lane-instructions per second of MI355X (157.3 TFLOP/s counts an fma as two flops) and the cost of
-# one S6 state update in full-rate issue slots: exp2 (a transcendental, quarter rate: 4 slots), dt*A, dt*x*B,
-# the fma into h and the fma into y (4 slots).
-VALU_LANE_OPS = 157.3e12 / 2
+# fp32 VALU lane-operations per second this build can issue on MI355X: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz = 39.3e12, i.e. one wave64 instruction per SIMD every 4 cycles.  The 157.3 TFLOP/s headline counts an
+# fma as two flops AND assumes packed fp32 (two lanes per instruction slot), which the build turns off; the SQ
+# counters of the scan kernels show 4.3 cycles per VALU instruction.  One S6 state update costs 8 issue slots:
+# exp2 (a transcendental, quarter rate: 4 slots), dt*A, dt*x*B, the fma into h and the fma into y (4 slots).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 S6_SLOTS_PER_UPDATE = 8
 
 
@@ -380,26 +382,42 @@ def bwd_bench(ssd, synth, torch, wl, steps, warmup, seed=0):
             "workspace_bytes": ws.numel()}
 
 
-def cpu_baseline(synth, wl, rows):
-    """The fp64 oracle (conv + scan, as it stands) on `rows` batch rows of the workload."""
+def oracle_seconds(synth, wl, rows):
+    """Seconds the fp64 oracle (conv + scan, as it stands) takes on `rows` batch rows of the workload, with the
+    OpenMP threads of this process."""
     import oracle
     prm = synth.params(wl, 0)
     raw = synth.raw_inputs(wl, 0, B=rows)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     oracle.build()
     t0 = time.perf_counter()
     oracle.forward(raw["xbc_raw"], prm["conv_w"], None, raw["dt_raw"], prm["dt_bias"], prm["A"], prm["D"], raw["z"],
                    H=wl.H, P=wl.P, N=wl.N, G=wl.G, round_bf16=True)
-    sec = time.perf_counter() - t0
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(synth, wl, rows, rows_1t=1):
+    """The fp64 oracle on `rows` batch rows with every OpenMP thread of the host (OMP_NUM_THREADS or the CPU
+    count), and on `rows_1t` rows with one thread (a child process started with OMP_NUM_THREADS=1)."""
+    import subprocess
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    sec = oracle_seconds(synth, wl, rows)
     model = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": rows * wl.L * wl.H / sec, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {wl.B} batch rows of the {wl.name} workload (L={wl.L}, all {wl.H} heads), "
-                      f"conv + scan in fp64, {sec:.2f} s on {threads} threads of {model}"}
+    out = {"value": rows * wl.L * wl.H / sec, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows} of {wl.B} batch rows of the {wl.name} workload (L={wl.L}, all {wl.H} heads), "
+                     f"conv + scan in fp64, {sec:.2f} s on {threads} threads of {model}"}
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-seconds", str(rows_1t)], env=env,
+                       capture_output=True, text=True)
+    if r.returncode == 0 and r.stdout.strip():
+        sec1 = float(r.stdout.strip().split()[-1])
+        out["single_thread"] = {"value": rows_1t * wl.L * wl.H / sec1, "unit": "head-tokens/s", "cores": 1,
+                                "sample": f"{rows_1t} of {wl.B} batch rows, {sec1:.2f} s on 1 thread"}
+    return out
 
 
 def main():
@@ -412,7 +430,12 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=5)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
+    ap.add_argument("--oracle-seconds", type=int, default=0, help=argparse.SUPPRESS)   # the single-thread child
     args = ap.parse_args()
+    if args.oracle_seconds:
+        import synth
+        print(oracle_seconds(synth, synth.WORKLOADS["mini_k3_bf16"], args.oracle_seconds))
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this build runs on one GPU only (the scan shards by batch row and "
               "head with no exchange; multi-GPU runs are not part of it)", file=sys.stderr)
