@@ -168,6 +168,11 @@ __device__ __forceinline__ FragBF plain_read(const unsigned char* p) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     return {v.x, v.y};
 }
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
+// then s_barrier.  (A fence-based barrier would also wait for the copies in
+// flight.)  The memory clobber keeps the compiler from moving accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // LDS plan of the fp32 kernel, in fp32 slots; every matrix region is split
 // (Split4: the hi plane, then the lo plane, in the region's byte size).
@@ -209,7 +214,9 @@ struct ChunkRegs {
 // batch row; the next chunk's inputs are prefetched into registers while the
 // current one is computed.  B and C are staged (split into bf16 halves) once
 // for the HPW heads and each G^T tile is built once and turned into every
-// head's M^T tile.  MODE kFull: the scan itself.  MODE kStateOnly: the
+// head's M^T tile.  Barriers wait for LDS traffic only, so the register
+// prefetch stays in flight across them (the compiler waits for each load
+// before its first use).  MODE kFull: the scan itself.  MODE kStateOnly: the
 // pre-pass of the sequence split -- for superchunk k < K-1 it runs the
 // chunk-state recurrence from a zero state and stores the local end state and
 // the superchunk's total decay (negative if a document starts inside it, i.e.
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             for (int ti = 0; ti < 4; ++ti)
                 if (t0 + 16 * ti + j16 >= tend) xv[ti] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        __syncthreads();   // the previous chunk's LDS readers are done
+        lds_barrier();     // the previous chunk's LDS readers are done
 
         // chunk-state weight of token `lane`: decay to the chunk end, last segment only
         sWw[lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             // Yoff applies while no document has started in [chunk start, t]
             sEo[lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
         }
-        __syncthreads();
+        lds_barrier();     // staged tiles and scalars are visible
         if (c + 1 < nchunks) {
             load_bc(t0 + Q, regs);
             if (!FULL) load_xz(t0 + Q, regs);
@@ -497,7 +504,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             Split4 hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = split4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-            __syncthreads();   // all M^T tiles are in LDS
+            lds_barrier();     // all M^T tiles are in LDS
 
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, then the output
 #pragma unroll
@@ -552,8 +559,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
 
         // ---- chunk state S = B^T (w o X): lane holds S[n = 16nt + 4q4 + r][p0 + j16],
         // then the state passing, strictly in chunk order.  B^T comes from the
-        // row-major B planes through transposed reads.
-        const float dec = fast_exp2(cs_end);
+        // row-major B planes through transposed reads.  A chunk holding a
+        // document start drops the carried state: decay 0 (a multiply by
+        // exactly zero of a finite state, so the result is S).
+        const float dec = has_bnd ? 0.0f : fast_exp2(cs_end);
         // this wave's (w o X)^T fragments are the same for every n tile
         Split4 xwf[4];
 #pragma unroll
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
                 acc = mma_split(acc, a0, a1, xwf[sb], xwf[sb + 1]);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Hs[nt][r] = has_bnd ? acc[r] : fmaf(dec, Hs[nt][r], acc[r]);
+            for (int r = 0; r < 4; ++r) Hs[nt][r] = fmaf(dec, Hs[nt][r], acc[r]);
         }
         if (!FULL) {
             log2dec += cs_end;
@@ -673,11 +682,6 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, const unsi
         : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
         : "memory");
 }
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
-// then s_barrier.  (A fence-based barrier would also wait for the copies in
-// flight.)  The memory clobber keeps the compiler from moving accesses across.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // At most n of this wave's vector-memory operations still outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
