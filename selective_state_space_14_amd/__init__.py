@@ -32,7 +32,8 @@ __all__ = ["load", "ssd_conv_fwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_sta
            "ssd_conv_bwd_workspace_size", "ssd_mixer_bwd_workspace_size",
            "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_ACT_SILU", "SSD_ACT_NONE"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+# SSD_LIBRARY names another build of the same library (the host-sanitized one the ABI checks use)
+LIB_PATH = os.environ.get("SSD_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_STATIC_SCRATCH_BYTES = 32 << 20     # include/ssd.h

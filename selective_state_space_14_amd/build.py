@@ -1,6 +1,12 @@
 """Build libssd.so in-tree with hipcc for gfx950.
 
 Usage: python -m selective_state_space_14_amd.build   (always recompiles)
+       python -m selective_state_space_14_amd.build --host-sanitized
+           also builds _build/libssd_hostsan.so: the same library with its host
+           code (the C ABI's validation in api.cpp) under AddressSanitizer and
+           UndefinedBehaviorSanitizer, for the CPU-side ABI checks.  Load it with
+           SSD_LIBRARY=<path> and the clang ASan runtime preloaded
+           (host_sanitizer_runtime()).
 """
 from __future__ import annotations
 
@@ -49,6 +55,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-only sanitizer flags: every -fsanitize= sits behind -Xarch_host, so no
+# device code is instrumented.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libasan"]
+
+
+def host_sanitizer_runtime() -> str:
+    """The clang ASan runtime (shared) that a host-sanitized build needs preloaded."""
+    root = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(root), reverse=True) if os.path.isdir(root) else []:
+        p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise RuntimeError(f"no libclang_rt.asan-x86_64.so under {root}")
+
+
+def build_host_sanitized(verbose: bool = True) -> str:
+    """_build/libssd_hostsan.so: api.cpp compiled with host ASan + UBSan, linked with the device objects."""
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "api.cpp":
+            obj = os.path.join(obj_dir, "api.hostsan.o")
+            cmd = [HIPCC, *CFLAGS, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(obj_dir, src + ".o")
+            objs.append(obj if os.path.exists(obj) else _compile(src, obj_dir))
+    out = os.path.join(obj_dir, "libssd_hostsan.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, *objs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build()
+    if "--host-sanitized" in sys.argv[1:]:
+        build_host_sanitized()
     sys.exit(0)
