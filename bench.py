@@ -6,9 +6,10 @@ ssd_conv_fwd (causal conv + SiLU + dt softplus) then ssd_chunk_scan_fwd
 (chunked scan, groups, D skip, z gate, final state), at the Mini-K3 mixer
 shape B=5, L=8192, H=32, P=64, N=64, G=8, bf16 inputs, fp32 state and y.
 Inputs are resident in HBM before the timed region; two input sets alternate
-so no step runs out of the 256 MB last-level cache.  The default warm-up of 50
-steps (~15 ms) runs past the GPU's ramp from idle: from a cold start the first
-~40 steps run up to 10% slower than the steady state.
+so no step runs out of the 256 MB last-level cache.  From a cold start the
+first ~40 steps run up to 10% slower than the steady state while the GPU ramps
+up from idle, so the headline step runs ~30 ms untimed (settle) before its W
+warm-up steps; every other timed loop follows it on a GPU already busy.
 
 Prints ONE JSON line: value = head-tokens (B*L*H) per second over the whole
 step; "roofline" = the scan call's algorithmic bytes / its average duration
@@ -168,6 +169,19 @@ def mixer_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed
             "mixer_bytes": mb, "mixer_GBs": mb / (ms * 1e-3) / 1e9, "mixer_workspace_bytes": ws_bytes}
 
 
+def settle(torch, fns, ms=30.0):
+    """Run fns round-robin, untimed, for about `ms` of wall time (at least 4 calls), so that the timed loop that
+    follows does not start on a GPU still ramping up from idle."""
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while i < 4 or (time.perf_counter() - t0) * 1e3 < ms:
+        fns[i % len(fns)]()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, seed=0):
     """The two-call path: ssd_conv_fwd then ssd_chunk_scan_fwd."""
     dev = "cuda"
@@ -196,6 +210,7 @@ def prefill_bench(ssd, synth, torch, wl, steps, warmup, docs=False, h0=False, se
             D=prm["D"], z=raw["z"], doc_ids=ids, init_state=raw["h0"] if h0 else None, final_state=fs, y=y,
             workspace=ws))
     steps_fn = [lambda k=k: (convs[k](), scans[k]()) for k in range(2)]
+    settle(torch, steps_fn)
     for i in range(warmup):
         steps_fn[i % 2]()
     # the step (conv then scan, back to back), then each call alone over as many launches
