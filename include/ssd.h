@@ -462,7 +462,8 @@ size_t ssd_s6_workspace_size(int B, int L, int D, int N, int dtype);
  *               ssd_chunk_scan_bwd_workspace_size() bytes, 16-byte aligned,
  *               caller-owned, not shared by concurrent calls
  * Outputs must not overlap the inputs or each other.  Supported: N in
- * {16, 32, 64}, P = 64, chunk = 64.  L = 0 writes zero parameter gradients.
+ * {16, 32, 64, 128}, P = 64, chunk = 64.  L = 0 writes zero parameter
+ * gradients.
  */
 int ssd_chunk_scan_bwd(int B, int L, int H, int P, int N, int G, int chunk, int dtype,
                        const void *x, int64_t x_row_stride,

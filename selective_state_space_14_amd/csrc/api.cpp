@@ -523,8 +523,6 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
 
 static int check_bwd_dims(const char* fn, int B, int L, int H, int P, int N, int G, int dtype) {
     TRY(check_dims(fn, B, L, H, P, N, G, 4, dtype));
-    if (N > 64)
-        return fail(SSD_ERR_UNSUPPORTED, "%s: N=%d is not supported by the backward (16, 32 or 64)", fn, N);
     return SSD_OK;
 }
 

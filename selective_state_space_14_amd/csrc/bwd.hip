@@ -32,6 +32,7 @@
 // All arithmetic is fp32: the 64x64 products of the chunk kernel and of the
 // first pass run on the fp32 MFMA from LDS tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
@@ -115,9 +116,12 @@ __device__ __forceinline__ const T* z_or_gy(const BwdArgs& a, int64_t& stride) {
 // (offsets multiples of 4 floats).  Lane (q, i) = (lane / 16, lane % 16) supplies A(r0 + i, 4q..4q+3)
 // and B(4q..4q+3, c0 + 16c + i) of each 16-wide K block, and element e of
 // acc[c] is the output at row r0 + 4q + e, column c0 + 16c + i.
-template <bool AT, bool BT, int NC>
+template <bool AT, bool BT, int NC, int UN = 2>
 __device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
                                            int ldb, int c0, int K, int q, int li) {
+    // UN K blocks per iteration: unrolled fully, the chunk kernel's strips
+    // hoist every LDS read and run out of registers
+#pragma unroll UN
     for (int kb = 0; kb < K; kb += 16) {
         const int k0 = kb + 4 * q;
         float4 af;
@@ -208,17 +212,21 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
     // [N][64] = W^T V on the fp32 MFMA: the N/16 x 4 output tiles are dealt
     // to the four waves, NC 16-column tiles of one 16-row strip each
     {
-        constexpr int NC = N / 16;
+        constexpr int NC = N >= 64 ? 4 : N / 16;         // 16-column tiles per strip
+        constexpr int RS = N >= 64 ? N / 64 : 1;         // 16-row strips per wave
         const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, li = lane & 15;
-        const int r0 = 16 * ((wave * NC) / 4);            // this wave's rows (state index n)
-        const int c0 = 16 * NC * (wave % (4 / NC));       // its first column (head channel p)
-        f32x4 acc[NC] = {};
-        mfma_strip<true, false, NC>(acc, sW, LDN, r0, sV, kLD, c0, kQ, q, li);
+        const int c0 = 16 * NC * (wave % (4 / NC));       // the first column (head channel p)
         float* out = (mode == 0 ? a.S : a.dS) + (((size_t)b * a.H + h) * nc + c) * N * P;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
+        for (int rs = 0; rs < RS; ++rs) {
+            const int r0 = 16 * ((wave * NC) / 4 * RS + rs);   // this strip's rows (state index n)
+            f32x4 acc[NC] = {};
+            mfma_strip<true, false, NC>(acc, sW, LDN, r0, sV, kLD, c0, kQ, q, li);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[(size_t)(r0 + 4 * q + e) * P + c0 + 16 * cc + li] = acc[cc][e];
+            for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[(size_t)(r0 + 4 * q + e) * P + c0 + 16 * cc + li] = acc[cc][e];
+        }
     }
 }
 
@@ -290,10 +298,22 @@ constexpr int kCT = 512;     // chunk kernel: eight waves
 // a lane holds rows R(e) = 16 (w % 4) + 4q + e (e < 4) at columns
 // 32 (w / 4) + 16c + li (c < 2).  Row sums of the two halves meet in LDS and
 // are added in a fixed order.
+//
+// The state dimension is held in LDS in blocks of NB = min(N, 64) columns of B
+// and C and NB rows of the states entering / leaving the chunk.  With N = 128
+// the two blocks take turns: C B^T sums the two blocks' products, and for each
+// head the block still resident from the previous head is used first, so one
+// block of B and C is reloaded per head.  Every product that contracts over N
+// (C Hin, B Gout) is accumulated over the blocks.  The dB / dC columns of the
+// block used first are kept in aB[0] / aC[0], those of the other in aB[1] /
+// aC[1]; the two swap when the resident block changes.
 template <typename T, int N>
 __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
-    constexpr int P = 64, LDN = N + 4;
-    constexpr int NCN = N / 32 > 0 ? N / 32 : 1;   // dB / dC tiles per half (N = 16: half 0 only)
+    constexpr int P = 64;
+    constexpr int NB = N < 64 ? N : 64;
+    constexpr int NH = N / NB;
+    constexpr int LDN = NB + 4;
+    constexpr int NCN = NB / 32 > 0 ? NB / 32 : 1;   // dB / dC tiles per half and block (NB = 16: half 0 only)
     __shared__ __attribute__((aligned(16))) float sB[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sC[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sG[kQ * kLD];
@@ -301,9 +321,9 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sDy[kQ * kLD];
     __shared__ __attribute__((aligned(16))) float sM[kQ * kLD];
     __shared__ __attribute__((aligned(16))) float sDG[kQ * kLD];
-    __shared__ __attribute__((aligned(16))) float sHin[N * kLD];
-    __shared__ __attribute__((aligned(16))) float sGo[N * kLD];
-    __shared__ float s_dt[kQ], s_cs[kQ], s_chain[kQ], s_ddt[kQ];
+    __shared__ __attribute__((aligned(16))) float sHin[NB * kLD];
+    __shared__ __attribute__((aligned(16))) float sGo[NB * kLD];
+    __shared__ float s_dt[kQ], s_cs[kQ], s_chain[kQ];
     __shared__ float s_dcs2[2][kQ], s_u2[2][kQ];   // row sums per column half
     __shared__ int s_seg[kQ];
     __shared__ float s_red[2][4][kQ];
@@ -320,32 +340,84 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     const int hpg = a.H / a.G;
     const int t0 = c * kQ, Qv = min(kQ, a.L - t0);
     const size_t row0 = (size_t)b * a.L + t0;
-    // the [64][N] products (dB, dC) split their N columns the same way: N/2
-    // per half (N = 16: one tile, half 0 only)
-    const bool nact = N >= 32 || half == 0;
-    const int c0N = N >= 32 ? half * (N / 2) : 0;
+    // the [64][NB] products (dB, dC) split their NB columns the same way: NB/2
+    // per half (NB = 16: one tile, half 0 only)
+    const bool nact = NB >= 32 || half == 0;
+    const int c0N = NB >= 32 ? half * (NB / 2) : 0;
     auto R = [&](int e) { return r0 + 4 * q + e; };
 
-    // the group's B and C rows (fp32, zero past the valid rows) and G = C B^T
+    // into LDS: block k of the group's B and C rows (fp32, zero past the valid
+    // rows) if bc, and block k of the states entering and leaving the chunk of
+    // the head at bhc (rows n = k NB .. +NB of [N][P]) if st; every load is
+    // issued before the first LDS write
+    constexpr int NU = kQ * NB / kCT;
+    constexpr int NS4 = (NB * P / 4 + kCT - 1) / kCT;
+    auto stage = [&](size_t bhc, int k, bool bc, bool st) __attribute__((always_inline)) {
+        float bv[NU], cv[NU];
+        float4 hv[NS4], ov[NS4];
+        if (bc) {
+            // the chunk's rows from a uniform base: offsets within 64 rows fit in 32 bits
+            const T* Bb = static_cast<const T*>(a.Bm) + row0 * a.B_stride + (size_t)g * N + k * NB;
+            const T* Cb = static_cast<const T*>(a.Cm) + row0 * a.C_stride + (size_t)g * N + k * NB;
 #pragma unroll
-    for (int u = 0; u < kQ * N / kCT; ++u) {
-        const int i = tid + u * kCT, r = i / N, n = i % N;
-        const size_t rr = row0 + min(r, Qv - 1);
-        const float bv = ldT(static_cast<const T*>(a.Bm) + rr * a.B_stride + (size_t)g * N + n);
-        const float cv = ldT(static_cast<const T*>(a.Cm) + rr * a.C_stride + (size_t)g * N + n);
-        sB[r * LDN + n] = r < Qv ? bv : 0.0f;
-        sC[r * LDN + n] = r < Qv ? cv : 0.0f;
-    }
-    __syncthreads();
+            for (int u = 0; u < NU; ++u) {
+                const int i = tid + u * kCT, r = min(i / NB, Qv - 1), n = i % NB;
+                bv[u] = ldT(Bb + (uint32_t)(r * (uint32_t)a.B_stride + n));
+                cv[u] = ldT(Cb + (uint32_t)(r * (uint32_t)a.C_stride + n));
+            }
+        }
+        if (st) {
+#pragma unroll
+            for (int u = 0; u < NS4; ++u) {
+                const int i4 = min(tid + u * kCT, NB * P / 4 - 1);
+                const uint32_t o = (uint32_t)(k * NB * P + 4 * i4);
+                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + o);
+                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + o);
+            }
+        }
+        if (bc) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int i = tid + u * kCT, r = i / NB, n = i % NB;   // rows past Qv: zero
+                sB[r * LDN + n] = r < Qv ? bv[u] : 0.0f;
+                sC[r * LDN + n] = r < Qv ? cv[u] : 0.0f;
+            }
+        }
+        if (st) {
+#pragma unroll
+            for (int u = 0; u < NS4; ++u) {
+                const int i4 = tid + u * kCT;
+                if (i4 < NB * P / 4) {
+                    const int n = 4 * i4 / P, p = 4 * i4 % P;
+                    *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
+                    *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
+                }
+            }
+        }
+    };
+    auto state_dot = [&]() __attribute__((always_inline)) {                       // <Gout, Hin> over the resident block, this thread's share
+        float v = 0.0f;
+        for (int i = tid; i < NB * P; i += kCT) v = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], v);
+        return v;
+    };
+
+    // G = C B^T, summed over the blocks
     {
         f32x4 acc[2] = {};
-        mfma_strip<false, true, 2>(acc, sC, LDN, r0, sB, LDN, c0, N, q, li);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+            if (k) __syncthreads();                // every wave is done with the previous block
+            stage(0, k, true, false);
+            __syncthreads();
+            mfma_strip<false, true, 2>(acc, sC, LDN, r0, sB, LDN, c0, NB, q, li);
+        }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sG[R(e) * kLD + c0 + 16 * cc + li] = acc[cc][e];
     }
-    f32x4 aB[NCN] = {}, aC[NCN] = {};             // dB, dC of the group, summed over its heads
+    f32x4 aB[NH][NCN] = {}, aC[NH][NCN] = {};     // dB, dC of the group, summed over its heads
+    int cur = NH - 1;                              // the block of B and C in LDS (aB[0], aC[0])
 
     for (int hh = 0; hh < hpg; ++hh) {
         const int h = g * hpg + hh;
@@ -359,32 +431,25 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             s_cs[lane] = cs;
             s_seg[lane] = seg;
             s_chain[lane] = chain;
-            s_ddt[lane] = 0.0f;
         }
         // x, dyr = dy silu(z) and qd = dy silu'(z) at this lane's elements, so
-        // dz = qd o y needs no reload; the states entering and leaving the chunk
+        // dz = qd o y needs no reload; the resident block of the states
         float qd[2][4];
         {
-            constexpr int NS = (N * P / 4 + kCT - 1) / kCT;
-            float4 hv[NS], ov[NS];
-#pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                const int i4 = min(tid + u * kCT, N * P / 4 - 1);
-                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + 4 * i4);
-                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + 4 * i4);
-            }
             int64_t zs;
-            const T* zp = z_or_gy<T>(a, zs);
+            const T* zp = z_or_gy<T>(a, zs) + row0 * zs;
+            const T* xp = static_cast<const T*>(a.x) + row0 * a.x_stride;
+            const float* gp = a.gy + row0 * a.gy_stride;
             float xv[2][4], gv[2][4], zv[2][4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const size_t rr = row0 + min(R(e), Qv - 1);   // a valid row; zeroed below past Qv
+                const uint32_t rr = min(R(e), Qv - 1);   // a valid row; zeroed below past Qv
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    const size_t col = (size_t)h * P + c0 + 16 * cc + li;
-                    xv[cc][e] = ldT(static_cast<const T*>(a.x) + rr * a.x_stride + col);
-                    gv[cc][e] = a.gy[rr * a.gy_stride + col];
-                    zv[cc][e] = ldT(zp + rr * zs + col);
+                    const uint32_t col = h * P + c0 + 16 * cc + li;
+                    xv[cc][e] = ldT(xp + (rr * (uint32_t)a.x_stride + col));
+                    gv[cc][e] = gp[rr * (uint32_t)a.gy_stride + col];
+                    zv[cc][e] = ldT(zp + (rr * (uint32_t)zs + col));
                 }
             }
 #pragma unroll
@@ -399,20 +464,11 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                     qd[cc][e] = a.z ? gg * dsilu_acc(zz) : 0.0f;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                const int i4 = tid + u * kCT;
-                if (i4 < N * P / 4) {
-                    const int n = 4 * i4 / P, p = 4 * i4 % P;
-                    *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
-                    *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
-                }
-            }
+            stage(bhc, cur, false, true);
         }
         __syncthreads();
 
-        float hg = 0.0f;                           // <Gout, Hin> partial
-        for (int i = tid; i < N * P; i += kCT) hg = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], hg);
+        float hg = state_dot();                    // <Gout, Hin> partial
         const int end = Qv - 1;
         const float cs_end = s_cs[end];
         const int seg_end = s_seg[end];
@@ -438,34 +494,6 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         __syncthreads();
 
         float rowD[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this half's share of dcs per row
-        // y (before the gate) = M X + in o (C Hin) + D X; dz; the in_t share of dcs; dD
-        {
-            f32x4 y1[2] = {}, y2[2] = {};
-            mfma_strip<false, false, 2>(y1, sM, kLD, r0, sX, kLD, c0, kQ, q, li);
-            mfma_strip<false, false, 2>(y2, sC, LDN, r0, sHin, kLD, c0, N, q, li);
-            float pD = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = R(e);
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int p = c0 + 16 * cc + li;
-                    const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
-                    rowD[e] = fmaf(in_r[e] * y2[cc][e], dy, rowD[e]);
-                    pD = fmaf(dy, xv, pD);
-                    if (a.dz && t < Qv)
-                        a.dz[(row0 + t) * a.dz_stride + (size_t)h * P + p] =
-                            qd[cc][e] * (y1[cc][e] + in_r[e] * y2[cc][e] + Dh * xv);
-                }
-            }
-            pD = sum64(pD);
-            hg = sum64(hg);
-            if (lane == 0) {
-                s_scal[0][wave] = pD;
-                s_scal[1][wave] = hg;
-            }
-        }
-
         // dM = dyr X^T -> dG, the Lm share of dcs, the direct share of ddt
         {
             f32x4 dm[2] = {};
@@ -487,11 +515,6 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = sum16(rowD[e]);
-                if (li == 0) s_dcs2[half][R(e)] = v;
-            }
-#pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 float v = colT[cc], w = colD[cc];
                 v += __shfl_xor(v, 16);
@@ -504,47 +527,93 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();                           // dG
 
+        // the products over the state dimension, block by block:
+        //   y_off = C Hin, B Gout (accumulated);  dB += dG^T C + (el o dt) o (X Gout^T),
+        //   dC += dG B + in o (dyr Hin^T) (the block's columns)
+        f32x4 y2[2] = {}, bgo[2] = {};
+        auto block = [&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;   // 0: the block used first
+            mfma_strip<false, false, 2>(y2, sC, LDN, r0, sHin, kLD, c0, NB, q, li);
+            mfma_strip<false, false, 2>(bgo, sB, LDN, r0, sGo, kLD, c0, NB, q, li);
+            if (nact) {
+                mfma_strip<true, false, NCN>(aB[k], sDG, kLD, r0, sC, LDN, c0N, kQ, q, li);
+                mfma_strip<false, false, NCN>(aC[k], sDG, kLD, r0, sB, LDN, c0N, kQ, q, li);
+                f32x4 xg[NCN] = {}, dh[NCN] = {};
+                mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, c0N, P, q, li);
+                mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, c0N, P, q, li);
+#pragma unroll
+                for (int cc = 0; cc < NCN; ++cc)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        aB[k][cc][e] = fmaf(we_r[e], xg[cc][e], aB[k][cc][e]);
+                        aC[k][cc][e] = fmaf(in_r[e], dh[cc][e], aC[k][cc][e]);
+                    }
+            }
+        };
+        block(std::integral_constant<int, 0>{});
+        if constexpr (NH == 2) {
+            const int nxt = 1 - cur;
+            __syncthreads();                       // every wave is done with the resident block
+            stage(bhc, nxt, true, true);
+            __syncthreads();
+            hg += state_dot();
+            block(std::integral_constant<int, 1>{});
+            cur = nxt;                             // now resident: used first by the next head
+#pragma unroll
+            for (int cc = 0; cc < NCN; ++cc) {
+                const f32x4 tb = aB[0][cc], tc = aC[0][cc];
+                aB[0][cc] = aB[1][cc];
+                aC[0][cc] = aC[1][cc];
+                aB[1][cc] = tb;
+                aC[1][cc] = tc;
+            }
+        }
+
+        // y (before the gate) = M X + in o (C Hin) + D X; dz; the in_t share of dcs; dD;
         // dX = M^T dyr + D dyr + (el o dt) o (B Gout); u_s = (B Gout)_s . x_s
         {
-            f32x4 d1[2] = {}, bgo[2] = {};
+            f32x4 y1[2] = {}, d1[2] = {};
+            mfma_strip<false, false, 2>(y1, sM, kLD, r0, sX, kLD, c0, kQ, q, li);
             mfma_strip<true, false, 2>(d1, sM, kLD, r0, sDy, kLD, c0, kQ, q, li);
-            mfma_strip<false, false, 2>(bgo, sB, LDN, r0, sGo, kLD, c0, N, q, li);
+            float pD = 0.0f;
             float ru[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int s = R(e);
-                const float we = we_r[e];
+                const int t = R(e);
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
                     const int p = c0 + 16 * cc + li;
-                    ru[e] = fmaf(bgo[cc][e], sX[s * kLD + p], ru[e]);
-                    if (s < Qv)
-                        a.dx[(row0 + s) * a.dx_stride + (size_t)h * P + p] =
-                            d1[cc][e] + Dh * sDy[s * kLD + p] + we * bgo[cc][e];
+                    const float xv = sX[t * kLD + p], dy = sDy[t * kLD + p];
+                    rowD[e] = fmaf(in_r[e] * y2[cc][e], dy, rowD[e]);
+                    pD = fmaf(dy, xv, pD);
+                    ru[e] = fmaf(bgo[cc][e], xv, ru[e]);
+                    if (t < Qv) {
+                        const uint32_t col = h * P + p;
+                        if (a.dz)
+                            a.dz[row0 * a.dz_stride + (t * (uint32_t)a.dz_stride + col)] =
+                                qd[cc][e] * (y1[cc][e] + in_r[e] * y2[cc][e] + Dh * xv);
+                        a.dx[row0 * a.dx_stride + (t * (uint32_t)a.dx_stride + col)] =
+                            d1[cc][e] + Dh * dy + we_r[e] * bgo[cc][e];
+                    }
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = sum16(ru[e]);
-                if (li == 0) s_u2[half][R(e)] = v;
-            }
-        }
-        // dB += dG^T C + (el o dt) o (X Gout^T);  dC += dG B + in o (dyr Hin^T)
-        if (nact) {
-            mfma_strip<true, false, NCN>(aB, sDG, kLD, r0, sC, LDN, c0N, kQ, q, li);
-            mfma_strip<false, false, NCN>(aC, sDG, kLD, r0, sB, LDN, c0N, kQ, q, li);
-            f32x4 xg[NCN] = {}, dh[NCN] = {};
-            mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, c0N, P, q, li);
-            mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, c0N, P, q, li);
-#pragma unroll
-            for (int cc = 0; cc < NCN; ++cc)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    aB[cc][e] = fmaf(we_r[e], xg[cc][e], aB[cc][e]);
-                    aC[cc][e] = fmaf(in_r[e], dh[cc][e], aC[cc][e]);
+                const float v = sum16(rowD[e]);
+                const float u = sum16(ru[e]);
+                if (li == 0) {
+                    s_dcs2[half][R(e)] = v;
+                    s_u2[half][R(e)] = u;
                 }
+            }
+            pD = sum64(pD);
+            hg = sum64(hg);
+            if (lane == 0) {
+                s_scal[0][wave] = pD;
+                s_scal[1][wave] = hg;
+            }
         }
         __syncthreads();
 
@@ -592,11 +661,14 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             const int r = R(e);
             if (r < Qv) {
 #pragma unroll
-                for (int cc = 0; cc < NCN; ++cc) {
-                    const size_t col = (size_t)g * N + c0N + 16 * cc + li;
-                    a.dB[(row0 + r) * a.dB_stride + col] = aB[cc][e];
-                    a.dC[(row0 + r) * a.dC_stride + col] = aC[cc][e];
-                }
+                for (int k = 0; k < NH; ++k)
+#pragma unroll
+                    for (int cc = 0; cc < NCN; ++cc) {
+                        const int blk = k == 0 ? cur : NH - 1 - cur;
+                        const size_t col = (size_t)g * N + blk * NB + c0N + 16 * cc + li;
+                        a.dB[row0 * a.dB_stride + (r * (uint32_t)a.dB_stride + (uint32_t)col)] = aB[k][cc][e];
+                        a.dC[row0 * a.dC_stride + (r * (uint32_t)a.dC_stride + (uint32_t)col)] = aC[k][cc][e];
+                    }
             }
         }
     }
@@ -810,6 +882,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
         case 16: return launch_bwd_n<T, 16>(a, stream);
         case 32: return launch_bwd_n<T, 32>(a, stream);
         case 64: return launch_bwd_n<T, 64>(a, stream);
+        case 128: return launch_bwd_n<T, 128>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -328,7 +328,7 @@ def call_bwd(lib, a):
 
 
 @pytest.mark.parametrize("over,status,needle", [
-    (dict(N=128), 3, "N=128 is not supported by the backward"),
+    (dict(N=256), 3, "N=256"),
     (dict(chunk=32), 3, "chunk=32"),
     (dict(dtype=5), 3, "dtype=5"),
     (dict(gy=None), 1, "grad_y is NULL"),

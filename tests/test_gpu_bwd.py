@@ -61,6 +61,10 @@ SCAN_CASES = [
     ("f32", 2, 331, 4, 32, 4, True, True, False),
     ("bf16", 2, 257, 8, 64, 2, True, True, True),     # four heads per group
     ("bf16", 1, 130, 2, 16, 2, False, True, True),
+    # N = 128: the state dimension in two blocks of 64 that take turns in LDS
+    ("f32", 2, 200, 4, 128, 2, True, True, True),     # two heads per group
+    ("bf16", 1, 270, 6, 128, 1, True, True, False),   # six heads: the resident block alternates
+    ("f32", 1, 64, 1, 128, 1, False, False, True),    # one head, one chunk
 ]
 
 
@@ -169,10 +173,10 @@ def _mixer_oracle_on_gpu_conv(lib, wl, prm, raw, ids, gy, rows=None):
     return out
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_mixer_bwd_vs_oracle(gpu_lib, dtype):
-    wl = synth.Workload(f"mbwd_{dtype}", 2, 333, 8, 64, 64, 2, dtype)
-    _say(f"mixer bwd {dtype}")
+@pytest.mark.parametrize("dtype,N", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_mixer_bwd_vs_oracle(gpu_lib, dtype, N):
+    wl = synth.Workload(f"mbwd_{dtype}_{N}", 2, 333, 8, 64, N, 2, dtype)
+    _say(f"mixer bwd {dtype} N={N}")
     prm, raw, ids, gy = _mixer_inputs(wl, 6, True, mean_len=100.0)
     got = _mixer_gpu(gpu_lib, wl, prm, raw, ids, gy)
     ref = _mixer_oracle(wl, prm, raw, ids, gy)
@@ -244,9 +248,10 @@ def test_bwd_empty_and_refusals(gpu_lib):
     torch.cuda.synchronize()
     assert torch.count_nonzero(got["A"]).item() == 0 and torch.count_nonzero(got["D"]).item() == 0
     x = torch.zeros(1, 8, 128, device=DEV)
-    b = torch.zeros(1, 8, 128, device=DEV)
-    with pytest.raises(gpu_lib.SSDError, match="N=128 is not supported by the backward"):
-        gpu_lib.ssd_chunk_scan_bwd(x, b, b, torch.zeros(1, 8, 2, device=DEV), prm["A"], x, H=2, P=64, N=128, G=1)
+    b256 = torch.zeros(1, 8, 256, device=DEV)
+    with pytest.raises(gpu_lib.SSDError, match="N=256"):
+        gpu_lib.ssd_chunk_scan_bwd(x, b256, b256, torch.zeros(1, 8, 2, device=DEV), prm["A"], x, H=2, P=64, N=256,
+                                   G=1)
     with pytest.raises(gpu_lib.SSDError, match="workspace_bytes"):
         gpu_lib.ssd_chunk_scan_bwd(x, x[..., :16].contiguous(), x[..., :16].contiguous(),
                                    torch.zeros(1, 8, 2, device=DEV), prm["A"], x, H=2, P=64, N=16, G=1,
@@ -296,3 +301,41 @@ def test_scan_bwd_full_workload_bf16(gpu_lib):
                           dt_softplus=True, dt_bias=_np(prm["dt_bias"]))
     for k in ref:
         _check(got[k], ref[k], f"d{k}")
+
+
+def test_scan_bwd_large_layer_f32(gpu_lib):
+    """ssd_chunk_scan_bwd at the large-layer shape (B=4, L=4096, H=128, P=64, N=128, G=8) with fp32 inputs,
+    documents, gate and softplus on dt: every per-token gradient of rows 0 and 3 of the full-batch call
+    element-wise against the oracle on those rows, and the parameter gradients of a call on those two rows
+    alone against the oracle's."""
+    wl = synth.WORKLOADS["large_layer_bf16"].with_(dtype="f32")
+    rows = [0, wl.B - 1]
+    _say("scan bwd large layer f32")
+    inp = synth.scan_inputs(wl, 2)
+    prm = synth.params(wl, 2)
+    ids = synth.doc_ids(wl, 2, mean_len=1024.0)
+    gy = torch.randn(wl.B, wl.L, wl.H * wl.P, generator=torch.Generator().manual_seed(12))
+    g = lambda t: None if t is None else t.to(DEV)
+
+    def run(sl):
+        out = gpu_lib.ssd_chunk_scan_bwd(g(sl(inp["x"])), g(sl(inp["Bm"])), g(sl(inp["Cm"])), g(sl(inp["dt_raw"])),
+                                         g(prm["A"]), g(sl(gy)), H=wl.H, P=wl.P, N=wl.N, G=wl.G, D=g(prm["D"]),
+                                         z=g(sl(inp["z"])), doc_ids=g(sl(ids)), dt_softplus=True,
+                                         dt_bias=g(prm["dt_bias"]))
+        torch.cuda.synchronize()
+        return {k: v.cpu() for k, v in out.items()}
+
+    full = run(lambda t: t)
+    part = run(lambda t: t[rows].contiguous())
+    _say("scan bwd large layer f32: oracle rows")
+    sl = lambda t: t[rows]
+    ref = oracle.scan_bwd(_np(sl(inp["x"])), _np(sl(inp["Bm"])), _np(sl(inp["Cm"])), _np(sl(inp["dt_raw"])),
+                          _np(prm["A"]), _np(sl(gy)), _np(prm["D"]), _np(sl(inp["z"])), sl(ids).numpy(), H=wl.H,
+                          P=wl.P, N=wl.N, G=wl.G, dt_softplus=True, dt_bias=_np(prm["dt_bias"]))
+    assert set(full) == set(ref), (sorted(full), sorted(ref))
+    for k in ref:
+        if full[k].dim() == 3:                     # per token: rows of the full-batch call
+            _check(full[k][rows], ref[k], f"d{k} (rows {rows} of the full batch)")
+            assert torch.equal(full[k][rows], part[k]), f"d{k}: the two-row call differs from the full batch"
+        else:                                      # per head: summed over the two rows
+            _check(part[k], ref[k], f"d{k} (rows {rows} alone)")
