@@ -22,7 +22,8 @@ kernels), the other workloads (packed documents, the large layer, the decode
 step), the chunk-resume decode (ssd_resume_fwd) and the fp32 4096-token
 prefill (conv + scan) on the decode workload, the
 Mamba-1 selective scan (ssd_s6_scan_fwd) priced against the VALU rate, and
-the backward of the mixer (ssd_mixer_bwd) on the Mini-K3 batch.
+the backward of the mixer (ssd_mixer_bwd) on the Mini-K3 batch and on the
+large layer.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
@@ -510,6 +511,9 @@ def main():
         torch.cuda.empty_cache()
         extras.append(s6_bench(ssd, synth, torch, synth.WORKLOADS["s6_bf16"], args.steps, args.warmup))
         extras.append(bwd_bench(ssd, synth, torch, wl, max(5, args.steps // 5), args.warmup))
+        torch.cuda.empty_cache()
+        extras.append(bwd_bench(ssd, synth, torch, synth.WORKLOADS["large_layer_bf16"], max(3, args.steps // 10),
+                                min(args.warmup, 5)))
 
     cpu = None
     if not args.no_cpu_baseline:

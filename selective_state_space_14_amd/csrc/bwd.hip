@@ -119,8 +119,8 @@ __device__ __forceinline__ const T* z_or_gy(const BwdArgs& a, int64_t& stride) {
 template <bool AT, bool BT, int NC, int UN = 2>
 __device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int lda, int r0, const float* Bm,
                                            int ldb, int c0, int K, int q, int li) {
-    // UN K blocks per iteration: unrolled fully, the chunk kernel's strips
-    // hoist every LDS read and run out of registers
+    // UN K blocks per iteration (the chunk kernel picks the most its registers
+    // hold without spilling: unrolled fully, a strip hoists every LDS read)
 #pragma unroll UN
     for (int kb = 0; kb < K; kb += 16) {
         const int k0 = kb + 4 * q;
@@ -314,6 +314,9 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     constexpr int NH = N / NB;
     constexpr int LDN = NB + 4;
     constexpr int NCN = NB / 32 > 0 ? NB / 32 : 1;   // dB / dC tiles per half and block (NB = 16: half 0 only)
+    // K blocks per unrolled step of the products: all four where the kernel
+    // still fits its 256 registers without spilling (N = 16, 64), else two
+    constexpr int UN = (N == 16 || N == 64) ? 4 : 2;
     __shared__ __attribute__((aligned(16))) float sB[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sC[kQ * LDN];
     __shared__ __attribute__((aligned(16))) float sG[kQ * kLD];
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     constexpr int NS4 = (NB * P / 4 + kCT - 1) / kCT;
     auto stage = [&](size_t bhc, int k, bool bc, bool st) __attribute__((always_inline)) {
         float bv[NU], cv[NU];
-        float4 hv[NS4], ov[NS4];
+        f32x4 hv[NS4], ov[NS4];
         if (bc) {
             // the chunk's rows from a uniform base: offsets within 64 rows fit in 32 bits
             const T* Bb = static_cast<const T*>(a.Bm) + row0 * a.B_stride + (size_t)g * N + k * NB;
@@ -371,8 +374,8 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             for (int u = 0; u < NS4; ++u) {
                 const int i4 = min(tid + u * kCT, NB * P / 4 - 1);
                 const uint32_t o = (uint32_t)(k * NB * P + 4 * i4);
-                hv[u] = *reinterpret_cast<const float4*>(a.S + bhc * N * P + o);
-                ov[u] = *reinterpret_cast<const float4*>(a.dS + bhc * N * P + o);
+                hv[u] = *reinterpret_cast<const f32x4*>(a.S + bhc * N * P + o);
+                ov[u] = *reinterpret_cast<const f32x4*>(a.dS + bhc * N * P + o);
             }
         }
         if (bc) {
@@ -389,8 +392,8 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 const int i4 = tid + u * kCT;
                 if (i4 < NB * P / 4) {
                     const int n = 4 * i4 / P, p = 4 * i4 % P;
-                    *reinterpret_cast<float4*>(sHin + n * kLD + p) = hv[u];
-                    *reinterpret_cast<float4*>(sGo + n * kLD + p) = ov[u];
+                    *reinterpret_cast<f32x4*>(sHin + n * kLD + p) = hv[u];
+                    *reinterpret_cast<f32x4*>(sGo + n * kLD + p) = ov[u];
                 }
             }
         }
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             if (k) __syncthreads();                // every wave is done with the previous block
             stage(0, k, true, false);
             __syncthreads();
-            mfma_strip<false, true, 2>(acc, sC, LDN, r0, sB, LDN, c0, NB, q, li);
+            mfma_strip<false, true, 2, UN>(acc, sC, LDN, r0, sB, LDN, c0, NB, q, li);
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         // dM = dyr X^T -> dG, the Lm share of dcs, the direct share of ddt
         {
             f32x4 dm[2] = {};
-            mfma_strip<false, true, 2>(dm, sDy, kLD, r0, sX, kLD, c0, P, q, li);
+            mfma_strip<false, true, 2, UN>(dm, sDy, kLD, r0, sX, kLD, c0, P, q, li);
             float colT[2] = {0.0f, 0.0f}, colD[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -535,14 +538,14 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         f32x4 y2[2] = {}, bgo[2] = {};
         auto block = [&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;   // 0: the block used first
-            mfma_strip<false, false, 2>(y2, sC, LDN, r0, sHin, kLD, c0, NB, q, li);
-            mfma_strip<false, false, 2>(bgo, sB, LDN, r0, sGo, kLD, c0, NB, q, li);
+            mfma_strip<false, false, 2, UN>(y2, sC, LDN, r0, sHin, kLD, c0, NB, q, li);
+            mfma_strip<false, false, 2, UN>(bgo, sB, LDN, r0, sGo, kLD, c0, NB, q, li);
             if (nact) {
-                mfma_strip<true, false, NCN>(aB[k], sDG, kLD, r0, sC, LDN, c0N, kQ, q, li);
-                mfma_strip<false, false, NCN>(aC[k], sDG, kLD, r0, sB, LDN, c0N, kQ, q, li);
+                mfma_strip<true, false, NCN, UN>(aB[k], sDG, kLD, r0, sC, LDN, c0N, kQ, q, li);
+                mfma_strip<false, false, NCN, UN>(aC[k], sDG, kLD, r0, sB, LDN, c0N, kQ, q, li);
                 f32x4 xg[NCN] = {}, dh[NCN] = {};
-                mfma_strip<false, true, NCN>(xg, sX, kLD, r0, sGo, kLD, c0N, P, q, li);
-                mfma_strip<false, true, NCN>(dh, sDy, kLD, r0, sHin, kLD, c0N, P, q, li);
+                mfma_strip<false, true, NCN, UN>(xg, sX, kLD, r0, sGo, kLD, c0N, P, q, li);
+                mfma_strip<false, true, NCN, UN>(dh, sDy, kLD, r0, sHin, kLD, c0N, P, q, li);
 #pragma unroll
                 for (int cc = 0; cc < NCN; ++cc)
 #pragma unroll
@@ -575,8 +578,8 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         // dX = M^T dyr + D dyr + (el o dt) o (B Gout); u_s = (B Gout)_s . x_s
         {
             f32x4 y1[2] = {}, d1[2] = {};
-            mfma_strip<false, false, 2>(y1, sM, kLD, r0, sX, kLD, c0, kQ, q, li);
-            mfma_strip<true, false, 2>(d1, sM, kLD, r0, sDy, kLD, c0, kQ, q, li);
+            mfma_strip<false, false, 2, UN>(y1, sM, kLD, r0, sX, kLD, c0, kQ, q, li);
+            mfma_strip<true, false, 2, UN>(d1, sM, kLD, r0, sDy, kLD, c0, kQ, q, li);
             float pD = 0.0f;
             float ru[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll

@@ -96,84 +96,6 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // dropped there) into the workspace.
 enum { kFull = 0, kStateOnly = 1 };
 
-// fp32 operands of the generic kernel's contractions are held in LDS as two
-// bf16 planes, v = hi + lo + e with hi = bf16(v), lo = bf16(v - hi) (both
-// rounded to nearest even; v - hi is exact), so |e| <= 2^-18 |v|.  A matrix
-// region of `cnt` fp32 slots keeps its byte size: the hi plane is its first
-// cnt 16-bit elements, the lo plane the next cnt.  A product of two split
-// operands is formed on the bf16 MFMA as lo*hi + hi*lo + hi*hi with fp32
-// accumulation (the lo*lo term, ~2^-16 of the product, is dropped): three
-// 16x16x32 MFMAs replace the eight 16x16x4 fp32 ones for the same 32-wide K
-// range, at ~2^-16 relative error per product.
-struct Split4 { FragBF hi, lo; };      // 4 consecutive K elements of a fragment
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-    hi = pack_bf16x2(a, b);
-    lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
-}
-__device__ __forceinline__ Split4 split4(float a, float b, float c, float d) {
-    Split4 r;
-    split_pair(a, b, r.hi.a, r.lo.a);
-    split_pair(c, d, r.hi.b, r.lo.b);
-    return r;
-}
-__device__ __forceinline__ Split4 split_zero() { return {{0u, 0u}, {0u, 0u}}; }
-// the 4 elements at index i (a multiple of 4) of a split region of cnt slots
-__device__ __forceinline__ Split4 pld(const uint16_t* p, int cnt, int i) {
-    const uint2 h = *reinterpret_cast<const uint2*>(p + i);
-    const uint2 l = *reinterpret_cast<const uint2*>(p + cnt + i);
-    return {{h.x, h.y}, {l.x, l.y}};
-}
-__device__ __forceinline__ void pst4(uint16_t* p, int cnt, int i, float a, float b, float c, float d) {
-    const Split4 v = split4(a, b, c, d);
-    *reinterpret_cast<uint2*>(p + i) = make_uint2(v.hi.a, v.hi.b);
-    *reinterpret_cast<uint2*>(p + cnt + i) = make_uint2(v.lo.a, v.lo.b);
-}
-// two consecutive elements at index i (even)
-__device__ __forceinline__ void pst2(uint16_t* p, int cnt, int i, float a, float b) {
-    uint32_t hi, lo;
-    split_pair(a, b, hi, lo);
-    *reinterpret_cast<uint32_t*>(p + i) = hi;
-    *reinterpret_cast<uint32_t*>(p + cnt + i) = lo;
-}
-__device__ __forceinline__ void pst1(uint16_t* p, int cnt, int i, float v) {
-    const uint32_t hi = f32_to_bf16_bits(v);
-    p[i] = (uint16_t)hi;
-    p[cnt + i] = (uint16_t)f32_to_bf16_bits(v - __uint_as_float(hi << 16));
-}
-// acc += A B over two 16-wide K blocks (a0/b0: block 0, a1/b1: block 1)
-__device__ __forceinline__ f32x4 mma_split(f32x4 acc, const Split4& a0, const Split4& a1, const Split4& b0,
-                                           const Split4& b1) {
-    acc = mma_bf16(acc, a0.lo, a1.lo, b0.hi, b1.hi);
-    acc = mma_bf16(acc, a0.hi, a1.hi, b0.lo, b1.lo);
-    return mma_bf16(acc, a0.hi, a1.hi, b0.hi, b1.hi);
-}
-
-// Transposed reads of 16-bit tiles (ds_read_b64_tr_b16): in each 16-lane
-// group, result lane j element e is element (j mod 4) of source lane 4e + j/4,
-// so a lane (q, m) that addresses row 4q + m/4, column 4(m mod 4) of a tile
-// receives column m, rows 4q..4q+3 -- the operand fragment of the transposed
-// tile.
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-#define SSD_LDS __attribute__((address_space(3)))
-
-__device__ __forceinline__ FragBF tr_read(const unsigned char* lds_base, uint32_t byte_off) {
-    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS v4i16_t*)(lds_base + byte_off));
-    FragBF f;
-    f.a = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
-    f.b = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
-    return f;
-}
-__device__ __forceinline__ FragBF plain_read(const unsigned char* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    return {v.x, v.y};
-}
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
-// then s_barrier.  (A fence-based barrier would also wait for the copies in
-// flight.)  The memory clobber keeps the compiler from moving accesses across.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // LDS plan of the fp32 kernel, in fp32 slots; every matrix region is split
 // (Split4: the hi plane, then the lo plane, in the region's byte size).
 // B and C row-major [Q][NS] for the group of the workgroup's HPW heads; per
