@@ -123,6 +123,20 @@ def step_bytes(wl):
     return b
 
 
+def resume_bytes(wl):
+    """Bytes one ssd_resume_fwd call at working-chunk position pos must move, averaged over pos = 0 .. 63: the new
+    token's conv (raw row, conv state read and written, its chunk row), the rescan of rows 0 .. pos (convolved row,
+    dt and gate row read, chunk_y row written), the state at the chunk's start (read every call, written on the
+    chunk's last token) and the new token's y copied out."""
+    es = 2 if wl.dtype == "bf16" else 4
+    C, HP, B = wl.conv_dim, wl.H * wl.P, wl.B
+    conv = B * (C * es + 2 * 3 * C * es + C * es + wl.H * (es + 4))
+    rows = 32.5                                   # mean of pos + 1 over a chunk
+    scan = B * rows * (C * es + wl.H * 4 + (HP * es if wl.gate else 0) + HP * 4)
+    state = B * wl.H * wl.P * wl.N * 4 * (1 + 1 / 64)
+    return conv + scan + state + 2 * B * HP * 4
+
+
 def loop_ms(torch, calls, n):
     """Mean duration in ms of one call when `n` calls run back to back on the launch stream (cycling through
     `calls`, e.g. one per input set), bracketed by ONE pair of HIP events: no event or host work sits between
@@ -313,8 +327,10 @@ def resume_bench(ssd, synth, torch, wl, warmup, seed=0):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / 64
+    nb = resume_bytes(wl)
     return {"workload": wl.name + " (ssd_resume_fwd, one token per call, mean over a 64-token chunk)",
-            "ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "unit": "head-tokens/s (B*H per step)"}
+            "ms_per_step": ms, "value": wl.B * wl.H / (ms * 1e-3), "unit": "head-tokens/s (B*H per step)",
+            "hbm_bytes": nb, "hbm_GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 # fp32 VALU lane-operations per second this build can issue on MI355X: 256 CUs x 4 SIMDs x 16 lanes x
