@@ -1,0 +1,86 @@
+"""GPU parity of ssd_chunk_scan_fwd and ssd_chunk_scan_bwd against the fp64 oracle over seeded random
+configurations: state sizes,
+group layouts (heads per group 1, 2, 3, 4, 6, 8, so every workgroup plan the library picks), lengths from one
+token to several superchunks, documents, carried states, the gate, both dt forms, and the sequence split where
+the sizes take it.  Inputs reach both sides identically, so the bars are the per-call ones: fp32 1e-3 * RMS,
+bf16 0.03125 absolute, the backward 1e-3 * RMS per gradient; the split result is held to the same bars."""
+import random
+
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import helpers as hp
+from tests.test_gpu_bwd import DEV, _check, _np
+from tests.test_gpu_conv_scan import run_scan, small_wl, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _configs(n, seed=2024):
+    r = random.Random(seed)
+    out = []
+    for i in range(n):
+        dtype = r.choice(["bf16", "bf16", "f32"])
+        N = r.choice([16, 32, 64, 128])
+        G = r.choice([1, 2, 4])
+        hpg = r.choice([1, 2, 3, 4, 6, 8])
+        if G * hpg > 16:
+            hpg = max(1, 16 // G)
+        L = r.choice([1, 2, 63, 64, 65, r.randint(3, 600), r.randint(600, 2600)])
+        B = r.choice([1, 2, 3])
+        docs = r.random() < 0.5
+        h0 = r.random() < 0.5
+        gate = r.random() < 0.7
+        softplus = r.random() < 0.7
+        out.append((i, dtype, N, G, G * hpg, L, B, docs, h0, gate, softplus))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,N,G,H,L,B,docs,h0,gate,softplus", _configs(48))
+def test_scan_random_config(gpu_lib, i, dtype, N, G, H, L, B, docs, h0, gate, softplus):
+    print(f"random scan #{i}: {dtype} N={N} G={G} H={H} L={L} B={B} docs={docs} h0={h0} gate={gate} "
+          f"softplus={softplus}", flush=True)
+    wl = small_wl(dtype, H=H, N=N, G=G, L=L, B=B, docs=docs, h0=h0, gate=gate)
+    prm = synth.params(wl, 100 + i)
+    inp = synth.scan_inputs(wl, 100 + i)
+    if not softplus:        # dt given directly (positive), as the conv prologue would deliver it
+        inp["dt_raw"] = torch.nn.functional.softplus(inp["dt_raw"] + prm["dt_bias"])
+    ids = synth.doc_ids(wl, 100 + i, mean_len=float(max(2, L // 3))) if docs else None
+    check = hp.assert_fp32 if dtype == "f32" else hp.assert_bf16
+    y, fs = run_scan(gpu_lib, wl, inp, prm, ids, dt_softplus=softplus)
+    yr, fr = oracle.scan(inp["x"], inp["Bm"], inp["Cm"], inp["dt_raw"].float(), prm["A"], prm["D"], inp["z"], ids,
+                          inp["h0"], H=wl.H, P=wl.P, N=wl.N, G=wl.G, dt_softplus=softplus,
+                          dt_bias=prm["dt_bias"] if softplus else None, want_state=True)
+    check(y, yr, "y")
+    check(fs, fr, "final_state")
+    if workspace(gpu_lib, wl.B, wl.L, wl.H, wl.P, wl.N, wl.G, wl.dtype) is not None:
+        ys, fss = run_scan(gpu_lib, wl, inp, prm, ids, dt_softplus=softplus, split=True)
+        check(ys, yr, "y (sequence split)")
+        check(fss, fr, "final_state (sequence split)")
+
+
+@pytest.mark.parametrize("i,dtype,N,G,H,L,B,docs,h0,gate,softplus", _configs(16, seed=4048))
+def test_scan_bwd_random_config(gpu_lib, i, dtype, N, G, H, L, B, docs, h0, gate, softplus):
+    """The backward from a zero state (h0 unused) on the same kind of random configurations."""
+    print(f"random scan bwd #{i}: {dtype} N={N} G={G} H={H} L={L} B={B} docs={docs} gate={gate} "
+          f"softplus={softplus}", flush=True)
+    wl = small_wl(dtype, H=H, N=N, G=G, L=L, B=B, docs=docs, gate=gate)
+    prm = synth.params(wl, 200 + i)
+    inp = synth.scan_inputs(wl, 200 + i)
+    dt = inp["dt_raw"] if softplus else torch.nn.functional.softplus(inp["dt_raw"] + prm["dt_bias"])
+    ids = synth.doc_ids(wl, 200 + i, mean_len=float(max(2, L // 3))) if docs else None
+    gy = torch.randn(B, L, H * 64, generator=torch.Generator().manual_seed(300 + i))
+    g = lambda t: None if t is None else t.to(DEV)
+    z = inp["z"] if gate else None
+    got = gpu_lib.ssd_chunk_scan_bwd(g(inp["x"]), g(inp["Bm"]), g(inp["Cm"]), g(dt), g(prm["A"]), g(gy), H=H, P=64,
+                                     N=N, G=G, D=g(prm["D"]), z=g(z), doc_ids=g(ids), dt_softplus=softplus,
+                                     dt_bias=g(prm["dt_bias"]) if softplus else None)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(_np(inp["x"]), _np(inp["Bm"]), _np(inp["Cm"]), _np(dt), _np(prm["A"]), _np(gy),
+                          _np(prm["D"]), _np(z), None if ids is None else ids.numpy(), H=H, P=64, N=N, G=G,
+                          dt_softplus=softplus, dt_bias=_np(prm["dt_bias"]) if softplus else None)
+    assert set(got) == set(ref), (sorted(got), sorted(ref))
+    for k in ref:
+        _check(got[k], ref[k], f"d{k}")
