@@ -154,8 +154,12 @@ __device__ __forceinline__ void mfma_strip(f32x4 (&acc)[NC], const float* A, int
 template <typename T, int N, int MODE>
 __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
     constexpr int P = 64, LDN = N + 4;
-    __shared__ __attribute__((aligned(16))) float sW[kQ * LDN];
-    __shared__ __attribute__((aligned(16))) float sV[kQ * kLD];
+    // W [64][LDN] and V [64][kLD]; after the product the same memory stages the
+    // [N][kLD] result so it leaves in whole rows
+    static_assert(N * kLD <= kQ * LDN + kQ * kLD, "output staging fits");
+    __shared__ __attribute__((aligned(16))) float smem[kQ * LDN + kQ * kLD];
+    float* sW = smem;
+    float* sV = smem + kQ * LDN;
     __shared__ float s_coef[kQ];
     const int tid = threadIdx.x, nc = a.nc;
     const int c = blockIdx.x % nc;
@@ -216,17 +220,29 @@ __global__ __launch_bounds__(kBT) void ssd_bwd_sums_kernel(BwdArgs a) {
         constexpr int RS = N >= 64 ? N / 64 : 1;         // 16-row strips per wave
         const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, li = lane & 15;
         const int c0 = 16 * NC * (wave % (4 / NC));       // the first column (head channel p)
-        float* out = (mode == 0 ? a.S : a.dS) + (((size_t)b * a.H + h) * nc + c) * N * P;
+        f32x4 acc[RS][NC] = {};
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs) {
             const int r0 = 16 * ((wave * NC) / 4 * RS + rs);   // this strip's rows (state index n)
-            f32x4 acc[NC] = {};
-            mfma_strip<true, false, NC>(acc, sW, LDN, r0, sV, kLD, c0, kQ, q, li);
+            mfma_strip<true, false, NC>(acc[rs], sW, LDN, r0, sV, kLD, c0, kQ, q, li);
+        }
+        __syncthreads();                           // every wave is done reading W and V
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) {
+            const int r0 = 16 * ((wave * NC) / 4 * RS + rs);
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[(size_t)(r0 + 4 * q + e) * P + c0 + 16 * cc + li] = acc[cc][e];
+                for (int e = 0; e < 4; ++e) smem[(r0 + 4 * q + e) * kLD + c0 + 16 * cc + li] = acc[rs][cc][e];
         }
+    }
+    __syncthreads();
+    // the [N][64] result, contiguous in the workspace: 16 bytes per lane, whole rows per instruction
+    float* out = (mode == 0 ? a.S : a.dS) + (((size_t)b * a.H + h) * nc + c) * N * P;
+#pragma unroll
+    for (int u = 0; u < N * P / 4 / kBT; ++u) {
+        const int i4 = tid + u * kBT, n = i4 / (P / 4), p = 4 * (i4 % (P / 4));
+        *reinterpret_cast<f32x4*>(out + (size_t)n * P + p) = *reinterpret_cast<const f32x4*>(smem + n * kLD + p);
     }
 }
 
