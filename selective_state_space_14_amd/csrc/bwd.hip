@@ -414,7 +414,8 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             }
         }
     };
-    auto state_dot = [&]() __attribute__((always_inline)) {                       // <Gout, Hin> over the resident block, this thread's share
+    // <Gout, Hin> over the resident block: this thread's share
+    auto state_dot = [&]() __attribute__((always_inline)) {
         float v = 0.0f;
         for (int i = tid; i < NB * P; i += kCT) v = fmaf(sHin[(i / P) * kLD + i % P], sGo[(i / P) * kLD + i % P], v);
         return v;
