@@ -748,7 +748,7 @@ struct LdsBf {
     static constexpr int oDs = oZs + (ZR ? NW * ZW : 0);   // the heads' dt / doc ids (ZR)
     static constexpr int STAGE = oDs + (ZR ? DB : 0);
     // one head's M^T tiles as bf16 fragments: the high halves of the 10 tiles,
-    // then (MS) the low halves (M = hi + lo to ~2^-17 relative)
+    // then (MS) the low halves (M = hi + lo to 2^-16 relative)
     static constexpr int MB = (MS ? 2 : 1) * kNumMTiles * 512;
     static constexpr int oM = NS * STAGE;
     static constexpr int oZ1 = oM + HPW * MB;         // the waves' z tiles (!ZR)
