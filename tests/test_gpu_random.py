@@ -1,5 +1,5 @@
-"""GPU parity of ssd_chunk_scan_fwd and ssd_chunk_scan_bwd against the fp64 oracle over seeded random
-configurations: state sizes,
+"""GPU parity of ssd_chunk_scan_fwd, ssd_chunk_scan_bwd, ssd_mixer_fwd and ssd_s6_scan_fwd against the fp64
+oracle over seeded random configurations: state sizes,
 group layouts (heads per group 1, 2, 3, 4, 6, 8, so every workgroup plan the library picks), lengths from one
 token to several superchunks, documents, carried states, the gate, both dt forms, and the sequence split where
 the sizes take it.  Inputs reach both sides identically, so the bars are the per-call ones: fp32 1e-3 * RMS,
@@ -14,6 +14,8 @@ import synth
 from tests import helpers as hp
 from tests.test_gpu_bwd import DEV, _check, _np
 from tests.test_gpu_conv_scan import run_scan, small_wl, workspace
+from tests.test_gpu_mixer import check_oracle, inputs, mix_wl, run_mixer, run_two_call
+from tests.test_gpu_s6 import _check as s6_check, _docs, _oracle as s6_oracle, _run as s6_run, _wl as s6_wl
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +86,69 @@ def test_scan_bwd_random_config(gpu_lib, i, dtype, N, G, H, L, B, docs, h0, gate
     assert set(got) == set(ref), (sorted(got), sorted(ref))
     for k in ref:
         _check(got[k], ref[k], f"d{k}")
+
+
+def _mixer_configs(n, seed=7077):
+    r = random.Random(seed)
+    out = []
+    for i in range(n):
+        dtype = r.choice(["bf16", "bf16", "bf16", "f32"])
+        N = r.choice([16, 32, 64, 128])
+        G = r.choice([1, 2, 4])
+        H = G * r.choice([1, 2, 3, 4])
+        if dtype == "bf16" and H % 2:
+            H *= 2                    # bf16 dt_raw rows are read in 4-byte words: an even row stride
+        L = r.choice([1, 3, 64, 65, r.randint(4, 500), r.randint(500, 2400)])
+        B = r.choice([1, 2])
+        out.append((i, dtype, N, G, H, L, B, r.random() < 0.5, r.random() < 0.5, r.random() < 0.5,
+                    r.random() < 0.8, r.choice([0, 0, 1]), r.random() < 0.5))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,N,G,H,L,B,docs,cs,h0,gate,act,bias", _mixer_configs(16))
+def test_mixer_random_config(gpu_lib, i, dtype, N, G, H, L, B, docs, cs, h0, gate, act, bias):
+    """ssd_mixer_fwd in both plans (fp32: the staged one) bit-identical to ssd_conv_fwd + ssd_chunk_scan_fwd,
+    and call by call against the oracle (the conv within one bf16 ulp, the scan at the flat bar on the GPU
+    conv's output, the outgoing conv state exactly)."""
+    print(f"random mixer #{i}: {dtype} N={N} G={G} H={H} L={L} B={B} docs={docs} cs={cs} h0={h0} gate={gate} "
+          f"act={act} bias={bias}", flush=True)
+    wl = mix_wl(dtype, H, N, G, L, B=B, gate=gate)
+    prm, raw, ids, cs_in = inputs(wl, 400 + i, docs, cs, h0, bias, mean_len=float(max(2, L // 3)))
+    plans = ["staged"] if dtype == "f32" else ["fused", "staged"]
+    for plan in plans:
+        y, fs, co = run_mixer(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, plan=plan)
+        y2, fs2, co2 = run_two_call(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, plan=plan)
+        assert torch.equal(y, y2), hp.report(f"{plan}: mixer vs two-call y", y, y2)
+        assert torch.equal(fs, fs2), hp.report(f"{plan}: mixer vs two-call final_state", fs, fs2)
+        assert torch.equal(co, co2), f"{plan}: mixer vs two-call conv_state_out"
+    check_oracle(gpu_lib, wl, raw, prm, ids, cs_in, raw["h0"], act, y, fs, co)
+
+
+def _s6_configs(n, seed=9099):
+    r = random.Random(seed)
+    out = []
+    for i in range(n):
+        out.append((i, r.choice(["bf16", "f32"]), r.choice([1, 2, 3]),
+                    r.choice([1, 2, 63, 64, 65, r.randint(3, 700), r.randint(700, 2100)]),
+                    # channels: rows of 16-byte multiples (the call's stride rule), ragged workgroups included
+                    r.choice([8, 64, 248, 256, 264, 8 * r.randint(2, 90)]), r.choice([8, 16, 32]),
+                    r.random() < 0.5, r.random() < 0.5, r.random() < 0.7, r.random() < 0.7, r.random() < 0.5))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,B,L,Dn,N,docs,h0,gate,softplus,split", _s6_configs(20))
+def test_s6_random_config(gpu_lib, i, dtype, B, L, Dn, N, docs, h0, gate, softplus, split):
+    """ssd_s6_scan_fwd against the oracle's S6 routine: any channel count (ragged 256-channel workgroups),
+    N = 8 / 16 / 32, documents, carried state, gate, both dt forms, with and without the sequence split."""
+    print(f"random s6 #{i}: {dtype} B={B} L={L} D={Dn} N={N} docs={docs} h0={h0} gate={gate} softplus={softplus} "
+          f"split={split}", flush=True)
+    wl = s6_wl(dtype, B, L, Dn, N, h0=h0, gate=gate)
+    prm = synth.s6_params(wl, 500 + i)
+    inp = synth.s6_inputs(wl, 500 + i)
+    if not softplus:
+        inp["dt_raw"] = torch.nn.functional.softplus(inp["dt_raw"].float() - 2.5).to(inp["dt_raw"].dtype)
+    ids = _docs(wl, 600 + i, L, float(max(2, L // 3))) if docs else None
+    y, fs = s6_run(gpu_lib, inp, prm, softplus=softplus, gate=gate, docs=ids, h0=inp["h0"], split=split)
+    yr, fr = s6_oracle(inp, prm, softplus=softplus, gate=gate, docs=ids, h0=inp["h0"])
+    s6_check(dtype, y, yr, "y")
+    s6_check(dtype, fs, fr, "final_state")
