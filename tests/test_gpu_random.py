@@ -1,11 +1,13 @@
-"""GPU parity of ssd_chunk_scan_fwd, ssd_chunk_scan_bwd, ssd_mixer_fwd and ssd_s6_scan_fwd against the fp64
-oracle over seeded random configurations: state sizes,
+"""GPU parity of ssd_chunk_scan_fwd, ssd_chunk_scan_bwd, ssd_mixer_fwd, ssd_s6_scan_fwd and the two decode
+calls (ssd_step against the oracle, ssd_resume_fwd bit for bit against the forward) over seeded random
+configurations: state sizes,
 group layouts (heads per group 1, 2, 3, 4, 6, 8, so every workgroup plan the library picks), lengths from one
 token to several superchunks, documents, carried states, the gate, both dt forms, and the sequence split where
 the sizes take it.  Inputs reach both sides identically, so the bars are the per-call ones: fp32 1e-3 * RMS,
 bf16 0.03125 absolute, the backward 1e-3 * RMS per gradient; the split result is held to the same bars."""
 import random
 
+import numpy as np
 import pytest
 import torch
 
@@ -15,7 +17,9 @@ from tests import helpers as hp
 from tests.test_gpu_bwd import DEV, _check, _np
 from tests.test_gpu_conv_scan import run_scan, small_wl, workspace
 from tests.test_gpu_mixer import check_oracle, inputs, mix_wl, run_mixer, run_two_call
+from tests.test_gpu_resume import Resumer, forward as resume_forward, setup as resume_setup
 from tests.test_gpu_s6 import _check as s6_check, _docs, _oracle as s6_oracle, _run as s6_run, _wl as s6_wl
+from tests.test_gpu_step import decode_run, oracle_single_pass
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +156,69 @@ def test_s6_random_config(gpu_lib, i, dtype, B, L, Dn, N, docs, h0, gate, softpl
     yr, fr = s6_oracle(inp, prm, softplus=softplus, gate=gate, docs=ids, h0=inp["h0"])
     s6_check(dtype, y, yr, "y")
     s6_check(dtype, fs, fr, "final_state")
+
+
+def _decode_configs(n, seed=1312):
+    r = random.Random(seed)
+    out = []
+    for i in range(n):
+        dtype = r.choice(["bf16", "f32"])
+        N = r.choice([16, 32, 64, 128])
+        G = r.choice([1, 2])
+        H = G * r.choice([1, 2, 3, 4])
+        if dtype == "bf16" and H % 2:
+            H *= 2
+        out.append((i, dtype, N, G, H, 64 * r.randint(1, 4), r.randint(20, 140), r.choice([1, 2, 3])))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,N,G,H,L0,steps,B", _decode_configs(12))
+def test_resume_random_config(gpu_lib, i, dtype, N, G, H, L0, steps, B):
+    """ssd_resume_fwd after a prefill of L0 tokens, appending random runs of tokens (crossing chunk ends): every
+    output equals the one-call forward over the whole sequence bit for bit, and so does the state at every chunk
+    end."""
+    print(f"random resume #{i}: {dtype} N={N} G={G} H={H} prefill={L0} steps={steps} B={B}", flush=True)
+    wl = synth.Workload("rresume_" + dtype, B, L0, H, 64, N, G, dtype)
+    prm, raw, h0 = resume_setup(wl, 700 + i, L0 + steps, h0=i % 2 == 0)
+    y_ref, _, _ = resume_forward(gpu_lib, wl, raw, prm, L0 + steps, h0=h0)
+    _, fs, cs = resume_forward(gpu_lib, wl, raw, prm, L0, h0=h0)
+    rs = Resumer(gpu_lib, wl, prm, B, fs, cs)
+    r = random.Random(800 + i)
+    ys, t = [], L0
+    while t < L0 + steps:
+        n = min(r.choice([1, 1, 1, 2, 5, 17]), 64 - rs.pos, L0 + steps - t)
+        ys.append(rs.append(raw, t, n))
+        t += n
+        if rs.pos == 0:
+            _, f_at, _ = resume_forward(gpu_lib, wl, raw, prm, t, h0=h0)
+            assert torch.equal(rs.state, f_at), f"state after the chunk ending at token {t}"
+    torch.cuda.synchronize()
+    y = torch.cat(ys, 1)
+    assert torch.equal(y, y_ref[:, L0:]), hp.report("resumed y vs one forward", y, y_ref[:, L0:])
+
+
+def r_off(i):
+    """A ragged prefill length for the step tests (the step itself needs no chunk alignment)."""
+    return (37 * i) % 64
+
+
+@pytest.mark.parametrize("i,dtype,N,G,H,L0,steps,B", _decode_configs(12, seed=2626))
+def test_step_random_config(gpu_lib, i, dtype, N, G, H, L0, steps, B):
+    """ssd_step after a GPU prefill, against the oracle's single pass over prefill and steps (fp32: 1e-3 * RMS;
+    bf16: the conv -> scan pipeline bound), the conv state exactly."""
+    print(f"random step #{i}: {dtype} N={N} G={G} H={H} prefill={L0} steps={steps} B={B}", flush=True)
+    L = L0 + r_off(i)
+    wl = synth.Workload("rstep_" + dtype, B, L, H, 64, N, G, dtype, steps=steps)
+    prm = synth.params(wl, 900 + i, conv_bias=i % 2 == 1)
+    raw = synth.raw_inputs(wl, 900 + i)
+    y, ys, fs, cs = decode_run(gpu_lib, wl, prm, raw, steps, 900 + i, "cpu")
+    yr, fr, cr, xr, _ = oracle_single_pass(wl, prm, raw, steps, 900 + i, list(range(B)), "cpu")
+    yall = torch.cat([y.cpu()] + [s.cpu()[:, None] for s in ys], 1)
+    if dtype == "f32":
+        hp.assert_fp32(yall, yr, "prefill ++ decode y")
+        hp.assert_fp32(fs, fr, "ssm state")
+    else:
+        z = torch.cat([raw["z"]] + [synth.step_inputs(wl, s, 900 + i)["z"][:, None] for s in range(steps)], 1)
+        hp.assert_pipeline(yall, yr, xr[..., :H * 64], z, prm["D"], H, 64, "prefill ++ decode y")
+        hp.assert_bf16(fs, fr, "ssm state")
+    np.testing.assert_array_equal(hp.np64(cs), cr)
