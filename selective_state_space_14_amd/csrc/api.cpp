@@ -514,6 +514,7 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
     a.init_state = chunk_state; a.final_state = pos + n == 64 ? chunk_state : nullptr;
     a.y = chunk_y; a.y_stride = HP;
     a.K = 1; a.S = 64;
+    a.y_row0 = pos;   // rows before pos were output by earlier calls
     e = ssd::launch_scan(a, s);
     if (e != hipSuccess) return hip_status(fn, e);
     // 4. the new tokens' outputs

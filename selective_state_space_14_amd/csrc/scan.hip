@@ -385,6 +385,11 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             load_bc(t0 + Q, regs);
             if (!FULL) load_xz(t0 + Q, regs);
         }
+        // kFull: the first token tile whose rows need output (rows before
+        // y_row0 need none), and whether this chunk's state is still needed:
+        // by a later chunk, or as the final state
+        const int T0 = FULL ? min(max(a.y_row0 - t0, 0), Q) / 16 : 0;
+        const bool need_state = !FULL || c + 1 < nchunks || (a.final_state && k == a.K - 1);
 
         if (FULL) {
             // ---- G^T tiles (this wave's share of the lower triangle), each turned
@@ -392,6 +397,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             for (int kt = wave; kt < kNumMTiles; kt += NW) {
                 int si, ti;
                 mtile(kt, si, ti);
+                if (ti < T0) continue;                    // feeds only rows that need no output
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nb = 0; nb < NT; nb += 2) {
@@ -431,6 +437,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             // ---- per token tile: Ydiag^T = X^T M^T, Yoff^T = H^T C^T, then the output
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
+                if (ti < T0) continue;
                 f32x4 yd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sb = 0; sb <= ti; sb += 2) {
@@ -470,14 +477,17 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             }
             // ---- w o X over this wave's own X columns (only this wave reads them,
             // and its LDS operations are performed in order)
+            if (need_state) {
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const int t = 16 * ti + j16;
-                const float w = sWw[t];
-                pst4(sX, cX, t * kXS + p0 + 4 * q4, w * xv[ti].x, w * xv[ti].y, w * xv[ti].z, w * xv[ti].w);
+                for (int ti = 0; ti < 4; ++ti) {
+                    const int t = 16 * ti + j16;
+                    const float w = sWw[t];
+                    pst4(sX, cX, t * kXS + p0 + 4 * q4, w * xv[ti].x, w * xv[ti].y, w * xv[ti].z, w * xv[ti].w);
+                }
             }
             if (c + 1 < nchunks) load_xz(t0 + Q, regs);
         }
+        if (!need_state) continue;   // the last chunk, no final state wanted: its state goes nowhere
 
         // ---- chunk state S = B^T (w o X): lane holds S[n = 16nt + 4q4 + r][p0 + j16],
         // then the state passing, strictly in chunk order.  B^T comes from the

@@ -52,6 +52,10 @@ struct ScanArgs {
     const float* conv_w; const float* conv_b;
     const void* cstate_in; void* cstate_out;   // [B][3][conv_dim]
     const uint16_t* dt16; int64_t dt16_stride;
+    // fp32 kernel: rows before y_row0 need no output (chunk-resume decode
+    // reruns the working chunk for its newest rows only); their y is left as
+    // it was.  0 for every public scan call.
+    int y_row0;
 };
 
 struct StepArgs {
