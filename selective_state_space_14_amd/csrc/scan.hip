@@ -813,13 +813,18 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int hh = wave >> 2;                  // head of this wave within the workgroup
     const int h = hq * HPW + hh;
     const int g = (hq * HPW) / (H / G);
-    const bool lead = (wave & 3) == 0;         // computes its head's per-token scalars
+    // Lead waves: wave e < HPW computes the per-token scalars of head e.  They
+    // are the first wave of each SIMD, which the SIMD's issue arbitration
+    // favours, so the scalar work starts as soon as the chunk's inputs land.
+    const bool lead = wave < HPW;
+    const int lh = lead ? wave : hh;           // the head whose scalars a lead wave computes
+    const int h_l = hq * HPW + lh;
     const int q4 = lane >> 4;
     const int j16 = lane & 15;
     const int p0 = (wave & 3) * 16;
-    const float A2 = a.A[h] * kLog2e;
+    const float A2l = a.A[h_l] * kLog2e;
     const float Dh = a.D ? a.D[h] : 0.0f;
-    const float dtb = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h] : 0.0f;
+    const float dtbl = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h_l] : 0.0f;
     const int tbeg = k * a.S;
     const int tend = min(tbeg + a.S, L);
     const int tl = tend - 1;
@@ -834,8 +839,8 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * a.Lb * a.B_stride + (size_t)g * N;
     const uint16_t* Cbase = static_cast<const uint16_t*>(a.Cm) + (size_t)b * a.Lb * a.C_stride + (size_t)g * N;
     // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
-    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h & ~1))
-                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h);
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h_l & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h_l);
     const int32_t* docbase = a.doc + (size_t)b * a.Lb;
     float* ybase = a.y + (size_t)b * a.Lb * a.y_stride + h * 64;
     const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
@@ -846,7 +851,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         return ZR ? smem + st * LD::STAGE + LD::oZs + wave * LD::ZW : smem + LD::oZ1 + wave * LD::ZW;
     };
     auto dbuf = [&](int st) {
-        return (ZR ? smem + st * LD::STAGE + LD::oDs : smem + LD::oD1) + hh * 3 * Q * 4;
+        return (ZR ? smem + st * LD::STAGE + LD::oDs : smem + LD::oD1) + lh * 3 * Q * 4;
     };
 
     // Copy slots of this wave: slot j is copy instruction wave + NW j of the
@@ -1121,14 +1126,14 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             if (!ZR && more) issue_scalars(t0 + Q, 0);     // refilled right after it is read
             if (CV) {
                 const uint32_t wd = __float_as_uint(dtl);
-                dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                dtl = (h_l & 1) ? bf16_hi(wd) : bf16_lo(wd);
             }
-            if (SP) dtl = softplus_f(dtl + dtb);
+            if (SP) dtl = softplus_f(dtl + dtbl);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
             if (CV) {
                 const uint64_t m = __ballot(bnd);
-                if (hh == 0 && lane == 0) {
+                if (lh == 0 && lane == 0) {
                     int* sci = reinterpret_cast<int*>(sc);
                     sci[LD::SC_ST] = (int)(uint32_t)m;
                     sci[LD::SC_ST + 1] = (int)(uint32_t)(m >> 32);
@@ -1136,20 +1141,21 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                 }
                 pbits = (int)(m >> 63) | (int)((m >> 61) & 2);   // for the next chunk
             }
-            float cs = dtl * A2;
+            float cs = dtl * A2l;
             int seg = bnd ? lane : -1;
             wave_segscan(cs, bnd, seg);
             const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
             const int last_seg = __builtin_amdgcn_readlane(seg, 63);
             const int wseg = last_seg >= 0 ? last_seg : 0;
-            sch[lane] = cs;
-            sch[Q + lane] = dtl;
-            sch[2 * Q + lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
-            sch[3 * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
-            if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_SEG + lane] = seg < 0 ? 0 : seg;
+            float* schl = sc + lh * 4 * Q;         // head lh's cs, dt, eo, w
+            schl[lane] = cs;
+            schl[Q + lane] = dtl;
+            schl[2 * Q + lane] = seg < 0 ? fast_exp2(cs) : 0.0f;
+            schl[3 * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
+            if (lh == 0) reinterpret_cast<int*>(sc)[LD::SC_SEG + lane] = seg < 0 ? 0 : seg;
             if (lane == 0) {
-                sc[LD::SC_END + hh] = cs_end;
-                if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
+                sc[LD::SC_END + lh] = cs_end;
+                if (lh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
             }
         }
         lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
@@ -1425,12 +1431,16 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     const int hh = wave / WPH;                 // head of this wave within the workgroup
     const int h = hq * HPW + hh;
     const int g = (hq * HPW) / (H / G);
-    const bool lead = wave % WPH == 0;         // computes its head's per-token weights
+    // Lead waves: wave e < HPW computes the per-token weights of head e (the
+    // first wave of each SIMD, which its issue arbitration favours).
+    const bool lead = wave < HPW;
+    const int lh = lead ? wave : hh;           // the head whose weights a lead wave computes
+    const int h_l = hq * HPW + lh;
     const int q4 = lane >> 4;
     const int j16 = lane & 15;
     const int p0 = (wave % WPH) * 16 * PB;     // first channel of this wave's blocks
-    const float A2 = a.A[h] * kLog2e;
-    const float dtb = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h] : 0.0f;
+    const float A2l = a.A[h_l] * kLog2e;
+    const float dtbl = (a.dt_softplus && a.dt_bias) ? a.dt_bias[h_l] : 0.0f;
     const int tbeg = k * a.S;
     const int tend = min(tbeg + a.S, L);
     const int tl = tend - 1;
@@ -1439,8 +1449,8 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     const uint16_t* xhead = static_cast<const uint16_t*>(a.x) + (size_t)b * a.Lb * a.x_stride + (size_t)hq * HPW * 64;
     const uint16_t* Bbase = static_cast<const uint16_t*>(a.Bm) + (size_t)b * a.Lb * a.B_stride + (size_t)g * N;
     // dt: fp32, or (CV) the raw bf16 dt, read as the 4-byte word holding heads h & ~1 and h | 1
-    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h & ~1))
-                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h);
+    const void* dtbase = CV ? static_cast<const void*>(a.dt16 + (size_t)b * a.Lb * a.dt16_stride + (h_l & ~1))
+                            : static_cast<const void*>(a.dt + (size_t)b * a.Lb * a.dt_stride + h_l);
     const int32_t* docbase = a.doc + (size_t)b * a.Lb;
     const int Ds4 = CV ? (int)a.dt16_stride * 2 : (int)a.dt_stride * 4;
 
@@ -1486,7 +1496,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             }
         }
     };
-    auto dbuf_of = [&](int st) -> unsigned char* { return smem + st * LD::STAGE + LD::oD + hh * 3 * Q * 4; };
+    auto dbuf_of = [&](int st) -> unsigned char* { return smem + st * LD::STAGE + LD::oD + lh * 3 * Q * 4; };
     auto issue_scalars = [&](int t0, int st) {
         unsigned char* dbuf = dbuf_of(st);
         const int rowl = min(lane, tl - t0);
@@ -1599,14 +1609,14 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             if (cn < nchunks) issue_scalars(t0 + (NS - 1) * Q, sn);
             if (CV) {
                 const uint32_t wd = __float_as_uint(dtl);
-                dtl = (h & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                dtl = (h_l & 1) ? bf16_hi(wd) : bf16_lo(wd);
             }
-            if (SP) dtl = softplus_f(dtl + dtb);
+            if (SP) dtl = softplus_f(dtl + dtbl);
             if (!tok_ok) dtl = 0.0f;
             const int bnd = (docs && tok_ok && t0 + lane > 0 && d0 != d1) ? 1 : 0;
             if (CV) {
                 const uint64_t m = __ballot(bnd);
-                if (hh == 0 && lane == 0) {
+                if (lh == 0 && lane == 0) {
                     int* sci = reinterpret_cast<int*>(sc);
                     sci[LD::SC_ST] = (int)(uint32_t)m;
                     sci[LD::SC_ST + 1] = (int)(uint32_t)(m >> 32);
@@ -1614,16 +1624,16 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
                 }
                 pbits = (int)(m >> 63) | (int)((m >> 61) & 2);   // for the next chunk
             }
-            float cs = dtl * A2;
+            float cs = dtl * A2l;
             int seg = bnd ? lane : -1;
             wave_segscan(cs, bnd, seg);
             const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
             const int last_seg = __builtin_amdgcn_readlane(seg, 63);
             const int wseg = last_seg >= 0 ? last_seg : 0;
-            sc[hh * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
+            sc[lh * Q + lane] = lane >= wseg ? fast_exp2(cs_end - cs) * dtl : 0.0f;
             if (lane == 0) {
-                sc[LD::SC_END + hh] = cs_end;
-                if (hh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
+                sc[LD::SC_END + lh] = cs_end;
+                if (lh == 0) reinterpret_cast<int*>(sc)[LD::SC_LAST] = last_seg;
             }
         }
         lds_barrier();                   // chunk c tiles + weights visible; chunk c-1 readers done
@@ -1710,7 +1720,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             *reinterpret_cast<float4*>(hl + 16 * nt) =
                 make_float4(Hs[pb][nt][0], Hs[pb][nt][1], Hs[pb][nt][2], Hs[pb][nt][3]);
     }
-    if (lead && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);
+    if (wave % WPH == 0 && lane == 0) a.dec[u] = reset ? -1.0f : fast_exp2(log2dec);   // the head's first wave
     if (k == 0 && a.h0) {
         // the main pass reads this copy instead of init_state
 #pragma unroll
