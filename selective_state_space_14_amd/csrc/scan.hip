@@ -68,17 +68,17 @@ template <> struct Tr<float> {             // fp32 storage (register side of the
 };
 
 // Tiles of the lower triangle, dealt round-robin to the waves: tile k -> (si, ti).
-// Order: diagonal tiles first, then (0,1) (0,2) (0,3) (1,2) (1,3) (2,3); the
-// table lives in two immediates (4 bits per tile) so no memory is touched.
+// Order: by token tile ti, then si -- (0,0) (0,1) (1,1) (0,2) (1,2) (2,2) (0,3)
+// (1,3) (2,3) (3,3) -- so the two tiles (sb, ti), (sb+1, ti) an output tile
+// reads together sit next to each other.  The table lives in two immediates
+// (4 bits per tile) so no memory is touched.
 __device__ __forceinline__ void mtile(int k, int& si, int& ti) {
-    constexpr unsigned long long kS = 0x2110003210ull;   // si of tile k in nibble k
-    constexpr unsigned long long kT = 0x3323213210ull;   // ti of tile k in nibble k
+    constexpr unsigned long long kS = 0x3210210100ull;   // si of tile k in nibble k
+    constexpr unsigned long long kT = 0x3333222110ull;   // ti of tile k in nibble k
     si = (int)((kS >> (4 * k)) & 0xF);
     ti = (int)((kT >> (4 * k)) & 0xF);
 }
-__device__ __forceinline__ int mtile_index(int si, int ti) {
-    return si == ti ? si : (si == 0 ? 3 + ti : (si == 1 ? 5 + ti : 9));
-}
+__device__ __forceinline__ int mtile_index(int si, int ti) { return ti * (ti + 1) / 2 + si; }
 
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that a
 // contiguous range of (b, h) -- heads of the same group, which share B and C
@@ -460,17 +460,12 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
                 // lane holds y[t = 16ti + j16][p = p0 + 4q4 + r]
                 const int t = 16 * ti + j16;
                 const float eo = sEo[t];
-                float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-                if (gate) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) gz[r] = silu_f((&zv[ti].x)[r]);
-                }
                 float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = fmaf(eo, yo[r], yd[r]);
-                    v = fmaf(Dh, (&xv[ti].x)[r], v);
-                    o[r] = v * gz[r];
+                for (int r = 0; r < 4; ++r) o[r] = fmaf(Dh, (&xv[ti].x)[r], fmaf(eo, yo[r], yd[r]));
+                if (gate) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] *= silu_f((&zv[ti].x)[r]);
                 }
                 if (!tail || t0 + t < tend)
                     *reinterpret_cast<float4*>(yg + (size_t)(t0 + t) * a.y_stride) = make_float4(o[0], o[1], o[2], o[3]);
@@ -1270,16 +1265,13 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                     const FragBF a0 = tr_read(sX, xtr + 16 * sb * XB);
                     const int m0 = mtile_index(sb, ti) * 512 + lane * 8;
                     const FragBF b0 = plain_read(sMh + m0);
-                    FragBF a1 = {0u, 0u}, b1 = {0u, 0u};
-                    if (sb + 1 <= ti) {
-                        a1 = tr_read(sX, xtr + 16 * (sb + 1) * XB);
-                        b1 = plain_read(sMh + mtile_index(sb + 1, ti) * 512 + lane * 8);
-                    }
+                    // the tile pair (sb, ti), (sb+1, ti) is adjacent (mtile_index)
+                    const bool two = sb + 1 <= ti;
+                    const FragBF a1 = two ? tr_read(sX, xtr + 16 * (sb + 1) * XB) : FragBF{0u, 0u};
+                    const FragBF b1 = two ? plain_read(sMh + m0 + 512) : FragBF{0u, 0u};
                     if constexpr (MS) {
                         const FragBF l0 = plain_read(sMh + kNumMTiles * 512 + m0);
-                        const FragBF l1 = sb + 1 <= ti
-                                              ? plain_read(sMh + (kNumMTiles + mtile_index(sb + 1, ti)) * 512 + lane * 8)
-                                              : FragBF{0u, 0u};
+                        const FragBF l1 = two ? plain_read(sMh + kNumMTiles * 512 + m0 + 512) : FragBF{0u, 0u};
                         yd = mma_bf16(yd, a0, a1, l0, l1);
                     }
                     yd = mma_bf16(yd, a0, a1, b0, b1);
@@ -1299,21 +1291,18 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                 const float eo = sch[2 * Q + t];
                 const uint2 xr = *reinterpret_cast<const uint2*>(sX + SX::off(t, p0 + 4 * q4));
                 const float xs[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
-                // the gate factors silu(z) of the lane's 4 outputs (1 without a gate)
-                float gz[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-                if (gate) {
-                    gz[0] = silu_f(bf16_lo(zr[ti].x));
-                    gz[1] = silu_f(bf16_hi(zr[ti].x));
-                    gz[2] = silu_f(bf16_lo(zr[ti].y));
-                    gz[3] = silu_f(bf16_hi(zr[ti].y));
-                }
-                u32x4_t o;
+                float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = fmaf(eo, yo[r], yd[r]);
-                    v = fmaf(Dh, xs[r], v);
-                    o[r] = __float_as_uint(v * gz[r]);
+                for (int r = 0; r < 4; ++r) v[r] = fmaf(Dh, xs[r], fmaf(eo, yo[r], yd[r]));
+                // the gate factors silu(z) of the lane's 4 outputs
+                if (gate) {
+                    v[0] *= silu_f(bf16_lo(zr[ti].x));
+                    v[1] *= silu_f(bf16_hi(zr[ti].x));
+                    v[2] *= silu_f(bf16_lo(zr[ti].y));
+                    v[3] *= silu_f(bf16_hi(zr[ti].y));
                 }
+                const u32x4_t o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                   __float_as_uint(v[3])};
                 // rows past the unit's end fall outside the buffer range and are dropped
                 __builtin_amdgcn_raw_buffer_store_b128(o, yr, (uint32_t)(t * Ys + p0 + 4 * q4) * 4, 0, 0);
             }
