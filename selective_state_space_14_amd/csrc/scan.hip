@@ -891,17 +891,19 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
     const int n_tiles = (LD::NI - wave + NW - 1) / NW;
     const int n_scal = lead ? (docs ? 3 : 1) : 0;
     // B, C, X copies of the chunk at t0 into stage st; rows clamp to the unit's end
-    auto issue_tiles = [&](int t0, int st) {
+    // (slots j0 .. j1-1 of them)
+    auto issue_tiles = [&](int t0, int st, int j0 = 0, int j1 = LD::NI_W) {
         const int lim = tl - t0;
         unsigned char* base = smem + st * LD::STAGE;
         if (lim >= Q - 1) {          // every row inside the unit: the precomputed offsets
 #pragma unroll
             for (int j = 0; j < LD::NI_W; ++j)
-                if (kAllOn || s_on[j]) dma16(s_base[j] + (size_t)t0 * s_stride[j], s_off[j], base + s_lds[j]);
+                if (j >= j0 && j < j1 && (kAllOn || s_on[j]))
+                    dma16(s_base[j] + (size_t)t0 * s_stride[j], s_off[j], base + s_lds[j]);
         } else {
 #pragma unroll
             for (int j = 0; j < LD::NI_W; ++j)
-                if (kAllOn || s_on[j])
+                if (j >= j0 && j < j1 && (kAllOn || s_on[j]))
                     dma16(s_base[j] + (size_t)t0 * s_stride[j], (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j],
                           base + s_lds[j]);
         }
@@ -937,6 +939,20 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             issue_z(t0, st);
         } else {
             issue_tiles(t0, st);
+        }
+    };
+    // The same operations in two parts (part 0: dt / doc ids and the first half
+    // of the tile copies; part 1: the rest and z), issued at two points of the
+    // chunk loop: all waves issuing a chunk's copies at once would queue behind
+    // one another in the CU's memory pipeline before their own compute.
+    constexpr int kHalf = (LD::NI_W + 1) / 2;
+    auto issue_chunk_part = [&](int t0, int st, int part) {
+        if (part == 0) {
+            if (ZR && lead) issue_scalars(t0, st);
+            issue_tiles(t0, st, 0, kHalf);
+        } else {
+            issue_tiles(t0, st, kHalf, LD::NI_W);
+            if constexpr (ZR) issue_z(t0, st);
         }
     };
 
@@ -1154,8 +1170,11 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
             }
         }
         lds_barrier();                   // A: chunk c tiles + scalars visible; chunk c-1 readers done
-        // refill the stage chunk c-1 used with chunk c + NS - 1
-        if (c + NS - 1 < nchunks) issue_chunk(t0 + (NS - 1) * Q, (c + NS - 1) % NS);
+        // refill the stage chunk c-1 used with chunk c + NS - 1: part 0 now, part 1
+        // after this wave's first G^T product (or its tile loop)
+        const bool refill = c + NS - 1 < nchunks;
+        bool refill1 = refill;
+        if (refill) issue_chunk_part(t0 + (NS - 1) * Q, (c + NS - 1) % NS, 0);
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
@@ -1207,6 +1226,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                     }
                     acc = mma_bf16(acc, a0, a1, b0, b1);
                 }
+                if (refill1) {
+                    issue_chunk_part(t0 + (NS - 1) * Q, (c + NS - 1) % NS, 1);
+                    refill1 = false;
+                }
                 const int t = 16 * ti + j16;
                 const int segt = reinterpret_cast<const int*>(sc)[LD::SC_SEG + t];
                 bool ok[4];
@@ -1235,6 +1258,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
                     }
                 }
             }
+            if (refill1) issue_chunk_part(t0 + (NS - 1) * Q, (c + NS - 1) % NS, 1);   // a wave without tiles
             FragBF hf[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) hf[nt] = frag_from_f32(Hs[nt]);
