@@ -1498,12 +1498,13 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     }
     const int n_tiles = (LD::NI - wave + NW - 1) / NW;
     const int n_scal = lead ? (docs ? 3 : 1) : 0;
-    auto issue_tiles = [&](int t0, int st) {
+    // (slots j0 .. j1-1 of them)
+    auto issue_tiles = [&](int t0, int st, int j0, int j1) {
         const int lim = tl - t0;
         unsigned char* base = smem + st * LD::STAGE;
 #pragma unroll
         for (int j = 0; j < LD::NI_W; ++j) {
-            if (s_on[j]) {
+            if (j >= j0 && j < j1 && s_on[j]) {
                 const char* src = s_base[j] + (size_t)t0 * s_stride[j];
                 dma16(src, (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j], base + s_lds[j]);
             }
@@ -1594,7 +1595,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     for (int j = 0; j < NS - 1; ++j) {
         if (j < nchunks) {
             if (lead) issue_scalars(tbeg + j * Q, j);
-            issue_tiles(tbeg + j * Q, j);
+            issue_tiles(tbeg + j * Q, j, 0, LD::NI_W);
         }
     }
 
@@ -1650,7 +1651,11 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             }
         }
         lds_barrier();                   // chunk c tiles + weights visible; chunk c-1 readers done
-        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn);
+        // chunk cn's copies in two halves, the second after this wave's (w o X)
+        // fragments: all waves issuing them at once would queue behind one
+        // another in the CU's memory pipeline before their own compute
+        constexpr int kHalfP = (LD::NI_W + 1) / 2;
+        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn, 0, kHalfP);
         const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc[LD::SC_END + hh])));
         const int last_seg = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(sc)[LD::SC_LAST]);
         const bool has_bnd = last_seg >= 0;
@@ -1700,6 +1705,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
                 xw[pb][sb].b = pack_bf16x2(w.z * bf16_lo(xf.b), w.w * bf16_hi(xf.b));
             }
         }
+        if (cn < nchunks) issue_tiles(t0 + (NS - 1) * Q, sn, kHalfP, LD::NI_W);
         // ---- S = B^T (w o X) per block; H = dec H + S (dec = 0 past a document start)
         const float dec = has_bnd ? 0.0f : fast_exp2(cs_end);
 #pragma unroll
