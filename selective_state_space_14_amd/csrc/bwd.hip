@@ -372,6 +372,11 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     constexpr int NU = kQ * NB / kCT;
     constexpr int NS4 = (NB * P / 4 + kCT - 1) / kCT;
     auto stage = [&](size_t bhc, int k, bool bc, bool st) __attribute__((always_inline)) {
+        // the thread index, opaque to the compiler: the addresses below are
+        // rebuilt at every call instead of being hoisted out of the head loop
+        // and held in registers across it (which made the N = 128 kernel spill)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
         float bv[NU], cv[NU];
         f32x4 hv[NS4], ov[NS4];
         if (bc) {
@@ -446,7 +451,9 @@ __global__ __launch_bounds__(kCT, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         if (wave == 0) {
             float dtv, chain, cs;
             int seg;
-            chunk_rows(a, b, h, t0, Qv, lane, dtv, chain, cs, seg);
+            int ln = lane;                         // opaque, as in stage(): the row pointers are per head
+            asm volatile("" : "+v"(ln));
+            chunk_rows(a, b, h, t0, Qv, ln, dtv, chain, cs, seg);
             s_dt[lane] = dtv;
             s_cs[lane] = cs;
             s_seg[lane] = seg;
