@@ -691,11 +691,13 @@ __device__ __forceinline__ uint32_t conv_off(const ConvWord& w, int r) {
 // v2, v1: the raw words of rows r0-3 .. r0-1, already cut at document
 // starts before r0; smask bit r: row r starts a document (the history is
 // zeroed before it).  Rows are independent given the raw history, so they are
-// read four at a time ahead of the arithmetic.
-template <int RBU>
-__device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw, int r0, int r1, uint64_t smask,
-                                          uint32_t v3, uint32_t v2, uint32_t v1, const float (&w)[2][4],
-                                          const float (&cb)[2], bool silu) {
+// read four at a time ahead of the arithmetic.  DOCS: some row of [r0, r1)
+// starts a document (else the per-row test is left out); SILU: the
+// activation (else the identity).
+template <int RBU, bool DOCS, bool SILU>
+__device__ __forceinline__ void conv_rows_t(unsigned char* stg, const ConvWord& cw, int r0, int r1, uint64_t smask,
+                                            uint32_t v3, uint32_t v2, uint32_t v1, const float (&w)[2][4],
+                                            const float (&cb)[2]) {
     float h3[2] = {bf16_lo(v3), bf16_hi(v3)}, h2[2] = {bf16_lo(v2), bf16_hi(v2)},
           h1[2] = {bf16_lo(v1), bf16_hi(v1)};
 #pragma unroll 1
@@ -707,7 +709,7 @@ __device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (r + u < r1) {
-                if ((smask >> (r + u)) & 1) {
+                if (DOCS && ((smask >> (r + u)) & 1)) {
                     h3[0] = h3[1] = h2[0] = h2[1] = h1[0] = h1[1] = 0.0f;
                 }
                 const float c[2] = {bf16_lo(cur[u]), bf16_hi(cur[u])};
@@ -719,7 +721,7 @@ __device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw
                     v = fmaf(w[e][1], h2[e], v);
                     v = fmaf(w[e][2], h1[e], v);
                     v = fmaf(w[e][3], c[e], v);
-                    o[e] = silu ? silu_f(v) : v;
+                    o[e] = SILU ? silu_f(v) : v;
                     h3[e] = h2[e];
                     h2[e] = h1[e];
                     h1[e] = c[e];
@@ -727,6 +729,22 @@ __device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw
                 *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r + u)) = pack_bf16x2(o[0], o[1]);
             }
         }
+    }
+}
+// The row loop specialised on the (wave-uniform) document starts among its
+// rows and the activation, so neither costs a select per row.
+template <int RBU>
+__device__ __forceinline__ void conv_rows(unsigned char* stg, const ConvWord& cw, int r0, int r1, uint64_t smask,
+                                          uint32_t v3, uint32_t v2, uint32_t v1, const float (&w)[2][4],
+                                          const float (&cb)[2], bool silu) {
+    const int n = r1 - r0;
+    const uint64_t rows = n >= 64 ? ~0ull : ((1ull << n) - 1) << r0;
+    if (smask & rows) {
+        if (silu) conv_rows_t<RBU, true, true>(stg, cw, r0, r1, smask, v3, v2, v1, w, cb);
+        else conv_rows_t<RBU, true, false>(stg, cw, r0, r1, smask, v3, v2, v1, w, cb);
+    } else {
+        if (silu) conv_rows_t<RBU, false, true>(stg, cw, r0, r1, smask, v3, v2, v1, w, cb);
+        else conv_rows_t<RBU, false, false>(stg, cw, r0, r1, smask, v3, v2, v1, w, cb);
     }
 }
 
