@@ -690,9 +690,10 @@ __device__ __forceinline__ uint32_t conv_off(const ConvWord& w, int r) {
 // The in-place conv of one lane's word over rows [r0, r1) of a stage.  v3,
 // v2, v1: the raw words of rows r0-3 .. r0-1, already cut at document
 // starts before r0; smask bit r: row r starts a document (the history is
-// zeroed before it).  Rows are independent given the raw history, so they are
-// read four at a time ahead of the arithmetic.  DOCS: some row of [r0, r1)
-// starts a document (else the per-row test is left out); SILU: the
+// zeroed before it).  Rows are independent given the raw history, so whole
+// groups of four are read ahead of their arithmetic, with no per-row bound
+// test; the last r1 - r0 mod 4 rows go one at a time.  DOCS: some row of
+// [r0, r1) starts a document (else the per-row test is left out); SILU: the
 // activation (else the identity).
 template <int RBU, bool DOCS, bool SILU>
 __device__ __forceinline__ void conv_rows_t(unsigned char* stg, const ConvWord& cw, int r0, int r1, uint64_t smask,
@@ -700,36 +701,37 @@ __device__ __forceinline__ void conv_rows_t(unsigned char* stg, const ConvWord& 
                                             const float (&cb)[2]) {
     float h3[2] = {bf16_lo(v3), bf16_hi(v3)}, h2[2] = {bf16_lo(v2), bf16_hi(v2)},
           h1[2] = {bf16_lo(v1), bf16_hi(v1)};
+    auto row = [&](int r, uint32_t cur) __attribute__((always_inline)) {
+        if (DOCS && ((smask >> r) & 1)) {
+            h3[0] = h3[1] = h2[0] = h2[1] = h1[0] = h1[1] = 0.0f;
+        }
+        const float c[2] = {bf16_lo(cur), bf16_hi(cur)};
+        float o[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float v = cb[e];
+            v = fmaf(w[e][0], h3[e], v);
+            v = fmaf(w[e][1], h2[e], v);
+            v = fmaf(w[e][2], h1[e], v);
+            v = fmaf(w[e][3], c[e], v);
+            o[e] = SILU ? silu_f(v) : v;
+            h3[e] = h2[e];
+            h2[e] = h1[e];
+            h1[e] = c[e];
+        }
+        *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r)) = pack_bf16x2(o[0], o[1]);
+    };
+    int r = r0;
 #pragma unroll 1
-    for (int r = r0; r < r1; r += 4) {
+    for (; r + 4 <= r1; r += 4) {
         uint32_t cur[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            cur[u] = r + u < r1 ? *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r + u)) : 0u;
+        for (int u = 0; u < 4; ++u) cur[u] = *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r + u));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (r + u < r1) {
-                if (DOCS && ((smask >> (r + u)) & 1)) {
-                    h3[0] = h3[1] = h2[0] = h2[1] = h1[0] = h1[1] = 0.0f;
-                }
-                const float c[2] = {bf16_lo(cur[u]), bf16_hi(cur[u])};
-                float o[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    float v = cb[e];
-                    v = fmaf(w[e][0], h3[e], v);
-                    v = fmaf(w[e][1], h2[e], v);
-                    v = fmaf(w[e][2], h1[e], v);
-                    v = fmaf(w[e][3], c[e], v);
-                    o[e] = SILU ? silu_f(v) : v;
-                    h3[e] = h2[e];
-                    h2[e] = h1[e];
-                    h1[e] = c[e];
-                }
-                *reinterpret_cast<uint32_t*>(stg + conv_off<RBU>(cw, r + u)) = pack_bf16x2(o[0], o[1]);
-            }
-        }
+        for (int u = 0; u < 4; ++u) row(r + u, cur[u]);
     }
+#pragma unroll 1
+    for (; r < r1; ++r) row(r, *reinterpret_cast<const uint32_t*>(stg + conv_off<RBU>(cw, r)));
 }
 // The row loop specialised on the (wave-uniform) document starts among its
 // rows and the activation, so neither costs a select per row.
@@ -974,6 +976,14 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         }
     };
 
+    // the first chunks' copies go out before the state loads, so their latencies overlap
+    const int nchunks = (tend - tbeg + Q - 1) / Q;
+    if (!ZR && lead && nchunks > 0) issue_scalars(tbeg, 0);
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+        if (j < nchunks) issue_chunk(tbeg + j * Q, j);
+    if (!ZR && nchunks > 0) issue_z(tbeg, 0);
+
     // ---- initial state: the given one, then the superchunks before k folded in
     f32x4 Hs[NT];
     const size_t st_off = (((size_t)b * H + h) * 64 + p0 + j16) * N + 4 * q4;
@@ -1114,12 +1124,6 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_bf16_kernel(ScanArgs a) {
         asm volatile("" : "+v"(hw3), "+v"(hw2), "+v"(hw1));
     }
 
-    const int nchunks = (tend - tbeg + Q - 1) / Q;
-    if (!ZR && lead && nchunks > 0) issue_scalars(tbeg, 0);
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-        if (j < nchunks) issue_chunk(tbeg + j * Q, j);
-    if (!ZR && nchunks > 0) issue_z(tbeg, 0);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = tbeg + c * Q;
