@@ -335,6 +335,7 @@ size_t ssd_mixer_workspace_size(int B, int L, int H, int P, int N, int G, int dt
  * length is not a multiple of 64 passes its last L mod 64 tokens through
  * this call.  No document ids: appended tokens continue the working chunk's
  * document.  All buffers 16-byte aligned (chunk_dt, dt_raw: 4-byte).
+ * conv_dim at most 4194304 (the working chunk's row width).
  */
 int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos, int n,
                    const void *xbc_raw, const void *dt_raw, const void *z,

@@ -458,6 +458,8 @@ int ssd_resume_fwd(int B, int H, int P, int N, int G, int K, int dtype, int pos,
     const bool work = B > 0;
     const int64_t C = (int64_t)H * P + 2LL * G * N;
     const int es = esize(dtype);
+    if (C > (1 << 22))   // the working chunk's rows are C elements apart
+        return fail(SSD_ERR_BAD_SHAPE, "%s: conv_dim=%lld above 4194304 is not supported", fn, (long long)C);
     TRY(check_ptr(fn, "xbc_raw", xbc_raw, work, true));
     TRY(check_ptr(fn, "dt_raw", dt_raw, work, false));
     TRY(check_ptr(fn, "z", z, false, true));

@@ -80,6 +80,18 @@ __device__ __forceinline__ void mtile(int k, int& si, int& ti) {
 }
 __device__ __forceinline__ int mtile_index(int si, int ti) { return ti * (ti + 1) / 2 + si; }
 
+// Byte offset of a lane's row inside a chunk: row < 64 and a row stride of at
+// most 2^22 elements (the entry points refuse longer rows) keep both factors
+// below 2^24 and the product below 2^32, so the full-rate 24-bit multiplier
+// gives it exactly (a 32-bit multiply issues at a quarter of the rate).
+// (The empty asm keeps the compiler from folding the scale into the multiply's
+// operands, which turns it back into a 32-bit multiply.)
+__device__ __forceinline__ uint32_t row_bytes(int row, int stride, int col, int esize) {
+    uint32_t m = __umul24((uint32_t)row, (uint32_t)stride);
+    asm("" : "+v"(m));
+    return (m + (uint32_t)col) * (uint32_t)esize;
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that a
 // contiguous range of (b, h) -- heads of the same group, which share B and C
 // -- runs on one XCD and shares its L2.
@@ -225,10 +237,10 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
             for (int kk = 0; kk < 2; ++kk) {
                 int row = 2 * rp + kk;
                 if (clamp) row = min(row, lim);
-                const uint32_t ob = (uint32_t)(row * (int)a.B_stride + col) * 4;
+                const uint32_t ob = row_bytes(row, (int)a.B_stride, col, 4);
                 r.b[it][kk] = *reinterpret_cast<const uint4*>(Bb + ob);
                 if (FULL) {
-                    const uint32_t oc = (uint32_t)(row * (int)a.C_stride + col) * 4;
+                    const uint32_t oc = row_bytes(row, (int)a.C_stride, col, 4);
                     r.c[it][kk] = *reinterpret_cast<const uint4*>(Cb + oc);
                 }
             }
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
         int row = lane;
         if (clamp) row = min(row, lim);
         const char* db = reinterpret_cast<const char*>(dtbase + (size_t)t0 * a.dt_stride + h);
-        r.dt = *reinterpret_cast<const float*>(db + (uint32_t)(row * (int)a.dt_stride) * 4);
+        r.dt = *reinterpret_cast<const float*>(db + row_bytes(row, (int)a.dt_stride, 0, 4));
         r.d0 = docsrc[t0 + row];
         r.d1 = docsrc[max(t0 + row - 1, 0)];
     };
@@ -250,8 +262,8 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
         for (int ti = 0; ti < 4; ++ti) {
             int row = 16 * ti + j16;
             if (clamp) row = min(row, lim);
-            r.x[ti] = *reinterpret_cast<const float4*>(xb + (uint32_t)(row * (int)a.x_stride) * 4);
-            if (FULL) r.z[ti] = *reinterpret_cast<const float4*>(zb + (uint32_t)(row * (int)zs) * 4);
+            r.x[ti] = *reinterpret_cast<const float4*>(xb + row_bytes(row, (int)a.x_stride, 0, 4));
+            if (FULL) r.z[ti] = *reinterpret_cast<const float4*>(zb + row_bytes(row, (int)zs, 0, 4));
         }
     };
 
@@ -468,7 +480,8 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
                     for (int r = 0; r < 4; ++r) o[r] *= silu_f((&zv[ti].x)[r]);
                 }
                 if (!tail || t0 + t < tend)
-                    *reinterpret_cast<float4*>(yg + (size_t)(t0 + t) * a.y_stride) = make_float4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<float4*>(reinterpret_cast<char*>(yg + (size_t)t0 * a.y_stride) +
+                                               row_bytes(t, (int)a.y_stride, 0, 4)) = make_float4(o[0], o[1], o[2], o[3]);
             }
             // ---- w o X over this wave's own X columns (only this wave reads them,
             // and its LDS operations are performed in order)

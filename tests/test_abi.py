@@ -192,6 +192,30 @@ def test_step_refusals(lib, over, status, needle):
     assert needle in lib.ssd_last_error().decode()
 
 
+def call_resume(lib, **over):
+    a = dict(B=4, H=64, P=64, N=128, G=1, K=4, dtype=0, pos=0, n=1, raw=FAKE, dtr=FAKE, z=None, w=FAKE, b=None,
+             dtb=None, A=FAKE, D=None, act=0, cst=FAKE, cx=FAKE, cdt=FAKE, cz=None, cs=FAKE, cy=FAKE, y=FAKE,
+             stream=None)
+    a.update(over)
+    return lib.ssd_resume_fwd(a["B"], a["H"], a["P"], a["N"], a["G"], a["K"], a["dtype"], a["pos"], a["n"],
+                              a["raw"], a["dtr"], a["z"], a["w"], a["b"], a["dtb"], a["A"], a["D"], a["act"],
+                              a["cst"], a["cx"], a["cdt"], a["cz"], a["cs"], a["cy"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(pos=64), 2, "pos=64"),
+    (dict(pos=60, n=5), 2, "pos + n = 65"),
+    (dict(act=2), 3, "act=2"),
+    (dict(z=FAKE), 1, "z and chunk_z"),
+    (dict(cs=None), 1, "chunk_state is NULL"),
+    (dict(H=65536, G=1), 2, "conv_dim=4194560"),
+])
+def test_resume_refusals(lib, over, status, needle):
+    st = call_resume(lib, **over)
+    assert st == status, (st, lib.ssd_last_error())
+    assert needle in lib.ssd_last_error().decode()
+
+
 def test_static_scan_refuses_workspace_beyond_static_scratch(lib):
     """ssd_chunk_scan_fwd_static: sizes whose split workspace exceeds SSD_STATIC_SCRATCH_BYTES are refused on
     the host, before any HIP call (the pointers here are never dereferenced)."""
