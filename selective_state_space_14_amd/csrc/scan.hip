@@ -589,8 +589,11 @@ __global__ __launch_bounds__(256 * HPW) void ssd_scan_kernel(ScanArgs a) {
 // before any LDS read it cannot prove disjoint.  M0 (the LDS destination) is
 // saved and restored inside the statement; one wait state separates its write
 // from the copy.
+// The LDS address of a generic pointer into LDS is its low 32 bits (the LDS
+// aperture is 4 GiB aligned); an address-space cast would add null checks of
+// both pointer forms to every copy.
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const SSD_LDS unsigned char*)p);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -1509,6 +1512,7 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
     int s_row[LD::NI_W];
     uint32_t s_col[LD::NI_W];
     bool s_on[LD::NI_W];
+    uint32_t s_off[LD::NI_W];   // the lane's offset when no row clamps
 #pragma unroll
     for (int j = 0; j < LD::NI_W; ++j) {
         const int i = wave + NW * j;
@@ -1530,18 +1534,21 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
             s_row[j] = r;
             s_col[j] = (uint32_t)(((lane % (XB / 16)) ^ SX::f(r)) * 16);
         }
+        s_off[j] = (uint32_t)(s_row[j] * s_stride[j]) + s_col[j];
     }
     const int n_tiles = (LD::NI - wave + NW - 1) / NW;
     const int n_scal = lead ? (docs ? 3 : 1) : 0;
     // (slots j0 .. j1-1 of them)
     auto issue_tiles = [&](int t0, int st, int j0, int j1) {
         const int lim = tl - t0;
+        const bool whole = lim >= Q - 1;   // uniform: every row inside the unit
         unsigned char* base = smem + st * LD::STAGE;
 #pragma unroll
         for (int j = 0; j < LD::NI_W; ++j) {
             if (j >= j0 && j < j1 && s_on[j]) {
                 const char* src = s_base[j] + (size_t)t0 * s_stride[j];
-                dma16(src, (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j], base + s_lds[j]);
+                dma16(src, whole ? s_off[j] : (uint32_t)(min(s_row[j], lim) * s_stride[j]) + s_col[j],
+                      base + s_lds[j]);
             }
         }
     };
