@@ -36,6 +36,9 @@ constexpr int kConvThreads = 128;   // two waves: 2 KiB of each bf16 row per blo
 constexpr int kTile = 64;     // tokens per block (a multiple of 64)
 constexpr int kStartWords = kTile / 64;
 constexpr int kBatch = 16;    // rows loaded before use
+// the ring below refills slot u with the row kBatch further on: whole tiles
+// must be a whole number of rings, or the last refills run past the tile
+static_assert(kTile % kBatch == 0 && kTile >= kBatch, "a tile is a whole number of load rings");
 constexpr int kDtBatch = 8;   // dt elements loaded per lane before use
 
 template <typename T> struct CV;
