@@ -35,6 +35,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int esize(int dtype) { return dtype == SSD_F32 ? 4 : 2; }
 
+constexpr int kMaxL = 1 << 30;   // tokens per batch row
+
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Shared size checks; returns SSD_OK or a failure with the message set.
@@ -44,6 +46,8 @@ int check_dims(const char* fn, int B, int L, int H, int P, int N, int G, int K, 
                     "fp16, fp64 and other types are refused, not converted)", fn, dtype);
     if (B < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: B=%d must be >= 0", fn, B);
     if (L < 0) return fail(SSD_ERR_BAD_SHAPE, "%s: L=%d must be >= 0", fn, L);
+    // the scans address a row's document ids with 32-bit byte offsets
+    if (L > kMaxL) return fail(SSD_ERR_BAD_SHAPE, "%s: L=%d is above the %d tokens a row may hold", fn, L, kMaxL);
     if (H <= 0) return fail(SSD_ERR_BAD_SHAPE, "%s: H=%d must be > 0", fn, H);
     if (G <= 0) return fail(SSD_ERR_BAD_SHAPE, "%s: G=%d must be > 0", fn, G);
     if (H % G != 0) return fail(SSD_ERR_BAD_SHAPE, "%s: H=%d is not divisible by G=%d", fn, H, G);

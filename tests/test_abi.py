@@ -76,6 +76,7 @@ def call_scan(lib, a):
     (dict(dtype=2), 3, "dtype=2"),
     (dict(B=-1), 2, "B=-1"),
     (dict(L=-5), 2, "L=-5"),
+    (dict(L=(1 << 30) + 1), 2, "L=1073741825 is above"),
     (dict(x=None), 1, "x is NULL"),
     (dict(dt=None), 1, "dt is NULL"),
     (dict(A=None), 1, "A is NULL"),
@@ -104,6 +105,7 @@ def call_conv(lib, **over):
 
 @pytest.mark.parametrize("over,status,needle", [
     (dict(K=3), 3, "K=3"),
+    (dict(L=(1 << 30) + 1), 2, "L=1073741825 is above"),
     (dict(act=7), 3, "act=7"),
     (dict(dtype=5), 3, "dtype=5"),
     (dict(w=None), 1, "conv_w is NULL"),
