@@ -1801,6 +1801,43 @@ __global__ __launch_bounds__(64 * (4 / PB) * HPW) void ssd_scan_state_kernel(Sca
 // for resident workgroups.  z goes in the ring and M^T is split into halves
 // where the layout fits a CU; otherwise z is single-buffered, then M^T is
 // one bf16 rounding.  ok: some layout fits.
+// One-time preparation of a kernel on the current device, before its first
+// launch there: refuse a build whose kernel uses scratch (no_scratch: the
+// kernel's explicit vector-memory waits count only its own copies, stores and
+// loads, so register spills would add uncounted operations), and raise its
+// dynamic-LDS cap to `lds`.  Thread-safe; each (kernel, device) pair is
+// prepared once per process.
+hipError_t prepare_kernel(const void* fn, size_t lds, bool no_scratch) {
+    constexpr int kMaxDevices = 64;
+    constexpr int kMaxKernels = 256;
+    static std::mutex mu;
+    static const void* fns[kMaxKernels] = {};
+    static uint64_t ready[kMaxKernels] = {};   // bit d: prepared on device d
+    static int nfns = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    int i = 0;
+    while (i < nfns && fns[i] != fn) ++i;
+    if (i < nfns && (ready[i] >> dev & 1)) return hipSuccess;
+    if (no_scratch) {
+        hipFuncAttributes fa;
+        e = hipFuncGetAttributes(&fa, fn);
+        if (e != hipSuccess) return e;
+        if (fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
+    }
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if (i == nfns) {
+        if (nfns == kMaxKernels) return hipSuccess;   // not remembered: prepared again next time
+        fns[nfns++] = fn;
+    }
+    ready[i] |= uint64_t(1) << dev;
+    return hipSuccess;
+}
+
 template <int N, int HPW>
 struct BfPlan {
     static constexpr int NS = 2;
@@ -1814,18 +1851,7 @@ hipError_t launch_scan_bf16_k(const ScanArgs& a, int units, hipStream_t stream) 
     using PL = BfPlan<N, HPW>;
     const void* fn = reinterpret_cast<const void*>(&ssd_scan_bf16_kernel<N, SP, HPW, CV, PL::NS, PL::ZR, PL::MS>);
     const size_t lds = PL::LD::bytes;
-    static bool checked = false;
-    if (!checked) {
-        // The kernel's explicit vector-memory waits count only its own copies,
-        // stores and loads: register spills would add uncounted operations.
-        hipFuncAttributes fa;
-        hipError_t e = hipFuncGetAttributes(&fa, fn);
-        if (e != hipSuccess) return e;
-        if (fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        checked = true;
-    }
+    if (hipError_t e = prepare_kernel(fn, lds, true); e != hipSuccess) return e;
     hipLaunchKernelGGL((ssd_scan_bf16_kernel<N, SP, HPW, CV, PL::NS, PL::ZR, PL::MS>), dim3(units), dim3(256 * HPW),
                        lds, stream, a);
     return hipGetLastError();
@@ -1846,16 +1872,7 @@ hipError_t launch_scan_state_k(const ScanArgs& a, hipStream_t stream) {
     constexpr int PB = CV ? 1 : kPrePB;
     using LD = LdsPre<N, PRE_HPW, PB, kPreStages>;
     const void* fn = reinterpret_cast<const void*>(&ssd_scan_state_kernel<N, SP, PRE_HPW, PB, kPreStages, CV>);
-    static bool checked = false;
-    if (!checked) {
-        hipFuncAttributes fa;                   // see launch_scan_bf16_k: no scratch allowed
-        hipError_t e = hipFuncGetAttributes(&fa, fn);
-        if (e != hipSuccess) return e;
-        if (fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LD::bytes);
-        if (e != hipSuccess) return e;
-        checked = true;
-    }
+    if (hipError_t e = prepare_kernel(fn, LD::bytes, true); e != hipSuccess) return e;
     const int units = a.B * (a.H / PRE_HPW) * (a.K - 1);
     hipLaunchKernelGGL((ssd_scan_state_kernel<N, SP, PRE_HPW, PB, kPreStages, CV>), dim3(units), dim3(64 * LD::NW),
                        LD::bytes, stream, a);
@@ -1881,13 +1898,9 @@ hipError_t launch_scan_bf16(const ScanArgs& a, int pre_hpw, hipStream_t stream) 
 template <typename T, int N, int MODE, int HPW>
 hipError_t launch_scan_mode(const ScanArgs& a, hipStream_t stream) {
     const size_t lds = Lds<N, MODE, HPW>::bytes;
-    static bool attr_set = false;   // raise the dynamic-LDS cap once per process
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_scan_kernel<T, N, MODE, HPW>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    if (hipError_t e = prepare_kernel(reinterpret_cast<const void*>(&ssd_scan_kernel<T, N, MODE, HPW>), lds, false);
+        e != hipSuccess)
+        return e;
     const int units = a.B * (a.H / HPW) * (MODE == kFull ? a.K : a.K - 1);
     hipLaunchKernelGGL((ssd_scan_kernel<T, N, MODE, HPW>), dim3(units), dim3(256 * HPW), lds, stream, a);
     return hipGetLastError();
