@@ -64,7 +64,9 @@
  * - Supported sizes: P = 64, N in {16, 32, 64, 128}, K = 4, chunk = 64,
  *   G divides H, B >= 1, 0 <= L <= 2^30 = 1073741824 tokens per row (L = 0
  *   is a no-op apart from copying the states through; a partial last chunk
- *   is handled; a larger L is refused with SSD_ERR_BAD_SHAPE).
+ *   is handled; a larger L is refused with SSD_ERR_BAD_SHAPE), and one batch
+ *   row of the widest activation -- L * max(conv_dim * sizeof(T),
+ *   H * P * 4) bytes -- below 2^31 bytes (refused with SSD_ERR_BAD_SHAPE).
  * - Alignment: every tensor base must be 16-byte aligned, and row strides
  *   of T tensors must be multiples of 16 bytes (8 bf16 or 4 fp32 elements).
  * - Errors: arguments are validated on the host before anything is

@@ -2,6 +2,7 @@
 // validation with messages that name the offending argument and its values,
 // then one launch on the caller's stream.  Nothing here touches device
 // memory or calls HIP before validation has passed.
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -58,6 +59,12 @@ int check_dims(const char* fn, int B, int L, int H, int P, int N, int G, int K, 
     const long long total_heads = (long long)B * H;
     if (total_heads > 0x7fffffffLL)
         return fail(SSD_ERR_BAD_SHAPE, "%s: B*H=%lld is too large", fn, total_heads);
+    // one batch row of the widest activation (the [x | B | C] columns in T, or y in fp32) must stay below
+    // 2^31 bytes: longer rows are not validated (a scan over 4.4 GB rows gave wrong outputs past 2^31 bytes)
+    const long long row_bytes = std::max((long long)(H * P + 2 * G * N) * esize(dtype), (long long)H * P * 4);
+    if ((long long)L * row_bytes >= (1LL << 31))
+        return fail(SSD_ERR_BAD_SHAPE, "%s: L=%d rows of %lld bytes reach 2^31 bytes per batch row (not supported)",
+                    fn, L, row_bytes);
     return SSD_OK;
 }
 

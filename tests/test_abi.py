@@ -77,6 +77,7 @@ def call_scan(lib, a):
     (dict(B=-1), 2, "B=-1"),
     (dict(L=-5), 2, "L=-5"),
     (dict(L=(1 << 30) + 1), 2, "L=1073741825 is above"),
+    (dict(L=266240, H=128, G=8), 2, "reach 2^31 bytes per batch row"),
     (dict(x=None), 1, "x is NULL"),
     (dict(dt=None), 1, "dt is NULL"),
     (dict(A=None), 1, "A is NULL"),
